@@ -1,0 +1,199 @@
+"""ctypes wrapper of the FP64 CPU oracle (vqmlp_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the benchmark's CPU-baseline
+leg, never by the HIP library or its binding.  Arguments are the unpacked arrays drawn by
+``bit_vector_lut_amd.synth`` (plain numpy), so nothing here depends on the GPU path.
+
+The arithmetic lives in vqmlp_oracle.c, whose header gives the definitions and the passages of
+the pages they follow.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "vqmlp_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP over output rows)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+               "-o", tmp, SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = C.CDLL(LIB)
+        P, I, D = C.c_void_p, C.c_int, C.c_double
+        L.orc_f16_to_f64.restype = D
+        L.orc_f16_to_f64.argtypes = [C.c_uint16]
+        L.orc_f16_array.argtypes = [C.c_size_t, P, P]
+        L.orc_hadamard_entry.argtypes = [I, I]
+        L.orc_hadamard.argtypes = [I, P]
+        L.orc_rotate.argtypes = [I, I, I, P, P, P]
+        L.orc_silu_1.restype = D
+        L.orc_silu_1.argtypes = [D]
+        L.orc_silu.argtypes = [C.c_size_t, P, P]
+        L.orc_vq3_weight.argtypes = [I, I, P, P, P, P]
+        L.orc_vq3_matmul.argtypes = [I, I, I, P, P, P, P, P]
+        L.orc_mlp_forward.argtypes = [I] * 5 + [P] * 4 + [P] * 9 + [P] * 6
+        L.orc_lut_weight.argtypes = [I, I, I, P, P, P, P]
+        L.orc_lut_forward.argtypes = [I] * 6 + [P] * 3 + [P] * 5 + [P, P]
+        L.orc_num_threads.restype = I
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+def _u16(a):
+    """float16 (or its raw bits) as contiguous uint16."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.float16:
+        return a.view(np.uint16)
+    if a.dtype != np.uint16:
+        raise TypeError("expected float16 or uint16, got %s" % a.dtype)
+    return a
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc, what):
+    if rc:
+        raise OracleError("%s: invalid arguments" % what)
+
+
+def f16_to_f64(h) -> np.ndarray:
+    h = _u16(np.asarray(h))
+    out = np.empty(h.shape, np.float64)
+    lib().orc_f16_array(h.size, _p(h), _p(out))
+    return out
+
+
+def hadamard(b: int) -> np.ndarray:
+    out = np.empty((b, b), np.int8)
+    lib().orc_hadamard(b, _p(out))
+    return out
+
+
+def rotate(u, b: int, sign=None) -> np.ndarray:
+    """Block Hadamard rotation of the rows of u (float64 [T, n]); sign (+-1 [n]) applied first."""
+    u = np.ascontiguousarray(np.atleast_2d(u), np.float64)
+    out = np.empty_like(u)
+    _check(lib().orc_rotate(u.shape[0], u.shape[1], b, _p(u), _p(_c(sign, np.int8)), _p(out)),
+           "rotate")
+    return out
+
+
+def silu(g) -> np.ndarray:
+    g = np.ascontiguousarray(g, np.float64)
+    out = np.empty_like(g)
+    lib().orc_silu(g.size, _p(g), _p(out))
+    return out
+
+
+def vq3_weight(codes, cb, sc) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    cb, sc = _u16(cb), _u16(sc)
+    N, K = sc.shape[0], codes.shape[1]
+    W = np.empty((N, K), np.float64)
+    _check(lib().orc_vq3_weight(N, K, _p(codes), _p(cb), _p(sc), _p(W)), "vq3_weight")
+    return W
+
+
+def vq3_matmul(codes, cb, sc, xin) -> np.ndarray:
+    """out[t][r] = sum_j W[r][j] xin[t][j] with W decoded on the fly."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    cb, sc = _u16(cb), _u16(sc)
+    xin = np.ascontiguousarray(np.atleast_2d(xin), np.float64)
+    N, K = sc.shape[0], codes.shape[1]
+    out = np.empty((xin.shape[0], N), np.float64)
+    _check(lib().orc_vq3_matmul(xin.shape[0], N, K, _p(codes), _p(cb), _p(sc), _p(xin), _p(out)),
+           "vq3_matmul")
+    return out
+
+
+def mlp_forward(layer, tokens=None, intermediates: bool = False):
+    """FP64 forward of a ``synth.MLPLayer``; ``tokens`` selects rows of x (each token is
+    independent).  Returns y [T', H] or, with intermediates, a dict with xt, g, v, a, at, y."""
+    x = layer.x if tokens is None else layer.x[np.asarray(tokens)]
+    x = _u16(x)
+    T, H, I = x.shape[0], layer.H, layer.I
+    y = np.empty((T, H), np.float64)
+    inter = {}
+    if intermediates:
+        inter = {"xt": np.empty((T, H)), "g": np.empty((T, I)), "v": np.empty((T, I)),
+                 "a": np.empty((T, I)), "at": np.empty((T, I))}
+    mats = []
+    for m in (layer.gate, layer.up, layer.down):
+        mats += [np.ascontiguousarray(m.codes, np.uint8), _u16(m.cb), _u16(m.sc)]
+    rc = lib().orc_mlp_forward(
+        T, H, I, layer.had_block_h, layer.had_block_i, _p(x), _p(_u16(layer.s)),
+        _p(_c(layer.sign_h, np.int8)), _p(_c(layer.sign_i, np.int8)),
+        *[_p(a) for a in mats], _p(y),
+        *[_p(inter.get(k)) for k in ("xt", "g", "v", "a", "at")])
+    _check(rc, "mlp_forward")
+    if intermediates:
+        inter["y"] = y
+        return inter
+    return y
+
+
+def lut_weight(bits, codes, lut, sc) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    lut, sc = _u16(lut), _u16(sc)
+    N, K = codes.shape
+    W = np.empty((N, K), np.float64)
+    _check(lib().orc_lut_weight(bits, N, K, _p(codes), _p(lut), _p(sc), _p(W)), "lut_weight")
+    return W
+
+
+def lut_forward(proj, x, tokens=None, with_xt: bool = False):
+    """FP64 forward of a ``synth.LUTProjection`` on x (float16 [T, K])."""
+    x = x if tokens is None else x[np.asarray(tokens)]
+    x = _u16(x)
+    T, K = x.shape
+    N = proj.N
+    y = np.empty((T, N), np.float64)
+    xt = np.empty((T, K), np.float64) if with_xt else None
+    rank = proj.rank
+    rc = lib().orc_lut_forward(
+        proj.bits, N, K, T, proj.had_block, rank, _p(x), _p(_u16(proj.s)),
+        _p(_c(proj.sign, np.int8)), _p(np.ascontiguousarray(proj.codes, np.uint8)),
+        _p(_u16(proj.lut)), _p(_u16(proj.sc)), _p(_u16(proj.U)), _p(_u16(proj.V)), _p(y), _p(xt))
+    _check(rc, "lut_forward")
+    return (y, xt) if with_xt else y
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
+
+
+if __name__ == "__main__":
+    print(build(force="--force" in sys.argv))
