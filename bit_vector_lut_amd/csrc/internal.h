@@ -1,0 +1,75 @@
+// internal.h -- declarations shared by the host half (vqmlp_host.cpp) and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vqmlp {
+
+// ---- packed VQ3 layout (version 1); see include/vqmlp.h for the byte-level description
+constexpr uint32_t kMagic = 0x50335156u;  // "VQ3P" little-endian
+constexpr int kHeaderBytes = 256;
+constexpr int kTilePairs = 16;            // row pairs per tile (one matrix-core operand height)
+constexpr int kTileRows = 2 * kTilePairs; // 32 output rows
+constexpr int kTileCols = 64;             // input columns per tile (4 steps of 16)
+constexpr int kTileBytes = 768;           // 64 lanes x 12 bytes (16 six-bit codes)
+constexpr int kGroupRows = 8;             // rows sharing one codebook
+constexpr int kCodebook = 64;             // entries per codebook (2 x binary16 each)
+
+struct PackedHeader {
+    uint32_t magic, version, N, K, group_rows, entries, kind, reserved;
+    uint64_t codes_off, codes_bytes, cb_off, cb_bytes, sc_off, sc_bytes, total;
+};
+static_assert(sizeof(PackedHeader) <= kHeaderBytes, "header");
+
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct VQ3View {          // device pointers into one packed buffer
+    const uint8_t* codes;     // tiles
+    const uint32_t* cb;       // [N/8][64] dwords: (binary16 even row) | (binary16 odd row) << 16
+    const uint16_t* sc;       // [N]
+    int N, K;
+};
+
+// ---- skinny path (T <= 8)
+constexpr int kSkinnyT = 8;            // rows of the matrix-core operand (8 tokens x 2 components)
+constexpr int kSkinnyWaves = 8;        // waves per workgroup, each owning a K range
+constexpr int kSkinnyMaxTPW = 10;      // 64-column tiles per wave held in registers
+
+// ---- launchers (kernels.hip).  All return hipError_t of the launch.
+hipError_t launch_dequant(const VQ3View& m, float* w, hipStream_t s);
+
+// out[t][.] = R(x . s) for a binary16 or float input.  mode: 0 = FP32 row-major [T][n],
+// 1 = binary16 row-major [T][n], 2 = skinny operand layout (T <= 8, expanded binary16 pairs).
+hipError_t launch_rotate(int T, int n, int b, const void* x, int x_is_f32, const uint16_t* s,
+                         const int8_t* sign, void* out, int mode, hipStream_t st);
+
+struct SkinnyArgs {
+    VQ3View mat[2];
+    int nmat;              // 2 = gate+up (shared operand), 1 = down
+    int T;
+    int slices;            // K split into this many slices of 8*tpw tiles
+    int tpw;               // tiles per wave
+    const uint32_t* bexp;  // expanded operand [K/16][64][4] dwords
+    // epilogues
+    const int8_t* sign_i;  // gate+up: sign of the intermediate rotation (NULL = +1)
+    float* a_out;          // gate+up: a [8][I] fp32
+    float* part;           // down, slices > 1: [slices][8][N] fp32
+    uint16_t* y;           // down, slices == 1: y [T][N] binary16
+};
+hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st);
+hipError_t launch_reduce_down(int T, int N, int slices, const float* part, const uint16_t* sc,
+                              uint16_t* y, hipStream_t st);
+
+struct TiledArgs {
+    VQ3View mat[2];
+    int nmat;
+    int T;
+    const uint16_t* xt;    // [T][K] binary16 operand
+    const int8_t* sign_i;
+    float* a_out;          // gate+up: [T][I] fp32
+    uint16_t* y;           // down: [T][N] binary16
+};
+hipError_t launch_tiled(const TiledArgs& a, hipStream_t st);
+
+}  // namespace vqmlp

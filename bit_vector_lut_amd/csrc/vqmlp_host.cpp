@@ -1,0 +1,669 @@
+// vqmlp_host.cpp -- host half of the VQ3 MLP library: argument checking, packing, plans,
+// workspace carving and kernel dispatch.  Every public entry point is extern "C" and returns a
+// vqmlp_status; failures set a per-thread message and launch nothing.
+#include "internal.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "vqmlp.h"
+
+using namespace vqmlp;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+vqmlp_status fail(vqmlp_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+vqmlp_status ok() {
+    g_last_error.clear();
+    return VQMLP_OK;
+}
+
+vqmlp_status hip_fail(hipError_t e, const char* what) {
+    return fail(VQMLP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int default_block(int n) {
+    int b = 1;
+    while (b * 2 <= 128 && n % (b * 2) == 0) b *= 2;
+    return b;
+}
+
+// ---------------------------------------------------------------- VQ3 packed layout
+
+struct Layout {
+    size_t codes_off, codes_bytes, cb_off, cb_bytes, sc_off, sc_bytes, total;
+};
+
+vqmlp_status check_shape(int N, int K) {
+    if (N <= 0 || K <= 0 || N > (1 << 20) || K > (1 << 20))
+        return fail(VQMLP_ERR_INVALID_ARG, "matrix shape %dx%d out of range", N, K);
+    if (N % kTileRows)
+        return fail(VQMLP_ERR_INVALID_ARG, "N=%d must be a multiple of %d", N, kTileRows);
+    if (K % kTileCols)
+        return fail(VQMLP_ERR_INVALID_ARG, "K=%d must be a multiple of %d", K, kTileCols);
+    return VQMLP_OK;
+}
+
+Layout layout_of(int N, int K) {
+    Layout L;
+    L.codes_off = kHeaderBytes;
+    L.codes_bytes = size_t(N / kTileRows) * (K / kTileCols) * kTileBytes;
+    L.cb_off = align256(L.codes_off + L.codes_bytes);
+    L.cb_bytes = size_t(N / kGroupRows) * kCodebook * 4;
+    L.sc_off = align256(L.cb_off + L.cb_bytes);
+    L.sc_bytes = size_t(N) * 2;
+    L.total = align256(L.sc_off + L.sc_bytes);
+    return L;
+}
+
+PackedHeader header_of(int N, int K, uint32_t kind, uint32_t entries, const Layout& L) {
+    PackedHeader h;
+    memset(&h, 0, sizeof h);
+    h.magic = kMagic;
+    h.version = VQMLP_LAYOUT_VERSION;
+    h.N = uint32_t(N);
+    h.K = uint32_t(K);
+    h.group_rows = kGroupRows;
+    h.entries = entries;
+    h.kind = kind;
+    h.codes_off = L.codes_off;
+    h.codes_bytes = L.codes_bytes;
+    h.cb_off = L.cb_off;
+    h.cb_bytes = L.cb_bytes;
+    h.sc_off = L.sc_off;
+    h.sc_bytes = L.sc_bytes;
+    h.total = L.total;
+    return h;
+}
+
+vqmlp_status check_header(const PackedHeader& h, int N, int K, uint32_t kind, uint32_t entries,
+                          const Layout& L, const char* name) {
+    if (h.magic != kMagic)
+        return fail(VQMLP_ERR_INVALID_ARG, "%s: bad magic 0x%08x (not a packed buffer)", name,
+                    h.magic);
+    if (h.version != VQMLP_LAYOUT_VERSION)
+        return fail(VQMLP_ERR_INVALID_ARG, "%s: layout version %u, library expects %d", name,
+                    h.version, VQMLP_LAYOUT_VERSION);
+    if (int(h.N) != N || int(h.K) != K)
+        return fail(VQMLP_ERR_INVALID_ARG, "%s: packed shape %ux%u, expected %dx%d", name, h.N,
+                    h.K, N, K);
+    if (h.kind != kind || h.entries != entries || h.group_rows != uint32_t(kGroupRows))
+        return fail(VQMLP_ERR_INVALID_ARG, "%s: packed kind %u/%u entries, expected %u/%u", name,
+                    h.kind, h.entries, kind, entries);
+    if (h.codes_off != L.codes_off || h.cb_off != L.cb_off || h.sc_off != L.sc_off ||
+        h.total != L.total)
+        return fail(VQMLP_ERR_INVALID_ARG, "%s: section offsets do not match the layout", name);
+    return VQMLP_OK;
+}
+
+// code q of tile lane l: pair 16m + l%16, column 64k + 16*(q/4) + 4*(l/16) + q%4
+inline void put6(uint8_t* lane12, int q, unsigned code) {
+    // 96-bit little-endian word; code q occupies bits 6q .. 6q+5
+    const int bit = 6 * q;
+    uint32_t w[3];
+    memcpy(w, lane12, 12);
+    uint64_t lo = (uint64_t(w[1]) << 32) | w[0];
+    uint64_t hi = w[2];
+    if (bit + 6 <= 64) {
+        lo |= uint64_t(code) << bit;
+    } else if (bit >= 64) {
+        hi |= uint64_t(code) << (bit - 64);
+    } else {
+        lo |= uint64_t(code) << bit;
+        hi |= uint64_t(code) >> (64 - bit);
+    }
+    w[0] = uint32_t(lo);
+    w[1] = uint32_t(lo >> 32);
+    w[2] = uint32_t(hi);
+    memcpy(lane12, w, 12);
+}
+
+inline unsigned get6(const uint8_t* lane12, int q) {
+    const int bit = 6 * q;
+    uint32_t w[3];
+    memcpy(w, lane12, 12);
+    const uint64_t lo = (uint64_t(w[1]) << 32) | w[0];
+    const uint64_t hi = w[2];
+    uint64_t v;
+    if (bit + 6 <= 64)
+        v = lo >> bit;
+    else if (bit >= 64)
+        v = hi >> (bit - 64);
+    else
+        v = (lo >> bit) | (hi << (64 - bit));
+    return unsigned(v & 63);
+}
+
+VQ3View view_of(const void* packed, int N, int K) {
+    const Layout L = layout_of(N, K);
+    const uint8_t* base = static_cast<const uint8_t*>(packed);
+    VQ3View v;
+    v.codes = base + L.codes_off;
+    v.cb = reinterpret_cast<const uint32_t*>(base + L.cb_off);
+    v.sc = reinterpret_cast<const uint16_t*>(base + L.sc_off);
+    v.N = N;
+    v.K = K;
+    return v;
+}
+
+vqmlp_status read_device_header(const void* dev, PackedHeader* h, const char* name) {
+    if (!dev) return fail(VQMLP_ERR_INVALID_ARG, "%s: null packed buffer", name);
+    if (!aligned(dev, 256))
+        return fail(VQMLP_ERR_INVALID_ARG, "%s: packed buffer must be 256-byte aligned", name);
+    hipError_t e = hipMemcpy(h, dev, sizeof *h, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "reading a packed header");
+    return VQMLP_OK;
+}
+
+vqmlp_status check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    if (strncmp(p.gcnArchName, "gfx950", 6) != 0)
+        return fail(VQMLP_ERR_UNSUPPORTED, "device %d is %s; this library is built for gfx950",
+                    dev, p.gcnArchName);
+    return VQMLP_OK;
+}
+
+// ---------------------------------------------------------------- skinny path geometry
+
+struct SkinnyGeom {
+    int tpw, slices;
+};
+
+// Tiles per wave and slices of the K range for a matrix with K columns on the skinny path.
+// need_single: the epilogue needs whole sums (gate+up), so K must fit in one slice.
+bool skinny_geom(int K, bool need_single, SkinnyGeom* g) {
+    const int KT = K / kTileCols;
+    if (need_single) {
+        const int tpw = (KT + kSkinnyWaves - 1) / kSkinnyWaves;
+        if (tpw > kSkinnyMaxTPW) return false;
+        g->tpw = tpw;
+        g->slices = 1;
+        return true;
+    }
+    // down: two tiles per wave keeps the operand small and the work items many
+    int tpw = 2;
+    if (KT <= kSkinnyWaves * tpw) tpw = (KT + kSkinnyWaves - 1) / kSkinnyWaves;
+    g->tpw = tpw;
+    g->slices = (KT + kSkinnyWaves * tpw - 1) / (kSkinnyWaves * tpw);
+    return true;
+}
+
+}  // namespace
+
+// ==================================================================== plan
+
+struct vqmlp_plan {
+    vqmlp_desc d;
+    int bh, bi;
+    VQ3View gate, up, down;
+    SkinnyGeom g_gu, g_dn;
+    bool skinny_ok, tiled_ok;
+};
+
+namespace {
+
+struct Workspace {
+    // skinny
+    uint32_t* xexp;   // [H/16][64][4]
+    float* a;         // [8][I]
+    uint32_t* aexp;   // [I/16][64][4]
+    float* part;      // [slices][8][H]
+    // tiled
+    uint16_t* xt;     // [T][H]
+    float* a_t;       // [T][I]
+    uint16_t* at;     // [T][I]
+    size_t bytes;
+};
+
+Workspace carve(const vqmlp_plan* p, int T, void* base) {
+    Workspace w;
+    memset(&w, 0, sizeof w);
+    const int H = p->d.H, I = p->d.I;
+    size_t off = 256;  // control block
+    auto take = [&](size_t n) {
+        size_t o = off;
+        off = align256(off + n);
+        return o;
+    };
+    uint8_t* b = static_cast<uint8_t*>(base);
+    // skinny region
+    size_t o_xexp = take(size_t(H) * 64);
+    size_t o_a = take(size_t(kSkinnyT) * I * 4);
+    size_t o_aexp = take(size_t(I) * 64);
+    size_t o_part = take(size_t(p->g_dn.slices) * kSkinnyT * H * 4);
+    size_t skinny_end = off;
+    // tiled region overlaps the skinny one (a forward uses one of them)
+    off = 256;
+    const int Tt = T > 0 ? T : 1;
+    size_t o_xt = take(size_t(Tt) * H * 2);
+    size_t o_at32 = take(size_t(Tt) * I * 4);
+    size_t o_at = take(size_t(Tt) * I * 2);
+    size_t tiled_end = off;
+    w.bytes = skinny_end > tiled_end ? skinny_end : tiled_end;
+    if (b) {
+        w.xexp = reinterpret_cast<uint32_t*>(b + o_xexp);
+        w.a = reinterpret_cast<float*>(b + o_a);
+        w.aexp = reinterpret_cast<uint32_t*>(b + o_aexp);
+        w.part = reinterpret_cast<float*>(b + o_part);
+        w.xt = reinterpret_cast<uint16_t*>(b + o_xt);
+        w.a_t = reinterpret_cast<float*>(b + o_at32);
+        w.at = reinterpret_cast<uint16_t*>(b + o_at);
+    }
+    return w;
+}
+
+vqmlp_status run_skinny(const vqmlp_plan* p, int T, const void* x, void* y, const Workspace& w,
+                        hipStream_t st) {
+    const int H = p->d.H, I = p->d.I;
+    hipError_t e = launch_rotate(T, H, p->bh, x, 0, p->d.s_in, p->d.sign_h, w.xexp, 2, st);
+    if (e != hipSuccess) return hip_fail(e, "rotate (input)");
+    SkinnyArgs a;
+    memset(&a, 0, sizeof a);
+    a.mat[0] = p->gate;
+    a.mat[1] = p->up;
+    a.nmat = 2;
+    a.T = T;
+    a.slices = 1;
+    a.tpw = p->g_gu.tpw;
+    a.bexp = w.xexp;
+    a.sign_i = p->d.sign_i;
+    a.a_out = w.a;
+    e = launch_skinny(a, st);
+    if (e != hipSuccess) return hip_fail(e, "skinny gate/up");
+    e = launch_rotate(T, I, p->bi, w.a, 1, nullptr, nullptr, w.aexp, 2, st);
+    if (e != hipSuccess) return hip_fail(e, "rotate (intermediate)");
+    SkinnyArgs d;
+    memset(&d, 0, sizeof d);
+    d.mat[0] = p->down;
+    d.nmat = 1;
+    d.T = T;
+    d.slices = p->g_dn.slices;
+    d.tpw = p->g_dn.tpw;
+    d.bexp = w.aexp;
+    d.part = w.part;
+    d.y = static_cast<uint16_t*>(y);
+    e = launch_skinny(d, st);
+    if (e != hipSuccess) return hip_fail(e, "skinny down");
+    if (d.slices > 1) {
+        e = launch_reduce_down(T, H, d.slices, w.part, p->down.sc, static_cast<uint16_t*>(y), st);
+        if (e != hipSuccess) return hip_fail(e, "down reduction");
+    }
+    return ok();
+}
+
+vqmlp_status run_tiled(const vqmlp_plan* p, int T, const void* x, void* y, const Workspace& w,
+                       hipStream_t st) {
+    const int H = p->d.H, I = p->d.I;
+    hipError_t e = launch_rotate(T, H, p->bh, x, 0, p->d.s_in, p->d.sign_h, w.xt, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "rotate (input)");
+    TiledArgs a;
+    memset(&a, 0, sizeof a);
+    a.mat[0] = p->gate;
+    a.mat[1] = p->up;
+    a.nmat = 2;
+    a.T = T;
+    a.xt = w.xt;
+    a.sign_i = p->d.sign_i;
+    a.a_out = w.a_t;
+    e = launch_tiled(a, st);
+    if (e != hipSuccess) return hip_fail(e, "tiled gate/up");
+    e = launch_rotate(T, I, p->bi, w.a_t, 1, nullptr, nullptr, w.at, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "rotate (intermediate)");
+    TiledArgs d;
+    memset(&d, 0, sizeof d);
+    d.mat[0] = p->down;
+    d.nmat = 1;
+    d.T = T;
+    d.xt = w.at;
+    d.y = static_cast<uint16_t*>(y);
+    e = launch_tiled(d, st);
+    if (e != hipSuccess) return hip_fail(e, "tiled down");
+    return ok();
+}
+
+}  // namespace
+
+// ==================================================================== extern "C"
+
+extern "C" {
+
+int vqmlp_abi_version(void) { return VQMLP_ABI_VERSION; }
+
+const char* vqmlp_last_error(void) { return g_last_error.c_str(); }
+
+vqmlp_status vqmlp_packed_bytes(int N, int K, size_t* bytes) {
+    if (!bytes) return fail(VQMLP_ERR_INVALID_ARG, "bytes is NULL");
+    vqmlp_status st = check_shape(N, K);
+    if (st) return st;
+    *bytes = layout_of(N, K).total;
+    return ok();
+}
+
+vqmlp_status vqmlp_pack(int N, int K, const uint8_t* codes, const uint16_t* codebook,
+                        const uint16_t* row_scale, void* packed, size_t packed_bytes) {
+    vqmlp_status st = check_shape(N, K);
+    if (st) return st;
+    if (!codes || !codebook || !row_scale || !packed)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_pack: null pointer");
+    const Layout L = layout_of(N, K);
+    if (packed_bytes < L.total)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_pack: buffer holds %zu bytes, needs %zu",
+                    packed_bytes, L.total);
+    const size_t ncodes = size_t(N / 2) * K;
+    for (size_t i = 0; i < ncodes; ++i)
+        if (codes[i] > 63)
+            return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_pack: code %u at pair %zu column %zu > 63",
+                        codes[i], i / K, i % K);
+    uint8_t* out = static_cast<uint8_t*>(packed);
+    memset(out, 0, L.total);
+    PackedHeader h = header_of(N, K, 0, kCodebook, L);
+    memcpy(out, &h, sizeof h);
+    const int MT = N / kTileRows, KT = K / kTileCols;
+    uint8_t* tiles = out + L.codes_off;
+    for (int m = 0; m < MT; ++m)
+        for (int k = 0; k < KT; ++k) {
+            uint8_t* tile = tiles + (size_t(m) * KT + k) * kTileBytes;
+            for (int l = 0; l < 64; ++l) {
+                const int pair = m * kTilePairs + (l % 16);
+                const uint8_t* crow = codes + size_t(pair) * K;
+                for (int q = 0; q < 16; ++q) {
+                    const int col = k * kTileCols + 16 * (q / 4) + 4 * (l / 16) + (q % 4);
+                    put6(tile + 12 * l, q, crow[col]);
+                }
+            }
+        }
+    memcpy(out + L.cb_off, codebook, L.cb_bytes);
+    memcpy(out + L.sc_off, row_scale, L.sc_bytes);
+    return ok();
+}
+
+vqmlp_status vqmlp_unpack(int N, int K, const void* packed, size_t packed_bytes, uint8_t* codes,
+                          uint16_t* codebook, uint16_t* row_scale) {
+    vqmlp_status st = check_shape(N, K);
+    if (st) return st;
+    if (!packed || !codes || !codebook || !row_scale)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_unpack: null pointer");
+    const Layout L = layout_of(N, K);
+    if (packed_bytes < L.total)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_unpack: buffer holds %zu bytes, needs %zu",
+                    packed_bytes, L.total);
+    const uint8_t* in = static_cast<const uint8_t*>(packed);
+    PackedHeader h;
+    memcpy(&h, in, sizeof h);
+    st = check_header(h, N, K, 0, kCodebook, L, "vqmlp_unpack");
+    if (st) return st;
+    const int MT = N / kTileRows, KT = K / kTileCols;
+    const uint8_t* tiles = in + L.codes_off;
+    for (int m = 0; m < MT; ++m)
+        for (int k = 0; k < KT; ++k) {
+            const uint8_t* tile = tiles + (size_t(m) * KT + k) * kTileBytes;
+            for (int l = 0; l < 64; ++l) {
+                const int pair = m * kTilePairs + (l % 16);
+                for (int q = 0; q < 16; ++q) {
+                    const int col = k * kTileCols + 16 * (q / 4) + 4 * (l / 16) + (q % 4);
+                    codes[size_t(pair) * K + col] = uint8_t(get6(tile + 12 * l, q));
+                }
+            }
+        }
+    memcpy(codebook, in + L.cb_off, L.cb_bytes);
+    memcpy(row_scale, in + L.sc_off, L.sc_bytes);
+    return ok();
+}
+
+vqmlp_status vqmlp_dequant(int N, int K, const void* packed, float* w, void* stream) {
+    vqmlp_status st = check_shape(N, K);
+    if (st) return st;
+    if (!w) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_dequant: null output");
+    st = check_device();
+    if (st) return st;
+    PackedHeader h;
+    st = read_device_header(packed, &h, "vqmlp_dequant");
+    if (st) return st;
+    st = check_header(h, N, K, 0, kCodebook, layout_of(N, K), "vqmlp_dequant");
+    if (st) return st;
+    hipError_t e = launch_dequant(view_of(packed, N, K), w, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "dequant launch");
+    return ok();
+}
+
+vqmlp_status vqmlp_rotate(int T, int n, int b, const uint16_t* x, const uint16_t* s,
+                          const int8_t* sign, float* out, void* stream) {
+    if (T < 0 || n <= 0 || !is_pow2(b) || b < 2 || b > 1024 || n % b)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_rotate: bad shape T=%d n=%d b=%d", T, n, b);
+    if (T == 0) return ok();
+    if (!x || !out) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_rotate: null pointer");
+    vqmlp_status st = check_device();
+    if (st) return st;
+    hipError_t e = launch_rotate(T, n, b, x, 0, s, sign, out, 0, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "rotate launch");
+    return ok();
+}
+
+vqmlp_status vqmlp_create(const vqmlp_desc* desc, vqmlp_plan** out) {
+    if (!desc || !out) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_create: null pointer");
+    *out = nullptr;
+    const vqmlp_desc& d = *desc;
+    vqmlp_status st;
+    if ((st = check_shape(d.I, d.H))) return st;  // gate/up: N = I, K = H
+    if ((st = check_shape(d.H, d.I))) return st;  // down:    N = H, K = I
+    if (d.t_max < 0 || d.t_max > (1 << 20))
+        return fail(VQMLP_ERR_INVALID_ARG, "t_max=%d out of range", d.t_max);
+    const int bh = d.had_block_h ? d.had_block_h : default_block(d.H);
+    const int bi = d.had_block_i ? d.had_block_i : default_block(d.I);
+    if (!is_pow2(bh) || bh < 2 || bh > 1024 || d.H % bh)
+        return fail(VQMLP_ERR_INVALID_ARG, "Hadamard block %d does not divide H=%d", bh, d.H);
+    if (!is_pow2(bi) || bi < 2 || bi > 1024 || d.I % bi)
+        return fail(VQMLP_ERR_INVALID_ARG, "Hadamard block %d does not divide I=%d", bi, d.I);
+    if (!d.s_in) return fail(VQMLP_ERR_INVALID_ARG, "s_in is NULL");
+    if (!aligned(d.s_in, 16) || (d.sign_h && !aligned(d.sign_h, 16)) ||
+        (d.sign_i && !aligned(d.sign_i, 16)))
+        return fail(VQMLP_ERR_INVALID_ARG, "s_in / sign pointers must be 16-byte aligned");
+    if ((st = check_device())) return st;
+    PackedHeader hg, hu, hd;
+    if ((st = read_device_header(d.gate, &hg, "gate"))) return st;
+    if ((st = read_device_header(d.up, &hu, "up"))) return st;
+    if ((st = read_device_header(d.down, &hd, "down"))) return st;
+    if ((st = check_header(hg, d.I, d.H, 0, kCodebook, layout_of(d.I, d.H), "gate"))) return st;
+    if ((st = check_header(hu, d.I, d.H, 0, kCodebook, layout_of(d.I, d.H), "up"))) return st;
+    if ((st = check_header(hd, d.H, d.I, 0, kCodebook, layout_of(d.H, d.I), "down"))) return st;
+    vqmlp_plan* p = new (std::nothrow) vqmlp_plan;
+    if (!p) return fail(VQMLP_ERR_INVALID_ARG, "out of host memory");
+    p->d = d;
+    p->bh = bh;
+    p->bi = bi;
+    p->gate = view_of(d.gate, d.I, d.H);
+    p->up = view_of(d.up, d.I, d.H);
+    p->down = view_of(d.down, d.H, d.I);
+    p->skinny_ok = skinny_geom(d.H, true, &p->g_gu);
+    p->tiled_ok = d.H % 64 == 0 && d.I % 64 == 0;
+    skinny_geom(d.I, false, &p->g_dn);
+    if (!p->skinny_ok) {
+        p->g_gu.tpw = 0;
+        p->g_gu.slices = 0;
+    }
+    *out = p;
+    return ok();
+}
+
+vqmlp_status vqmlp_destroy(vqmlp_plan* plan) {
+    delete plan;
+    return ok();
+}
+
+vqmlp_status vqmlp_workspace_bytes(const vqmlp_plan* p, int T, size_t* bytes) {
+    if (!p || !bytes) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_workspace_bytes: null pointer");
+    if (T < 0 || T > p->d.t_max)
+        return fail(VQMLP_ERR_INVALID_ARG, "T=%d outside [0, t_max=%d]", T, p->d.t_max);
+    *bytes = carve(p, T, nullptr).bytes;
+    return ok();
+}
+
+vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void* y,
+                                void* workspace, size_t workspace_bytes, int path,
+                                void* stream) {
+    if (!p) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_forward: null plan");
+    if (T < 0 || T > p->d.t_max)
+        return fail(VQMLP_ERR_INVALID_ARG, "T=%d outside [0, t_max=%d]", T, p->d.t_max);
+    if (path < 0 || path > 3) return fail(VQMLP_ERR_INVALID_ARG, "unknown path %d", path);
+    if (T == 0) return ok();
+    if (!x || !y || !workspace) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_forward: null pointer");
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256))
+        return fail(VQMLP_ERR_INVALID_ARG,
+                    "x and y must be 16-byte aligned, the workspace 256-byte aligned");
+    const Workspace w = carve(p, T, workspace);
+    if (workspace_bytes < w.bytes)
+        return fail(VQMLP_ERR_WORKSPACE, "workspace holds %zu bytes, this forward needs %zu",
+                    workspace_bytes, w.bytes);
+    const uint8_t* wb = static_cast<const uint8_t*>(workspace);
+    const uint8_t* xb = static_cast<const uint8_t*>(x);
+    const uint8_t* yb = static_cast<const uint8_t*>(y);
+    const size_t xy = size_t(T) * p->d.H * 2;
+    if ((xb < wb + w.bytes && wb < xb + xy) || (yb < wb + w.bytes && wb < yb + xy))
+        return fail(VQMLP_ERR_INVALID_ARG, "x or y overlaps the workspace");
+    bool skinny;
+    if (path == 0)
+        skinny = T <= kSkinnyT && p->skinny_ok;
+    else if (path == 2)
+        skinny = false;
+    else {
+        if (T > kSkinnyT)
+            return fail(VQMLP_ERR_UNSUPPORTED, "the skinny path takes T <= %d (T=%d)", kSkinnyT, T);
+        if (!p->skinny_ok)
+            return fail(VQMLP_ERR_UNSUPPORTED, "the skinny path takes H <= %d (H=%d)",
+                        kSkinnyWaves * kSkinnyMaxTPW * kTileCols, p->d.H);
+        skinny = true;
+    }
+    if (!skinny && !p->tiled_ok)
+        return fail(VQMLP_ERR_UNSUPPORTED, "the tiled path takes H and I multiples of 64");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return skinny ? run_skinny(p, T, x, y, w, st) : run_tiled(p, T, x, y, w, st);
+}
+
+vqmlp_status vqmlp_forward(const vqmlp_plan* p, int T, const void* x, void* y, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return vqmlp_forward_path(p, T, x, y, workspace, workspace_bytes, 0, stream);
+}
+
+// ------------------------------------------------------------------ scalar-LUT projection
+
+static vqmlp_status lut_shape(int bits, int N, int K) {
+    if (bits != 2 && bits != 4) return fail(VQMLP_ERR_INVALID_ARG, "bits=%d (2 or 4)", bits);
+    if (N <= 0 || K <= 0 || N > (1 << 20) || K > (1 << 20) || N % 64 || K % 64)
+        return fail(VQMLP_ERR_INVALID_ARG, "LUT matrix %dx%d: both must be multiples of 64", N, K);
+    return VQMLP_OK;
+}
+
+static Layout lut_layout(int bits, int N, int K) {
+    Layout L;
+    L.codes_off = kHeaderBytes;
+    L.codes_bytes = size_t(N) * K * bits / 8;
+    L.cb_off = align256(L.codes_off + L.codes_bytes);
+    L.cb_bytes = size_t(N / 8) * (1u << bits) * 2;
+    L.sc_off = align256(L.cb_off + L.cb_bytes);
+    L.sc_bytes = size_t(N) * 2;
+    L.total = align256(L.sc_off + L.sc_bytes);
+    return L;
+}
+
+vqmlp_status vqmlp_lut_packed_bytes(int bits, int N, int K, size_t* bytes) {
+    if (!bytes) return fail(VQMLP_ERR_INVALID_ARG, "bytes is NULL");
+    vqmlp_status st = lut_shape(bits, N, K);
+    if (st) return st;
+    *bytes = lut_layout(bits, N, K).total;
+    return ok();
+}
+
+vqmlp_status vqmlp_lut_pack(int bits, int N, int K, const uint8_t* codes, const uint16_t* lut,
+                            const uint16_t* row_scale, void* packed, size_t bytes) {
+    vqmlp_status st = lut_shape(bits, N, K);
+    if (st) return st;
+    if (!codes || !lut || !row_scale || !packed)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_pack: null pointer");
+    const Layout L = lut_layout(bits, N, K);
+    if (bytes < L.total)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_pack: buffer holds %zu bytes, needs %zu",
+                    bytes, L.total);
+    const unsigned lim = 1u << bits;
+    for (size_t i = 0; i < size_t(N) * K; ++i)
+        if (codes[i] >= lim)
+            return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_pack: code %u >= %u at %zu", codes[i],
+                        lim, i);
+    uint8_t* out = static_cast<uint8_t*>(packed);
+    memset(out, 0, L.total);
+    PackedHeader h = header_of(N, K, uint32_t(bits), lim, L);
+    memcpy(out, &h, sizeof h);
+    const int per = 32 / bits;
+    uint32_t* words = reinterpret_cast<uint32_t*>(out + L.codes_off);
+    for (int n = 0; n < N; ++n)
+        for (int j = 0; j < K; ++j)
+            words[(size_t(n) * K + j) / per] |= uint32_t(codes[size_t(n) * K + j])
+                                                << (bits * (j % per));
+    memcpy(out + L.cb_off, lut, L.cb_bytes);
+    memcpy(out + L.sc_off, row_scale, L.sc_bytes);
+    return ok();
+}
+
+vqmlp_status vqmlp_lut_unpack(int bits, int N, int K, const void* packed, size_t bytes,
+                              uint8_t* codes, uint16_t* lut, uint16_t* row_scale) {
+    vqmlp_status st = lut_shape(bits, N, K);
+    if (st) return st;
+    if (!packed || !codes || !lut || !row_scale)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_unpack: null pointer");
+    const Layout L = lut_layout(bits, N, K);
+    if (bytes < L.total)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_unpack: buffer holds %zu bytes, needs %zu",
+                    bytes, L.total);
+    const uint8_t* in = static_cast<const uint8_t*>(packed);
+    PackedHeader h;
+    memcpy(&h, in, sizeof h);
+    st = check_header(h, N, K, uint32_t(bits), 1u << bits, L, "vqmlp_lut_unpack");
+    if (st) return st;
+    const int per = 32 / bits;
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(in + L.codes_off);
+    for (int n = 0; n < N; ++n)
+        for (int j = 0; j < K; ++j)
+            codes[size_t(n) * K + j] = uint8_t(
+                (words[(size_t(n) * K + j) / per] >> (bits * (j % per))) & ((1u << bits) - 1));
+    memcpy(lut, in + L.cb_off, L.cb_bytes);
+    memcpy(row_scale, in + L.sc_off, L.sc_bytes);
+    return ok();
+}
+
+vqmlp_status vqmlp_lut_workspace_bytes(int N, int K, int T, int r, size_t* bytes) {
+    if (!bytes) return fail(VQMLP_ERR_INVALID_ARG, "bytes is NULL");
+    if (N <= 0 || K <= 0 || T < 0 || r < 0 || r > 256)
+        return fail(VQMLP_ERR_INVALID_ARG, "bad LUT workspace query");
+    *bytes = align256(size_t(T ? T : 1) * K * 2) + align256(size_t(T ? T : 1) * (r ? r : 1) * 4) + 256;
+    return ok();
+}
+
+vqmlp_status vqmlp_lut_forward(int, int, int, int, const void*, const uint16_t*, const uint16_t*,
+                               int, const uint16_t*, const int8_t*, int, const void*, void*, void*,
+                               size_t, void*) {
+    return fail(VQMLP_ERR_UNSUPPORTED, "vqmlp_lut_forward: not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,161 @@
+/*
+ * vqmlp.h -- C ABI of the VQ3 quantized-MLP forward for AMD MI355X (gfx950).
+ *
+ * The operation (web page: model card "anemll/anemll-forge-qwen3.8-27B"):
+ *   - every MLP matrix (gate, up, down) is a three-bit vector lookup table "2x64": 64
+ *     two-component FP16 centroids, one six-bit index per pair of output channels, per-channel
+ *     scales (section "Release 0.2: three-bit MLP, token-mixer rotations, distilled weights",
+ *     format table and first bullet).  This library stores one 64-entry codebook per group of 8
+ *     output rows; code[p][j] selects (W[2p][j], W[2p+1][j]); the row scale multiplies the row;
+ *   - the MLP input is scaled per channel and rotated online by block-Hadamard matrices with
+ *     seeded signs, the weights living in the rotated basis (same section, second bullet; section
+ *     "Files and runtime compatibility", first bullet);
+ *   - the activation is silu(g) = g*sigmoid(g) ("ANEMLL ANE LLM conversion pipeline", Facts, item
+ *     on Forge numerics), applied as silu(gate) * up, followed by the rotated down projection.
+ *
+ * So, for x [T][H]:
+ *   x~ = R_H(x . s),  a = silu(W_gate x~) . (W_up x~),  y = W_down R_I(a),
+ *   R_n = (I (x) H_b / sqrt(b)) diag(sign),  H_b the Sylvester Hadamard matrix of order b,
+ *   W[r][j] = cb[r/8][code[r/2][j]][r%2] * sc[r].
+ * y is rounded to FP16 (round to nearest even); everything before it accumulates in FP32, with
+ * x~ and the rotated activation held in FP16 as matrix-core operands.
+ *
+ * Conventions: every entry point returns a vqmlp_status (0 = OK); no C++ exception crosses the
+ * ABI.  On failure nothing has been launched and vqmlp_last_error() (per thread) explains why.
+ * "DEVICE" pointers are HIP device allocations owned by the caller; "HOST" pointers are plain
+ * host memory owned by the caller.  `stream` is a hipStream_t (NULL = the legacy default
+ * stream); device work is only enqueued, never waited for, and asynchronous device faults
+ * surface at the caller's next synchronisation.
+ */
+#ifndef VQMLP_H
+#define VQMLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VQMLP_ABI_VERSION 1
+#define VQMLP_LAYOUT_VERSION 1
+
+typedef enum {
+    VQMLP_OK = 0,
+    VQMLP_ERR_INVALID_ARG = 1, /* null pointer, bad shape, bad code, bad header, misalignment  */
+    VQMLP_ERR_UNSUPPORTED = 2, /* valid but not handled: shape limits, non-gfx950 device       */
+    VQMLP_ERR_WORKSPACE = 3,   /* workspace too small                                         */
+    VQMLP_ERR_HIP = 4          /* a HIP runtime call or launch failed                         */
+} vqmlp_status;
+
+int vqmlp_abi_version(void);
+/* Text of the last failure on the calling thread ("" if none).  Valid until the next call. */
+const char *vqmlp_last_error(void);
+
+/* ------------------------------------------------------------------ one VQ3 matrix W[N][K]
+ * Requirements: N % 32 == 0 (16 row pairs per tile), K % 64 == 0, N, K <= 1<<20.
+ *
+ * Packed layout (version 1), one contiguous buffer:
+ *   [0, 256)      header: u32 magic 'VQ3P', u32 layout version, u32 N, u32 K, u32 group rows (8),
+ *                 u32 codebook entries (64), u32 kind (0 = VQ3), u32 reserved,
+ *                 u64 codes offset, u64 codes bytes, u64 codebook offset, u64 codebook bytes,
+ *                 u64 scale offset, u64 scale bytes, u64 total bytes; the rest zero.
+ *   codes         (N/32) x (K/64) tiles of 768 bytes, tile (m, k) at (m*(K/64) + k)*768.  A tile
+ *                 covers row pairs 16m..16m+15 and columns 64k..64k+63.  Bytes 12*l..12*l+11 of
+ *                 the tile form a 96-bit little-endian word for lane l = 0..63 holding 16 six-bit
+ *                 codes: code q = 4s+i (bits 6q..6q+5) belongs to pair 16m + (l % 16) and column
+ *                 64k + 16s + 4*(l / 16) + i.  (This is the order in which a 64-lane wave consumes
+ *                 them as matrix-core operands, so every wave load is one contiguous 768-byte run.)
+ *   codebook      [N/8][64][2] binary16, natural order, 256-byte aligned.
+ *   scale         [N] binary16, 256-byte aligned.
+ */
+vqmlp_status vqmlp_packed_bytes(int N, int K, size_t *bytes);
+
+/* Pack HOST arrays into a HOST buffer of at least vqmlp_packed_bytes() bytes.
+ *   codes     [N/2][K] uint8, values 0..63 (row p covers output rows 2p, 2p+1)
+ *   codebook  [N/8][64][2] binary16 bits; [g][c][0] goes to the even row, [g][c][1] to the odd
+ *   row_scale [N] binary16 bits
+ * Returns INVALID_ARG for a code above 63, a short buffer or a bad shape. */
+vqmlp_status vqmlp_pack(int N, int K, const uint8_t *codes, const uint16_t *codebook,
+                        const uint16_t *row_scale, void *packed, size_t packed_bytes);
+
+/* Inverse of vqmlp_pack (HOST to HOST); validates the header first. */
+vqmlp_status vqmlp_unpack(int N, int K, const void *packed, size_t packed_bytes, uint8_t *codes,
+                          uint16_t *codebook, uint16_t *row_scale);
+
+/* Test hook: w[r][j] = float(cb) * float(sc), exactly (an FP16 x FP16 product fits FP32), for a
+ * DEVICE packed buffer; w is DEVICE float [N][K]. */
+vqmlp_status vqmlp_dequant(int N, int K, const void *packed, float *w, void *stream);
+
+/* ------------------------------------------------------------------ the MLP plan */
+typedef struct {
+    int H, I;           /* hidden and intermediate sizes                                    */
+    int had_block_h;    /* Hadamard block of the input rotation, power of two in [2, 1024];
+                           0 = the largest power of two <= 128 dividing H                    */
+    int had_block_i;    /* same for the down projection's input (64 for I = 704)            */
+    int t_max;          /* largest T a forward may pass (sizes the workspace)               */
+    const void *gate;   /* DEVICE packed VQ3 buffer, N = I, K = H                           */
+    const void *up;     /* DEVICE packed VQ3 buffer, N = I, K = H                           */
+    const void *down;   /* DEVICE packed VQ3 buffer, N = H, K = I                           */
+    const uint16_t *s_in;   /* DEVICE binary16 [H] per-channel input scale                  */
+    const int8_t *sign_h;   /* DEVICE int8 [H] +-1, or NULL for all +1                      */
+    const int8_t *sign_i;   /* DEVICE int8 [I] +-1, or NULL for all +1                      */
+} vqmlp_desc;
+
+typedef struct vqmlp_plan vqmlp_plan;
+
+/* Validate the description (shapes, alignment, gfx950 device, and each packed header through
+ * one synchronous device-to-host copy) and build an immutable host-side plan.  The plan keeps
+ * the pointers only: it allocates no device memory and the caller keeps every buffer alive. */
+vqmlp_status vqmlp_create(const vqmlp_desc *desc, vqmlp_plan **out);
+vqmlp_status vqmlp_destroy(vqmlp_plan *plan);
+
+/* Workspace a forward with T rows needs (DEVICE bytes, 256-byte aligned).  The workspace must
+ * be zero-filled before its first use; every forward leaves its control words zero again. */
+vqmlp_status vqmlp_workspace_bytes(const vqmlp_plan *plan, int T, size_t *bytes);
+
+/* y = MLP(x).  x, y: DEVICE binary16 [T][H], 16-byte aligned, may not overlap the workspace.
+ * T == 0 is a no-op.  T <= 8 runs the bandwidth-bound skinny kernels, T > 8 the matrix-core
+ * tiled kernels.  Calls that share a workspace must not overlap in time. */
+vqmlp_status vqmlp_forward(const vqmlp_plan *plan, int T, const void *x, void *y, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/* Same as vqmlp_forward with the kernel family chosen by the caller: path 0 = automatic,
+ * 1 = skinny (T <= 8 only), 2 = tiled matrix-core, 3 = skinny as separate per-phase kernels. */
+vqmlp_status vqmlp_forward_path(const vqmlp_plan *plan, int T, const void *x, void *y,
+                                void *workspace, size_t workspace_bytes, int path, void *stream);
+
+/* Test hook for the rotation kernels: out[t][.] = R_n(x[t][.] . s) with block b (power of two,
+ * 2..1024), FP32 output.  x DEVICE binary16 [T][n]; s DEVICE binary16 [n] or NULL (all 1);
+ * sign DEVICE int8 [n] or NULL; out DEVICE float [T][n]. */
+vqmlp_status vqmlp_rotate(int T, int n, int b, const uint16_t *x, const uint16_t *s,
+                          const int8_t *sign, float *out, void *stream);
+
+/* ------------------------------------------------------------------ scalar-LUT projection
+ * Token-mixer format of the same model card (format table, "Token mixers" row; rotation bullet):
+ * bits in {2, 4}, one table of 2^bits binary16 scalars per 8 output rows, a binary16 scale per
+ * output row, optional rank-r binary16 factors U [N][r] and V [r][K]:
+ *   y = W x~ + U (V x~),  x~ = R_K(x . s) with 1024-wide (or had_block) Hadamard blocks.
+ * Requirements: N % 64 == 0, K % 64 == 0, r <= 256.
+ * Packed layout (version 1): 256-byte header as above (kind 2 for 2-bit, 4 for 4-bit), then
+ * codes as [N][K/ (32/bits)] little-endian 32-bit words (code j of row n at bits
+ * bits*(j % (32/bits)) of word j / (32/bits)), then the tables [N/8][2^bits] binary16, then the
+ * scales [N] binary16, each section 256-byte aligned. */
+vqmlp_status vqmlp_lut_packed_bytes(int bits, int N, int K, size_t *bytes);
+vqmlp_status vqmlp_lut_pack(int bits, int N, int K, const uint8_t *codes /* [N][K] */,
+                            const uint16_t *lut /* [N/8][1<<bits] */,
+                            const uint16_t *row_scale /* [N] */, void *packed, size_t bytes);
+vqmlp_status vqmlp_lut_unpack(int bits, int N, int K, const void *packed, size_t bytes,
+                              uint8_t *codes, uint16_t *lut, uint16_t *row_scale);
+vqmlp_status vqmlp_lut_workspace_bytes(int N, int K, int T, int r, size_t *bytes);
+/* x DEVICE binary16 [T][K] -> y DEVICE binary16 [T][N].  packed, U, V, s, sign DEVICE.  U, V
+ * NULL or r == 0: no factors.  s, sign NULL: all 1.  had_block 0: no rotation. */
+vqmlp_status vqmlp_lut_forward(int bits, int N, int K, int T, const void *packed,
+                               const uint16_t *U, const uint16_t *V, int r, const uint16_t *s,
+                               const int8_t *sign, int had_block, const void *x, void *y,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VQMLP_H */

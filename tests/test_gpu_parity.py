@@ -1,0 +1,196 @@
+"""GPU parity: the HIP library against the FP64 oracle on identical seeded inputs.
+
+Bars: dequantised weights bit-exact; rotation within 1e-6 relative; MLP outputs within a
+relative Frobenius error of 2e-3 (FP32 accumulation and FP16 operands against FP64).
+Every call goes through the C ABI (the ctypes binding only marshals arguments).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from bit_vector_lut_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+MLP_TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def torch_dev():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+@pytest.fixture(scope="module")
+def vq(torch_dev):
+    from bit_vector_lut_amd import vqmlp
+
+    vqmlp.lib()
+    return vqmlp
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _f64(t):
+    return t.cpu().numpy().view(np.float16).astype(np.float64)
+
+
+def _rel_fro(y, ref):
+    return np.linalg.norm(y - ref) / np.linalg.norm(ref)
+
+
+def _report(name, y, ref):
+    err = _rel_fro(y, ref)
+    row = np.linalg.norm(y - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    _say("%s: rel_fro=%.3e max_abs=%.3e worst_row=%.3e" % (name, err, np.abs(y - ref).max(),
+                                                          row.max()))
+    return err
+
+
+# ------------------------------------------------------------------ dequantisation
+
+
+@pytest.mark.parametrize("N,K", [(32, 64), (64, 256), (704, 256), (256, 704), (96, 128)])
+def test_dequant_bit_exact(vq, oracle_mod, torch_dev, N, K):
+    m = synth.vq3_matrix(np.random.default_rng(N * 7 + K), N, K)
+    # force a few subnormal and signed-zero centroids into play
+    cb = m.cb.copy()
+    cb.view(np.uint16)[0, :4, 0] = [0x0001, 0x8003, 0x03FF, 0x8000]
+    m = synth.VQ3Matrix(m.codes, cb, m.sc)
+    _say("dequant N=%d K=%d" % (N, K))
+    w = vq.dequant(N, K, vq.to_device(vq.pack(*m.as_u16()))).cpu().numpy()
+    ref = oracle_mod.vq3_weight(m.codes, m.cb, m.sc).astype(np.float32)
+    assert np.array_equal(w.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequant_full_size_row_blocks(vq, oracle_mod, torch_dev):
+    """The 27B-like down matrix (5120 x 17408): sampled 32-row blocks, bit-exact."""
+    rng = np.random.default_rng(3)
+    N, K = 5120, 17408
+    m = synth.vq3_matrix(rng, N, K)
+    _say("dequant full 5120x17408")
+    w = vq.dequant(N, K, vq.to_device(vq.pack(*m.as_u16())))
+    for r0 in (0, 2048, 5088):
+        sub = synth.VQ3Matrix(m.codes[r0 // 2:r0 // 2 + 16], m.cb[r0 // 8:r0 // 8 + 4],
+                              m.sc[r0:r0 + 32])
+        ref = oracle_mod.vq3_weight(sub.codes, sub.cb, sub.sc).astype(np.float32)
+        got = w[r0:r0 + 32].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), r0
+
+
+# ------------------------------------------------------------------ rotation
+
+
+@pytest.mark.parametrize("T,n,b", [(1, 256, 128), (3, 704, 64), (8, 5120, 128), (13, 2048, 1024),
+                                   (2, 64, 2), (9, 17408, 128)])
+def test_rotate_matches_oracle(vq, oracle_mod, torch_dev, T, n, b):
+    rng = np.random.default_rng(T * n + b)
+    x = rng.standard_normal((T, n)).astype(np.float16)
+    s = rng.lognormal(0, 0.3, n).astype(np.float16)
+    sign = (2 * rng.integers(0, 2, n) - 1).astype(np.int8)
+    _say("rotate T=%d n=%d b=%d" % (T, n, b))
+    got = vq.rotate(vq.to_device(x), b, vq.to_device(s), vq.to_device(sign)).cpu().numpy()
+    ref = oracle_mod.rotate(x.astype(np.float64) * s.astype(np.float64), b, sign)
+    assert _rel_fro(got.astype(np.float64), ref) <= 1e-6
+    assert np.abs(got - ref).max() <= 1e-6 * np.abs(ref).max() * 4
+
+
+# ------------------------------------------------------------------ MLP forward
+
+
+def _run(vq, torch_dev, layer, path=0, mlp=None):
+    mlp = mlp or vq.MLP.from_layer(layer, t_max=max(layer.T, 8))
+    x = vq.to_device(layer.x)
+    y = mlp.forward(x, path=path)
+    torch_dev.cuda.synchronize()
+    return _f64(y)
+
+
+@pytest.mark.parametrize("path", [0, 2])
+def test_config1_tiny(vq, oracle_mod, torch_dev, path):
+    L = synth.config1()
+    _say("config1 path=%d" % path)
+    y = _run(vq, torch_dev, L, path)
+    ref = oracle_mod.mlp_forward(L)
+    assert _report("config1 path %d" % path, y, ref) <= MLP_TOL
+
+
+SMALL = [(256, 704), (128, 192), (512, 1024), (320, 640)]
+
+
+@pytest.mark.parametrize("T", [1, 2, 7, 8, 9, 16, 33, 64, 65])
+@pytest.mark.parametrize("H,I", SMALL)
+def test_mlp_small_shapes(vq, oracle_mod, torch_dev, H, I, T):
+    L = synth.mlp_layer(H, I, T, seed=H * 31 + I + T, outliers=(T % 2 == 1))
+    _say("small H=%d I=%d T=%d" % (H, I, T))
+    mlp = vq.MLP.from_layer(L, t_max=max(T, 8))
+    ref = oracle_mod.mlp_forward(L)
+    for path in ([0, 2] if T <= 8 else [0]):
+        y = _run(vq, torch_dev, L, path, mlp)
+        assert _report("H=%d I=%d T=%d path %d" % (H, I, T, path), y, ref) <= MLP_TOL
+
+
+@pytest.fixture(scope="module")
+def config2():
+    return synth.config2()
+
+
+@pytest.fixture(scope="module")
+def config2_ref(oracle_mod, config2):
+    return oracle_mod.mlp_forward(config2)
+
+
+def test_config2_full(vq, oracle_mod, torch_dev, config2, config2_ref):
+    _say("config2 skinny")
+    y = _run(vq, torch_dev, config2, 0)
+    assert _report("config2", y, config2_ref) <= MLP_TOL
+
+
+def test_config2_tiled_path(vq, oracle_mod, torch_dev, config2, config2_ref):
+    _say("config2 tiled")
+    y = _run(vq, torch_dev, config2, 2)
+    assert _report("config2 tiled", y, config2_ref) <= MLP_TOL
+
+
+def test_config2_deterministic(vq, torch_dev, config2):
+    mlp = vq.MLP.from_layer(config2)
+    x = vq.to_device(config2.x)
+    ws = mlp.workspace(8)
+    _say("config2 determinism")
+    y1 = mlp.forward(x, workspace=ws).clone()
+    y2 = mlp.forward(x, workspace=ws).clone()
+    torch_dev.cuda.synchronize()
+    assert torch_dev.equal(y1, y2)
+
+
+def test_config3_sampled_tokens(vq, oracle_mod, torch_dev):
+    L = synth.config3()
+    _say("config3 T=64")
+    y = _run(vq, torch_dev, L, 0)
+    toks = [0, 17, 42, 63]
+    ref = oracle_mod.mlp_forward(L, tokens=toks)
+    assert _report("config3", y[toks], ref) <= MLP_TOL
+
+
+def test_errors_on_device(vq, torch_dev):
+    L = synth.mlp_layer(256, 704, 4, seed=1)
+    mlp = vq.MLP.from_layer(L, t_max=8)
+    x = vq.to_device(L.x)
+    small = torch_dev.zeros(256, dtype=torch_dev.uint8, device="cuda")
+    with pytest.raises(vq.VqmlpError) as e:
+        mlp.forward(x, workspace=small)
+    assert e.value.status == vq.ERR_WORKSPACE
+    big = vq.to_device(np.zeros((9, 256), np.float16))
+    with pytest.raises(vq.VqmlpError) as e:
+        mlp.forward(big)
+    assert e.value.status == vq.ERR_INVALID_ARG
+    with pytest.raises(vq.VqmlpError) as e:
+        mlp.forward(vq.to_device(np.zeros((9, 256), np.float16)), path=1)
+    empty = vq.to_device(np.zeros((0, 256), np.float16))
+    assert mlp.forward(empty).shape == (0, 256)
