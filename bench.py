@@ -1,0 +1,209 @@
+"""Benchmark of the VQ3 quantized-MLP forward on one MI355X.
+
+A step is one pass of the T=8 hot path over the 64-layer stream: 64 independent 27B-like MLP
+layers (H=5120, I=17408), each with its own seeded codes, codebooks, scales, signs and input,
+run back to back from one captured HIP graph.  The weights (6.5 GB) exceed every on-die cache,
+so the stream is HBM-bound.  The metric is the effective weight bandwidth: algorithmic weight
+bytes (codes at exactly 3 bits per weight + codebooks + row scales) per second.
+
+Beside it: the T=512 prefill MLP (TFLOP/s against the FP16 matrix-core peak), the roofline of
+the dominant kernel, and the FP64 CPU oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--layers 64] [--no-cpu] [--no-t512]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+H, I = 5120, 17408
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense FP16 matrix cores, published
+
+
+def weight_bytes(H, I):
+    """Algorithmic bytes of one layer: 3-bit codes + 64x2 FP16 codebooks per 8 rows + FP16 row
+    scales, for gate (I x H), up (I x H) and down (H x I)."""
+    per = lambda N, K: N * K * 3 // 8 + (N // 8) * 64 * 2 * 2 + N * 2
+    return 2 * per(I, H) + per(H, I)
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def build_stream(n_layers, device):
+    """Generate, pack and upload the 64-layer stream (host copies dropped as we go)."""
+    import numpy as np
+    import torch
+    from concurrent.futures import ThreadPoolExecutor
+
+    from bit_vector_lut_amd import synth, vqmlp
+
+    seqs = np.random.SeedSequence(0).spawn(64)
+
+    def job(i):
+        L = synth.mlp_layer(H, I, 8, seed=np.random.default_rng(seqs[i]), outliers=True)
+        packs = [vqmlp.pack(*m.as_u16()) for m in (L.gate, L.up, L.down)]
+        return L, packs
+
+    layers = []
+    t0 = time.time()
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        for i, (L, packs) in enumerate(ex.map(job, range(n_layers))):
+            dev = [vqmlp.to_device(p, device) for p in packs]
+            mlp = vqmlp.MLP(H, I, *dev, vqmlp.to_device(L.s, device),
+                            vqmlp.to_device(L.sign_h, device), vqmlp.to_device(L.sign_i, device),
+                            L.had_block_h, L.had_block_i, t_max=8)
+            layers.append((mlp, vqmlp.to_device(L.x, device)))
+            if i == 0 or (i + 1) % 16 == 0:
+                log("layer %d/%d ready (%.1f s)" % (i + 1, n_layers, time.time() - t0))
+    return layers
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--layers", type=int, default=64)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-t512", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d "
+              "requested); run with --gpus 1" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from bit_vector_lut_amd import synth, vqmlp
+
+    device = "cuda:0"
+    torch.cuda.set_device(0)
+    vqmlp.lib()
+
+    # ---------------------------------------------------------------- T = 8, 64-layer stream
+    layers = build_stream(args.layers, device)
+    ws = layers[0][0].workspace(8)
+    ys = [torch.empty_like(x) for _, x in layers]
+    stream = torch.cuda.Stream()
+    log("capturing the %d-layer graph" % len(layers))
+    with torch.cuda.stream(stream):
+        for (m, x), y in zip(layers, ys):  # eager warm-up before capture
+            m.forward(x, y, ws, stream=stream)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for (m, x), y in zip(layers, ys):
+            m.forward(x, y, ws, stream=stream)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        with torch.cuda.stream(stream):
+            graph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    bytes_step = weight_bytes(H, I) * len(layers)
+    gbs = bytes_step / (ms_step * 1e-3) / 1e9
+    log("T=8 stream: %.3f ms/step, %.1f GB/s" % (ms_step, gbs))
+
+    # dominant kernel: one layer's forward, timed with events on its own stream, layers cycled
+    # so that every launch reads weights that are not cache-resident
+    n_fw = min(len(layers), 64)
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    durs = []
+    with torch.cuda.stream(stream):
+        for i in range(n_fw):
+            m, x = layers[i]
+            f0.record(stream)
+            m.forward(x, ys[i], ws, stream=stream)
+            f1.record(stream)
+            f1.synchronize()
+            durs.append(f0.elapsed_time(f1))
+    fw_ms = float(np.mean(durs[1:])) if len(durs) > 1 else durs[0]
+    fw_gbs = weight_bytes(H, I) / (fw_ms * 1e-3) / 1e9
+    log("single forward (events): %.1f us, %.1f GB/s" % (fw_ms * 1e3, fw_gbs))
+
+    result = {
+        "metric": "VQ3 MLP effective weight GB/s at T=8 + TFLOP/s at T=512, % of roofline",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 operands / f32 accumulate (3-bit VQ weights)",
+        "data": "synthetic",
+        "config": {"workload": "64 independent 27B-like VQ3 MLP layers streamed at T=8 "
+                               "(H=5120, I=17408, one HIP graph, 6.50 GB of weights)",
+                   "layers": len(layers), "T": 8, "H": H, "I": I,
+                   "weight_bytes_per_layer": weight_bytes(H, I)},
+        "roofline": {"bound": "hbm", "kernel": "vqmlp_forward (one layer, T=8)",
+                     "achieved": round(fw_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(fw_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    del graph
+    layers_keep = layers  # noqa: F841
+
+    # ---------------------------------------------------------------- T = 512 prefill MLP
+    if not args.no_t512:
+        del ys
+        L5, _, _ = synth.config5()
+        m5 = vqmlp.MLP.from_layer(L5, device=device, t_max=512)
+        x5 = vqmlp.to_device(L5.x, device)
+        y5 = torch.empty_like(x5)
+        ws5 = m5.workspace(512)
+        for _ in range(3):
+            m5.forward(x5, y5, ws5)
+        torch.cuda.synchronize()
+        reps = 10
+        e0.record()
+        for _ in range(reps):
+            m5.forward(x5, y5, ws5)
+        e1.record()
+        torch.cuda.synchronize()
+        ms5 = e0.elapsed_time(e1) / reps
+        flops = 2.0 * 512 * 3 * H * I
+        tf = flops / (ms5 * 1e-3) / 1e12
+        log("T=512 MLP: %.1f us, %.1f TFLOP/s" % (ms5 * 1e3, tf))
+        result["t512"] = {"workload": "27B-like VQ3 MLP prefill, T=512", "us": round(ms5 * 1e3, 1),
+                          "tflops": round(tf, 1), "peak_tflops": MFMA_F16_PEAK_TFLOPS,
+                          "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    if not args.no_cpu:
+        from oracle import oracle as O
+
+        L0 = synth.mlp_layer(H, I, 8, seed=np.random.default_rng(np.random.SeedSequence(0).spawn(64)[0]),
+                             outliers=True)
+        t0 = time.time()
+        O.mlp_forward(L0)
+        dt = time.time() - t0
+        result["cpu_baseline"] = {"value": round(weight_bytes(H, I) / dt / 1e9, 5), "unit": "GB/s",
+                                  "cores": O.num_threads(), "kind": "oracle",
+                                  "sample": "layer 0 of the 64-layer stream, all 8 tokens "
+                                            "(one full FP64 forward, %.1f s)" % dt}
+        log("oracle: %.2f s for one layer on %d threads" % (dt, O.num_threads()))
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,14 +33,16 @@ struct VQ3View {          // device pointers into one packed buffer
 
 // ---- skinny path (T <= 8)
 constexpr int kSkinnyT = 8;            // rows of the matrix-core operand (8 tokens x 2 components)
-constexpr int kSkinnyWaves = 8;        // waves per workgroup, each owning a K range
-constexpr int kSkinnyMaxTPW = 10;      // 64-column tiles per wave held in registers
+constexpr int kSkinnyWaves = 16;       // waves per workgroup, each owning a K range
+constexpr int kSkinnyMaxTPW = 5;       // 64-column tiles per wave held in registers
+enum { kEpiGateUp = 0, kEpiDownFinal = 1, kEpiDownPart = 2 };
 
 // ---- launchers (kernels.hip).  All return hipError_t of the launch.
 hipError_t launch_dequant(const VQ3View& m, float* w, hipStream_t s);
 
 // out[t][.] = R(x . s) for a binary16 or float input.  mode: 0 = FP32 row-major [T][n],
-// 1 = binary16 row-major [T][n], 2 = skinny operand layout (T <= 8, expanded binary16 pairs).
+// 1 = binary16 row-major [T][n], 2 = expanded pair layout (T <= 8), 3 = binary16 row-major
+// [8][n] with the rows past T zero (T <= 8).
 hipError_t launch_rotate(int T, int n, int b, const void* x, int x_is_f32, const uint16_t* s,
                          const int8_t* sign, void* out, int mode, hipStream_t st);
 
@@ -50,7 +52,8 @@ struct SkinnyArgs {
     int T;
     int slices;            // K split into this many slices of 8*tpw tiles
     int tpw;               // tiles per wave
-    const uint32_t* bexp;  // expanded operand [K/16][64][4] dwords
+    int contig;            // 1: each workgroup takes a contiguous item range; 0: round robin
+    const uint16_t* bx;    // activation operand, binary16 [8][K] (rows past T zero)
     // epilogues
     const int8_t* sign_i;  // gate+up: sign of the intermediate rotation (NULL = +1)
     float* a_out;          // gate+up: a [8][I] fp32

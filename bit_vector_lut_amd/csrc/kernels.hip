@@ -4,42 +4,10 @@
 // Weight format (model card "anemll/anemll-forge-qwen3.8-27B", section "Release 0.2: three-bit
 // MLP, token-mixer rotations, distilled weights"): W[r][j] = cb[r/8][code[r/2][j]][r%2] * sc[r],
 // six-bit codes into 64 two-component binary16 centroids per group of 8 output rows.
+#include "device.h"
 #include "internal.h"
 
 namespace vqmlp {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float h2f(uint32_t h) {
-    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
-}
-__device__ __forceinline__ uint32_t f2h(float f) {  // round to nearest even
-    return __builtin_bit_cast(uint16_t, (_Float16)f);
-}
-
-// Code q (0..15) of a lane's 96-bit word, placed at bits 8..13 of the result (i.e. code * 256),
-// which is the stride of one code in the lane-private lookup tables.
-template <int Q>
-__device__ __forceinline__ uint32_t code_x256(uint32_t d0, uint32_t d1, uint32_t d2) {
-    constexpr int bit = 6 * Q;
-    if constexpr (bit < 8) {
-        return (d0 << (8 - bit)) & 0x3F00u;
-    } else {
-        constexpr int sh = bit - 8;
-        constexpr int w = sh / 32, r = sh % 32;
-        const uint32_t lo = w == 0 ? d0 : (w == 1 ? d1 : d2);
-        const uint32_t hi = w == 0 ? d1 : (w == 1 ? d2 : 0u);
-        const uint32_t v = r ? __builtin_amdgcn_alignbit(hi, lo, r) : lo;
-        return v & 0x3F00u;
-    }
-}
-
-template <int Q>
-__device__ __forceinline__ uint32_t code_of(uint32_t d0, uint32_t d1, uint32_t d2) {
-    return code_x256<Q>(d0, d1, d2) >> 8;
-}
 
 // ==================================================================== dequantisation (test hook)
 
@@ -125,6 +93,9 @@ __global__ void __launch_bounds__(256) k_rotate(int T, int n, int b, const void*
             if (tt < nt) static_cast<float*>(out)[size_t(t0 + tt) * n + col] = v;
         } else if (mode == 1) {
             if (tt < nt) static_cast<uint16_t*>(out)[size_t(t0 + tt) * n + col] = (uint16_t)f2h(v);
+        } else if (mode == 3) {
+            // skinny operand: 8 rows, rows past T zero
+            static_cast<uint16_t*>(out)[size_t(tt) * n + col] = (uint16_t)f2h(v);
         } else {
             // skinny operand: K-step col/16, lane 16*kc + 2*tt + c', dword col%4; component c'
             // of the pair-interleaved product gets the value, the other half stays zero.
@@ -140,159 +111,11 @@ __global__ void __launch_bounds__(256) k_rotate(int T, int n, int b, const void*
 
 hipError_t launch_rotate(int T, int n, int b, const void* x, int x_is_f32, const uint16_t* s,
                          const int8_t* sign, void* out, int mode, hipStream_t st) {
-    if (mode == 2 && T > kSkinnyT) return hipErrorInvalidValue;
-    const dim3 grid(n / b, mode == 2 ? 1 : (T + kRotRows - 1) / kRotRows);
+    if ((mode == 2 || mode == 3) && T > kSkinnyT) return hipErrorInvalidValue;
+    const dim3 grid(n / b, mode >= 2 ? 1 : (T + kRotRows - 1) / kRotRows);
     const float norm = float(1.0 / __builtin_sqrt(double(b)));
     hipLaunchKernelGGL(k_rotate, grid, dim3(256), 0, st, T, n, b, x, x_is_f32, s, sign, out, mode,
                        norm);
-    return hipGetLastError();
-}
-
-// ==================================================================== skinny VQ3 projection
-//
-// T <= 8.  The matrix-core product v_mfma_f32_16x16x32_f16 runs with
-//   A (16 x 32): row i = row pair 16*mt + i, column k = 2*jj + c = component c of the centroid
-//                selected by code[pair][16*step + jj]   (the 32-bit table entry, as is),
-//   B (32 x 16): B[2*jj + c][2*t + c'] = x~[t][16*step + jj] if c == c' else 0,
-// so D[i][2t + c'] is row 2*(16*mt + i) + c' of W x~ for token t: eight tokens times two
-// components fill the 16 columns and no repacking of the decoded pairs is needed.
-// Each lane looks codes up in its own copy of the tables (entry c of lane l at LDS word
-// 64*c + l), so the 64 lanes of a lookup always hit 64 different banks.
-
-template <int NMAT, int TPW>
-__global__ void __launch_bounds__(512, 1) k_skinny(SkinnyArgs a) {
-    __shared__ uint32_t tab[NMAT][64 * 64];
-    __shared__ f32x4 red[kSkinnyWaves][NMAT][64];
-    const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
-    const int K = a.mat[0].K, N = a.mat[0].N;
-    const int KT = K / kTileCols, MT = N / kTileRows;
-    const int items = a.slices * MT;
-    const uint32_t lane4 = uint32_t(l) << 2;
-    int cur_slice = -1;
-    u32x4 B[TPW * 4];
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
-        const int sl = item / MT, mt = item % MT;
-        __syncthreads();  // the previous item's lookups and reductions are finished
-        for (int m = 0; m < NMAT; ++m) {
-            const uint32_t* cb = a.mat[m].cb + size_t(mt) * 4 * 64;
-            for (int idx = tid; idx < 64 * 64; idx += 512) {
-                const int c = idx >> 6, ll = idx & 63;
-                tab[m][idx] = cb[((ll & 15) >> 2) * 64 + c];
-            }
-        }
-        const int kt0 = sl * kSkinnyWaves * TPW + w * TPW;
-        if (sl != cur_slice) {
-#pragma unroll
-            for (int t = 0; t < TPW; ++t)
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int kt = kt0 + t;
-                    if (kt < KT)
-                        B[t * 4 + s] = *reinterpret_cast<const u32x4*>(
-                            a.bexp + (size_t(4 * kt + s) * 64 + l) * 4);
-                    else
-                        B[t * 4 + s] = u32x4{0u, 0u, 0u, 0u};
-                }
-            cur_slice = sl;
-        }
-        __syncthreads();
-        f32x4 acc[NMAT];
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int kt = kt0 + t;
-            if (kt < KT) {
-                uint32_t d[NMAT][3];
-#pragma unroll
-                for (int m = 0; m < NMAT; ++m) {
-                    const uint32_t* p = reinterpret_cast<const uint32_t*>(
-                        a.mat[m].codes + (size_t(mt) * KT + kt) * kTileBytes) + 3 * l;
-                    d[m][0] = p[0];
-                    d[m][1] = p[1];
-                    d[m][2] = p[2];
-                }
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-#pragma unroll
-                    for (int m = 0; m < NMAT; ++m) {
-                        const char* tb = reinterpret_cast<const char*>(&tab[m][0]);
-                        u32x4 A;
-                        const uint32_t d0 = d[m][0], d1 = d[m][1], d2 = d[m][2];
-#define VQ_LOOK(i, Q) A[i] = *reinterpret_cast<const uint32_t*>(tb + (code_x256<Q>(d0, d1, d2) | lane4))
-                        if (s == 0) { VQ_LOOK(0, 0); VQ_LOOK(1, 1); VQ_LOOK(2, 2); VQ_LOOK(3, 3); }
-                        if (s == 1) { VQ_LOOK(0, 4); VQ_LOOK(1, 5); VQ_LOOK(2, 6); VQ_LOOK(3, 7); }
-                        if (s == 2) { VQ_LOOK(0, 8); VQ_LOOK(1, 9); VQ_LOOK(2, 10); VQ_LOOK(3, 11); }
-                        if (s == 3) { VQ_LOOK(0, 12); VQ_LOOK(1, 13); VQ_LOOK(2, 14); VQ_LOOK(3, 15); }
-#undef VQ_LOOK
-                        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                            __builtin_bit_cast(half8, A), __builtin_bit_cast(half8, B[t * 4 + s]),
-                            acc[m], 0, 0, 0);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < NMAT; ++m) red[w][m][l] = acc[m];
-        __syncthreads();
-        if (tid < 256) {
-            const int r = tid >> 6, ll = tid & 63;
-            float v[NMAT];
-#pragma unroll
-            for (int m = 0; m < NMAT; ++m) {
-                float sum = 0.f;
-                for (int ww = 0; ww < kSkinnyWaves; ++ww) sum += red[ww][m][ll][r];
-                v[m] = sum;
-            }
-            const int pair_local = 4 * (ll >> 4) + r, n = ll & 15, t = n >> 1, c = n & 1;
-            const int row = mt * kTileRows + 2 * pair_local + c;
-            if (NMAT == 2) {
-                const float g = v[0] * h2f(a.mat[0].sc[row]);
-                const float u = v[1] * h2f(a.mat[1].sc[row]);
-                float act = g / (1.f + expf(-g)) * u;
-                if (a.sign_i && a.sign_i[row] < 0) act = -act;
-                a.a_out[size_t(t) * N + row] = act;
-            } else if (a.slices == 1) {
-                if (t < a.T) a.y[size_t(t) * N + row] = (uint16_t)f2h(v[0] * h2f(a.mat[0].sc[row]));
-            } else {
-                a.part[(size_t(sl) * kSkinnyT + t) * N + row] = v[0];
-            }
-        }
-    }
-}
-
-template <int NMAT, int TPW>
-static hipError_t launch_skinny_t(const SkinnyArgs& a, hipStream_t st) {
-    const int items = a.slices * (a.mat[0].N / kTileRows);
-    const int grid = items < 256 ? items : 256;
-    hipLaunchKernelGGL((k_skinny<NMAT, TPW>), dim3(grid), dim3(512), 0, st, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st) {
-#define VQ_CASE(NM, TP) \
-    if (a.nmat == NM && a.tpw == TP) return launch_skinny_t<NM, TP>(a, st);
-    VQ_CASE(2, 1) VQ_CASE(2, 2) VQ_CASE(2, 3) VQ_CASE(2, 4) VQ_CASE(2, 5)
-    VQ_CASE(2, 6) VQ_CASE(2, 7) VQ_CASE(2, 8) VQ_CASE(2, 9) VQ_CASE(2, 10)
-    VQ_CASE(1, 1) VQ_CASE(1, 2)
-#undef VQ_CASE
-    return hipErrorInvalidValue;
-}
-
-__global__ void __launch_bounds__(256) k_reduce_down(int T, int N, int slices, const float* part,
-                                                     const uint16_t* sc, uint16_t* y) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= T * N) return;
-    const int t = i / N, row = i % N;
-    float sum = 0.f;
-    for (int s = 0; s < slices; ++s) sum += part[(size_t(s) * kSkinnyT + t) * N + row];
-    y[i] = (uint16_t)f2h(sum * h2f(sc[row]));
-}
-
-hipError_t launch_reduce_down(int T, int N, int slices, const float* part, const uint16_t* sc,
-                              uint16_t* y, hipStream_t st) {
-    hipLaunchKernelGGL(k_reduce_down, dim3((T * N + 255) / 256), dim3(256), 0, st, T, N, slices,
-                       part, sc, y);
     return hipGetLastError();
 }
 

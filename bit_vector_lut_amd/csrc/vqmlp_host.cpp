@@ -115,27 +115,6 @@ vqmlp_status check_header(const PackedHeader& h, int N, int K, uint32_t kind, ui
 }
 
 // code q of tile lane l: pair 16m + l%16, column 64k + 16*(q/4) + 4*(l/16) + q%4
-inline void put6(uint8_t* lane12, int q, unsigned code) {
-    // 96-bit little-endian word; code q occupies bits 6q .. 6q+5
-    const int bit = 6 * q;
-    uint32_t w[3];
-    memcpy(w, lane12, 12);
-    uint64_t lo = (uint64_t(w[1]) << 32) | w[0];
-    uint64_t hi = w[2];
-    if (bit + 6 <= 64) {
-        lo |= uint64_t(code) << bit;
-    } else if (bit >= 64) {
-        hi |= uint64_t(code) << (bit - 64);
-    } else {
-        lo |= uint64_t(code) << bit;
-        hi |= uint64_t(code) >> (64 - bit);
-    }
-    w[0] = uint32_t(lo);
-    w[1] = uint32_t(lo >> 32);
-    w[2] = uint32_t(hi);
-    memcpy(lane12, w, 12);
-}
-
 inline unsigned get6(const uint8_t* lane12, int q) {
     const int bit = 6 * q;
     uint32_t w[3];
@@ -203,11 +182,22 @@ bool skinny_geom(int K, bool need_single, SkinnyGeom* g) {
         g->slices = 1;
         return true;
     }
-    // down: two tiles per wave keeps the operand small and the work items many
-    int tpw = 2;
-    if (KT <= kSkinnyWaves * tpw) tpw = (KT + kSkinnyWaves - 1) / kSkinnyWaves;
-    g->tpw = tpw;
-    g->slices = (KT + kSkinnyWaves * tpw - 1) / (kSkinnyWaves * tpw);
+    // down: K in slices of the waves x tpw tiles (the operand stays in registers);
+    // pick the largest tpw that wastes at most 1/16 of the tile slots past K (long work
+    // items amortise the per-item table build and reduction), else the least wasteful one
+    int best_tpw = 0, least_tpw = 1, least_waste = 1 << 30;
+    for (int tpw = 1; tpw <= kSkinnyMaxTPW; ++tpw) {
+        const int slices = (KT + kSkinnyWaves * tpw - 1) / (kSkinnyWaves * tpw);
+        const int waste = slices * kSkinnyWaves * tpw - KT;
+        if (16 * waste <= slices * kSkinnyWaves * tpw) best_tpw = tpw;
+        if (waste < least_waste) {
+            least_waste = waste;
+            least_tpw = tpw;
+        }
+    }
+    if (!best_tpw) best_tpw = least_tpw;
+    g->tpw = best_tpw;
+    g->slices = (KT + kSkinnyWaves * best_tpw - 1) / (kSkinnyWaves * best_tpw);
     return true;
 }
 
@@ -227,9 +217,9 @@ namespace {
 
 struct Workspace {
     // skinny
-    uint32_t* xexp;   // [H/16][64][4]
+    uint16_t* xb;     // [8][H] binary16 rotated input
     float* a;         // [8][I]
-    uint32_t* aexp;   // [I/16][64][4]
+    uint16_t* ab;     // [8][I] binary16 rotated intermediate
     float* part;      // [slices][8][H]
     // tiled
     uint16_t* xt;     // [T][H]
@@ -250,9 +240,9 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
     };
     uint8_t* b = static_cast<uint8_t*>(base);
     // skinny region
-    size_t o_xexp = take(size_t(H) * 64);
+    size_t o_xb = take(size_t(kSkinnyT) * H * 2);
     size_t o_a = take(size_t(kSkinnyT) * I * 4);
-    size_t o_aexp = take(size_t(I) * 64);
+    size_t o_ab = take(size_t(kSkinnyT) * I * 2);
     size_t o_part = take(size_t(p->g_dn.slices) * kSkinnyT * H * 4);
     size_t skinny_end = off;
     // tiled region overlaps the skinny one (a forward uses one of them)
@@ -264,9 +254,9 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
     size_t tiled_end = off;
     w.bytes = skinny_end > tiled_end ? skinny_end : tiled_end;
     if (b) {
-        w.xexp = reinterpret_cast<uint32_t*>(b + o_xexp);
+        w.xb = reinterpret_cast<uint16_t*>(b + o_xb);
         w.a = reinterpret_cast<float*>(b + o_a);
-        w.aexp = reinterpret_cast<uint32_t*>(b + o_aexp);
+        w.ab = reinterpret_cast<uint16_t*>(b + o_ab);
         w.part = reinterpret_cast<float*>(b + o_part);
         w.xt = reinterpret_cast<uint16_t*>(b + o_xt);
         w.a_t = reinterpret_cast<float*>(b + o_at32);
@@ -278,7 +268,7 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
 vqmlp_status run_skinny(const vqmlp_plan* p, int T, const void* x, void* y, const Workspace& w,
                         hipStream_t st) {
     const int H = p->d.H, I = p->d.I;
-    hipError_t e = launch_rotate(T, H, p->bh, x, 0, p->d.s_in, p->d.sign_h, w.xexp, 2, st);
+    hipError_t e = launch_rotate(T, H, p->bh, x, 0, p->d.s_in, p->d.sign_h, w.xb, 3, st);
     if (e != hipSuccess) return hip_fail(e, "rotate (input)");
     SkinnyArgs a;
     memset(&a, 0, sizeof a);
@@ -288,12 +278,13 @@ vqmlp_status run_skinny(const vqmlp_plan* p, int T, const void* x, void* y, cons
     a.T = T;
     a.slices = 1;
     a.tpw = p->g_gu.tpw;
-    a.bexp = w.xexp;
+    a.contig = 0;
+    a.bx = w.xb;
     a.sign_i = p->d.sign_i;
     a.a_out = w.a;
     e = launch_skinny(a, st);
     if (e != hipSuccess) return hip_fail(e, "skinny gate/up");
-    e = launch_rotate(T, I, p->bi, w.a, 1, nullptr, nullptr, w.aexp, 2, st);
+    e = launch_rotate(T, I, p->bi, w.a, 1, nullptr, nullptr, w.ab, 3, st);
     if (e != hipSuccess) return hip_fail(e, "rotate (intermediate)");
     SkinnyArgs d;
     memset(&d, 0, sizeof d);
@@ -302,7 +293,8 @@ vqmlp_status run_skinny(const vqmlp_plan* p, int T, const void* x, void* y, cons
     d.T = T;
     d.slices = p->g_dn.slices;
     d.tpw = p->g_dn.tpw;
-    d.bexp = w.aexp;
+    d.contig = 1;
+    d.bx = w.ab;
     d.part = w.part;
     d.y = static_cast<uint16_t*>(y);
     e = launch_skinny(d, st);
@@ -388,11 +380,23 @@ vqmlp_status vqmlp_pack(int N, int K, const uint8_t* codes, const uint16_t* code
             uint8_t* tile = tiles + (size_t(m) * KT + k) * kTileBytes;
             for (int l = 0; l < 64; ++l) {
                 const int pair = m * kTilePairs + (l % 16);
-                const uint8_t* crow = codes + size_t(pair) * K;
+                const uint8_t* c = codes + size_t(pair) * K + size_t(k) * kTileCols + 4 * (l / 16);
+                // 16 codes: q = 4s + i at bits 6q..6q+5 of a 96-bit little-endian word
+                uint64_t lo = 0, hi = 0;
                 for (int q = 0; q < 16; ++q) {
-                    const int col = k * kTileCols + 16 * (q / 4) + 4 * (l / 16) + (q % 4);
-                    put6(tile + 12 * l, q, crow[col]);
+                    const uint64_t v = c[16 * (q / 4) + (q % 4)];
+                    const int bit = 6 * q;
+                    if (bit + 6 <= 64) {
+                        lo |= v << bit;
+                    } else if (bit >= 64) {
+                        hi |= v << (bit - 64);
+                    } else {
+                        lo |= v << bit;
+                        hi |= v >> (64 - bit);
+                    }
                 }
+                const uint32_t w[3] = {uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi)};
+                memcpy(tile + 12 * l, w, 12);
             }
         }
     memcpy(out + L.cb_off, codebook, L.cb_bytes);
