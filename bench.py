@@ -165,27 +165,44 @@ def main():
     # ---------------------------------------------------------------- T = 512 prefill MLP
     if not args.no_t512:
         del ys
-        L5, _, _ = synth.config5()
+        L5, p2, p4 = synth.config5()
         m5 = vqmlp.MLP.from_layer(L5, device=device, t_max=512)
+        mixers = [vqmlp.LUTProjection.from_proj(p, device) for p in (p2, p4)]
         x5 = vqmlp.to_device(L5.x, device)
         y5 = torch.empty_like(x5)
         ws5 = m5.workspace(512)
-        for _ in range(3):
-            m5.forward(x5, y5, ws5)
-        torch.cuda.synchronize()
+        ym = [torch.empty((512, p.N), dtype=x5.dtype, device=device) for p in (p2, p4)]
+        wsm = [mx.workspace(512) for mx in mixers]
         reps = 10
-        e0.record()
-        for _ in range(reps):
-            m5.forward(x5, y5, ws5)
-        e1.record()
-        torch.cuda.synchronize()
-        ms5 = e0.elapsed_time(e1) / reps
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        ms5 = timed(lambda: m5.forward(x5, y5, ws5))
+        ms_mix = [timed(lambda mx=mx, y=y, w=w: mx.forward(x5, y, w))
+                  for mx, y, w in zip(mixers, ym, wsm)]
         flops = 2.0 * 512 * 3 * H * I
         tf = flops / (ms5 * 1e-3) / 1e12
         log("T=512 MLP: %.1f us, %.1f TFLOP/s" % (ms5 * 1e3, tf))
         result["t512"] = {"workload": "27B-like VQ3 MLP prefill, T=512", "us": round(ms5 * 1e3, 1),
                           "tflops": round(tf, 1), "peak_tflops": MFMA_F16_PEAK_TFLOPS,
-                          "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+                          "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "token_mixers": []}
+        for p, ms in zip((p2, p4), ms_mix):
+            fl = 2.0 * 512 * (p.N * p.K + p.rank * (p.N + p.K))
+            tfm = fl / (ms * 1e-3) / 1e12
+            log("T=512 %d-bit mixer %dx%d r=%d: %.1f us, %.1f TFLOP/s" % (p.bits, p.N, p.K, p.rank,
+                                                                         ms * 1e3, tfm))
+            result["t512"]["token_mixers"].append(
+                {"bits": p.bits, "N": p.N, "K": p.K, "rank": p.rank, "us": round(ms * 1e3, 1),
+                 "tflops": round(tfm, 1), "frac": round(tfm / MFMA_F16_PEAK_TFLOPS, 4)})
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu:

@@ -64,15 +64,32 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st);
 hipError_t launch_reduce_down(int T, int N, int slices, const float* part, const uint16_t* sc,
                               uint16_t* y, hipStream_t st);
 
-struct TiledArgs {
-    VQ3View mat[2];
-    int nmat;
-    int T;
-    const uint16_t* xt;    // [T][K] binary16 operand
-    const int8_t* sign_i;
-    float* a_out;          // gate+up: [T][I] fp32
-    uint16_t* y;           // down: [T][N] binary16
+// ---- tiled matrix-core path (T > 8): decoders, epilogues, kinds
+enum { kDecVQ3 = 0, kDecLUT2 = 1, kDecLUT4 = 2, kDecDense = 3 };
+enum { kEgGateUp32 = 0, kEgGateUpRot = 1, kEgScale16 = 2, kEgLUT = 3, kEgPlain32 = 4 };
+enum {
+    kGemmVQ3GateUp = 0,     // gate+up -> a fp32 [T][N] (sign applied)
+    kGemmVQ3GateUpRot = 1,  // gate+up -> rotated a binary16 [T][N] (128-wide blocks)
+    kGemmVQ3Down = 2,       // down -> y binary16 [T][N]
+    kGemmLUT2 = 3,          // scalar LUT 2-bit + rank-r factors -> y binary16
+    kGemmLUT4 = 4,          // scalar LUT 4-bit + rank-r factors -> y binary16
+    kGemmDense32 = 5        // dense binary16 rows -> fp32 [T][N]
 };
-hipError_t launch_tiled(const TiledArgs& a, hipStream_t st);
+struct GemmArgs {
+    int kind, N, K, T;
+    const uint16_t* x;         // [T][K] binary16
+    const uint8_t* codes[2];   // packed code sections
+    const uint32_t* cb[2];     // VQ3 codebooks / LUT tables (binary16 pairs)
+    const uint16_t* sc[2];     // row scales
+    const uint16_t* dense;     // dense rows [N][K]
+    const int8_t* sign;        // intermediate rotation sign (gate+up)
+    float* out32;
+    uint16_t* out16;
+    const float* z;            // rank-r activations [T][r]
+    const uint16_t* U;         // rank-r factor [N][r]
+    int r;
+    float norm;                // 1/sqrt(rotation block)
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 
 }  // namespace vqmlp

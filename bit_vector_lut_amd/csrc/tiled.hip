@@ -1,0 +1,384 @@
+// tiled.hip -- matrix-core GEMM with on-the-fly weight decoding, for T > 8 rows (gfx950).
+//
+//   D[t][n] = sum_k X[t][k] W[n][k],   X binary16 [T][K] (rotated activations), W decoded per tile.
+//
+// Decoders (one 64-column K tile of BN rows at a time, into LDS as binary16):
+//   VQ3   model card "anemll/anemll-forge-qwen3.8-27B", section "Release 0.2: three-bit MLP,
+//         token-mixer rotations, distilled weights": six-bit codes select (W[2p][j], W[2p+1][j])
+//         from 64 two-component centroids per 8 rows (the packed tile layout of the library);
+//   LUT2 / LUT4   same card, format table row "Token mixers": two- and four-bit lookup tables,
+//         one table of 2^bits binary16 scalars per 8 rows;
+//   DENSE binary16 rows (the rank-r factor V).
+// Row scales are applied to the accumulators in the epilogue (exact in real arithmetic).
+//
+// Work: a workgroup of 8 waves owns BM tokens x BN rows (of each of NMAT matrices sharing X).
+// Waves form a 2 x 4 grid; each wave holds (BM/2) x (BN/4) outputs per matrix as 16x16 fp32
+// tiles of v_mfma_f32_16x16x32_f16.  The K loop is double-buffered: while the matrix cores work
+// on tile k from LDS, the raw bytes of tile k+1 are already in registers and are decoded into
+// the other LDS buffer afterwards.
+#include "device.h"
+#include "internal.h"
+
+namespace vqmlp {
+
+constexpr int kGK = 64;        // K tile
+constexpr int kGPad = 8;       // LDS row padding (halves)
+constexpr int kGThreads = 512;
+
+template <int DEC>
+struct DecTraits;
+template <> struct DecTraits<kDecVQ3> { static constexpr int bits = 6; };
+template <> struct DecTraits<kDecLUT2> { static constexpr int bits = 2; };
+template <> struct DecTraits<kDecLUT4> { static constexpr int bits = 4; };
+template <> struct DecTraits<kDecDense> { static constexpr int bits = 16; };
+
+template <int BM, int BN, int NMAT, int DEC, int EPI>
+__global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
+    constexpr int LDK = kGK + kGPad;
+    constexpr int WM = BM / 2, WN = BN / 4;   // per-wave outputs per matrix
+    constexpr int TM = WM / 16, TN = WN / 16;  // 16x16 tiles per wave per matrix
+    static_assert(TM >= 1 && TN >= 1, "tile too small");
+    __shared__ __attribute__((aligned(16))) uint16_t Xs[2][BM][LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[2][NMAT][BN][LDK];
+    // VQ3: NMAT x (BN/8) groups x 64 dwords; LUT: (BN/8) x 16 halves
+    __shared__ uint32_t tabs[DEC == kDecVQ3 ? NMAT * (BN / 8) * 64 : (BN / 8) * 8];
+
+    const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+    const int N = a.N, K = a.K, T = a.T;
+    const int KT = K / kGK;
+    const int row0 = blockIdx.x * BN, tok0 = blockIdx.y * BM;
+    const int wm = w >> 2, wn = w & 3;
+
+    // ---- tables
+    if constexpr (DEC == kDecVQ3) {
+        for (int i = tid; i < NMAT * (BN / 8) * 64; i += kGThreads) {
+            const int m = i / ((BN / 8) * 64), r = i % ((BN / 8) * 64);
+            tabs[i] = a.cb[m][size_t(row0 / 8) * 64 + r];
+        }
+    } else if constexpr (DEC == kDecLUT2 || DEC == kDecLUT4) {
+        constexpr int E = 1 << DecTraits<DEC>::bits;
+        const uint16_t* lut = reinterpret_cast<const uint16_t*>(a.cb[0]);
+        uint16_t* t16 = reinterpret_cast<uint16_t*>(tabs);
+        for (int i = tid; i < (BN / 8) * E; i += kGThreads)
+            t16[(i / E) * 16 + (i % E)] = lut[size_t(row0 / 8) * E + i];
+    }
+
+    // ---- per-thread global fetch of one K tile
+    // X: BM x 64 halves = BM*8 chunks of 16 bytes
+    constexpr int XCH = BM * 8 / kGThreads;  // 16-byte chunks per thread
+    u32x4 xr[XCH];
+    // weights: VQ3 -> NMAT*(BN/32) packed tiles x 64 lanes x 12 B (one lane record per thread);
+    // LUT2 -> BN rows x 4 words (16 codes each); LUT4 -> BN rows x 8 words (2 per task);
+    // DENSE -> BN rows x 64 halves (8 chunks of 16 B per row)
+    constexpr int WTASKS = DEC == kDecVQ3 ? NMAT * (BN / 32) * 64
+                         : DEC == kDecLUT2 ? BN * 4
+                         : DEC == kDecLUT4 ? BN * 4
+                                           : BN * 8;
+    constexpr int WPT = (WTASKS + kGThreads - 1) / kGThreads;
+    uint32_t wr[WPT][4];
+
+    auto fetch = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) {
+            const int c = tid + i * kGThreads;
+            const int tt = c >> 3, c8 = (c & 7) * 8;
+            const int tok = tok0 + tt;
+            const uint16_t* src = a.x + size_t(tok < T ? tok : T - 1) * K + kt * kGK + c8;
+            xr[i] = *reinterpret_cast<const u32x4*>(src);
+            if (tok >= T) xr[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int task = tid + i * kGThreads;
+            if (task >= WTASKS) break;
+            if constexpr (DEC == kDecVQ3) {
+                const int m = task / ((BN / 32) * 64), pt = (task / 64) % (BN / 32), ll = task & 63;
+                const int mt = row0 / 32 + pt;
+                const uint32_t* p = reinterpret_cast<const uint32_t*>(
+                    a.codes[m] + (size_t(mt) * KT + kt) * kTileBytes) + 3 * ll;
+                wr[i][0] = p[0];
+                wr[i][1] = p[1];
+                wr[i][2] = p[2];
+            } else if constexpr (DEC == kDecLUT2) {
+                const int r = task >> 2, q = task & 3;  // 16 codes per word
+                const uint32_t* p = reinterpret_cast<const uint32_t*>(a.codes[0]) +
+                                    (size_t(row0 + r) * K + kt * kGK) / 16 + q;
+                wr[i][0] = p[0];
+            } else if constexpr (DEC == kDecLUT4) {
+                const int r = task >> 2, q = task & 3;  // 2 words = 16 codes per task
+                const uint32_t* p = reinterpret_cast<const uint32_t*>(a.codes[0]) +
+                                    (size_t(row0 + r) * K + kt * kGK) / 8 + 2 * q;
+                wr[i][0] = p[0];
+                wr[i][1] = p[1];
+            } else {
+                const int r = task >> 3, c8 = (task & 7) * 8;
+                const int row = row0 + r < N ? row0 + r : N - 1;
+                const u32x4 v = *reinterpret_cast<const u32x4*>(a.dense + size_t(row) * K +
+                                                                  kt * kGK + c8);
+                wr[i][0] = v[0];
+                wr[i][1] = v[1];
+                wr[i][2] = v[2];
+                wr[i][3] = v[3];
+            }
+        }
+    };
+
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) {
+            const int c = tid + i * kGThreads;
+            *reinterpret_cast<u32x4*>(&Xs[buf][c >> 3][(c & 7) * 8]) = xr[i];
+        }
+#pragma unroll
+        for (int i = 0; i < WPT; ++i) {
+            const int task = tid + i * kGThreads;
+            if (task >= WTASKS) break;
+            if constexpr (DEC == kDecVQ3) {
+                const int m = task / ((BN / 32) * 64), pt = (task / 64) % (BN / 32), ll = task & 63;
+                const int pl = pt * 16 + (ll & 15);  // row pair within the block
+                const uint32_t* tg = &tabs[(m * (BN / 8) + (pl >> 2)) * 64];
+                const uint32_t d0 = wr[i][0], d1 = wr[i][1], d2 = wr[i][2];
+                uint16_t* re = &Ws[buf][m][2 * pl][0];
+                uint16_t* ro = &Ws[buf][m][2 * pl + 1][0];
+                const int cb4 = 4 * (ll >> 4);
+#define VQ_STEP(S)                                                                   \
+    {                                                                                \
+        const uint32_t e0 = tg[code_of<4 * S + 0>(d0, d1, d2)];                      \
+        const uint32_t e1 = tg[code_of<4 * S + 1>(d0, d1, d2)];                      \
+        const uint32_t e2 = tg[code_of<4 * S + 2>(d0, d1, d2)];                      \
+        const uint32_t e3 = tg[code_of<4 * S + 3>(d0, d1, d2)];                      \
+        const u32x2 ev = u32x2{__builtin_amdgcn_perm(e1, e0, 0x05040100u),           \
+                               __builtin_amdgcn_perm(e3, e2, 0x05040100u)};          \
+        const u32x2 ov = u32x2{__builtin_amdgcn_perm(e1, e0, 0x07060302u),           \
+                               __builtin_amdgcn_perm(e3, e2, 0x07060302u)};          \
+        *reinterpret_cast<u32x2*>(re + 16 * S + cb4) = ev;                           \
+        *reinterpret_cast<u32x2*>(ro + 16 * S + cb4) = ov;                           \
+    }
+                VQ_STEP(0) VQ_STEP(1) VQ_STEP(2) VQ_STEP(3)
+#undef VQ_STEP
+            } else if constexpr (DEC == kDecLUT2 || DEC == kDecLUT4) {
+                constexpr int B = DecTraits<DEC>::bits;
+                const int r = task >> 2, q = task & 3;
+                const uint16_t* t16 = reinterpret_cast<const uint16_t*>(tabs) + (r >> 3) * 16;
+                uint32_t out[8];
+#pragma unroll
+                for (int h = 0; h < 8; ++h) {
+                    const int j0 = 2 * h, j1 = 2 * h + 1;  // code index within the 16
+                    const uint32_t w0 = B == 2 ? wr[i][0] : wr[i][j0 >> 3];
+                    const uint32_t w1 = B == 2 ? wr[i][0] : wr[i][j1 >> 3];
+                    const uint32_t c0 = (w0 >> (B * (j0 & (32 / B - 1)))) & ((1u << B) - 1);
+                    const uint32_t c1 = (w1 >> (B * (j1 & (32 / B - 1)))) & ((1u << B) - 1);
+                    out[h] = uint32_t(t16[c0]) | (uint32_t(t16[c1]) << 16);
+                }
+                uint16_t* dst = &Ws[buf][0][r][16 * q];
+                *reinterpret_cast<u32x4*>(dst) = u32x4{out[0], out[1], out[2], out[3]};
+                *reinterpret_cast<u32x4*>(dst + 8) = u32x4{out[4], out[5], out[6], out[7]};
+            } else {
+                const int r = task >> 3, c8 = (task & 7) * 8;
+                *reinterpret_cast<u32x4*>(&Ws[buf][0][r][c8]) =
+                    u32x4{wr[i][0], wr[i][1], wr[i][2], wr[i][3]};
+            }
+        }
+    };
+
+    f32x4 acc[NMAT][TM][TN];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int ks = 0; ks < kGK / 32; ++ks) {
+            const int kk = ks * 32 + 8 * (l >> 4);
+            u32x4 A[TM];
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+                A[i] = *reinterpret_cast<const u32x4*>(&Xs[buf][wm * WM + 16 * i + (l & 15)][kk]);
+#pragma unroll
+            for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const u32x4 Bv =
+                        *reinterpret_cast<const u32x4*>(&Ws[buf][m][wn * WN + 16 * j + (l & 15)][kk]);
+#pragma unroll
+                    for (int i = 0; i < TM; ++i) acc[m][i][j] = mfma16x16x32(A[i], Bv, acc[m][i][j]);
+                }
+        }
+    };
+
+    __syncthreads();  // tables
+    fetch(0);
+    stage(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < KT) fetch(kt + 1);
+        compute(buf);
+        if (kt + 1 < KT) stage(buf ^ 1);
+        __syncthreads();
+    }
+
+    // ---- epilogues.  Lane l, register r of tile (i, j) holds D[token][row] with
+    // token = tok0 + wm*WM + 16 i + 4 (l/16) + r and row = row0 + wn*WN + 16 j + l%16.
+    if constexpr (EPI == kEgLUT) {
+        // scale, then add the rank-r product z U^T as one more K tile (z in X, U in W)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const float s = h2f(a.sc[0][row0 + wn * WN + 16 * j + (l & 15)]);
+#pragma unroll
+            for (int i = 0; i < TM; ++i) acc[0][i][j] *= s;
+        }
+        for (int kr = 0; kr < a.r; kr += kGK) {
+            for (int c = tid; c < BM * 8; c += kGThreads) {
+                const int tt = c >> 3, c8 = (c & 7) * 8, tok = tok0 + tt;
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float z0 = 0.f, z1 = 0.f;
+                    if (tok < T && kr + c8 + 2 * e < a.r) z0 = a.z[size_t(tok) * a.r + kr + c8 + 2 * e];
+                    if (tok < T && kr + c8 + 2 * e + 1 < a.r) z1 = a.z[size_t(tok) * a.r + kr + c8 + 2 * e + 1];
+                    h[e] = f2h(z0) | (f2h(z1) << 16);
+                }
+                *reinterpret_cast<u32x4*>(&Xs[0][tt][c8]) = u32x4{h[0], h[1], h[2], h[3]};
+            }
+            for (int c = tid; c < BN * 8; c += kGThreads) {
+                const int rr = c >> 3, c8 = (c & 7) * 8;
+                uint32_t h[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int q0 = kr + c8 + 2 * e;
+                    const uint32_t u0 = q0 < a.r ? a.U[size_t(row0 + rr) * a.r + q0] : 0u;
+                    const uint32_t u1 = q0 + 1 < a.r ? a.U[size_t(row0 + rr) * a.r + q0 + 1] : 0u;
+                    h[e] = u0 | (u1 << 16);
+                }
+                *reinterpret_cast<u32x4*>(&Ws[0][0][rr][c8]) = u32x4{h[0], h[1], h[2], h[3]};
+            }
+            __syncthreads();
+            compute(0);
+            __syncthreads();
+        }
+    }
+
+    if constexpr (EPI == kEgGateUpRot) {
+        // a = silu(g) u sign for BM tokens x BN (= one rotation block) rows, then the block
+        // Hadamard transform along the rows in LDS (fp32, reusing the W buffers)
+        static_assert(NMAT == 2, "gate+up");
+        float* Ab = reinterpret_cast<float*>(&Ws[0][0][0][0]);  // [BM][BN + 1]
+        static_assert(sizeof(Ws) >= sizeof(float) * BM * (BN + 1), "LDS for the rotation");
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+            const int rl = wn * WN + 16 * j + (l & 15);
+            const int row = row0 + rl;
+            const float sg = h2f(a.sc[0][row]), su = h2f(a.sc[1][row]);
+            const bool neg = a.sign && a.sign[row] < 0;
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int tl = wm * WM + 16 * i + 4 * (l >> 4) + r;
+                    const float g = acc[0][i][j][r] * sg, u = acc[1][i][j][r] * su;
+                    float v = g / (1.f + expf(-g)) * u;
+                    Ab[tl * (BN + 1) + rl] = neg ? -v : v;
+                }
+        }
+        __syncthreads();
+        for (int h = 1; h < BN; h <<= 1) {
+            for (int i = tid; i < BM * (BN / 2); i += kGThreads) {
+                const int tl = i / (BN / 2), jj = i % (BN / 2);
+                const int lo = (jj / h) * 2 * h + (jj % h), hi = lo + h;
+                const float x0 = Ab[tl * (BN + 1) + lo], x1 = Ab[tl * (BN + 1) + hi];
+                Ab[tl * (BN + 1) + lo] = x0 + x1;
+                Ab[tl * (BN + 1) + hi] = x0 - x1;
+            }
+            __syncthreads();
+        }
+        for (int i = tid; i < BM * BN / 2; i += kGThreads) {
+            const int tl = i / (BN / 2), cc = (i % (BN / 2)) * 2;
+            const int tok = tok0 + tl;
+            if (tok < T) {
+                const uint32_t h = f2h(Ab[tl * (BN + 1) + cc] * a.norm) |
+                                   (f2h(Ab[tl * (BN + 1) + cc + 1] * a.norm) << 16);
+                *reinterpret_cast<uint32_t*>(a.out16 + size_t(tok) * N + row0 + cc) = h;
+            }
+        }
+        return;
+    }
+
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int row = row0 + wn * WN + 16 * j + (l & 15);
+        if (row >= N) continue;
+        float s0 = 1.f, s1 = 1.f;
+        bool neg = false;
+        if constexpr (EPI == kEgGateUp32) {
+            s0 = h2f(a.sc[0][row]);
+            s1 = h2f(a.sc[1][row]);
+            neg = a.sign && a.sign[row] < 0;
+        } else if constexpr (EPI == kEgScale16) {
+            s0 = h2f(a.sc[0][row]);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = tok0 + wm * WM + 16 * i + 4 * (l >> 4) + r;
+                if (tok >= T) continue;
+                const float v0 = acc[0][i][j][r];
+                if constexpr (EPI == kEgGateUp32) {
+                    const float g = v0 * s0, u = acc[NMAT - 1][i][j][r] * s1;
+                    const float act = g / (1.f + expf(-g)) * u;
+                    a.out32[size_t(tok) * N + row] = neg ? -act : act;
+                } else if constexpr (EPI == kEgScale16 || EPI == kEgLUT) {
+                    a.out16[size_t(tok) * N + row] = (uint16_t)f2h(v0 * s0);
+                } else {
+                    a.out32[size_t(tok) * N + row] = v0;
+                }
+            }
+    }
+}
+
+template <int BM, int BN, int NMAT, int DEC, int EPI>
+static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t st) {
+    const dim3 grid((a.N + BN - 1) / BN, (a.T + BM - 1) / BM);
+    hipLaunchKernelGGL((k_gemm<BM, BN, NMAT, DEC, EPI>), grid, dim3(kGThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
+    if (a.T <= 0) return hipSuccess;
+    if (a.K % kGK || a.N <= 0) return hipErrorInvalidValue;
+    // only the dense decoder clamps its rows; the coded ones need whole 64-row tiles
+    if (a.kind != kGemmDense32 && a.N % 64) return hipErrorInvalidValue;
+    const bool big = a.T > 64;          // 128-token tiles beyond one 64-row chunk
+    const bool n128 = a.N % 128 == 0;   // 128-row tiles where the rows allow it
+#define VQ_BM_BN(NM, DEC, EPI)                                                              \
+    (big ? (n128 ? launch_gemm_t<128, 128, NM, DEC, EPI>(a, st)                             \
+                 : launch_gemm_t<128, 64, NM, DEC, EPI>(a, st))                             \
+         : (n128 ? launch_gemm_t<64, 128, NM, DEC, EPI>(a, st)                              \
+                 : launch_gemm_t<64, 64, NM, DEC, EPI>(a, st)))
+    switch (a.kind) {
+        case kGemmVQ3GateUp:
+            return VQ_BM_BN(2, kDecVQ3, kEgGateUp32);
+        case kGemmVQ3GateUpRot:  // the rotation block is the 128-row tile
+            if (!n128) return hipErrorInvalidValue;
+            return big ? launch_gemm_t<128, 128, 2, kDecVQ3, kEgGateUpRot>(a, st)
+                       : launch_gemm_t<64, 128, 2, kDecVQ3, kEgGateUpRot>(a, st);
+        case kGemmVQ3Down:  // 64-row tiles: the down projection has few rows
+            return big ? launch_gemm_t<128, 64, 1, kDecVQ3, kEgScale16>(a, st)
+                       : launch_gemm_t<64, 64, 1, kDecVQ3, kEgScale16>(a, st);
+        case kGemmLUT2:
+            return VQ_BM_BN(1, kDecLUT2, kEgLUT);
+        case kGemmLUT4:
+            return VQ_BM_BN(1, kDecLUT4, kEgLUT);
+        case kGemmDense32:
+            return big ? launch_gemm_t<128, 64, 1, kDecDense, kEgPlain32>(a, st)
+                       : launch_gemm_t<64, 64, 1, kDecDense, kEgPlain32>(a, st);
+    }
+#undef VQ_BM_BN
+    return hipErrorInvalidValue;
+}
+
+}  // namespace vqmlp

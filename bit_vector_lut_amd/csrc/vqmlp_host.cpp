@@ -311,27 +311,47 @@ vqmlp_status run_tiled(const vqmlp_plan* p, int T, const void* x, void* y, const
     const int H = p->d.H, I = p->d.I;
     hipError_t e = launch_rotate(T, H, p->bh, x, 0, p->d.s_in, p->d.sign_h, w.xt, 1, st);
     if (e != hipSuccess) return hip_fail(e, "rotate (input)");
-    TiledArgs a;
-    memset(&a, 0, sizeof a);
-    a.mat[0] = p->gate;
-    a.mat[1] = p->up;
-    a.nmat = 2;
-    a.T = T;
-    a.xt = w.xt;
-    a.sign_i = p->d.sign_i;
-    a.a_out = w.a_t;
-    e = launch_tiled(a, st);
-    if (e != hipSuccess) return hip_fail(e, "tiled gate/up");
-    e = launch_rotate(T, I, p->bi, w.a_t, 1, nullptr, nullptr, w.at, 1, st);
-    if (e != hipSuccess) return hip_fail(e, "rotate (intermediate)");
-    TiledArgs d;
+    GemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.N = I;
+    g.K = H;
+    g.T = T;
+    g.x = w.xt;
+    g.codes[0] = p->gate.codes;
+    g.codes[1] = p->up.codes;
+    g.cb[0] = p->gate.cb;
+    g.cb[1] = p->up.cb;
+    g.sc[0] = p->gate.sc;
+    g.sc[1] = p->up.sc;
+    g.sign = p->d.sign_i;
+    // the gate/up epilogue rotates a itself when a rotation block is one 128-row tile
+    const bool fused_rot = p->bi == 128 && I % 128 == 0;
+    if (fused_rot) {
+        g.kind = kGemmVQ3GateUpRot;
+        g.out16 = w.at;
+        g.norm = float(1.0 / 11.313708498984761);  // 1/sqrt(128)
+        e = launch_gemm(g, st);
+        if (e != hipSuccess) return hip_fail(e, "tiled gate/up");
+    } else {
+        g.kind = kGemmVQ3GateUp;
+        g.out32 = w.a_t;
+        e = launch_gemm(g, st);
+        if (e != hipSuccess) return hip_fail(e, "tiled gate/up");
+        e = launch_rotate(T, I, p->bi, w.a_t, 1, nullptr, nullptr, w.at, 1, st);
+        if (e != hipSuccess) return hip_fail(e, "rotate (intermediate)");
+    }
+    GemmArgs d;
     memset(&d, 0, sizeof d);
-    d.mat[0] = p->down;
-    d.nmat = 1;
+    d.kind = kGemmVQ3Down;
+    d.N = H;
+    d.K = I;
     d.T = T;
-    d.xt = w.at;
-    d.y = static_cast<uint16_t*>(y);
-    e = launch_tiled(d, st);
+    d.x = w.at;
+    d.codes[0] = p->down.codes;
+    d.cb[0] = p->down.cb;
+    d.sc[0] = p->down.sc;
+    d.out16 = static_cast<uint16_t*>(y);
+    e = launch_gemm(d, st);
     if (e != hipSuccess) return hip_fail(e, "tiled down");
     return ok();
 }
@@ -664,10 +684,72 @@ vqmlp_status vqmlp_lut_workspace_bytes(int N, int K, int T, int r, size_t* bytes
     return ok();
 }
 
-vqmlp_status vqmlp_lut_forward(int, int, int, int, const void*, const uint16_t*, const uint16_t*,
-                               int, const uint16_t*, const int8_t*, int, const void*, void*, void*,
-                               size_t, void*) {
-    return fail(VQMLP_ERR_UNSUPPORTED, "vqmlp_lut_forward: not built yet");
+vqmlp_status vqmlp_lut_forward(int bits, int N, int K, int T, const void* packed,
+                               const uint16_t* U, const uint16_t* V, int r, const uint16_t* s,
+                               const int8_t* sign, int had_block, const void* x, void* y,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    vqmlp_status st = lut_shape(bits, N, K);
+    if (st) return st;
+    if (T < 0 || r < 0 || r > 256)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_forward: T=%d r=%d", T, r);
+    if (had_block && (!is_pow2(had_block) || had_block < 2 || had_block > 1024 || K % had_block))
+        return fail(VQMLP_ERR_INVALID_ARG, "Hadamard block %d does not divide K=%d", had_block, K);
+    if (T == 0) return ok();
+    if (!packed || !x || !y || !workspace)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_forward: null pointer");
+    if (r > 0 && (!U || !V))
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_forward: r=%d needs U and V", r);
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256) ||
+        (U && !aligned(U, 16)) || (V && !aligned(V, 16)))
+        return fail(VQMLP_ERR_INVALID_ARG, "x, y, U, V must be 16-byte aligned, the workspace 256");
+    size_t need = 0;
+    vqmlp_lut_workspace_bytes(N, K, T, r, &need);
+    if (workspace_bytes < need)
+        return fail(VQMLP_ERR_WORKSPACE, "workspace holds %zu bytes, this forward needs %zu",
+                    workspace_bytes, need);
+    if ((st = check_device())) return st;
+    const Layout L = lut_layout(bits, N, K);
+    PackedHeader h;
+    if ((st = read_device_header(packed, &h, "lut"))) return st;
+    if ((st = check_header(h, N, K, uint32_t(bits), 1u << bits, L, "lut"))) return st;
+    uint8_t* wb = static_cast<uint8_t*>(workspace) + 256;
+    uint16_t* xt = reinterpret_cast<uint16_t*>(wb);
+    float* z = reinterpret_cast<float*>(wb + align256(size_t(T) * K * 2));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const uint8_t* base = static_cast<const uint8_t*>(packed);
+    // x~ = R(x . s): the rotation kernel with a 1-wide block is the plain scale and sign
+    hipError_t e = launch_rotate(T, K, had_block ? had_block : 1, x, 0, s, sign, xt, 1, hs);
+    if (e != hipSuccess) return hip_fail(e, "rotate (mixer input)");
+    if (r > 0) {
+        GemmArgs g;
+        memset(&g, 0, sizeof g);
+        g.kind = kGemmDense32;
+        g.N = r;
+        g.K = K;
+        g.T = T;
+        g.x = xt;
+        g.dense = V;
+        g.out32 = z;
+        e = launch_gemm(g, hs);
+        if (e != hipSuccess) return hip_fail(e, "rank-r projection");
+    }
+    GemmArgs g;
+    memset(&g, 0, sizeof g);
+    g.kind = bits == 2 ? kGemmLUT2 : kGemmLUT4;
+    g.N = N;
+    g.K = K;
+    g.T = T;
+    g.x = xt;
+    g.codes[0] = base + L.codes_off;
+    g.cb[0] = reinterpret_cast<const uint32_t*>(base + L.cb_off);
+    g.sc[0] = reinterpret_cast<const uint16_t*>(base + L.sc_off);
+    g.z = z;
+    g.U = U;
+    g.r = r;
+    g.out16 = static_cast<uint16_t*>(y);
+    e = launch_gemm(g, hs);
+    if (e != hipSuccess) return hip_fail(e, "scalar-LUT projection");
+    return ok();
 }
 
 }  // extern "C"

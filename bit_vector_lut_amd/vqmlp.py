@@ -234,3 +234,48 @@ class MLP:
         if getattr(self, "_plan", None) and _lib is not None:
             _lib.vqmlp_destroy(self._plan)
             self._plan = None
+
+
+class LUTProjection:
+    """Device-resident scalar-LUT projection (2- or 4-bit codes, group-8 tables, optional
+    rank-r factors) with its input scale, sign and Hadamard block."""
+
+    def __init__(self, bits, N, K, packed, U=None, V=None, s=None, sign=None, had_block=1024):
+        self.bits, self.N, self.K = bits, N, K
+        self.r = 0 if U is None else U.shape[1]
+        self.had_block = had_block
+        self.packed, self.U, self.V, self.s, self.sign = packed, U, V, s, sign
+        self.device = packed.device
+
+    @classmethod
+    def from_proj(cls, proj, device="cuda"):
+        """Pack a ``synth.LUTProjection`` on the host and upload it."""
+        packed = to_device(lut_pack(proj.bits, proj.codes, proj.lut, proj.sc), device)
+        up = lambda a: None if a is None else to_device(a, device)  # noqa: E731
+        return cls(proj.bits, proj.N, proj.K, packed, up(proj.U), up(proj.V), up(proj.s),
+                   up(proj.sign), proj.had_block)
+
+    def workspace_bytes(self, T: int) -> int:
+        n = C.c_size_t()
+        _check(lib().vqmlp_lut_workspace_bytes(self.N, self.K, T, self.r, C.byref(n)))
+        return n.value
+
+    def workspace(self, T: int):
+        import torch
+
+        return torch.zeros(self.workspace_bytes(T), dtype=torch.uint8, device=self.device)
+
+    def forward(self, x, y=None, workspace=None, stream=None):
+        """x: [T, K] int16 (binary16 bits) or float16 device tensor -> y [T, N] (same dtype)."""
+        import torch
+
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.N), dtype=x.dtype, device=x.device)
+        if workspace is None:
+            workspace = self.workspace(T)
+        _check(lib().vqmlp_lut_forward(self.bits, self.N, self.K, T, _dptr(self.packed),
+                                       _dptr(self.U), _dptr(self.V), self.r, _dptr(self.s),
+                                       _dptr(self.sign), self.had_block, _dptr(x), _dptr(y),
+                                       _dptr(workspace), workspace.numel(), _stream(stream)))
+        return y

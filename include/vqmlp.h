@@ -148,8 +148,12 @@ vqmlp_status vqmlp_lut_pack(int bits, int N, int K, const uint8_t *codes /* [N][
 vqmlp_status vqmlp_lut_unpack(int bits, int N, int K, const void *packed, size_t bytes,
                               uint8_t *codes, uint16_t *lut, uint16_t *row_scale);
 vqmlp_status vqmlp_lut_workspace_bytes(int N, int K, int T, int r, size_t *bytes);
-/* x DEVICE binary16 [T][K] -> y DEVICE binary16 [T][N].  packed, U, V, s, sign DEVICE.  U, V
- * NULL or r == 0: no factors.  s, sign NULL: all 1.  had_block 0: no rotation. */
+/* x DEVICE binary16 [T][K] -> y DEVICE binary16 [T][N].  packed, U, V, s, sign DEVICE; x, y,
+ * U, V 16-byte aligned, the workspace 256-byte aligned (no zero fill needed).  r == 0: no
+ * factors (U, V ignored); r > 0 needs both.  s, sign NULL: all 1.  had_block 0: no rotation,
+ * else a power of two in 2..1024 dividing K.  Returns VQMLP_ERR_INVALID_ARG for bad shapes,
+ * pointers or a packed buffer whose header does not match (bits, N, K), VQMLP_ERR_WORKSPACE
+ * when workspace_bytes is below vqmlp_lut_workspace_bytes, VQMLP_ERR_HIP for launch errors. */
 vqmlp_status vqmlp_lut_forward(int bits, int N, int K, int T, const void *packed,
                                const uint16_t *U, const uint16_t *V, int r, const uint16_t *s,
                                const int8_t *sign, int had_block, const void *x, void *y,

@@ -1,7 +1,8 @@
 """GPU parity: the HIP library against the FP64 oracle on identical seeded inputs.
 
-Bars: dequantised weights bit-exact; rotation within 1e-6 relative; MLP outputs within a
-relative Frobenius error of 2e-3 (FP32 accumulation and FP16 operands against FP64).
+Bars: dequantised weights bit-exact; rotation within 1e-6 relative; MLP and scalar-LUT
+projection outputs within a relative Frobenius error of 2e-3 (FP32 accumulation and FP16
+operands against FP64).
 Every call goes through the C ABI (the ctypes binding only marshals arguments).
 """
 import sys
@@ -124,7 +125,7 @@ def test_config1_tiny(vq, oracle_mod, torch_dev, path):
 SMALL = [(256, 704), (128, 192), (512, 1024), (320, 640)]
 
 
-@pytest.mark.parametrize("T", [1, 2, 7, 8, 9, 16, 33, 64, 65])
+@pytest.mark.parametrize("T", [1, 2, 7, 8, 9, 16, 33, 64, 65, 130])
 @pytest.mark.parametrize("H,I", SMALL)
 def test_mlp_small_shapes(vq, oracle_mod, torch_dev, H, I, T):
     L = synth.mlp_layer(H, I, T, seed=H * 31 + I + T, outliers=(T % 2 == 1))
@@ -194,3 +195,78 @@ def test_errors_on_device(vq, torch_dev):
         mlp.forward(vq.to_device(np.zeros((9, 256), np.float16)), path=1)
     empty = vq.to_device(np.zeros((0, 256), np.float16))
     assert mlp.forward(empty).shape == (0, 256)
+
+
+@pytest.fixture(scope="module")
+def config5():
+    return synth.config5()
+
+
+def test_config5_mlp_sampled_tokens(vq, oracle_mod, torch_dev, config5):
+    L = config5[0]
+    _say("config5 MLP T=512")
+    y = _run(vq, torch_dev, L, 0)
+    toks = [0, 1, 127, 128, 300, 511]
+    ref = oracle_mod.mlp_forward(L, tokens=toks)
+    assert _report("config5 MLP", y[toks], ref) <= MLP_TOL
+
+
+# ------------------------------------------------------------------ scalar-LUT projection
+
+LUT_CASES = [  # N, K, T, rank, Hadamard block (0 = none)
+    (64, 1024, 1, 64, 1024),
+    (192, 2048, 9, 40, 1024),
+    (256, 1024, 65, 64, 256),
+    (128, 512, 130, 0, 0),
+    (320, 2048, 33, 128, 512),
+    (64, 64, 3, 64, 64),
+]
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("N,K,T,rank,hb", LUT_CASES)
+def test_lut_small_shapes(vq, oracle_mod, torch_dev, bits, N, K, T, rank, hb):
+    rng = np.random.default_rng(N + 3 * K + 7 * T + bits)
+    p = synth.lut_projection(rng, bits, N, K, rank, hb)
+    x = rng.standard_normal((T, K)).astype(np.float16)
+    _say("lut bits=%d N=%d K=%d T=%d r=%d hb=%d" % (bits, N, K, T, rank, hb))
+    proj = vq.LUTProjection.from_proj(p)
+    y = _f64(proj.forward(vq.to_device(x)))
+    torch_dev.cuda.synchronize()
+    ref = oracle_mod.lut_forward(p, x)
+    assert _report("lut%d N=%d K=%d T=%d" % (bits, N, K, T), y, ref) <= MLP_TOL
+
+
+@pytest.mark.parametrize("which", [1, 2])
+def test_config5_lut_sampled_tokens(vq, oracle_mod, torch_dev, config5, which):
+    L, p = config5[0], config5[which]
+    _say("config5 lut%d T=512" % p.bits)
+    proj = vq.LUTProjection.from_proj(p)
+    y = _f64(proj.forward(vq.to_device(L.x)))
+    torch_dev.cuda.synchronize()
+    toks = [0, 5, 255, 256, 511]
+    ref = oracle_mod.lut_forward(p, L.x, tokens=toks)
+    assert _report("config5 lut%d" % p.bits, y[toks], ref) <= MLP_TOL
+
+
+def test_lut_errors_on_device(vq, torch_dev):
+    rng = np.random.default_rng(5)
+    p = synth.lut_projection(rng, 2, 64, 128, 64, 128)
+    proj = vq.LUTProjection.from_proj(p)
+    x = vq.to_device(rng.standard_normal((4, 128)).astype(np.float16))
+    small = torch_dev.zeros(256, dtype=torch_dev.uint8, device="cuda")
+    with pytest.raises(vq.VqmlpError) as e:
+        proj.forward(x, workspace=small)
+    assert e.value.status == vq.ERR_WORKSPACE
+    proj.bits = 4  # header says 2-bit
+    with pytest.raises(vq.VqmlpError) as e:
+        proj.forward(x)
+    assert e.value.status == vq.ERR_INVALID_ARG
+    proj.bits = 2
+    proj.had_block = 96
+    with pytest.raises(vq.VqmlpError) as e:
+        proj.forward(x)
+    assert e.value.status == vq.ERR_INVALID_ARG
+    proj.had_block = 128
+    empty = vq.to_device(np.zeros((0, 128), np.float16))
+    assert proj.forward(empty).shape == (0, 64)

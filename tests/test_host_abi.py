@@ -144,4 +144,18 @@ def test_null_arguments_are_rejected_without_device(vq):
     assert L.vqmlp_rotate(1, 96, 64, None, None, None, None, None) == vq.ERR_INVALID_ARG
     assert L.vqmlp_rotate(1, 128, 3, None, None, None, None, None) == vq.ERR_INVALID_ARG
     assert L.vqmlp_dequant(48, 64, None, None, None) == vq.ERR_INVALID_ARG
+    lf = L.vqmlp_lut_forward
+    assert lf(3, 64, 64, 1, None, None, None, 0, None, None, 0, None, None, None, 0,
+              None) == vq.ERR_INVALID_ARG  # bits
+    assert lf(2, 32, 64, 1, None, None, None, 0, None, None, 0, None, None, None, 0,
+              None) == vq.ERR_INVALID_ARG  # N % 64
+    assert lf(2, 64, 64, 1, None, None, None, 300, None, None, 0, None, None, None, 0,
+              None) == vq.ERR_INVALID_ARG  # rank
+    assert lf(2, 64, 192, 1, None, None, None, 0, None, None, 128, None, None, None, 0,
+              None) == vq.ERR_INVALID_ARG  # block does not divide K
+    assert lf(2, 64, 64, 0, None, None, None, 0, None, None, 0, None, None, None, 0,
+              None) == vq.OK  # empty batch
+    assert lf(2, 64, 64, 2, None, None, None, 0, None, None, 0, None, None, None, 0,
+              None) == vq.ERR_INVALID_ARG  # null buffers
+    assert L.vqmlp_lut_workspace_bytes(64, 64, 1, 257, C.byref(n)) == vq.ERR_INVALID_ARG
     assert L.vqmlp_last_error() != b""
