@@ -9,13 +9,16 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libvqmlp.so")
-SOURCES = ["vqmlp_host.cpp", "kernels.hip", "skinny.hip", "tiled.hip"]
+SOURCES = ["vqmlp_host.cpp", "kernels.hip", "skinny.hip", "fused.hip", "tiled.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-FP32 VALU forms are kept out of the generated code: hipcc -O3 would otherwise form
 # them from scalar float code by itself.
+# The atomic optimizer is off: it turns a single-lane atomic whose result is used much later into
+# a wave-wide reduction that needs the result at once, which stalls the code stream.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
              "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 

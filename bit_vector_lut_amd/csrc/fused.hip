@@ -1,0 +1,567 @@
+// fused.hip -- the whole T <= 8 MLP forward as one persistent kernel (gfx950).
+//
+//   x~ = R_H(x . s),  a = silu(W_gate x~) . (W_up x~) . sign_I,  y = W_down R_I(a)
+//
+// (model card "anemll/anemll-forge-qwen3.8-27B", section "Release 0.2: three-bit MLP, token-mixer
+// rotations, distilled weights": three-bit 2x64 vector tables for gate, up and down; online
+// block-Hadamard rotations with seeded signs on the MLP inputs.)
+//
+// One workgroup of 16 waves per CU; workgroup b takes streaming items b, b + G, b + 2G, ... (G
+// workgroups) after the input-rotation items r = b, b + G, ...:
+//   R  rotate input columns [r*rc, (r+1)*rc) of x into x~ (binary16), then raise flag r_rdy[r];
+//   G  gate and up of one 32-row tile over all of H (the matrix-core product of the skinny
+//      kernel: lane-private LDS codebooks, register code ring), epilogue silu(g) u sign;
+//   D  down projection of two 32-row tiles over one K slice of 16 * TPW tiles of I.
+// Work that needs several items is done right after the item that completes the set:
+//   F  the last G tile of a rotation unit (max(bi, 32) rows) rotates the unit's a into the
+//      binary16 down operand, then raises fu_rdy[unit];
+//   Y  the D item of the last K slice of a row pair sums the slices, scales and writes y.
+// Items hand data to later items through global memory.  High-volume hand-offs (a, the down
+// partial sums) are stored as 64-bit words {FP32 bits, tag}, tag = call epoch + 1, so the reader
+// checks each word itself and the writer never waits for its stores: on this GPU any wait for
+// a store also waits for every older load, which would drain the code prefetch.  The operand
+// hand-offs that many items read (x~ and the rotated a) use flags: the writer waits for its
+// stores and releases once, the reader acquires once.
+// Every wait is bounded by spin_limit; a wait that runs out sets a bit in the error word and
+// the kernel finishes with wrong values instead of hanging.  No item waits for a later item of
+// its own workgroup and the grid is one workgroup per CU, so every wait ends.
+#include "device.h"
+#include "internal.h"
+
+namespace vqmlp {
+
+namespace {
+
+constexpr int kW = kSkinnyWaves;   // 16 waves
+constexpr int kTab = 64 * 32;      // dwords of one lane-private table set (one tile, one matrix)
+constexpr int kKindG = 0, kKindD = 1, kKindNone = 2;
+
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_relaxed64(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_relaxed64(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void note_error(uint32_t* ctl, uint32_t bit) {
+    __hip_atomic_fetch_or(ctl + kCtlError, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Publish a flag after every thread's plain stores: each wave waits for its own stores to reach
+// L2 (vmcnt counts stores), the workgroup meets, then one thread writes dirty L2 lines back and
+// sets the flag.  One L2 write-back per flag instead of one per wave.
+__device__ __forceinline__ void publish(uint32_t* flag, uint32_t value) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+// Wait until flags[0..n) all equal want (n <= 64, polled by wave 0; bounded), then acquire once
+// and meet: loads after this see what the flags' writers stored.  Returns false on timeout.
+__device__ bool await_flags(const uint32_t* flags, int n, uint32_t want, unsigned limit,
+                            int* s_ok) {
+    if (threadIdx.x < 64) {
+        bool good = true;
+        const int lane = threadIdx.x;
+        if (lane < n) {
+            for (unsigned k = 0;; ++k) {
+                if (ld_relaxed(flags + lane) == want) break;
+                if (k >= limit) {
+                    good = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        const bool all = __all(good);
+        if (lane == 0) *s_ok = all ? 1 : 0;
+    }
+    __syncthreads();
+    return *s_ok != 0;
+}
+__device__ __forceinline__ float dpp_xor1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
+                                                              0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E,
+                                                              0xF, 0xF, false));
+}
+
+// A streaming item, decoded from its queue index (all fields uniform).
+struct Item {
+    int kind;   // kKindG, kKindD or kKindNone
+    int id;     // G: row tile m; D: row pair q
+    int sl;     // K slice (0 for G)
+    int t0, t1; // row tiles of the two operand slots
+    int KT;     // K tiles of the matrix
+};
+
+}  // namespace
+
+template <int TPW>
+__global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
+    constexpr int D = TPW;
+    constexpr int SWT = kW * TPW;  // K tiles per slice
+    constexpr int BROW = SWT * kTileCols + 16;  // padded row of the activation operand
+    // One LDS block with the lookup tables at address 0: a lookup address is then the code and
+    // lane bits alone, with no base to add.
+    constexpr int kOffRed = 2 * 2 * kTab * 4;
+    constexpr int kOffB = kOffRed + kW * 2 * 64 * 16;
+    constexpr int kOffEsc = kOffB + kSkinnyT * BROW * 2;
+    constexpr int kOffEsg = kOffEsc + 4 * 2 * 32 * 4;
+    constexpr int kOffOk = kOffEsg + 4 * 32 * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kOffOk + 16];
+    auto& tab = *reinterpret_cast<uint32_t (*)[2][2][kTab]>(lds);          // [buffer][slot][table]
+    auto& red = *reinterpret_cast<f32x4 (*)[kW][2][64]>(lds + kOffRed);   // partials, scratch
+    auto& bsh = *reinterpret_cast<uint16_t (*)[kSkinnyT][BROW]>(lds + kOffB);  // activations
+    auto& esc = *reinterpret_cast<float (*)[4][2][32]>(lds + kOffEsc);    // row scales
+    auto& esg = *reinterpret_cast<uint32_t (*)[4][32]>(lds + kOffEsg);    // sign bits
+    int& s_ok = *reinterpret_cast<int*>(lds + kOffOk);
+
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H, I = a.I, T = a.T;
+    const int MTh = H / kTileRows, KTh = H / kTileCols, KTi = I / kTileCols;
+    uint32_t* const ctl = a.ctl;
+    uint32_t* const r_rdy = ctl + kCtlHdr;
+    uint32_t* const fu_rdy = r_rdy + a.n_r;
+    const uint32_t tag = ld_relaxed(ctl + kCtlEpoch) + 1u;
+    const unsigned limit = a.spin_limit;
+
+    auto decode = [&](int u) -> Item {
+        Item it;
+        it.sl = 0;
+        if (u < a.n_r || u >= a.total) {
+            it.kind = kKindNone;
+            it.id = 0;
+            it.t0 = it.t1 = 0;
+            it.KT = KTh;
+        } else if (u < a.n_r + a.n_g) {
+            it.kind = kKindG;
+            it.id = u - a.n_r;
+            it.t0 = it.t1 = it.id;
+            it.KT = KTh;
+        } else {
+            const int v = u - a.n_r - a.n_g;
+            it.kind = kKindD;
+            it.sl = v / a.nqd;
+            it.id = v % a.nqd;
+            it.t0 = min(2 * it.id, MTh - 1);
+            it.t1 = min(2 * it.id + 1, MTh - 1);
+            it.KT = KTi;
+        }
+        return it;
+    };
+    // this wave's K tiles of an item: [kt0, kt0 + ntile), loads clamped to last_kt
+    auto wave_tiles = [&](const Item& it, int& kt0, int& ntile, int& last_kt) {
+        kt0 = it.sl * SWT + w * TPW;
+        ntile = it.KT - kt0;
+        ntile = ntile < TPW ? (ntile > 0 ? ntile : 0) : TPW;
+        last_kt = kt0 + (ntile > 0 ? ntile : 1) - 1;
+        last_kt = last_kt < it.KT ? last_kt : it.KT - 1;
+    };
+    auto tile_word = [&](const Item& it, int m, int kt) -> const uint32_t* {
+        const uint8_t* base = it.kind == kKindD ? a.down.codes : (m ? a.up.codes : a.gate.codes);
+        const int mt = m ? it.t1 : it.t0;
+        return reinterpret_cast<const uint32_t*>(base + (size_t(mt) * it.KT + kt) * kTileBytes) +
+               3 * l;
+    };
+
+    // ---- per-item table operands: threads 0..511 one codebook word each (slot, group, entry);
+    // waves 8 and 9 the row scales of slot 0 and 1; wave 10 the signs
+    const int cb_m = (w >> 2) & 1, cb_g = w & 3, cb_c = l;  // slot and group uniform per wave
+    // one register per thread: a codebook word (waves 0-7), a row scale (waves 8, 9) or a sign
+    // (wave 10)
+    auto load_tab = [&](const Item& it) -> uint32_t {
+        uint32_t v = 0u;
+        if (it.kind == kKindNone) return v;
+        if (w < 8) {
+            const uint32_t* cb = it.kind == kKindD ? a.down.cb : (cb_m ? a.up.cb : a.gate.cb);
+            const int mt = cb_m ? it.t1 : it.t0;
+            v = cb[size_t(mt * 4 + cb_g) * 64 + cb_c];
+        } else if ((w == 8 || w == 9) && l < 32) {
+            const int m = w - 8;
+            const uint16_t* sc = it.kind == kKindD ? a.down.sc : (m ? a.up.sc : a.gate.sc);
+            v = sc[(m ? it.t1 : it.t0) * kTileRows + l];
+        } else if (w == 10 && l < 32 && it.kind == kKindG && a.sign_i) {
+            v = uint32_t(uint8_t(a.sign_i[it.t0 * kTileRows + l]));
+        }
+        return v;
+    };
+    auto store_tab = [&](int buf, int eb, uint32_t v) {
+        if (w < 8) {
+            const u32x4 q = u32x4{v, v, v, v};
+            *reinterpret_cast<u32x4*>(&tab[buf][cb_m][cb_c * 32 + 4 * cb_g]) = q;
+            *reinterpret_cast<u32x4*>(&tab[buf][cb_m][cb_c * 32 + 4 * (cb_g + 4)]) = q;
+        } else if ((w == 8 || w == 9) && l < 32) {
+            esc[eb][w - 8][l] = h2f(v);
+        } else if (w == 10 && l < 32) {
+            esg[eb][l] = (v >> 7) << 31;
+        }
+    };
+
+    // ---- input rotation item r: columns [r*rc, (r+1)*rc), all 8 operand rows
+    auto rotate_in = [&](int r) {
+        float* sc = reinterpret_cast<float*>(&red[0][0][0]);  // 8 x rc <= 8192 floats
+        const int rc = a.rc, c0 = r * rc;
+        for (int i = tid; i < 8 * rc; i += kW * 64) {
+            const int t = i / rc, col = c0 + i % rc;
+            float v = 0.f;
+            if (t < T) {
+                v = h2f(a.x[size_t(t) * H + col]) * h2f(a.s[col]);
+                if (a.sign_h && a.sign_h[col] < 0) v = -v;
+            }
+            sc[i] = v;
+        }
+        __syncthreads();
+        for (int h = 1; h < a.bh; h <<= 1) {
+            for (int i = tid; i < 4 * rc; i += kW * 64) {
+                const int t = i / (rc / 2), jj = i % (rc / 2);
+                const int lo = (jj / h) * 2 * h + (jj % h), hi = lo + h;
+                const float x0 = sc[t * rc + lo], x1 = sc[t * rc + hi];
+                sc[t * rc + lo] = x0 + x1;
+                sc[t * rc + hi] = x0 - x1;
+            }
+            __syncthreads();
+        }
+        for (int i = tid; i < 8 * rc; i += kW * 64) {
+            const int t = i / rc, col = c0 + i % rc;
+            a.xb[size_t(t) * H + col] = (uint16_t)f2h(sc[i] * a.norm_h);
+        }
+        publish(r_rdy + r, tag);
+    };
+
+    // ---- F: rotate rotation unit u of a into the binary16 down operand (scratch: 8 x fu floats)
+    auto job_rotate_mid = [&](int u, float* sc) {
+        const int fu = a.fu, r0 = u * fu;
+        // 8 * fu <= 8192 values, read as tagged words two per thread at a time
+        bool good = true;
+        for (int i0 = 0; i0 < 8 * fu; i0 += 2 * kW * 64) {
+            const int ia = i0 + tid, ib = i0 + tid + kW * 64;
+            const bool ha = ia < 8 * fu, hb = ib < 8 * fu;
+            const uint64_t* pa = a.act + size_t(ha ? ia / fu : 0) * I + r0 + (ha ? ia % fu : 0);
+            const uint64_t* pb = a.act + size_t(hb ? ib / fu : 0) * I + r0 + (hb ? ib % fu : 0);
+            uint64_t va = 0, vb = 0;
+            for (unsigned n = 0;; ++n) {
+                va = ld_relaxed64(pa);
+                vb = ld_relaxed64(pb);
+                if ((!ha || uint32_t(va >> 32) == tag) && (!hb || uint32_t(vb >> 32) == tag)) break;
+                if (n >= limit) {
+                    good = false;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            if (ha) sc[ia] = __builtin_bit_cast(float, uint32_t(va));
+            if (hb) sc[ib] = __builtin_bit_cast(float, uint32_t(vb));
+        }
+        if (!good) note_error(ctl, 2u);
+        __syncthreads();
+        for (int h = 1; h < a.bi; h <<= 1) {
+            for (int i = tid; i < 4 * fu; i += kW * 64) {
+                const int t = i / (fu / 2), jj = i % (fu / 2);
+                const int lo = (jj / h) * 2 * h + (jj % h), hi = lo + h;
+                const float x0 = sc[t * fu + lo], x1 = sc[t * fu + hi];
+                sc[t * fu + lo] = x0 + x1;
+                sc[t * fu + hi] = x0 - x1;
+            }
+            __syncthreads();
+        }
+        for (int i = tid; i < 8 * fu; i += kW * 64) {
+            const int t = i / fu, row = r0 + i % fu;
+            a.ab[size_t(t) * I + row] = (uint16_t)f2h(sc[i] * a.norm_i);
+        }
+        publish(fu_rdy + u, tag);
+    };
+
+    // ---- Y: y rows of pair q = sum over slices of the tagged partials, scaled
+    auto job_reduce_y = [&](int q) {
+        if (tid < 512) {
+            const int t = tid >> 6, row = 64 * q + (tid & 63);
+            if (t < T && row < H) {
+                float sum = 0.f;
+                bool good = true;
+                for (int sl = 0; sl < a.nsl; ++sl) {
+                    const uint64_t* p = a.part + (size_t(sl) * kSkinnyT + t) * H + row;
+                    uint64_t v = ld_relaxed64(p);
+                    for (unsigned n = 0; uint32_t(v >> 32) != tag; ++n) {
+                        if (n >= limit) {
+                            good = false;
+                            break;
+                        }
+                        __builtin_amdgcn_s_sleep(2);
+                        v = ld_relaxed64(p);
+                    }
+                    sum += __builtin_bit_cast(float, uint32_t(v));
+                }
+                if (!good) note_error(ctl, 4u);
+                a.y[size_t(t) * H + row] = (uint16_t)f2h(sum * h2f(a.down.sc[row]));
+            }
+        }
+    };
+
+    // ================================================================ start: input rotations
+    const int G = gridDim.x, b = blockIdx.x;
+    for (int r = b; r < a.n_r; r += G) rotate_in(r);
+
+    // operand selectors: lane l holds column n = l%16 = 2*tok + cp of B
+    const int n16 = l & 15, tok = n16 >> 1, cp = n16 & 1;
+    const uint32_t sel_e = cp ? 0x05040C0Cu : 0x0C0C0504u;
+    const uint32_t sel_o = cp ? 0x07060C0Cu : 0x0C0C0706u;
+    const uint32_t lane4 = uint32_t(l & 31) << 2;
+    const char* tbase = reinterpret_cast<const char*>(&tab[0][0][0]);
+    // this lane's activation words: token tok, columns 16 s + 4 (l / 16) of each tile
+    const uint16_t* bl = &bsh[tok][w * TPW * kTileCols + 4 * (l >> 4)];
+
+    // streaming items b, b + G, b + 2G, ... of the gate/up items followed by the down items
+    int cur_u = a.n_r + b;
+    {
+        const Item c = decode(cur_u);
+        store_tab(0, 0, load_tab(c));
+    }
+    uint32_t ring[D][2][3];
+    {
+        const Item c = decode(cur_u);
+        int kt0, ntile, last_kt;
+        wave_tiles(c, kt0, ntile, last_kt);
+        if (c.kind != kKindNone) {
+#pragma unroll
+            for (int t = 0; t < D; ++t)
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int kt = kt0 + t < last_kt ? kt0 + t : last_kt;
+                    const uint32_t* p = tile_word(c, m, kt);
+                    ring[t][m][0] = p[0];
+                    ring[t][m][1] = p[1];
+                    ring[t][m][2] = p[2];
+                }
+        }
+    }
+    int prev_u = -1;   // the previous streaming item
+    int bstate = -1;   // activation slice in bsh: 0 = x~, 1 + s = rotated a slice s
+    const int tpu = a.fu / kTileRows;  // gate/up tiles per rotation unit
+
+    for (int j = 0;; ++j) {
+        const int buf = j & 1;
+        const int nxt_u = cur_u + G;
+        __syncthreads();  // (A) tables of cur and partials of prev are complete
+
+        // (C) epilogue of the previous item: reduce the 16 waves' partials
+        int job = -1;  // F: rotation unit; Y: (1 << 30) | row pair
+        if (prev_u >= 0) {
+            const Item prev = decode(prev_u);
+            const int eb = (j - 1) & 3;
+            if (prev.kind == kKindG) {
+                const int o = tid >> 2, qq = tid & 3;  // output o, quarter of the waves
+                const int e_l = o & 63, e_r = o >> 6;
+                float g = 0.f, u = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    g += red[4 * qq + i][0][e_l][e_r];
+                    u += red[4 * qq + i][1][e_l][e_r];
+                }
+                g += dpp_xor1(g);
+                u += dpp_xor1(u);
+                g += dpp_xor2(g);
+                u += dpp_xor2(u);
+                if (qq == 0) {
+                    const int rl = 2 * (4 * (e_l >> 4) + e_r) + (e_l & 1), t = (e_l & 15) >> 1;
+                    g *= esc[eb][0][rl];
+                    u *= esc[eb][1][rl];
+                    const float act = g / (1.f + expf(-g)) * u;
+                    const uint32_t bits = __builtin_bit_cast(uint32_t, act) ^ esg[eb][rl];
+                    st_relaxed64(a.act + size_t(t) * I + prev.id * kTileRows + rl,
+                                 (uint64_t(tag) << 32) | bits);
+                }
+                // the last tile of a rotation unit rotates the whole unit
+                if ((prev.id + 1) % tpu == 0) job = prev.id / tpu;
+            } else {
+                const int o = tid >> 1, hh = tid & 1;  // output o of 512, half of the waves
+                const int mm = o >> 8, e_l = o & 63, e_r = (o >> 6) & 3;
+                float v = 0.f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) v += red[8 * hh + i][mm][e_l][e_r];
+                v += dpp_xor1(v);
+                const int tile = 2 * prev.id + mm;
+                if (hh == 0 && tile < MTh) {
+                    const int rl = 2 * (4 * (e_l >> 4) + e_r) + (e_l & 1), t = (e_l & 15) >> 1;
+                    const int row = tile * kTileRows + rl;
+                    if (a.nsl == 1) {
+                        if (t < T) a.y[size_t(t) * H + row] = (uint16_t)f2h(v * esc[eb][mm][rl]);
+                    } else {
+                        st_relaxed64(a.part + (size_t(prev.sl) * kSkinnyT + t) * H + row,
+                                     (uint64_t(tag) << 32) | __builtin_bit_cast(uint32_t, v));
+                    }
+                }
+                // the last slice of a row pair sums the slices
+                if (a.nsl > 1 && prev.sl == a.nsl - 1) job = (1 << 30) | prev.id;
+            }
+        }
+        __syncthreads();  // (B) partials consumed: red is free
+        // (D) the rotation unit or row pair that this epilogue completed
+        if (job >= 0) {
+            float* scratch = reinterpret_cast<float*>(&red[0][0][0]);
+            if (job >> 30)
+                job_reduce_y(job & ((1 << 30) - 1));
+            else
+                job_rotate_mid(job, scratch);
+            __syncthreads();
+        }
+        if (cur_u >= a.total) break;
+
+        // (F) table operands of the next item (written after this item's products)
+        const uint32_t tv_next = load_tab(decode(nxt_u));
+
+        // (G) activation operand of this item: one K slice of x~ or of the rotated a, 8 rows
+        {
+            const Item cur = decode(cur_u);
+            const int want = cur.kind == kKindG ? 0 : 1 + cur.sl;
+            if (want != bstate) {
+                constexpr int cols = SWT * kTileCols;
+                const int c0 = cur.sl * cols;
+                bool good = true;
+                if (cur.kind == kKindG) {
+                    for (int f0 = 0; f0 < a.n_r; f0 += 64)
+                        good = await_flags(r_rdy + f0, min(64, a.n_r - f0), tag, limit, &s_ok) && good;
+                } else {
+                    const int u0 = c0 / a.fu, u1 = min(c0 + cols, I) / a.fu;
+                    for (int f0 = u0; f0 < u1; f0 += 64)
+                        good = await_flags(fu_rdy + f0, min(64, u1 - f0), tag, limit, &s_ok) && good;
+                }
+                if (!good && tid == 0) note_error(ctl, 1u);
+                const uint16_t* src = cur.kind == kKindG ? a.xb : a.ab;
+                const int K = cur.kind == kKindG ? H : I;
+                // every load first, then every store: one memory latency for the whole slice
+                constexpr int kChunks = kSkinnyT * cols / 8;
+                constexpr int kPer = (kChunks + kW * 64 - 1) / (kW * 64);
+                u32x4 v[kPer];
+#pragma unroll
+                for (int k = 0; k < kPer; ++k) {
+                    const int i = tid + k * kW * 64;
+                    const int t = (i / (cols / 8)) & 7, c8 = (i % (cols / 8)) * 8;
+                    v[k] = u32x4{0u, 0u, 0u, 0u};
+                    if (i < kChunks && c0 + c8 < K)
+                        v[k] = *reinterpret_cast<const u32x4*>(src + size_t(t) * K + c0 + c8);
+                }
+#pragma unroll
+                for (int k = 0; k < kPer; ++k) {
+                    const int i = tid + k * kW * 64;
+                    if (i < kChunks)
+                        *reinterpret_cast<u32x4*>(&bsh[i / (cols / 8)][(i % (cols / 8)) * 8]) = v[k];
+                }
+                __syncthreads();
+                bstate = want;
+            }
+        }
+
+        // (H) the products; the code ring streams on into the next item's tiles (or reloads
+        // this item's own when there is none)
+        {
+            const Item pit = decode(nxt_u < a.total ? nxt_u : cur_u);
+            int nkt0, nntile, nlast_kt;
+            wave_tiles(pit, nkt0, nntile, nlast_kt);
+            const uint8_t* nbase0 = (pit.kind == kKindD ? a.down.codes : a.gate.codes) +
+                                    size_t(pit.t0) * pit.KT * kTileBytes;
+            const uint8_t* nbase1 = (pit.kind == kKindD ? a.down.codes : a.up.codes) +
+                                    size_t(pit.t1) * pit.KT * kTileBytes;
+            uint32_t laneb[2];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) laneb[m] = lane4 | uint32_t((buf * 2 + m) * kTab * 4);
+            auto look = [&](const uint32_t (&c)[2][3], int s, u32x4 (&A)[2]) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const uint32_t d0 = c[m][0], d1 = c[m][1], d2 = c[m][2], lb = laneb[m];
+#define VQ_LOOK(i, Q) A[m][i] = *reinterpret_cast<const uint32_t*>(tbase + code_addr<Q, 7>(d0, d1, d2, lb))
+                    if (s == 0) { VQ_LOOK(0, 0); VQ_LOOK(1, 1); VQ_LOOK(2, 2); VQ_LOOK(3, 3); }
+                    if (s == 1) { VQ_LOOK(0, 4); VQ_LOOK(1, 5); VQ_LOOK(2, 6); VQ_LOOK(3, 7); }
+                    if (s == 2) { VQ_LOOK(0, 8); VQ_LOOK(1, 9); VQ_LOOK(2, 10); VQ_LOOK(3, 11); }
+                    if (s == 3) { VQ_LOOK(0, 12); VQ_LOOK(1, 13); VQ_LOOK(2, 14); VQ_LOOK(3, 15); }
+#undef VQ_LOOK
+                }
+            };
+            f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            u32x4 A[2][2];
+            look(ring[0], 0, A[0]);
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const int cp0 = (4 * t + s) & 1, cp1 = cp0 ^ 1;
+                    const u32x2 bv = *reinterpret_cast<const u32x2*>(bl + t * kTileCols + 16 * s);
+                    if (s < 3)
+                        look(ring[t % D], s + 1, A[cp1]);
+                    else if (t + 1 < TPW)
+                        look(ring[(t + 1) % D], 0, A[cp1]);
+                    if (s == 2) {
+                        const int kt = nkt0 + t < nlast_kt ? nkt0 + t : nlast_kt;
+                        const uint32_t* p0 = reinterpret_cast<const uint32_t*>(
+                                                 nbase0 + size_t(kt) * kTileBytes) + 3 * l;
+                        const uint32_t* p1 = reinterpret_cast<const uint32_t*>(
+                                                 nbase1 + size_t(kt) * kTileBytes) + 3 * l;
+                        ring[t % D][0][0] = p0[0];
+                        ring[t % D][0][1] = p0[1];
+                        ring[t % D][0][2] = p0[2];
+                        ring[t % D][1][0] = p1[0];
+                        ring[t % D][1][1] = p1[1];
+                        ring[t % D][1][2] = p1[2];
+                        // keep each refill where it is, one item ahead of its use
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
+                    const uint32_t b0 = bv[0], b1 = bv[1];
+                    const u32x4 Bx = u32x4{__builtin_amdgcn_perm(b0, 0u, sel_e),
+                                           __builtin_amdgcn_perm(b0, 0u, sel_o),
+                                           __builtin_amdgcn_perm(b1, 0u, sel_e),
+                                           __builtin_amdgcn_perm(b1, 0u, sel_o)};
+                    acc[0] = mfma16x16x32(A[cp0][0], Bx, acc[0]);
+                    acc[1] = mfma16x16x32(A[cp0][1], Bx, acc[1]);
+                }
+            }
+            // (I) next item's tables into the idle buffers, this item's partials
+            store_tab(buf ^ 1, (j + 1) & 3, tv_next);
+            red[w][0][l] = acc[0];
+            red[w][1][l] = acc[1];
+        }
+        prev_u = cur_u;
+        cur_u = nxt_u;
+    }
+
+    // ================================================================ exit: the last workgroup
+    // advances the epoch for the next call (flags and tags of this call then go stale)
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(ctl + kCtlExit, 1u, __ATOMIC_ACQ_REL,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        if (done + 1u == gridDim.x) {
+            ctl[kCtlExit] = 0u;
+            ctl[kCtlEpoch] = tag;
+        }
+    }
+}
+
+int fused_tpw(int H) {
+    const int KT = H / kTileCols;
+    const int tpw = (KT + kW - 1) / kW;
+    return tpw >= 1 && tpw <= kSkinnyMaxTPW ? tpw : 0;
+}
+
+hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, hipStream_t st) {
+    if (!a.x || !a.y || !a.ctl || !a.xb || !a.act || !a.ab || !a.s || grid < 1 ||
+        (a.nsl > 1 && !a.part) || a.fu < kTileRows || a.fu > 1024 || a.rc > 1024 ||
+        8 * a.rc > 8192 || a.n_r > kW * 64 || a.T < 1 || a.T > kSkinnyT)
+        return hipErrorInvalidValue;
+#define VQ_CASE(TP)                                                                  \
+    if (tpw == TP) {                                                                 \
+        hipLaunchKernelGGL(k_fused<TP>, dim3(grid), dim3(kW * 64), 0, st, a);        \
+        return hipGetLastError();                                                    \
+    }
+    VQ_CASE(1) VQ_CASE(2) VQ_CASE(3) VQ_CASE(4) VQ_CASE(5)
+#undef VQ_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace vqmlp

@@ -64,6 +64,36 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st);
 hipError_t launch_reduce_down(int T, int N, int slices, const float* part, const uint16_t* sc,
                               uint16_t* y, hipStream_t st);
 
+// ---- fused persistent forward (T <= 8): the whole MLP in one launch
+// Control block (32-bit words, zero before the first call): word 1 counts finished workgroups
+// (back to zero after each call), word 2 collects error bits, word 3 is the call epoch; the
+// ready flags of the input-rotation items and of the intermediate rotation units follow from
+// word kCtlHdr.  Word 0 is reserved.
+enum { kCtlReserved = 0, kCtlExit = 1, kCtlError = 2, kCtlEpoch = 3, kCtlHdr = 16 };
+struct FusedArgs {
+    VQ3View gate, up, down;
+    int H, I, T;
+    int bh, bi;          // Hadamard blocks
+    int rc;              // columns per input-rotation item (multiple of bh)
+    int fu;              // intermediate rows per rotation unit (max(bi, 32))
+    int n_r, n_g, nsl, nqd, n_fu, total;  // item counts: rotation, gate/up, down slices x pairs
+    float norm_h, norm_i;
+    const uint16_t* x;       // [T][H] binary16
+    const uint16_t* s;       // [H] input scale
+    const int8_t* sign_h;    // [H] or NULL
+    const int8_t* sign_i;    // [I] or NULL
+    uint16_t* y;             // [T][H] binary16
+    uint32_t* ctl;           // control block; flags follow at kCtlHdr: r_rdy[n_r], fu_rdy[n_fu]
+    uint16_t* xb;            // [8][H] rotated input, binary16, rows past T zero
+    uint64_t* act;           // [8][I] silu(g) u sign, FP32 bits tagged with the call's epoch
+    uint16_t* ab;            // [8][I] rotated intermediate, binary16
+    uint64_t* part;          // [nsl][8][H] tagged FP32 partial sums of the down projection
+    unsigned spin_limit;     // bound of every wait (then the error word records it)
+};
+inline size_t fused_ctl_words(int n_r, int n_fu) { return size_t(kCtlHdr) + n_r + n_fu; }
+int fused_tpw(int H);  // tiles per wave of the fused kernel for hidden size H (0 = unsupported)
+hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, hipStream_t st);
+
 // ---- tiled matrix-core path (T > 8): decoders, epilogues, kinds
 enum { kDecVQ3 = 0, kDecLUT2 = 1, kDecLUT4 = 2, kDecDense = 3 };
 enum { kEgGateUp32 = 0, kEgGateUpRot = 1, kEgScale16 = 2, kEgLUT = 3, kEgPlain32 = 4 };

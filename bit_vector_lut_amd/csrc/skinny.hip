@@ -201,6 +201,9 @@ __global__ void __launch_bounds__(kWaves * 64, 1) k_stream(SkinnyArgs a) {
                         ring[t % D][m][1] = p[1];
                         ring[t % D][m][2] = p[2];
                     }
+                    // keep the refill here: left to itself the scheduler sinks every refill to
+                    // the end of the item, which exposes a full memory latency per item
+                    __builtin_amdgcn_sched_barrier(0);
                 }
                 const uint32_t b0 = B[t * 4 + s][0], b1 = B[t * 4 + s][1];
                 const u32x4 Bx = u32x4{__builtin_amdgcn_perm(b0, 0u, sel_e),
@@ -255,7 +258,10 @@ template <int TPW, int D, int EPI>
 static hipError_t launch_stream_t(const SkinnyArgs& a, hipStream_t st) {
     const int MT = a.mat[0].N / kTileRows;
     const int items = a.slices * (EPI == kEpiGateUp ? MT : (MT + 1) / 2);
-    const int grid = items < 256 ? items : 256;
+    // as many workgroups as keep every one at the same item count: a partial last round of
+    // items would leave most of the chip idle while a few workgroups finish
+    const int per = (items + 255) / 256;
+    const int grid = (items + per - 1) / per;
     hipLaunchKernelGGL((k_stream<TPW, D, EPI>), dim3(grid), dim3(kWaves * 64), 0, st, a);
     return hipGetLastError();
 }

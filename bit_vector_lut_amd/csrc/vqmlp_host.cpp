@@ -3,6 +3,8 @@
 // vqmlp_status; failures set a per-thread message and launch nothing.
 #include "internal.h"
 
+#include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -205,55 +207,76 @@ bool skinny_geom(int K, bool need_single, SkinnyGeom* g) {
 
 // ==================================================================== plan
 
+struct FusedGeom {
+    int tpw;                              // 0: the fused kernel does not take this shape
+    int rc, fu, n_r, n_g, nsl, nqd, n_fu, total;
+    size_t ctl_words;
+};
+
 struct vqmlp_plan {
     vqmlp_desc d;
     int bh, bi;
     VQ3View gate, up, down;
     SkinnyGeom g_gu, g_dn;
+    FusedGeom fz;
+    int cus;                              // compute units: workgroups of the fused kernel
     bool skinny_ok, tiled_ok;
 };
 
 namespace {
 
 struct Workspace {
-    // skinny
+    uint32_t* ctl;    // fused control block (zero before the first call, left zero by each)
+    // fused region
+    uint16_t* fxb;    // [8][H]
+    uint64_t* fact;   // [8][I] tagged
+    uint16_t* fab;    // [8][I]
+    uint64_t* fpart;  // [nsl][8][H] tagged
+    // per-phase skinny region
     uint16_t* xb;     // [8][H] binary16 rotated input
     float* a;         // [8][I]
     uint16_t* ab;     // [8][I] binary16 rotated intermediate
     float* part;      // [slices][8][H]
-    // tiled
+    // tiled region
     uint16_t* xt;     // [T][H]
     float* a_t;       // [T][I]
     uint16_t* at;     // [T][I]
     size_t bytes;
 };
 
+// The regions are disjoint: the fused kernel's tagged words must never see another path's
+// data where it expects a tag.
 Workspace carve(const vqmlp_plan* p, int T, void* base) {
     Workspace w;
     memset(&w, 0, sizeof w);
     const int H = p->d.H, I = p->d.I;
-    size_t off = 256;  // control block
+    size_t off = 0;
     auto take = [&](size_t n) {
         size_t o = off;
         off = align256(off + n);
         return o;
     };
     uint8_t* b = static_cast<uint8_t*>(base);
-    // skinny region
-    size_t o_xb = take(size_t(kSkinnyT) * H * 2);
-    size_t o_a = take(size_t(kSkinnyT) * I * 4);
-    size_t o_ab = take(size_t(kSkinnyT) * I * 2);
-    size_t o_part = take(size_t(p->g_dn.slices) * kSkinnyT * H * 4);
-    size_t skinny_end = off;
-    // tiled region overlaps the skinny one (a forward uses one of them)
-    off = 256;
+    const size_t o_ctl = take(std::max<size_t>(p->fz.ctl_words, kCtlHdr) * 4);
+    const size_t o_fxb = take(size_t(kSkinnyT) * H * 2);
+    const size_t o_fact = take(size_t(kSkinnyT) * I * 8);
+    const size_t o_fab = take(size_t(kSkinnyT) * I * 2);
+    const size_t o_fpart = take(size_t(std::max(p->fz.nsl, 1)) * kSkinnyT * H * 8);
+    const size_t o_xb = take(size_t(kSkinnyT) * H * 2);
+    const size_t o_a = take(size_t(kSkinnyT) * I * 4);
+    const size_t o_ab = take(size_t(kSkinnyT) * I * 2);
+    const size_t o_part = take(size_t(p->g_dn.slices) * kSkinnyT * H * 4);
     const int Tt = T > 0 ? T : 1;
-    size_t o_xt = take(size_t(Tt) * H * 2);
-    size_t o_at32 = take(size_t(Tt) * I * 4);
-    size_t o_at = take(size_t(Tt) * I * 2);
-    size_t tiled_end = off;
-    w.bytes = skinny_end > tiled_end ? skinny_end : tiled_end;
+    const size_t o_xt = take(size_t(Tt) * H * 2);
+    const size_t o_at32 = take(size_t(Tt) * I * 4);
+    const size_t o_at = take(size_t(Tt) * I * 2);
+    w.bytes = off;
     if (b) {
+        w.ctl = reinterpret_cast<uint32_t*>(b + o_ctl);
+        w.fxb = reinterpret_cast<uint16_t*>(b + o_fxb);
+        w.fact = reinterpret_cast<uint64_t*>(b + o_fact);
+        w.fab = reinterpret_cast<uint16_t*>(b + o_fab);
+        w.fpart = reinterpret_cast<uint64_t*>(b + o_fpart);
         w.xb = reinterpret_cast<uint16_t*>(b + o_xb);
         w.a = reinterpret_cast<float*>(b + o_a);
         w.ab = reinterpret_cast<uint16_t*>(b + o_ab);
@@ -263,6 +286,26 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
         w.at = reinterpret_cast<uint16_t*>(b + o_at);
     }
     return w;
+}
+
+// Item counts of the fused kernel for this shape (tpw = 0 when it does not apply).
+FusedGeom fused_geom(int H, int I, int bh, int bi) {
+    FusedGeom g;
+    memset(&g, 0, sizeof g);
+    g.tpw = fused_tpw(H);
+    if (!g.tpw) return g;
+    const int swt = kSkinnyWaves * g.tpw;  // K tiles per slice
+    g.rc = std::max(bh, H % 128 == 0 ? 128 : 64);
+    g.fu = std::max(bi, kTileRows);
+    g.n_r = H / g.rc;
+    g.n_g = I / kTileRows;
+    g.nsl = (I / kTileCols + swt - 1) / swt;
+    g.nqd = (H / kTileRows + 1) / 2;
+    g.n_fu = I / g.fu;
+    g.total = g.n_r + g.n_g + g.nsl * g.nqd;
+    g.ctl_words = fused_ctl_words(g.n_r, g.n_fu);
+    if (g.n_r > 1024 || g.rc > 1024) g.tpw = 0;
+    return g;
 }
 
 vqmlp_status run_skinny(const vqmlp_plan* p, int T, const void* x, void* y, const Workspace& w,
@@ -303,6 +346,45 @@ vqmlp_status run_skinny(const vqmlp_plan* p, int T, const void* x, void* y, cons
         e = launch_reduce_down(T, H, d.slices, w.part, p->down.sc, static_cast<uint16_t*>(y), st);
         if (e != hipSuccess) return hip_fail(e, "down reduction");
     }
+    return ok();
+}
+
+vqmlp_status run_fused(const vqmlp_plan* p, int T, const void* x, void* y, const Workspace& w,
+                       hipStream_t st) {
+    const FusedGeom& g = p->fz;
+    FusedArgs a;
+    memset(&a, 0, sizeof a);
+    a.gate = p->gate;
+    a.up = p->up;
+    a.down = p->down;
+    a.H = p->d.H;
+    a.I = p->d.I;
+    a.T = T;
+    a.bh = p->bh;
+    a.bi = p->bi;
+    a.rc = g.rc;
+    a.fu = g.fu;
+    a.n_r = g.n_r;
+    a.n_g = g.n_g;
+    a.nsl = g.nsl;
+    a.nqd = g.nqd;
+    a.n_fu = g.n_fu;
+    a.total = g.total;
+    a.norm_h = float(1.0 / std::sqrt(double(p->bh)));
+    a.norm_i = float(1.0 / std::sqrt(double(p->bi)));
+    a.x = static_cast<const uint16_t*>(x);
+    a.s = p->d.s_in;
+    a.sign_h = p->d.sign_h;
+    a.sign_i = p->d.sign_i;
+    a.y = static_cast<uint16_t*>(y);
+    a.ctl = w.ctl;
+    a.xb = w.fxb;
+    a.act = w.fact;
+    a.ab = w.fab;
+    a.part = w.fpart;
+    a.spin_limit = 1u << 18;
+    const hipError_t e = launch_fused(a, g.tpw, p->cus, st);
+    if (e != hipSuccess) return hip_fail(e, "fused forward");
     return ok();
 }
 
@@ -521,6 +603,15 @@ vqmlp_status vqmlp_create(const vqmlp_desc* desc, vqmlp_plan** out) {
     p->gate = view_of(d.gate, d.I, d.H);
     p->up = view_of(d.up, d.I, d.H);
     p->down = view_of(d.down, d.H, d.I);
+    p->fz = fused_geom(d.H, d.I, bh, bi);
+    {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1)
+            cus = 256;
+        p->cus = cus;
+    }
     p->skinny_ok = skinny_geom(d.H, true, &p->g_gu);
     p->tiled_ok = d.H % 64 == 0 && d.I % 64 == 0;
     skinny_geom(d.I, false, &p->g_dn);
@@ -567,23 +658,25 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
     const size_t xy = size_t(T) * p->d.H * 2;
     if ((xb < wb + w.bytes && wb < xb + xy) || (yb < wb + w.bytes && wb < yb + xy))
         return fail(VQMLP_ERR_INVALID_ARG, "x or y overlaps the workspace");
-    bool skinny;
-    if (path == 0)
-        skinny = T <= kSkinnyT && p->skinny_ok;
-    else if (path == 2)
-        skinny = false;
-    else {
+    // 1: the fused single-launch kernel, 3: the per-phase skinny kernels, 2: tiled; 0 picks
+    // the per-phase kernels for T <= 8 (measured faster than the fused kernel so far), else
+    // the fused kernel where the per-phase ones do not apply, else tiled
+    const bool fused_ok = p->fz.tpw > 0;
+    if (path == 1 || path == 3) {
         if (T > kSkinnyT)
             return fail(VQMLP_ERR_UNSUPPORTED, "the skinny path takes T <= %d (T=%d)", kSkinnyT, T);
-        if (!p->skinny_ok)
+        if (!(path == 1 ? fused_ok : p->skinny_ok))
             return fail(VQMLP_ERR_UNSUPPORTED, "the skinny path takes H <= %d (H=%d)",
                         kSkinnyWaves * kSkinnyMaxTPW * kTileCols, p->d.H);
-        skinny = true;
     }
-    if (!skinny && !p->tiled_ok)
+    int use = path;
+    if (path == 0) use = T <= kSkinnyT ? (p->skinny_ok ? 3 : (fused_ok ? 1 : 2)) : 2;
+    if (use == 2 && !p->tiled_ok)
         return fail(VQMLP_ERR_UNSUPPORTED, "the tiled path takes H and I multiples of 64");
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return skinny ? run_skinny(p, T, x, y, w, st) : run_tiled(p, T, x, y, w, st);
+    if (use == 1) return run_fused(p, T, x, y, w, st);
+    if (use == 3) return run_skinny(p, T, x, y, w, st);
+    return run_tiled(p, T, x, y, w, st);
 }
 
 vqmlp_status vqmlp_forward(const vqmlp_plan* p, int T, const void* x, void* y, void* workspace,

@@ -120,8 +120,11 @@ vqmlp_status vqmlp_workspace_bytes(const vqmlp_plan *plan, int T, size_t *bytes)
 vqmlp_status vqmlp_forward(const vqmlp_plan *plan, int T, const void *x, void *y, void *workspace,
                            size_t workspace_bytes, void *stream);
 
-/* Same as vqmlp_forward with the kernel family chosen by the caller: path 0 = automatic,
- * 1 = skinny (T <= 8 only), 2 = tiled matrix-core, 3 = skinny as separate per-phase kernels. */
+/* Same as vqmlp_forward with the kernel family chosen by the caller: path 0 = automatic
+ * (T <= 8: path 3; larger T: path 2), 1 = the fused single-launch T <= 8 kernel, 2 = tiled
+ * matrix-core kernels, 3 = the T <= 8 kernels as separate per-phase launches.  Paths 1 and 3 take T <= 8 and H <= 5120; path 1 keeps
+ * its queue, counters and epoch in the first bytes of the workspace (the caller zero-fills the
+ * workspace once; every call leaves that control block ready for the next call). */
 vqmlp_status vqmlp_forward_path(const vqmlp_plan *plan, int T, const void *x, void *y,
                                 void *workspace, size_t workspace_bytes, int path, void *stream);
 
