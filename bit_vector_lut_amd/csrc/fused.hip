@@ -48,16 +48,18 @@ __device__ __forceinline__ void st_relaxed64(uint64_t* p, uint64_t v) {
 __device__ __forceinline__ void note_error(uint32_t* ctl, uint32_t bit) {
     __hip_atomic_fetch_or(ctl + kCtlError, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// Publish a flag after every thread's plain stores: each wave waits for its own stores to reach
-// L2 (vmcnt counts stores), the workgroup meets, then one thread writes dirty L2 lines back and
-// sets the flag.  One L2 write-back per flag instead of one per wave.
+// Publish a flag after the workgroup's hand-off stores.  Those stores are agent-coherent (they
+// write through to memory), so no L2 write-back is needed: each wave waits until its own stores
+// are done (vmcnt counts stores), the workgroup meets, and one thread sets the flag.
 __device__ __forceinline__ void publish(uint32_t* flag, uint32_t value) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (threadIdx.x == 0)
         __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+}
+__device__ __forceinline__ void st_coherent32(void* p, uint32_t v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 // Wait until flags[0..n) all equal want (n <= 64, polled by wave 0; bounded), then acquire once
 // and meet: loads after this see what the flags' writers stored.  Returns false on timeout.
@@ -229,9 +231,10 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
             }
             __syncthreads();
         }
-        for (int i = tid; i < 8 * rc; i += kW * 64) {
-            const int t = i / rc, col = c0 + i % rc;
-            a.xb[size_t(t) * H + col] = (uint16_t)f2h(sc[i] * a.norm_h);
+        for (int i2 = tid; i2 < 4 * rc; i2 += kW * 64) {
+            const int i = 2 * i2, t = i / rc, col = c0 + i % rc;
+            st_coherent32(a.xb + size_t(t) * H + col,
+                          f2h(sc[i] * a.norm_h) | (f2h(sc[i + 1] * a.norm_h) << 16));
         }
         publish(r_rdy + r, tag);
     };
@@ -272,9 +275,10 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
             }
             __syncthreads();
         }
-        for (int i = tid; i < 8 * fu; i += kW * 64) {
-            const int t = i / fu, row = r0 + i % fu;
-            a.ab[size_t(t) * I + row] = (uint16_t)f2h(sc[i] * a.norm_i);
+        for (int i2 = tid; i2 < 4 * fu; i2 += kW * 64) {
+            const int i = 2 * i2, t = i / fu, row = r0 + i % fu;
+            st_coherent32(a.ab + size_t(t) * I + row,
+                          f2h(sc[i] * a.norm_i) | (f2h(sc[i + 1] * a.norm_i) << 16));
         }
         publish(fu_rdy + u, tag);
     };

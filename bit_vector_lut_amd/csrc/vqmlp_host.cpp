@@ -659,8 +659,7 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
     if ((xb < wb + w.bytes && wb < xb + xy) || (yb < wb + w.bytes && wb < yb + xy))
         return fail(VQMLP_ERR_INVALID_ARG, "x or y overlaps the workspace");
     // 1: the fused single-launch kernel, 3: the per-phase skinny kernels, 2: tiled; 0 picks
-    // the per-phase kernels for T <= 8 (measured faster than the fused kernel so far), else
-    // the fused kernel where the per-phase ones do not apply, else tiled
+    // the fused kernel for T <= 8 where it applies, else the per-phase kernels, else tiled
     const bool fused_ok = p->fz.tpw > 0;
     if (path == 1 || path == 3) {
         if (T > kSkinnyT)
@@ -670,7 +669,7 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
                         kSkinnyWaves * kSkinnyMaxTPW * kTileCols, p->d.H);
     }
     int use = path;
-    if (path == 0) use = T <= kSkinnyT ? (p->skinny_ok ? 3 : (fused_ok ? 1 : 2)) : 2;
+    if (path == 0) use = T <= kSkinnyT ? (fused_ok ? 1 : (p->skinny_ok ? 3 : 2)) : 2;
     if (use == 2 && !p->tiled_ok)
         return fail(VQMLP_ERR_UNSUPPORTED, "the tiled path takes H and I multiples of 64");
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -121,7 +121,7 @@ vqmlp_status vqmlp_forward(const vqmlp_plan *plan, int T, const void *x, void *y
                            size_t workspace_bytes, void *stream);
 
 /* Same as vqmlp_forward with the kernel family chosen by the caller: path 0 = automatic
- * (T <= 8: path 3; larger T: path 2), 1 = the fused single-launch T <= 8 kernel, 2 = tiled
+ * (T <= 8: path 1; larger T: path 2), 1 = the fused single-launch T <= 8 kernel, 2 = tiled
  * matrix-core kernels, 3 = the T <= 8 kernels as separate per-phase launches.  Paths 1 and 3 take T <= 8 and H <= 5120; path 1 keeps
  * its queue, counters and epoch in the first bytes of the workspace (the caller zero-fills the
  * workspace once; every call leaves that control block ready for the next call). */

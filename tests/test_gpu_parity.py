@@ -179,7 +179,7 @@ def test_fused_control_block_is_left_ready(vq, oracle_mod, torch_dev):
         y = _f64(mlp.forward(x, workspace=ws, path=path))
         torch_dev.cuda.synchronize()
         assert _report("path %d" % path, y, ref) <= MLP_TOL
-        fused_calls += path == 1
+        fused_calls += path in (0, 1)  # path 0 takes the fused kernel at T <= 8
     ctl = ws[:64].cpu().numpy().view(np.uint32)
     assert ctl[0] == 0 and ctl[1] == 0, ctl[:4]  # queue head, exit count
     assert ctl[2] == 0, "a bounded wait ran out: error bits %#x" % ctl[2]
