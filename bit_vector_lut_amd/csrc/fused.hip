@@ -61,30 +61,6 @@ __device__ __forceinline__ void st_coherent32(void* p, uint32_t v) {
     __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
-// Wait until flags[0..n) all equal want (n <= 64, polled by wave 0; bounded), then acquire once
-// and meet: loads after this see what the flags' writers stored.  Returns false on timeout.
-__device__ bool await_flags(const uint32_t* flags, int n, uint32_t want, unsigned limit,
-                            int* s_ok) {
-    if (threadIdx.x < 64) {
-        bool good = true;
-        const int lane = threadIdx.x;
-        if (lane < n) {
-            for (unsigned k = 0;; ++k) {
-                if (ld_relaxed(flags + lane) == want) break;
-                if (k >= limit) {
-                    good = false;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        const bool all = __all(good);
-        if (lane == 0) *s_ok = all ? 1 : 0;
-    }
-    __syncthreads();
-    return *s_ok != 0;
-}
 __device__ __forceinline__ float dpp_xor1(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
                                                               0xF, 0xF, false));
@@ -123,7 +99,6 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
     auto& bsh = *reinterpret_cast<uint16_t (*)[kSkinnyT][BROW]>(lds + kOffB);  // activations
     auto& esc = *reinterpret_cast<float (*)[4][2][32]>(lds + kOffEsc);    // row scales
     auto& esg = *reinterpret_cast<uint32_t (*)[4][32]>(lds + kOffEsg);    // sign bits
-    int& s_ok = *reinterpret_cast<int*>(lds + kOffOk);
 
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -426,39 +401,51 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
             const Item cur = decode(cur_u);
             const int want = cur.kind == kKindG ? 0 : 1 + cur.sl;
             if (want != bstate) {
-                constexpr int cols = SWT * kTileCols;
-                const int c0 = cur.sl * cols;
-                bool good = true;
-                if (cur.kind == kKindG) {
-                    for (int f0 = 0; f0 < a.n_r; f0 += 64)
-                        good = await_flags(r_rdy + f0, min(64, a.n_r - f0), tag, limit, &s_ok) && good;
-                } else {
-                    const int u0 = c0 / a.fu, u1 = min(c0 + cols, I) / a.fu;
-                    for (int f0 = u0; f0 < u1; f0 += 64)
-                        good = await_flags(fu_rdy + f0, min(64, u1 - f0), tag, limit, &s_ok) && good;
-                }
-                if (!good && tid == 0) note_error(ctl, 1u);
-                const uint16_t* src = cur.kind == kKindG ? a.xb : a.ab;
+                // Each wave waits for, and loads, only the columns of its own tiles: a wave whose
+                // inputs are ready starts while the others still wait.  The columns are read
+                // with agent-coherent loads, matching the writers' write-through stores.
+                constexpr int wcols = TPW * kTileCols;
+                const int c0 = cur.sl * SWT * kTileCols + w * wcols;
                 const int K = cur.kind == kKindG ? H : I;
-                // every load first, then every store: one memory latency for the whole slice
-                constexpr int kChunks = kSkinnyT * cols / 8;
-                constexpr int kPer = (kChunks + kW * 64 - 1) / (kW * 64);
+                const int gran = cur.kind == kKindG ? a.rc : a.fu;  // columns per flag
+                const uint32_t* flags = cur.kind == kKindG ? r_rdy : fu_rdy;
+                bool good = true;
+                if (c0 < K) {
+                    const int f0 = c0 / gran, f1 = (min(c0 + wcols, K) - 1) / gran + 1;
+                    if (l < f1 - f0) {
+                        for (unsigned n = 0;; ++n) {
+                            if (ld_relaxed(flags + f0 + l) == tag) break;
+                            if (n >= limit) {
+                                good = false;
+                                break;
+                            }
+                            __builtin_amdgcn_s_sleep(2);
+                        }
+                    }
+                }
+                if (!__all(good) && l == 0) note_error(ctl, 1u);
+                const uint16_t* src = cur.kind == kKindG ? a.xb : a.ab;
+                constexpr int kPer = kSkinnyT * wcols / 8 / 64;  // 16-byte chunks per lane
                 u32x4 v[kPer];
 #pragma unroll
                 for (int k = 0; k < kPer; ++k) {
-                    const int i = tid + k * kW * 64;
-                    const int t = (i / (cols / 8)) & 7, c8 = (i % (cols / 8)) * 8;
+                    const int i = l + 64 * k;
+                    const int t = i / (wcols / 8), c8 = (i % (wcols / 8)) * 8;
                     v[k] = u32x4{0u, 0u, 0u, 0u};
-                    if (i < kChunks && c0 + c8 < K)
-                        v[k] = *reinterpret_cast<const u32x4*>(src + size_t(t) * K + c0 + c8);
+                    if (c0 + c8 < K) {
+                        const uint64_t* p =
+                            reinterpret_cast<const uint64_t*>(src + size_t(t) * K + c0 + c8);
+                        const uint64_t lo = ld_relaxed64(p), hi = ld_relaxed64(p + 1);
+                        v[k] = u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi),
+                                     uint32_t(hi >> 32)};
+                    }
                 }
 #pragma unroll
                 for (int k = 0; k < kPer; ++k) {
-                    const int i = tid + k * kW * 64;
-                    if (i < kChunks)
-                        *reinterpret_cast<u32x4*>(&bsh[i / (cols / 8)][(i % (cols / 8)) * 8]) = v[k];
+                    const int i = l + 64 * k;
+                    *reinterpret_cast<u32x4*>(
+                        &bsh[i / (wcols / 8)][w * wcols + (i % (wcols / 8)) * 8]) = v[k];
                 }
-                __syncthreads();
                 bstate = want;
             }
         }
