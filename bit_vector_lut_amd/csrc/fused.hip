@@ -12,9 +12,10 @@
 //   G  gate and up of one 32-row tile over all of H (the matrix-core product of the skinny
 //      kernel: lane-private LDS codebooks, register code ring), epilogue silu(g) u sign;
 //   D  down projection of two 32-row tiles over one K slice of 16 * TPW tiles of I.
-// Work that needs several items is done right after the item that completes the set:
-//   F  the last G tile of a rotation unit (max(bi, 32) rows) rotates the unit's a into the
-//      binary16 down operand, then raises fu_rdy[unit];
+// Work that needs several items is done right after one item of the set:
+//   F  one G tile of each rotation unit (max(bi, 32) rows; all tiles of a unit are processed
+//      in the same round by different workgroups) rotates the unit's a into the binary16 down
+//      operand once the other tiles' values are in, then raises fu_rdy[unit];
 //   Y  the D item of the last K slice of a row pair sums the slices, scales and writes y.
 // Items hand data to later items through global memory.  High-volume hand-offs (a, the down
 // partial sums) are stored as 64-bit words {FP32 bits, tag}, tag = call epoch + 1, so the reader
@@ -357,8 +358,11 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                     st_relaxed64(a.act + size_t(t) * I + prev.id * kTileRows + rl,
                                  (uint64_t(tag) << 32) | bits);
                 }
-                // the last tile of a rotation unit rotates the whole unit
-                if ((prev.id + 1) % tpu == 0) job = prev.id / tpu;
+                // One tile of each rotation unit rotates the whole unit once the others' values
+                // are in; which tile is hashed from the unit, so that round-robin assignment does
+                // not hand every rotation to the same workgroups.
+                const int unit = prev.id / tpu;
+                if (prev.id % tpu == int((unit ^ (unit >> 2) ^ (unit >> 5)) % tpu)) job = unit;
             } else {
                 const int o = tid >> 1, hh = tid & 1;  // output o of 512, half of the waves
                 const int mm = o >> 8, e_l = o & 63, e_r = (o >> 6) & 3;
