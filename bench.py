@@ -38,6 +38,58 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_fused_t8_27b_traffic.txt")
+KERNEL_SOURCES = ["fused.hip", "device.h", "internal.h"]
+
+
+def kernel_source_hash():
+    """SHA-256 of the sources the fused kernel is compiled from."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_vector_lut_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads for a copy of known size),
+    or None when that summary was taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            kv = dict(line.split(":", 1) for line in fh if ":" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def probe(device):
+    """Counter run: a device copy of known size, then a few fused forwards on distinct layers
+    (run under rocprofv3 --pmc to scale FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    layers = build_stream(4, device)
+    ws = layers[0][0].workspace(8)
+    for m, x in layers:
+        m.forward(x, torch.empty_like(x), ws)
+    torch.cuda.synchronize()
+    log("probe done: copy of %d bytes, %d forwards" % (n, len(layers)))
+
+
 def build_stream(n_layers, device):
     """Generate, pack and upload the 64-layer stream (host copies dropped as we go)."""
     import numpy as np
@@ -75,6 +127,8 @@ def main():
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-t512", action="store_true")
+    ap.add_argument("--probe", action="store_true",
+                    help="counter run only: a known-size copy and 4 forwards, no timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d "
@@ -89,6 +143,9 @@ def main():
     device = "cuda:0"
     torch.cuda.set_device(0)
     vqmlp.lib()
+    if args.probe:
+        probe(device)
+        return
 
     # ---------------------------------------------------------------- T = 8, 64-layer stream
     layers = build_stream(args.layers, device)
@@ -121,22 +178,26 @@ def main():
     gbs = bytes_step / (ms_step * 1e-3) / 1e9
     log("T=8 stream: %.3f ms/step, %.1f GB/s" % (ms_step, gbs))
 
-    # dominant kernel: one layer's forward, timed with events on its own stream, layers cycled
-    # so that every launch reads weights that are not cache-resident
-    n_fw = min(len(layers), 64)
-    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    durs = []
+    # dominant kernel: the T = 8 forward is one launch of the fused kernel; its average launch
+    # duration is timed with events on the stream it runs on, over back-to-back launches that
+    # cycle through the layers so that every launch reads weights that are not cache-resident
+    n_fw = len(layers)
     with torch.cuda.stream(stream):
-        for i in range(n_fw):
-            m, x = layers[i]
-            f0.record(stream)
-            m.forward(x, ys[i], ws, stream=stream)
-            f1.record(stream)
-            f1.synchronize()
-            durs.append(f0.elapsed_time(f1))
-    fw_ms = float(np.mean(durs[1:])) if len(durs) > 1 else durs[0]
+        for i in range(n_fw):  # warm
+            layers[i][0].forward(layers[i][1], ys[i], ws, stream=stream)
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 3
+        f0.record(stream)
+        for _ in range(reps):
+            for i in range(n_fw):
+                layers[i][0].forward(layers[i][1], ys[i], ws, stream=stream)
+        f1.record(stream)
+    f1.synchronize()
+    fw_ms = f0.elapsed_time(f1) / (reps * n_fw)
     fw_gbs = weight_bytes(H, I) / (fw_ms * 1e-3) / 1e9
-    log("single forward (events): %.1f us, %.1f GB/s" % (fw_ms * 1e3, fw_gbs))
+    log("fused forward launch (events, %d back-to-back): %.1f us, %.1f GB/s" % (reps * n_fw,
+                                                                              fw_ms * 1e3, fw_gbs))
+    traffic = measured_traffic()
 
     result = {
         "metric": "VQ3 MLP effective weight GB/s at T=8 + TFLOP/s at T=512, % of roofline",
@@ -155,9 +216,11 @@ def main():
                                "(H=5120, I=17408, one HIP graph, 6.50 GB of weights)",
                    "layers": len(layers), "T": 8, "H": H, "I": I,
                    "weight_bytes_per_layer": weight_bytes(H, I)},
-        "roofline": {"bound": "hbm", "kernel": "vqmlp_forward (one layer, T=8)",
+        "roofline": {"bound": "hbm", "kernel": "k_fused<5> (whole T=8 forward of one layer)",
                      "achieved": round(fw_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(fw_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(fw_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": weight_bytes(H, I),
+                     "us_per_launch": round(fw_ms * 1e3, 2)},
     }
     del graph
     layers_keep = layers  # noqa: F841
