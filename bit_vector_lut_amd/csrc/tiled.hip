@@ -38,10 +38,17 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
     constexpr int WM = BM / 2, WN = BN / 4;   // per-wave outputs per matrix
     constexpr int TM = WM / 16, TN = WN / 16;  // 16x16 tiles per wave per matrix
     static_assert(TM >= 1 && TN >= 1, "tile too small");
-    __shared__ __attribute__((aligned(16))) uint16_t Xs[2][BM][LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t Ws[2][NMAT][BN][LDK];
+    // One LDS block, the code tables first (address 0: a lookup address needs no base), then the
+    // two activation and the two weight tile buffers.
+    constexpr int kTabWords = DEC == kDecVQ3 ? NMAT * (BN / 8) * 64 : (BN / 8) * 8;
+    constexpr int kOffX = (kTabWords * 4 + 255) / 256 * 256;
+    constexpr int kOffW = kOffX + 2 * BM * LDK * 2;
+    constexpr int kLds = kOffW + 2 * NMAT * BN * LDK * 2;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
     // VQ3: NMAT x (BN/8) groups x 64 dwords; LUT: (BN/8) x 16 halves
-    __shared__ uint32_t tabs[DEC == kDecVQ3 ? NMAT * (BN / 8) * 64 : (BN / 8) * 8];
+    uint32_t* const tabs = reinterpret_cast<uint32_t*>(lds);
+    auto& Xs = *reinterpret_cast<uint16_t (*)[2][BM][LDK]>(lds + kOffX);
+    auto& Ws = *reinterpret_cast<uint16_t (*)[2][NMAT][BN][LDK]>(lds + kOffW);
 
     const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
     const int N = a.N, K = a.K, T = a.T;
@@ -53,7 +60,8 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
     if constexpr (DEC == kDecVQ3) {
         for (int i = tid; i < NMAT * (BN / 8) * 64; i += kGThreads) {
             const int m = i / ((BN / 8) * 64), r = i % ((BN / 8) * 64);
-            tabs[i] = a.cb[m][size_t(row0 / 8) * 64 + r];
+            const uint32_t* cb = (NMAT > 1 && m) ? a.cb[1] : a.cb[0];
+            tabs[i] = cb[size_t(row0 / 8) * 64 + r];
         }
     } else if constexpr (DEC == kDecLUT2 || DEC == kDecLUT4) {
         constexpr int E = 1 << DecTraits<DEC>::bits;
@@ -66,7 +74,7 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
     // ---- per-thread global fetch of one K tile
     // X: BM x 64 halves = BM*8 chunks of 16 bytes
     constexpr int XCH = BM * 8 / kGThreads;  // 16-byte chunks per thread
-    u32x4 xr[XCH];
+    u32x4 xr[2][XCH];  // two tiles in flight: the next one and the one after
     // weights: VQ3 -> NMAT*(BN/32) packed tiles x 64 lanes x 12 B (one lane record per thread);
     // LUT2 -> BN rows x 4 words (16 codes each); LUT4 -> BN rows x 8 words (2 per task);
     // DENSE -> BN rows x 64 halves (8 chunks of 16 B per row)
@@ -75,17 +83,16 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
                          : DEC == kDecLUT4 ? BN * 4
                                            : BN * 8;
     constexpr int WPT = (WTASKS + kGThreads - 1) / kGThreads;
-    uint32_t wr[WPT][4];
+    uint32_t wr[2][WPT][4];
 
-    auto fetch = [&](int kt) {
+    auto fetch = [&](int kt, int set) {
 #pragma unroll
         for (int i = 0; i < XCH; ++i) {
             const int c = tid + i * kGThreads;
             const int tt = c >> 3, c8 = (c & 7) * 8;
             const int tok = tok0 + tt;
             const uint16_t* src = a.x + size_t(tok < T ? tok : T - 1) * K + kt * kGK + c8;
-            xr[i] = *reinterpret_cast<const u32x4*>(src);
-            if (tok >= T) xr[i] = u32x4{0u, 0u, 0u, 0u};
+            xr[set][i] = *reinterpret_cast<const u32x4*>(src);  // rows past T zeroed at stage
         }
 #pragma unroll
         for (int i = 0; i < WPT; ++i) {
@@ -94,40 +101,45 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
             if constexpr (DEC == kDecVQ3) {
                 const int m = task / ((BN / 32) * 64), pt = (task / 64) % (BN / 32), ll = task & 63;
                 const int mt = row0 / 32 + pt;
+                // select between the two (uniform) base pointers instead of indexing the
+                // argument array per lane, which would load the pointer and wait for it
+                const uint8_t* cbase = (NMAT > 1 && m) ? a.codes[1] : a.codes[0];
                 const uint32_t* p = reinterpret_cast<const uint32_t*>(
-                    a.codes[m] + (size_t(mt) * KT + kt) * kTileBytes) + 3 * ll;
-                wr[i][0] = p[0];
-                wr[i][1] = p[1];
-                wr[i][2] = p[2];
+                    cbase + (size_t(mt) * KT + kt) * kTileBytes) + 3 * ll;
+                wr[set][i][0] = p[0];
+                wr[set][i][1] = p[1];
+                wr[set][i][2] = p[2];
             } else if constexpr (DEC == kDecLUT2) {
                 const int r = task >> 2, q = task & 3;  // 16 codes per word
                 const uint32_t* p = reinterpret_cast<const uint32_t*>(a.codes[0]) +
                                     (size_t(row0 + r) * K + kt * kGK) / 16 + q;
-                wr[i][0] = p[0];
+                wr[set][i][0] = p[0];
             } else if constexpr (DEC == kDecLUT4) {
                 const int r = task >> 2, q = task & 3;  // 2 words = 16 codes per task
                 const uint32_t* p = reinterpret_cast<const uint32_t*>(a.codes[0]) +
                                     (size_t(row0 + r) * K + kt * kGK) / 8 + 2 * q;
-                wr[i][0] = p[0];
-                wr[i][1] = p[1];
+                wr[set][i][0] = p[0];
+                wr[set][i][1] = p[1];
             } else {
                 const int r = task >> 3, c8 = (task & 7) * 8;
                 const int row = row0 + r < N ? row0 + r : N - 1;
                 const u32x4 v = *reinterpret_cast<const u32x4*>(a.dense + size_t(row) * K +
                                                                   kt * kGK + c8);
-                wr[i][0] = v[0];
-                wr[i][1] = v[1];
-                wr[i][2] = v[2];
-                wr[i][3] = v[3];
+                wr[set][i][0] = v[0];
+                wr[set][i][1] = v[1];
+                wr[set][i][2] = v[2];
+                wr[set][i][3] = v[3];
             }
         }
     };
 
-    auto stage = [&](int buf) {
+    auto stage = [&](int buf, int set) {
 #pragma unroll
         for (int i = 0; i < XCH; ++i) {
             const int c = tid + i * kGThreads;
-            *reinterpret_cast<u32x4*>(&Xs[buf][c >> 3][(c & 7) * 8]) = xr[i];
+            const bool valid = tok0 + (c >> 3) < T;
+            *reinterpret_cast<u32x4*>(&Xs[buf][c >> 3][(c & 7) * 8]) =
+                valid ? xr[set][i] : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int i = 0; i < WPT; ++i) {
@@ -137,7 +149,7 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
                 const int m = task / ((BN / 32) * 64), pt = (task / 64) % (BN / 32), ll = task & 63;
                 const int pl = pt * 16 + (ll & 15);  // row pair within the block
                 const uint32_t* tg = &tabs[(m * (BN / 8) + (pl >> 2)) * 64];
-                const uint32_t d0 = wr[i][0], d1 = wr[i][1], d2 = wr[i][2];
+                const uint32_t d0 = wr[set][i][0], d1 = wr[set][i][1], d2 = wr[set][i][2];
                 uint16_t* re = &Ws[buf][m][2 * pl][0];
                 uint16_t* ro = &Ws[buf][m][2 * pl + 1][0];
                 const int cb4 = 4 * (ll >> 4);
@@ -164,8 +176,8 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
 #pragma unroll
                 for (int h = 0; h < 8; ++h) {
                     const int j0 = 2 * h, j1 = 2 * h + 1;  // code index within the 16
-                    const uint32_t w0 = B == 2 ? wr[i][0] : wr[i][j0 >> 3];
-                    const uint32_t w1 = B == 2 ? wr[i][0] : wr[i][j1 >> 3];
+                    const uint32_t w0 = B == 2 ? wr[set][i][0] : wr[set][i][j0 >> 3];
+                    const uint32_t w1 = B == 2 ? wr[set][i][0] : wr[set][i][j1 >> 3];
                     const uint32_t c0 = (w0 >> (B * (j0 & (32 / B - 1)))) & ((1u << B) - 1);
                     const uint32_t c1 = (w1 >> (B * (j1 & (32 / B - 1)))) & ((1u << B) - 1);
                     out[h] = uint32_t(t16[c0]) | (uint32_t(t16[c1]) << 16);
@@ -176,7 +188,7 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
             } else {
                 const int r = task >> 3, c8 = (task & 7) * 8;
                 *reinterpret_cast<u32x4*>(&Ws[buf][0][r][c8]) =
-                    u32x4{wr[i][0], wr[i][1], wr[i][2], wr[i][3]};
+                    u32x4{wr[set][i][0], wr[set][i][1], wr[set][i][2], wr[set][i][3]};
             }
         }
     };
@@ -209,15 +221,24 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
         }
     };
 
+    // Two raw tiles in flight in registers: tile kt + 2 is requested while tile kt is multiplied,
+    // and decoded into LDS one step later, so its loads have two steps to arrive.
     __syncthreads();  // tables
-    fetch(0);
-    stage(0);
+    fetch(0, 0);
+    fetch(min(1, KT - 1), 1);
+    stage(0, 0);
     __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < KT) fetch(kt + 1);
-        compute(buf);
-        if (kt + 1 < KT) stage(buf ^ 1);
+    // The fetches are unconditional (tiles past the end reload the last one): a conditional
+    // load would make the wait before each stage count no younger loads and drain the queue.
+    for (int kt = 0; kt < KT; kt += 2) {
+        fetch(min(kt + 2, KT - 1), 0);
+        compute(0);
+        if (kt + 1 < KT) stage(1, 1);
+        __syncthreads();
+        if (kt + 1 >= KT) break;
+        fetch(min(kt + 3, KT - 1), 1);
+        compute(1);
+        if (kt + 2 < KT) stage(0, 0);
         __syncthreads();
     }
 
@@ -266,8 +287,8 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
         // a = silu(g) u sign for BM tokens x BN (= one rotation block) rows, then the block
         // Hadamard transform along the rows in LDS (fp32, reusing the W buffers)
         static_assert(NMAT == 2, "gate+up");
-        float* Ab = reinterpret_cast<float*>(&Ws[0][0][0][0]);  // [BM][BN + 1]
-        static_assert(sizeof(Ws) >= sizeof(float) * BM * (BN + 1), "LDS for the rotation");
+        float* Ab = reinterpret_cast<float*>(lds + kOffX);  // [BM][BN + 1] over X and W
+        static_assert(kLds - kOffX >= int(sizeof(float)) * BM * (BN + 1), "LDS for the rotation");
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
             const int rl = wn * WN + 16 * j + (l & 15);
