@@ -8,21 +8,21 @@
 //
 // One workgroup of 16 waves per CU; workgroup b takes streaming items b, b + G, b + 2G, ... (G
 // workgroups) after the input-rotation items r = b, b + G, ...:
-//   R  rotate input columns [r*rc, (r+1)*rc) of x into x~ (binary16), then raise flag r_rdy[r];
+//   R  rotate input columns [r*rc, (r+1)*rc) of x into x~ (binary16 pairs);
 //   G  gate and up of one 32-row tile over all of H (the matrix-core product of the skinny
 //      kernel: lane-private LDS codebooks, register code ring), epilogue silu(g) u sign;
 //   D  down projection of two 32-row tiles over one K slice of 16 * TPW tiles of I.
 // Work that needs several items is done right after one item of the set:
 //   F  one G tile of each rotation unit (max(bi, 32) rows; all tiles of a unit are processed
 //      in the same round by different workgroups) rotates the unit's a into the binary16 down
-//      operand once the other tiles' values are in, then raises fu_rdy[unit];
+//      operand once the other tiles' values are in;
 //   Y  the D item of the last K slice of a row pair sums the slices, scales and writes y.
-// Items hand data to later items through global memory.  High-volume hand-offs (a, the down
-// partial sums) are stored as 64-bit words {FP32 bits, tag}, tag = call epoch + 1, so the reader
-// checks each word itself and the writer never waits for its stores: on this GPU any wait for
-// a store also waits for every older load, which would drain the code prefetch.  The operand
-// hand-offs that many items read (x~ and the rotated a) use flags: the writer waits for its
-// stores and releases once, the reader acquires once.
+// Every hand-off between items goes through global memory as 64-bit words {32 data bits, tag},
+// tag = call epoch + 1: the reader checks each word itself and the writer never waits for its
+// stores.  On this GPU a wave's loads complete in order and any wait for a store also waits for
+// every older load, so a flag protocol (writer: wait for the stores, then raise a flag; reader:
+// see the flag, then load) would cost two more memory round trips per hand-off, each behind
+// the wave's code prefetch.  Rotations run in registers, one operand row per wave.
 // Every wait is bounded by spin_limit; a wait that runs out sets a bit in the error word and
 // the kernel finishes with wrong values instead of hanging.  No item waits for a later item of
 // its own workgroup and the grid is one workgroup per CU, so every wait ends.
@@ -43,24 +43,16 @@ __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
 __device__ __forceinline__ uint64_t ld_relaxed64(const uint64_t* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A 64-bit load that may hit caches (it can return an older value of the word; tagged words
+// make that visible to the reader).
+__device__ __forceinline__ uint64_t ld_cached64(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
 __device__ __forceinline__ void st_relaxed64(uint64_t* p, uint64_t v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void note_error(uint32_t* ctl, uint32_t bit) {
     __hip_atomic_fetch_or(ctl + kCtlError, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Publish a flag after the workgroup's hand-off stores.  Those stores are agent-coherent (they
-// write through to memory), so no L2 write-back is needed: each wave waits until its own stores
-// are done (vmcnt counts stores), the workgroup meets, and one thread sets the flag.
-__device__ __forceinline__ void publish(uint32_t* flag, uint32_t value) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    if (threadIdx.x == 0)
-        __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_coherent32(void* p, uint32_t v) {
-    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), v, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float dpp_xor1(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
@@ -69,6 +61,35 @@ __device__ __forceinline__ float dpp_xor1(float v) {
 __device__ __forceinline__ float dpp_xor2(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E,
                                                               0xF, 0xF, false));
+}
+
+constexpr int kRotVals = 4;  // values per lane of a rotated row (rows of up to 256 columns)
+
+// Walsh-Hadamard butterflies (Sylvester order, distances 1 .. b/2) over one row held by a wave:
+// value e < ne of lane l is column 64 e + l, or column l % 32 of a 32-column row (both halves
+// of the wave then hold it).  Distances below 64 pair lanes l and l ^ h; larger ones pair
+// values e and e ^ (h / 64) of one lane.
+__device__ __forceinline__ void wave_fwht(float (&v)[kRotVals], int ne, int b, int l) {
+    for (int h = 1; h < b && h < 64; h <<= 1) {
+        const bool upper = (l & h) != 0;
+#pragma unroll
+        for (int e = 0; e < kRotVals; ++e)
+            if (e < ne) {
+                const float p = __shfl_xor(v[e], h);
+                v[e] = upper ? p - v[e] : v[e] + p;
+            }
+    }
+#pragma unroll
+    for (int d = 1; d < kRotVals; d <<= 1)
+        if (64 * d < b) {
+#pragma unroll
+            for (int e = 0; e < kRotVals; ++e)
+                if (!(e & d) && (e | d) < ne) {
+                    const float x0 = v[e], x1 = v[e | d];
+                    v[e] = x0 + x1;
+                    v[e | d] = x0 - x1;
+                }
+        }
 }
 
 // A streaming item, decoded from its queue index (all fields uniform).
@@ -84,7 +105,11 @@ struct Item {
 
 template <int TPW>
 __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
-    constexpr int D = TPW;
+    constexpr int D = TPW;  // ring slots: slot t always holds tile t of some item
+    // Prefetch distance in tiles.  Code words are requested P tiles before their use, not a whole
+    // item ahead: the deeper the queue of streaming loads, the longer every other load of the
+    // workgroup (flags, hand-off words) waits behind it.
+    constexpr int P = TPW < 2 ? TPW : 2;
     constexpr int SWT = kW * TPW;  // K tiles per slice
     constexpr int BROW = SWT * kTileCols + 16;  // padded row of the activation operand
     // One LDS block with the lookup tables at address 0: a lookup address is then the code and
@@ -106,8 +131,6 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
     const int H = a.H, I = a.I, T = a.T;
     const int MTh = H / kTileRows, KTh = H / kTileCols, KTi = I / kTileCols;
     uint32_t* const ctl = a.ctl;
-    uint32_t* const r_rdy = ctl + kCtlHdr;
-    uint32_t* const fu_rdy = r_rdy + a.n_r;
     const uint32_t tag = ld_relaxed(ctl + kCtlEpoch) + 1u;
     const unsigned limit = a.spin_limit;
 
@@ -183,80 +206,69 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
         }
     };
 
-    // ---- input rotation item r: columns [r*rc, (r+1)*rc), all 8 operand rows
+    // ---- rotations: wave t < 8 rotates operand row t in registers (value e of lane l is column
+    // 64 e + l of the range, or column l % 32 of a 32-column range); even lanes store pairs
+    auto store_pairs = [&](uint64_t* dst, const float (&v)[kRotVals], int ne, int n, float norm) {
+#pragma unroll
+        for (int e = 0; e < kRotVals; ++e)
+            if (e < ne) {
+                const float mine = v[e] * norm, next = dpp_xor1(mine);
+                const int c = n >= 64 ? 64 * e + l : l;
+                if (!(l & 1) && c < n)
+                    st_relaxed64(dst + c / 2, (uint64_t(tag) << 32) | f2h(mine) | (f2h(next) << 16));
+            }
+    };
+    // input rotation item r: columns [r*rc, (r+1)*rc) of x . s . sign, all 8 operand rows
     auto rotate_in = [&](int r) {
-        float* sc = reinterpret_cast<float*>(&red[0][0][0]);  // 8 x rc <= 8192 floats
-        const int rc = a.rc, c0 = r * rc;
-        for (int i = tid; i < 8 * rc; i += kW * 64) {
-            const int t = i / rc, col = c0 + i % rc;
-            float v = 0.f;
-            if (t < T) {
-                v = h2f(a.x[size_t(t) * H + col]) * h2f(a.s[col]);
-                if (a.sign_h && a.sign_h[col] < 0) v = -v;
+        const int rc = a.rc, c0 = r * rc, ne = rc >= 64 ? rc / 64 : 1;
+        if (w < kSkinnyT) {
+            float v[kRotVals];
+#pragma unroll
+            for (int e = 0; e < kRotVals; ++e) {
+                v[e] = 0.f;
+                const int col = c0 + (rc >= 64 ? 64 * e + l : (l & 31));
+                if (e < ne && w < T) {
+                    v[e] = h2f(a.x[size_t(w) * H + col]) * h2f(a.s[col]);
+                    if (a.sign_h && a.sign_h[col] < 0) v[e] = -v[e];
+                }
             }
-            sc[i] = v;
+            wave_fwht(v, ne, a.bh, l);
+            store_pairs(a.xb + size_t(w) * (H / 2) + c0 / 2, v, ne, rc, a.norm_h);
         }
-        __syncthreads();
-        for (int h = 1; h < a.bh; h <<= 1) {
-            for (int i = tid; i < 4 * rc; i += kW * 64) {
-                const int t = i / (rc / 2), jj = i % (rc / 2);
-                const int lo = (jj / h) * 2 * h + (jj % h), hi = lo + h;
-                const float x0 = sc[t * rc + lo], x1 = sc[t * rc + hi];
-                sc[t * rc + lo] = x0 + x1;
-                sc[t * rc + hi] = x0 - x1;
-            }
-            __syncthreads();
-        }
-        for (int i2 = tid; i2 < 4 * rc; i2 += kW * 64) {
-            const int i = 2 * i2, t = i / rc, col = c0 + i % rc;
-            st_coherent32(a.xb + size_t(t) * H + col,
-                          f2h(sc[i] * a.norm_h) | (f2h(sc[i + 1] * a.norm_h) << 16));
-        }
-        publish(r_rdy + r, tag);
     };
 
-    // ---- F: rotate rotation unit u of a into the binary16 down operand (scratch: 8 x fu floats)
-    auto job_rotate_mid = [&](int u, float* sc) {
-        const int fu = a.fu, r0 = u * fu;
-        // 8 * fu <= 8192 values, read as tagged words two per thread at a time
-        bool good = true;
-        for (int i0 = 0; i0 < 8 * fu; i0 += 2 * kW * 64) {
-            const int ia = i0 + tid, ib = i0 + tid + kW * 64;
-            const bool ha = ia < 8 * fu, hb = ib < 8 * fu;
-            const uint64_t* pa = a.act + size_t(ha ? ia / fu : 0) * I + r0 + (ha ? ia % fu : 0);
-            const uint64_t* pb = a.act + size_t(hb ? ib / fu : 0) * I + r0 + (hb ? ib % fu : 0);
-            uint64_t va = 0, vb = 0;
+    // ---- F: rotate rotation unit u of a into the binary16 down operand
+    auto job_rotate_mid = [&](int u) {
+        const int fu = a.fu, r0 = u * fu, ne = fu >= 64 ? fu / 64 : 1;
+        if (w < kSkinnyT) {
+            const uint64_t* src = a.act + size_t(w) * I + r0;
+            uint64_t q[kRotVals];
+#pragma unroll
+            for (int e = 0; e < kRotVals; ++e)
+                q[e] = e < ne ? ld_relaxed64(src + (fu >= 64 ? 64 * e + l : (l & 31))) : 0;
+            // the other tiles of the unit may still be on their way: wait for every word's tag
             for (unsigned n = 0;; ++n) {
-                va = ld_relaxed64(pa);
-                vb = ld_relaxed64(pb);
-                if ((!ha || uint32_t(va >> 32) == tag) && (!hb || uint32_t(vb >> 32) == tag)) break;
+                bool ready = true;
+#pragma unroll
+                for (int e = 0; e < kRotVals; ++e)
+                    if (e < ne && uint32_t(q[e] >> 32) != tag) ready = false;
+                if (ready) break;
                 if (n >= limit) {
-                    good = false;
+                    note_error(ctl, 2u);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+                for (int e = 0; e < kRotVals; ++e)
+                    if (e < ne && uint32_t(q[e] >> 32) != tag)
+                        q[e] = ld_relaxed64(src + (fu >= 64 ? 64 * e + l : (l & 31)));
             }
-            if (ha) sc[ia] = __builtin_bit_cast(float, uint32_t(va));
-            if (hb) sc[ib] = __builtin_bit_cast(float, uint32_t(vb));
+            float v[kRotVals];
+#pragma unroll
+            for (int e = 0; e < kRotVals; ++e) v[e] = __builtin_bit_cast(float, uint32_t(q[e]));
+            wave_fwht(v, ne, a.bi, l);
+            store_pairs(a.ab + size_t(w) * (I / 2) + r0 / 2, v, ne, fu, a.norm_i);
         }
-        if (!good) note_error(ctl, 2u);
-        __syncthreads();
-        for (int h = 1; h < a.bi; h <<= 1) {
-            for (int i = tid; i < 4 * fu; i += kW * 64) {
-                const int t = i / (fu / 2), jj = i % (fu / 2);
-                const int lo = (jj / h) * 2 * h + (jj % h), hi = lo + h;
-                const float x0 = sc[t * fu + lo], x1 = sc[t * fu + hi];
-                sc[t * fu + lo] = x0 + x1;
-                sc[t * fu + hi] = x0 - x1;
-            }
-            __syncthreads();
-        }
-        for (int i2 = tid; i2 < 4 * fu; i2 += kW * 64) {
-            const int i = 2 * i2, t = i / fu, row = r0 + i % fu;
-            st_coherent32(a.ab + size_t(t) * I + row,
-                          f2h(sc[i] * a.norm_i) | (f2h(sc[i + 1] * a.norm_i) << 16));
-        }
-        publish(fu_rdy + u, tag);
     };
 
     // ---- Y: y rows of pair q = sum over slices of the tagged partials, scaled
@@ -311,7 +323,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
         wave_tiles(c, kt0, ntile, last_kt);
         if (c.kind != kKindNone) {
 #pragma unroll
-            for (int t = 0; t < D; ++t)
+            for (int t = 0; t < P; ++t)
 #pragma unroll
                 for (int m = 0; m < 2; ++m) {
                     const int kt = kt0 + t < last_kt ? kt0 + t : last_kt;
@@ -388,11 +400,10 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
         __syncthreads();  // (B) partials consumed: red is free
         // (D) the rotation unit or row pair that this epilogue completed
         if (job >= 0) {
-            float* scratch = reinterpret_cast<float*>(&red[0][0][0]);
             if (job >> 30)
                 job_reduce_y(job & ((1 << 30) - 1));
             else
-                job_rotate_mid(job, scratch);
+                job_rotate_mid(job);
             __syncthreads();
         }
         if (cur_u >= a.total) break;
@@ -406,50 +417,57 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
             const int want = cur.kind == kKindG ? 0 : 1 + cur.sl;
             if (want != bstate) {
                 // Each wave waits for, and loads, only the columns of its own tiles: a wave whose
-                // inputs are ready starts while the others still wait.  The columns are read
-                // with agent-coherent loads, matching the writers' write-through stores.
+                // inputs are ready starts while the others still wait.  The operand words carry
+                // the call's tag; a word whose tag is not yet this call's is read again.
                 constexpr int wcols = TPW * kTileCols;
+                constexpr int kPairs = wcols / 2;                 // pairs per operand row
+                constexpr int kM = (kPairs + 63) / 64;            // pairs per lane and row
                 const int c0 = cur.sl * SWT * kTileCols + w * wcols;
                 const int K = cur.kind == kKindG ? H : I;
-                const int gran = cur.kind == kKindG ? a.rc : a.fu;  // columns per flag
-                const uint32_t* flags = cur.kind == kKindG ? r_rdy : fu_rdy;
-                bool good = true;
-                if (c0 < K) {
-                    const int f0 = c0 / gran, f1 = (min(c0 + wcols, K) - 1) / gran + 1;
-                    if (l < f1 - f0) {
-                        for (unsigned n = 0;; ++n) {
-                            if (ld_relaxed(flags + f0 + l) == tag) break;
-                            if (n >= limit) {
-                                good = false;
-                                break;
-                            }
-                            __builtin_amdgcn_s_sleep(2);
-                        }
-                    }
-                }
-                if (!__all(good) && l == 0) note_error(ctl, 1u);
-                const uint16_t* src = cur.kind == kKindG ? a.xb : a.ab;
-                constexpr int kPer = kSkinnyT * wcols / 8 / 64;  // 16-byte chunks per lane
-                u32x4 v[kPer];
+                // lane l holds pairs l + 64 m of every row; pairs past K multiply zero (their
+                // code loads are clamped)
+                const uint64_t* src = (cur.kind == kKindG ? a.xb : a.ab) + c0 / 2 + l;
+                const int npair = min(kPairs, (K - c0) / 2);
+                uint64_t q[kSkinnyT][kM];
+                // first through the caches (the operand is shared by many workgroups), then
+                // coherently for the words that are not yet this call's
 #pragma unroll
-                for (int k = 0; k < kPer; ++k) {
-                    const int i = l + 64 * k;
-                    const int t = i / (wcols / 8), c8 = (i % (wcols / 8)) * 8;
-                    v[k] = u32x4{0u, 0u, 0u, 0u};
-                    if (c0 + c8 < K) {
-                        const uint64_t* p =
-                            reinterpret_cast<const uint64_t*>(src + size_t(t) * K + c0 + c8);
-                        const uint64_t lo = ld_relaxed64(p), hi = ld_relaxed64(p + 1);
-                        v[k] = u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi),
-                                     uint32_t(hi >> 32)};
+                for (int t = 0; t < kSkinnyT; ++t)
+#pragma unroll
+                    for (int m = 0; m < kM; ++m)
+                        q[t][m] = l + 64 * m < npair
+                                      ? ld_cached64(src + size_t(t) * (K / 2) + 64 * m)
+                                      : uint64_t(tag) << 32;
+                auto fetch = [&]() {
+#pragma unroll
+                    for (int t = 0; t < kSkinnyT; ++t)
+#pragma unroll
+                        for (int m = 0; m < kM; ++m)
+                            if (uint32_t(q[t][m] >> 32) != tag)
+                                q[t][m] = ld_relaxed64(src + size_t(t) * (K / 2) + 64 * m);
+                };
+                for (unsigned n = 0;; ++n) {
+                    bool ready = true;
+#pragma unroll
+                    for (int t = 0; t < kSkinnyT; ++t)
+#pragma unroll
+                        for (int m = 0; m < kM; ++m)
+                            if (uint32_t(q[t][m] >> 32) != tag) ready = false;
+                    if (ready) break;
+                    if (n >= limit) {
+                        note_error(ctl, 1u);
+                        break;
                     }
+                    fetch();
+                    __builtin_amdgcn_s_sleep(2);
                 }
 #pragma unroll
-                for (int k = 0; k < kPer; ++k) {
-                    const int i = l + 64 * k;
-                    *reinterpret_cast<u32x4*>(
-                        &bsh[i / (wcols / 8)][w * wcols + (i % (wcols / 8)) * 8]) = v[k];
-                }
+                for (int t = 0; t < kSkinnyT; ++t)
+#pragma unroll
+                    for (int m = 0; m < kM; ++m)
+                        if (l + 64 * m < kPairs)
+                            *reinterpret_cast<uint32_t*>(&bsh[t][w * wcols + 2 * (l + 64 * m)]) =
+                                uint32_t(q[t][m]);
                 bstate = want;
             }
         }
@@ -464,6 +482,13 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                                     size_t(pit.t0) * pit.KT * kTileBytes;
             const uint8_t* nbase1 = (pit.kind == kKindD ? a.down.codes : a.up.codes) +
                                     size_t(pit.t1) * pit.KT * kTileBytes;
+            const Item cit = decode(cur_u);
+            int ckt0, cntile, clast_kt;
+            wave_tiles(cit, ckt0, cntile, clast_kt);
+            const uint8_t* cbase0 = (cit.kind == kKindD ? a.down.codes : a.gate.codes) +
+                                    size_t(cit.t0) * cit.KT * kTileBytes;
+            const uint8_t* cbase1 = (cit.kind == kKindD ? a.down.codes : a.up.codes) +
+                                    size_t(cit.t1) * cit.KT * kTileBytes;
             uint32_t laneb[2];
 #pragma unroll
             for (int m = 0; m < 2; ++m) laneb[m] = lane4 | uint32_t((buf * 2 + m) * kTab * 4);
@@ -493,17 +518,22 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                     else if (t + 1 < TPW)
                         look(ring[(t + 1) % D], 0, A[cp1]);
                     if (s == 2) {
-                        const int kt = nkt0 + t < nlast_kt ? nkt0 + t : nlast_kt;
+                        // slot t + P: tile t + P of this item, or of the next one past the end
+                        const int tt = (t + P) % TPW;
+                        const bool own = t + P < TPW;
+                        int kt = own ? ckt0 + tt : nkt0 + tt;
+                        const int lim = own ? clast_kt : nlast_kt;
+                        kt = kt < lim ? kt : lim;
                         const uint32_t* p0 = reinterpret_cast<const uint32_t*>(
-                                                 nbase0 + size_t(kt) * kTileBytes) + 3 * l;
+                                                 (own ? cbase0 : nbase0) + size_t(kt) * kTileBytes) + 3 * l;
                         const uint32_t* p1 = reinterpret_cast<const uint32_t*>(
-                                                 nbase1 + size_t(kt) * kTileBytes) + 3 * l;
-                        ring[t % D][0][0] = p0[0];
-                        ring[t % D][0][1] = p0[1];
-                        ring[t % D][0][2] = p0[2];
-                        ring[t % D][1][0] = p1[0];
-                        ring[t % D][1][1] = p1[1];
-                        ring[t % D][1][2] = p1[2];
+                                                 (own ? cbase1 : nbase1) + size_t(kt) * kTileBytes) + 3 * l;
+                        ring[tt][0][0] = p0[0];
+                        ring[tt][0][1] = p0[1];
+                        ring[tt][0][2] = p0[2];
+                        ring[tt][1][0] = p1[0];
+                        ring[tt][1][1] = p1[1];
+                        ring[tt][1][2] = p1[2];
                         // keep each refill where it is, one item ahead of its use
                         __builtin_amdgcn_sched_barrier(0);
                     }
@@ -546,8 +576,8 @@ int fused_tpw(int H) {
 
 hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, hipStream_t st) {
     if (!a.x || !a.y || !a.ctl || !a.xb || !a.act || !a.ab || !a.s || grid < 1 ||
-        (a.nsl > 1 && !a.part) || a.fu < kTileRows || a.fu > 1024 || a.rc > 1024 ||
-        8 * a.rc > 8192 || a.n_r > kW * 64 || a.T < 1 || a.T > kSkinnyT)
+        (a.nsl > 1 && !a.part) || a.fu < kTileRows || a.fu > 64 * kRotVals ||
+        a.rc > 64 * kRotVals || a.n_r > kW * 64 || a.T < 1 || a.T > kSkinnyT)
         return hipErrorInvalidValue;
 #define VQ_CASE(TP)                                                                  \
     if (tpw == TP) {                                                                 \

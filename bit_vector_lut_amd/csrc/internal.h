@@ -65,10 +65,10 @@ hipError_t launch_reduce_down(int T, int N, int slices, const float* part, const
                               uint16_t* y, hipStream_t st);
 
 // ---- fused persistent forward (T <= 8): the whole MLP in one launch
-// Control block (32-bit words, zero before the first call): word 1 counts finished workgroups
-// (back to zero after each call), word 2 collects error bits, word 3 is the call epoch; the
-// ready flags of the input-rotation items and of the intermediate rotation units follow from
-// word kCtlHdr.  Word 0 is reserved.
+// Control block (kCtlHdr 32-bit words, zero before the first call): word 1 counts finished
+// workgroups (back to zero after each call), word 2 collects error bits, word 3 is the call
+// epoch.  Word 0 is reserved.  Every hand-off between workgroups is a 64-bit word carrying the
+// call's tag (epoch + 1) beside 32 bits of data, so readers need no separate ready flags.
 enum { kCtlReserved = 0, kCtlExit = 1, kCtlError = 2, kCtlEpoch = 3, kCtlHdr = 16 };
 struct FusedArgs {
     VQ3View gate, up, down;
@@ -83,14 +83,14 @@ struct FusedArgs {
     const int8_t* sign_h;    // [H] or NULL
     const int8_t* sign_i;    // [I] or NULL
     uint16_t* y;             // [T][H] binary16
-    uint32_t* ctl;           // control block; flags follow at kCtlHdr: r_rdy[n_r], fu_rdy[n_fu]
-    uint16_t* xb;            // [8][H] rotated input, binary16, rows past T zero
-    uint64_t* act;           // [8][I] silu(g) u sign, FP32 bits tagged with the call's epoch
-    uint16_t* ab;            // [8][I] rotated intermediate, binary16
+    uint32_t* ctl;           // control block (kCtlHdr words)
+    uint64_t* xb;            // [8][H/2] rotated input, binary16 pairs, tagged; rows past T zero
+    uint64_t* act;           // [8][I] silu(g) u sign, FP32 bits, tagged
+    uint64_t* ab;            // [8][I/2] rotated intermediate, binary16 pairs, tagged
     uint64_t* part;          // [nsl][8][H] tagged FP32 partial sums of the down projection
     unsigned spin_limit;     // bound of every wait (then the error word records it)
 };
-inline size_t fused_ctl_words(int n_r, int n_fu) { return size_t(kCtlHdr) + n_r + n_fu; }
+inline size_t fused_ctl_words() { return size_t(kCtlHdr); }
 int fused_tpw(int H);  // tiles per wave of the fused kernel for hidden size H (0 = unsupported)
 hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, hipStream_t st);
 

@@ -228,9 +228,9 @@ namespace {
 struct Workspace {
     uint32_t* ctl;    // fused control block (zero before the first call, left zero by each)
     // fused region
-    uint16_t* fxb;    // [8][H]
+    uint64_t* fxb;    // [8][H/2] tagged binary16 pairs
     uint64_t* fact;   // [8][I] tagged
-    uint16_t* fab;    // [8][I]
+    uint64_t* fab;    // [8][I/2] tagged binary16 pairs
     uint64_t* fpart;  // [nsl][8][H] tagged
     // per-phase skinny region
     uint16_t* xb;     // [8][H] binary16 rotated input
@@ -258,9 +258,9 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
     };
     uint8_t* b = static_cast<uint8_t*>(base);
     const size_t o_ctl = take(std::max<size_t>(p->fz.ctl_words, kCtlHdr) * 4);
-    const size_t o_fxb = take(size_t(kSkinnyT) * H * 2);
+    const size_t o_fxb = take(size_t(kSkinnyT) * H * 4);
     const size_t o_fact = take(size_t(kSkinnyT) * I * 8);
-    const size_t o_fab = take(size_t(kSkinnyT) * I * 2);
+    const size_t o_fab = take(size_t(kSkinnyT) * I * 4);
     const size_t o_fpart = take(size_t(std::max(p->fz.nsl, 1)) * kSkinnyT * H * 8);
     const size_t o_xb = take(size_t(kSkinnyT) * H * 2);
     const size_t o_a = take(size_t(kSkinnyT) * I * 4);
@@ -273,9 +273,9 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
     w.bytes = off;
     if (b) {
         w.ctl = reinterpret_cast<uint32_t*>(b + o_ctl);
-        w.fxb = reinterpret_cast<uint16_t*>(b + o_fxb);
+        w.fxb = reinterpret_cast<uint64_t*>(b + o_fxb);
         w.fact = reinterpret_cast<uint64_t*>(b + o_fact);
-        w.fab = reinterpret_cast<uint16_t*>(b + o_fab);
+        w.fab = reinterpret_cast<uint64_t*>(b + o_fab);
         w.fpart = reinterpret_cast<uint64_t*>(b + o_fpart);
         w.xb = reinterpret_cast<uint16_t*>(b + o_xb);
         w.a = reinterpret_cast<float*>(b + o_a);
@@ -303,8 +303,9 @@ FusedGeom fused_geom(int H, int I, int bh, int bi) {
     g.nqd = (H / kTileRows + 1) / 2;
     g.n_fu = I / g.fu;
     g.total = g.n_r + g.n_g + g.nsl * g.nqd;
-    g.ctl_words = fused_ctl_words(g.n_r, g.n_fu);
-    if (g.n_r > 1024 || g.rc > 1024) g.tpw = 0;
+    g.ctl_words = fused_ctl_words();
+    // the kernel rotates rows of up to 256 columns in registers
+    if (g.n_r > 1024 || g.rc > 256 || g.fu > 256) g.tpw = 0;
     return g;
 }
 
