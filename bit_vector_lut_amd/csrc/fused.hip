@@ -103,7 +103,11 @@ struct Item {
 
 }  // namespace
 
-template <int TPW>
+// PH = false: the whole forward in one launch.  PH = true: one phase per launch (the gate/up
+// items, or the down items), with the operands written by an earlier launch as plain binary16
+// rows (a.xb16 / a.ab16) and a written as plain FP32 (a.act32): the launch boundary orders
+// them, so they are read through the caches with no tags.
+template <int TPW, bool PH>
 __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
     constexpr int D = TPW;  // ring slots: slot t always holds tile t of some item
     // Prefetch distance in tiles.  Code words are requested P tiles before their use, not a whole
@@ -125,6 +129,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
     auto& bsh = *reinterpret_cast<uint16_t (*)[kSkinnyT][BROW]>(lds + kOffB);  // activations
     auto& esc = *reinterpret_cast<float (*)[4][2][32]>(lds + kOffEsc);    // row scales
     auto& esg = *reinterpret_cast<uint32_t (*)[4][32]>(lds + kOffEsg);    // sign bits
+    int& qslot = *reinterpret_cast<int*>(lds + kOffOk);                    // item after next
 
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -132,6 +137,10 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
     const int MTh = H / kTileRows, KTh = H / kTileCols, KTi = I / kTileCols;
     uint32_t* const ctl = a.ctl;
     const uint32_t tag = ld_relaxed(ctl + kCtlEpoch) + 1u;
+    // The operand hand-offs alternate between two buffers by call parity: a cached line of the
+    // previous call then never shadows this call's words (and the tags catch older ones).
+    uint64_t* const xbp = a.xb + (tag & 1u) * size_t(kSkinnyT) * (H / 2);
+    uint64_t* const abp = a.ab + (tag & 1u) * size_t(kSkinnyT) * (I / 2);
     const unsigned limit = a.spin_limit;
 
     auto decode = [&](int u) -> Item {
@@ -233,7 +242,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                 }
             }
             wave_fwht(v, ne, a.bh, l);
-            store_pairs(a.xb + size_t(w) * (H / 2) + c0 / 2, v, ne, rc, a.norm_h);
+            store_pairs(xbp + size_t(w) * (H / 2) + c0 / 2, v, ne, rc, a.norm_h);
         }
     };
 
@@ -267,7 +276,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
 #pragma unroll
             for (int e = 0; e < kRotVals; ++e) v[e] = __builtin_bit_cast(float, uint32_t(q[e]));
             wave_fwht(v, ne, a.bi, l);
-            store_pairs(a.ab + size_t(w) * (I / 2) + r0 / 2, v, ne, fu, a.norm_i);
+            store_pairs(abp + size_t(w) * (I / 2) + r0 / 2, v, ne, fu, a.norm_i);
         }
     };
 
@@ -338,10 +347,13 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
     int bstate = -1;   // activation slice in bsh: 0 = x~, 1 + s = rotated a slice s
     const int tpu = a.fu / kTileRows;  // gate/up tiles per rotation unit
 
+    // Items after the first two rounds come from the queue (a.dyn) or round-robin.  The queue
+    // is read one item ahead of the next one, whose codes are prefetched during this item.
+    int nxt_u = a.n_r + b + G;
     for (int j = 0;; ++j) {
         const int buf = j & 1;
-        const int nxt_u = cur_u + G;
         __syncthreads();  // (A) tables of cur and partials of prev are complete
+        if (j > 0) nxt_u = a.dyn ? qslot : cur_u + G;
 
         // (C) epilogue of the previous item: reduce the 16 waves' partials
         int job = -1;  // F: rotation unit; Y: (1 << 30) | row pair
@@ -367,14 +379,21 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                     u *= esc[eb][1][rl];
                     const float act = g / (1.f + expf(-g)) * u;
                     const uint32_t bits = __builtin_bit_cast(uint32_t, act) ^ esg[eb][rl];
-                    st_relaxed64(a.act + size_t(t) * I + prev.id * kTileRows + rl,
-                                 (uint64_t(tag) << 32) | bits);
+                    if constexpr (PH)
+                        reinterpret_cast<uint32_t*>(a.act32)[size_t(t) * I + prev.id * kTileRows + rl] = bits;
+                    else
+                        st_relaxed64(a.act + size_t(t) * I + prev.id * kTileRows + rl,
+                                     (uint64_t(tag) << 32) | bits);
                 }
                 // One tile of each rotation unit rotates the whole unit once the others' values
                 // are in; which tile is hashed from the unit, so that round-robin assignment does
                 // not hand every rotation to the same workgroups.
+                // Round-robin order: which tile is hashed from the unit, so that the rotations do
+                // not all fall to the same workgroups.  Queue order: the unit's last tile, so the
+                // rotation only ever waits for tiles handed out before it.
                 const int unit = prev.id / tpu;
-                if (prev.id % tpu == int((unit ^ (unit >> 2) ^ (unit >> 5)) % tpu)) job = unit;
+                const int owner = a.dyn ? tpu - 1 : int((unit ^ (unit >> 2) ^ (unit >> 5)) % tpu);
+                if (!PH && prev.id % tpu == owner) job = unit;
             } else {
                 const int o = tid >> 1, hh = tid & 1;  // output o of 512, half of the waves
                 const int mm = o >> 8, e_l = o & 63, e_r = (o >> 6) & 3;
@@ -410,6 +429,11 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
 
         // (F) table operands of the next item (written after this item's products)
         const uint32_t tv_next = load_tab(decode(nxt_u));
+        int nn = a.total;
+        if (a.dyn && tid == 0 && nxt_u < a.total)
+            nn = a.n_r + 2 * G +
+                 int(__hip_atomic_fetch_add(ctl + kCtlQueue, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT));
 
         // (G) activation operand of this item: one K slice of x~ or of the rotated a, 8 rows
         {
@@ -420,54 +444,74 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                 // inputs are ready starts while the others still wait.  The operand words carry
                 // the call's tag; a word whose tag is not yet this call's is read again.
                 constexpr int wcols = TPW * kTileCols;
-                constexpr int kPairs = wcols / 2;                 // pairs per operand row
-                constexpr int kM = (kPairs + 63) / 64;            // pairs per lane and row
-                const int c0 = cur.sl * SWT * kTileCols + w * wcols;
-                const int K = cur.kind == kKindG ? H : I;
-                // lane l holds pairs l + 64 m of every row; pairs past K multiply zero (their
-                // code loads are clamped)
-                const uint64_t* src = (cur.kind == kKindG ? a.xb : a.ab) + c0 / 2 + l;
-                const int npair = min(kPairs, (K - c0) / 2);
-                uint64_t q[kSkinnyT][kM];
-                // first through the caches (the operand is shared by many workgroups), then
-                // coherently for the words that are not yet this call's
+                if constexpr (PH) {
+                    const int c0 = cur.sl * SWT * kTileCols + w * wcols;
+                    const int K = cur.kind == kKindG ? H : I;
+                    const uint16_t* src = cur.kind == kKindG ? a.xb16 : a.ab16;
+                    constexpr int kPer = kSkinnyT * wcols / 8 / 64;  // 16-byte chunks per lane
+                    u32x4 v[kPer];
 #pragma unroll
-                for (int t = 0; t < kSkinnyT; ++t)
-#pragma unroll
-                    for (int m = 0; m < kM; ++m)
-                        q[t][m] = l + 64 * m < npair
-                                      ? ld_cached64(src + size_t(t) * (K / 2) + 64 * m)
-                                      : uint64_t(tag) << 32;
-                auto fetch = [&]() {
-#pragma unroll
-                    for (int t = 0; t < kSkinnyT; ++t)
-#pragma unroll
-                        for (int m = 0; m < kM; ++m)
-                            if (uint32_t(q[t][m] >> 32) != tag)
-                                q[t][m] = ld_relaxed64(src + size_t(t) * (K / 2) + 64 * m);
-                };
-                for (unsigned n = 0;; ++n) {
-                    bool ready = true;
-#pragma unroll
-                    for (int t = 0; t < kSkinnyT; ++t)
-#pragma unroll
-                        for (int m = 0; m < kM; ++m)
-                            if (uint32_t(q[t][m] >> 32) != tag) ready = false;
-                    if (ready) break;
-                    if (n >= limit) {
-                        note_error(ctl, 1u);
-                        break;
+                    for (int k = 0; k < kPer; ++k) {
+                        const int i = l + 64 * k, t = i / (wcols / 8), c8 = (i % (wcols / 8)) * 8;
+                        v[k] = c0 + c8 < K ? *reinterpret_cast<const u32x4*>(src + size_t(t) * K + c0 + c8)
+                                           : u32x4{0u, 0u, 0u, 0u};
                     }
-                    fetch();
-                    __builtin_amdgcn_s_sleep(2);
-                }
 #pragma unroll
-                for (int t = 0; t < kSkinnyT; ++t)
+                    for (int k = 0; k < kPer; ++k) {
+                        const int i = l + 64 * k;
+                        *reinterpret_cast<u32x4*>(
+                            &bsh[i / (wcols / 8)][w * wcols + (i % (wcols / 8)) * 8]) = v[k];
+                    }
+                } else {
+                    constexpr int kPairs = wcols / 2;                 // pairs per operand row
+                    constexpr int kM = (kPairs + 63) / 64;            // pairs per lane and row
+                    const int c0 = cur.sl * SWT * kTileCols + w * wcols;
+                    const int K = cur.kind == kKindG ? H : I;
+                    // lane l holds pairs l + 64 m of every row; pairs past K multiply zero (their
+                    // code loads are clamped)
+                    const uint64_t* src = (cur.kind == kKindG ? xbp : abp) + c0 / 2 + l;
+                    const int npair = min(kPairs, (K - c0) / 2);
+                    uint64_t q[kSkinnyT][kM];
+                    // first through the caches (the operand is shared by many workgroups), then
+                    // coherently for the words that are not yet this call's
 #pragma unroll
-                    for (int m = 0; m < kM; ++m)
-                        if (l + 64 * m < kPairs)
-                            *reinterpret_cast<uint32_t*>(&bsh[t][w * wcols + 2 * (l + 64 * m)]) =
-                                uint32_t(q[t][m]);
+                    for (int t = 0; t < kSkinnyT; ++t)
+#pragma unroll
+                        for (int m = 0; m < kM; ++m)
+                            q[t][m] = l + 64 * m < npair
+                                          ? ld_cached64(src + size_t(t) * (K / 2) + 64 * m)
+                                          : uint64_t(tag) << 32;
+                    auto fetch = [&]() {
+#pragma unroll
+                        for (int t = 0; t < kSkinnyT; ++t)
+#pragma unroll
+                            for (int m = 0; m < kM; ++m)
+                                if (uint32_t(q[t][m] >> 32) != tag)
+                                    q[t][m] = ld_relaxed64(src + size_t(t) * (K / 2) + 64 * m);
+                    };
+                    for (unsigned n = 0;; ++n) {
+                        bool ready = true;
+#pragma unroll
+                        for (int t = 0; t < kSkinnyT; ++t)
+#pragma unroll
+                            for (int m = 0; m < kM; ++m)
+                                if (uint32_t(q[t][m] >> 32) != tag) ready = false;
+                        if (ready) break;
+                        if (n >= limit) {
+                            note_error(ctl, 1u);
+                            break;
+                        }
+                        fetch();
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+#pragma unroll
+                    for (int t = 0; t < kSkinnyT; ++t)
+#pragma unroll
+                        for (int m = 0; m < kM; ++m)
+                            if (l + 64 * m < kPairs)
+                                *reinterpret_cast<uint32_t*>(&bsh[t][w * wcols + 2 * (l + 64 * m)]) =
+                                    uint32_t(q[t][m]);
+}
                 bstate = want;
             }
         }
@@ -550,6 +594,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
             store_tab(buf ^ 1, (j + 1) & 3, tv_next);
             red[w][0][l] = acc[0];
             red[w][1][l] = acc[1];
+            if (tid == 0) qslot = nn;
         }
         prev_u = cur_u;
         cur_u = nxt_u;
@@ -563,6 +608,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                                                      __HIP_MEMORY_SCOPE_AGENT);
         if (done + 1u == gridDim.x) {
             ctl[kCtlExit] = 0u;
+            ctl[kCtlQueue] = 0u;
             ctl[kCtlEpoch] = tag;
         }
     }
@@ -574,14 +620,20 @@ int fused_tpw(int H) {
     return tpw >= 1 && tpw <= kSkinnyMaxTPW ? tpw : 0;
 }
 
-hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, hipStream_t st) {
-    if (!a.x || !a.y || !a.ctl || !a.xb || !a.act || !a.ab || !a.s || grid < 1 ||
-        (a.nsl > 1 && !a.part) || a.fu < kTileRows || a.fu > 64 * kRotVals ||
-        a.rc > 64 * kRotVals || a.n_r > kW * 64 || a.T < 1 || a.T > kSkinnyT)
+hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, bool phased, hipStream_t st) {
+    if (!a.y || !a.ctl || grid < 1 || (a.nsl > 1 && !a.part) || a.fu < kTileRows ||
+        a.fu > 64 * kRotVals || a.rc > 64 * kRotVals || a.n_r > kW * 64 || a.T < 1 ||
+        a.T > kSkinnyT)
+        return hipErrorInvalidValue;
+    if (phased ? (a.n_r != 0 || !a.xb16 || !a.ab16 || !a.act32)
+               : (!a.x || !a.s || !a.xb || !a.act || !a.ab))
         return hipErrorInvalidValue;
 #define VQ_CASE(TP)                                                                  \
     if (tpw == TP) {                                                                 \
-        hipLaunchKernelGGL(k_fused<TP>, dim3(grid), dim3(kW * 64), 0, st, a);        \
+        if (phased)                                                                  \
+            hipLaunchKernelGGL((k_fused<TP, true>), dim3(grid), dim3(kW * 64), 0, st, a); \
+        else                                                                         \
+            hipLaunchKernelGGL((k_fused<TP, false>), dim3(grid), dim3(kW * 64), 0, st, a); \
         return hipGetLastError();                                                    \
     }
     VQ_CASE(1) VQ_CASE(2) VQ_CASE(3) VQ_CASE(4) VQ_CASE(5)

@@ -65,11 +65,11 @@ hipError_t launch_reduce_down(int T, int N, int slices, const float* part, const
                               uint16_t* y, hipStream_t st);
 
 // ---- fused persistent forward (T <= 8): the whole MLP in one launch
-// Control block (kCtlHdr 32-bit words, zero before the first call): word 1 counts finished
-// workgroups (back to zero after each call), word 2 collects error bits, word 3 is the call
-// epoch.  Word 0 is reserved.  Every hand-off between workgroups is a 64-bit word carrying the
+// Control block (kCtlHdr 32-bit words, zero before the first call): word 0 is the item queue
+// head and word 1 counts finished workgroups (both back to zero after each call), word 2
+// collects error bits, word 3 is the call epoch.  Every hand-off between workgroups is a 64-bit word carrying the
 // call's tag (epoch + 1) beside 32 bits of data, so readers need no separate ready flags.
-enum { kCtlReserved = 0, kCtlExit = 1, kCtlError = 2, kCtlEpoch = 3, kCtlHdr = 16 };
+enum { kCtlQueue = 0, kCtlExit = 1, kCtlError = 2, kCtlEpoch = 3, kCtlHdr = 16 };
 struct FusedArgs {
     VQ3View gate, up, down;
     int H, I, T;
@@ -84,15 +84,21 @@ struct FusedArgs {
     const int8_t* sign_i;    // [I] or NULL
     uint16_t* y;             // [T][H] binary16
     uint32_t* ctl;           // control block (kCtlHdr words)
-    uint64_t* xb;            // [8][H/2] rotated input, binary16 pairs, tagged; rows past T zero
+    uint64_t* xb;            // [2][8][H/2] rotated input, binary16 pairs, tagged; rows past T
+                             // zero; two buffers used by call parity
     uint64_t* act;           // [8][I] silu(g) u sign, FP32 bits, tagged
-    uint64_t* ab;            // [8][I/2] rotated intermediate, binary16 pairs, tagged
+    uint64_t* ab;            // [2][8][I/2] rotated intermediate, binary16 pairs, tagged
     uint64_t* part;          // [nsl][8][H] tagged FP32 partial sums of the down projection
+    // one-phase launches: operands and a written by the launches before, untagged
+    const uint16_t* xb16;    // [8][H] rotated input, binary16, rows past T zero
+    const uint16_t* ab16;    // [8][I] rotated intermediate, binary16
+    float* act32;            // [8][I] silu(g) u sign
     unsigned spin_limit;     // bound of every wait (then the error word records it)
+    int dyn;                 // items after the first two rounds from the queue (else round-robin)
 };
 inline size_t fused_ctl_words() { return size_t(kCtlHdr); }
 int fused_tpw(int H);  // tiles per wave of the fused kernel for hidden size H (0 = unsupported)
-hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, hipStream_t st);
+hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, bool phased, hipStream_t st);
 
 // ---- tiled matrix-core path (T > 8): decoders, epilogues, kinds
 enum { kDecVQ3 = 0, kDecLUT2 = 1, kDecLUT4 = 2, kDecDense = 3 };

@@ -228,9 +228,9 @@ namespace {
 struct Workspace {
     uint32_t* ctl;    // fused control block (zero before the first call, left zero by each)
     // fused region
-    uint64_t* fxb;    // [8][H/2] tagged binary16 pairs
+    uint64_t* fxb;    // [2][8][H/2] tagged binary16 pairs
     uint64_t* fact;   // [8][I] tagged
-    uint64_t* fab;    // [8][I/2] tagged binary16 pairs
+    uint64_t* fab;    // [2][8][I/2] tagged binary16 pairs
     uint64_t* fpart;  // [nsl][8][H] tagged
     // per-phase skinny region
     uint16_t* xb;     // [8][H] binary16 rotated input
@@ -258,9 +258,9 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
     };
     uint8_t* b = static_cast<uint8_t*>(base);
     const size_t o_ctl = take(std::max<size_t>(p->fz.ctl_words, kCtlHdr) * 4);
-    const size_t o_fxb = take(size_t(kSkinnyT) * H * 4);
+    const size_t o_fxb = take(2 * size_t(kSkinnyT) * H * 4);
     const size_t o_fact = take(size_t(kSkinnyT) * I * 8);
-    const size_t o_fab = take(size_t(kSkinnyT) * I * 4);
+    const size_t o_fab = take(2 * size_t(kSkinnyT) * I * 4);
     const size_t o_fpart = take(size_t(std::max(p->fz.nsl, 1)) * kSkinnyT * H * 8);
     const size_t o_xb = take(size_t(kSkinnyT) * H * 2);
     const size_t o_a = take(size_t(kSkinnyT) * I * 4);
@@ -384,8 +384,52 @@ vqmlp_status run_fused(const vqmlp_plan* p, int T, const void* x, void* y, const
     a.ab = w.fab;
     a.part = w.fpart;
     a.spin_limit = 1u << 18;
-    const hipError_t e = launch_fused(a, g.tpw, p->cus, st);
+    a.dyn = 1;
+    const hipError_t e = launch_fused(a, g.tpw, p->cus, false, st);
     if (e != hipSuccess) return hip_fail(e, "fused forward");
+    return ok();
+}
+
+// The same items as four launches: rotate x, the gate/up items, rotate a, the down items.
+vqmlp_status run_fused_phased(const vqmlp_plan* p, int T, const void* x, void* y,
+                              const Workspace& w, hipStream_t st) {
+    const FusedGeom& g = p->fz;
+    const int H = p->d.H, I = p->d.I;
+    hipError_t e = launch_rotate(T, H, p->bh, x, 0, p->d.s_in, p->d.sign_h, w.xb, 3, st);
+    if (e != hipSuccess) return hip_fail(e, "rotate (input)");
+    FusedArgs a;
+    memset(&a, 0, sizeof a);
+    a.gate = p->gate;
+    a.up = p->up;
+    a.down = p->down;
+    a.H = H;
+    a.I = I;
+    a.T = T;
+    a.bh = p->bh;
+    a.bi = p->bi;
+    a.rc = g.rc;
+    a.fu = g.fu;
+    a.nsl = g.nsl;
+    a.nqd = g.nqd;
+    a.n_fu = g.n_fu;
+    a.sign_i = p->d.sign_i;
+    a.y = static_cast<uint16_t*>(y);
+    a.ctl = w.ctl;
+    a.part = w.fpart;
+    a.xb16 = w.xb;
+    a.ab16 = w.ab;
+    a.act32 = w.a;
+    a.spin_limit = 1u << 18;
+    a.n_g = g.n_g;  // gate/up items only
+    a.total = g.n_g;
+    e = launch_fused(a, g.tpw, std::min(p->cus, a.total), true, st);
+    if (e != hipSuccess) return hip_fail(e, "gate/up phase");
+    e = launch_rotate(T, I, p->bi, w.a, 1, nullptr, nullptr, w.ab, 3, st);
+    if (e != hipSuccess) return hip_fail(e, "rotate (intermediate)");
+    a.n_g = 0;  // down items only
+    a.total = g.nsl * g.nqd;
+    e = launch_fused(a, g.tpw, std::min(p->cus, a.total), true, st);
+    if (e != hipSuccess) return hip_fail(e, "down phase");
     return ok();
 }
 
@@ -643,7 +687,7 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
     if (!p) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_forward: null plan");
     if (T < 0 || T > p->d.t_max)
         return fail(VQMLP_ERR_INVALID_ARG, "T=%d outside [0, t_max=%d]", T, p->d.t_max);
-    if (path < 0 || path > 3) return fail(VQMLP_ERR_INVALID_ARG, "unknown path %d", path);
+    if (path < 0 || path > 4) return fail(VQMLP_ERR_INVALID_ARG, "unknown path %d", path);
     if (T == 0) return ok();
     if (!x || !y || !workspace) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_forward: null pointer");
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256))
@@ -662,10 +706,10 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
     // 1: the fused single-launch kernel, 3: the per-phase skinny kernels, 2: tiled; 0 picks
     // the fused kernel for T <= 8 where it applies, else the per-phase kernels, else tiled
     const bool fused_ok = p->fz.tpw > 0;
-    if (path == 1 || path == 3) {
+    if (path == 1 || path == 3 || path == 4) {
         if (T > kSkinnyT)
             return fail(VQMLP_ERR_UNSUPPORTED, "the skinny path takes T <= %d (T=%d)", kSkinnyT, T);
-        if (!(path == 1 ? fused_ok : p->skinny_ok))
+        if (!(path == 3 ? p->skinny_ok : fused_ok))
             return fail(VQMLP_ERR_UNSUPPORTED, "the skinny path takes H <= %d (H=%d)",
                         kSkinnyWaves * kSkinnyMaxTPW * kTileCols, p->d.H);
     }
@@ -675,6 +719,7 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
         return fail(VQMLP_ERR_UNSUPPORTED, "the tiled path takes H and I multiples of 64");
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (use == 1) return run_fused(p, T, x, y, w, st);
+    if (use == 4) return run_fused_phased(p, T, x, y, w, st);
     if (use == 3) return run_skinny(p, T, x, y, w, st);
     return run_tiled(p, T, x, y, w, st);
 }

@@ -113,7 +113,7 @@ def _run(vq, torch_dev, layer, path=0, mlp=None):
     return _f64(y)
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4])
 def test_config1_tiny(vq, oracle_mod, torch_dev, path):
     L = synth.config1()
     _say("config1 path=%d" % path)
@@ -132,7 +132,7 @@ def test_mlp_small_shapes(vq, oracle_mod, torch_dev, H, I, T):
     _say("small H=%d I=%d T=%d" % (H, I, T))
     mlp = vq.MLP.from_layer(L, t_max=max(T, 8))
     ref = oracle_mod.mlp_forward(L)
-    for path in ([0, 1, 2, 3] if T <= 8 else [0]):
+    for path in ([0, 1, 2, 3, 4] if T <= 8 else [0]):
         y = _run(vq, torch_dev, L, path, mlp)
         assert _report("H=%d I=%d T=%d path %d" % (H, I, T, path), y, ref) <= MLP_TOL
 
@@ -159,10 +159,11 @@ def test_config2_tiled_path(vq, oracle_mod, torch_dev, config2, config2_ref):
     assert _report("config2 tiled", y, config2_ref) <= MLP_TOL
 
 
-def test_config2_fused_path(vq, oracle_mod, torch_dev, config2, config2_ref):
-    _say("config2 fused kernel")
-    y = _run(vq, torch_dev, config2, 1)
-    assert _report("config2 fused", y, config2_ref) <= MLP_TOL
+@pytest.mark.parametrize("path", [1, 4])
+def test_config2_fused_path(vq, oracle_mod, torch_dev, config2, config2_ref, path):
+    _say("config2 fused kernel path %d" % path)
+    y = _run(vq, torch_dev, config2, path)
+    assert _report("config2 fused path %d" % path, y, config2_ref) <= MLP_TOL
 
 
 def test_fused_control_block_is_left_ready(vq, oracle_mod, torch_dev):
@@ -174,19 +175,20 @@ def test_fused_control_block_is_left_ready(vq, oracle_mod, torch_dev):
     ws = mlp.workspace(8)
     ref = oracle_mod.mlp_forward(L)
     fused_calls = 0
-    for path in (1, 0, 2, 1, 3, 1, 1):
+    for path in (1, 0, 2, 1, 3, 4, 1, 1):
         _say("control block: path %d" % path)
         y = _f64(mlp.forward(x, workspace=ws, path=path))
         torch_dev.cuda.synchronize()
         assert _report("path %d" % path, y, ref) <= MLP_TOL
         fused_calls += path in (0, 1)  # path 0 takes the fused kernel at T <= 8
+        fused_calls += 2 * (path == 4)  # one launch per phase
     ctl = ws[:64].cpu().numpy().view(np.uint32)
     assert ctl[0] == 0 and ctl[1] == 0, ctl[:4]  # queue head, exit count
     assert ctl[2] == 0, "a bounded wait ran out: error bits %#x" % ctl[2]
     assert ctl[3] == fused_calls
 
 
-@pytest.mark.parametrize("path", [1, 3])
+@pytest.mark.parametrize("path", [1, 3, 4])
 def test_config2_deterministic(vq, torch_dev, config2, path):
     mlp = vq.MLP.from_layer(config2)
     x = vq.to_device(config2.x)
