@@ -40,9 +40,9 @@ enum { kEpiGateUp = 0, kEpiDownFinal = 1, kEpiDownPart = 2 };
 // ---- launchers (kernels.hip).  All return hipError_t of the launch.
 hipError_t launch_dequant(const VQ3View& m, float* w, hipStream_t s);
 
-// out[t][.] = R(x . s) for a binary16 or float input.  mode: 0 = FP32 row-major [T][n],
-// 1 = binary16 row-major [T][n], 2 = expanded pair layout (T <= 8), 3 = binary16 row-major
-// [8][n] with the rows past T zero (T <= 8).
+// out[t][.] = R(x . s . sign) for a binary16 or float input, Hadamard blocks of b (a power of
+// two up to 1024; 1 = no rotation).  mode: 0 = FP32 row-major [T][n], 1 = binary16 row-major
+// [T][n], 3 = binary16 row-major [8][n] with the rows past T zero (T <= 8).
 hipError_t launch_rotate(int T, int n, int b, const void* x, int x_is_f32, const uint16_t* s,
                          const int8_t* sign, void* out, int mode, hipStream_t st);
 

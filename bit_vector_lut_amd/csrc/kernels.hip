@@ -52,70 +52,85 @@ hipError_t launch_dequant(const VQ3View& m, float* w, hipStream_t s) {
 // in-place butterfly (a, c) -> (a + c, a - c) over strides 1, 2, 4, ..., b/2, in FP32.
 // One workgroup rotates one block of b columns for 8 rows.
 
-constexpr int kRotRows = 8;
-
-__global__ void __launch_bounds__(256) k_rotate(int T, int n, int b, const void* x, int x_is_f32,
-                                                const uint16_t* s, const int8_t* sign, void* out,
-                                                int mode, float norm) {
-    __shared__ float buf[kRotRows * 1024];
-    const int blk = blockIdx.x, t0 = blockIdx.y * kRotRows;
-    const int nt = min(kRotRows, T - t0);
-    const int cnt = kRotRows * b;
-    for (int i = threadIdx.x; i < cnt; i += 256) {
-        const int tt = i / b, k = i % b, col = blk * b + k;
-        float v = 0.f;
-        if (tt < nt) {
-            const size_t idx = size_t(t0 + tt) * n + col;
-            v = x_is_f32 ? static_cast<const float*>(x)[idx]
+// One wave rotates one chunk of 64 * NE columns of one row (one block when b >= 64, 64 / b blocks
+// otherwise), in registers: value e of lane l is column c0 + 64 e + l.  Butterfly distances
+// below 64 pair lanes (cross-lane shuffles), larger ones pair values of a lane.
+template <int NE>
+__global__ void __launch_bounds__(256) k_rotate(int T, int rows, int n, int b, const void* x,
+                                                int x_is_f32, const uint16_t* s,
+                                                const int8_t* sign, void* out, int mode,
+                                                float norm) {
+    const int l = threadIdx.x & 63;
+    const int chunks = (n + 64 * NE - 1) / (64 * NE);
+    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wv >= rows * chunks) return;
+    const int t = wv / chunks, c0 = (wv % chunks) * 64 * NE;
+    float v[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const int col = c0 + 64 * e + l;
+        float u = 0.f;
+        if (col < n && t < T) {
+            const size_t idx = size_t(t) * n + col;
+            u = x_is_f32 ? static_cast<const float*>(x)[idx]
                          : h2f(static_cast<const uint16_t*>(x)[idx]);
-            if (s) v *= h2f(s[col]);
-            if (sign && sign[col] < 0) v = -v;
+            if (s) u *= h2f(s[col]);
+            if (sign && sign[col] < 0) u = -u;
         }
-        buf[i] = v;
+        v[e] = u;
     }
-    __syncthreads();
-    const int half = b / 2;
-    for (int h = 1; h < b; h <<= 1) {
-        for (int i = threadIdx.x; i < kRotRows * half; i += 256) {
-            const int tt = i / half, j = i % half;
-            const int lo = (j / h) * 2 * h + (j % h), hi = lo + h;
-            const float a = buf[tt * b + lo], c = buf[tt * b + hi];
-            buf[tt * b + lo] = a + c;
-            buf[tt * b + hi] = a - c;
+    for (int h = 1; h < b && h < 64; h <<= 1) {
+        const bool upper = (l & h) != 0;
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const float p = __shfl_xor(v[e], h);
+            v[e] = upper ? p - v[e] : v[e] + p;
         }
-        __syncthreads();
     }
-    for (int i = threadIdx.x; i < cnt; i += 256) {
-        const int tt = i / b, k = i % b, col = blk * b + k;
-        const float v = buf[i] * norm;
-        if (mode == 0) {
-            if (tt < nt) static_cast<float*>(out)[size_t(t0 + tt) * n + col] = v;
-        } else if (mode == 1) {
-            if (tt < nt) static_cast<uint16_t*>(out)[size_t(t0 + tt) * n + col] = (uint16_t)f2h(v);
-        } else if (mode == 3) {
-            // skinny operand: 8 rows, rows past T zero
-            static_cast<uint16_t*>(out)[size_t(tt) * n + col] = (uint16_t)f2h(v);
-        } else {
-            // skinny operand: K-step col/16, lane 16*kc + 2*tt + c', dword col%4; component c'
-            // of the pair-interleaved product gets the value, the other half stays zero.
-            const uint32_t hv = f2h(v);
-            const int ks = col / 16, kc = (col % 16) / 4, m = col % 4;
-            uint32_t* o = static_cast<uint32_t*>(out);
-            const int l0 = 16 * kc + 2 * tt;
-            o[(size_t(ks) * 64 + l0) * 4 + m] = hv;
-            o[(size_t(ks) * 64 + l0 + 1) * 4 + m] = hv << 16;
+#pragma unroll
+    for (int d = 1; d < NE; d <<= 1)
+        if (64 * d < b) {
+#pragma unroll
+            for (int e = 0; e < NE; ++e)
+                if (!(e & d)) {
+                    const float x0 = v[e], x1 = v[e | d];
+                    v[e] = x0 + x1;
+                    v[e | d] = x0 - x1;
+                }
         }
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const int col = c0 + 64 * e + l;
+        if (col >= n) continue;
+        const size_t idx = size_t(t) * n + col;
+        const float r = v[e] * norm;
+        if (mode == 0)
+            static_cast<float*>(out)[idx] = r;
+        else
+            static_cast<uint16_t*>(out)[idx] = (uint16_t)f2h(r);
     }
 }
 
 hipError_t launch_rotate(int T, int n, int b, const void* x, int x_is_f32, const uint16_t* s,
                          const int8_t* sign, void* out, int mode, hipStream_t st) {
-    if ((mode == 2 || mode == 3) && T > kSkinnyT) return hipErrorInvalidValue;
-    const dim3 grid(n / b, mode >= 2 ? 1 : (T + kRotRows - 1) / kRotRows);
+    if (mode == 3 && T > kSkinnyT) return hipErrorInvalidValue;
+    if (mode < 0 || mode == 2 || mode > 3 || b < 1 || b > 1024 || (b & (b - 1)) || n % b)
+        return hipErrorInvalidValue;
+    const int rows = mode == 3 ? kSkinnyT : T;  // mode 3 writes the zero rows past T too
+    const int ne = b <= 64 ? 1 : b / 64;
+    const int chunks = (n + 64 * ne - 1) / (64 * ne);
+    const int waves = rows * chunks;
     const float norm = float(1.0 / __builtin_sqrt(double(b)));
-    hipLaunchKernelGGL(k_rotate, grid, dim3(256), 0, st, T, n, b, x, x_is_f32, s, sign, out, mode,
-                       norm);
-    return hipGetLastError();
+    const dim3 grid((waves + 3) / 4);
+#define VQ_ROT(NE)                                                                        \
+    if (ne == NE) {                                                                       \
+        hipLaunchKernelGGL(k_rotate<NE>, grid, dim3(256), 0, st, T, rows, n, b, x,        \
+                           x_is_f32, s, sign, out, mode, norm);                           \
+        return hipGetLastError();                                                         \
+    }
+    VQ_ROT(1) VQ_ROT(2) VQ_ROT(4) VQ_ROT(8) VQ_ROT(16)
+#undef VQ_ROT
+    return hipErrorInvalidValue;
 }
 
 }  // namespace vqmlp
