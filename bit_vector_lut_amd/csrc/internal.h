@@ -109,10 +109,12 @@ enum {
     kGemmVQ3Down = 2,       // down -> y binary16 [T][N]
     kGemmLUT2 = 3,          // scalar LUT 2-bit + rank-r factors -> y binary16
     kGemmLUT4 = 4,          // scalar LUT 4-bit + rank-r factors -> y binary16
-    kGemmDense32 = 5        // dense binary16 rows -> fp32 [T][N]
+    kGemmDense32 = 5,       // dense binary16 rows -> fp32 [T][N]
+    kGemmVQ3DownSplit = 6   // down, K split -> unscaled fp32 partials [ksplit][T][N]
 };
 struct GemmArgs {
     int kind, N, K, T;
+    int ksplit;                // K splits (blockIdx.z; kGemmVQ3DownSplit only), 0 or 1 = none
     const uint16_t* x;         // [T][K] binary16
     const uint8_t* codes[2];   // packed code sections
     const uint32_t* cb[2];     // VQ3 codebooks / LUT tables (binary16 pairs)
@@ -127,5 +129,9 @@ struct GemmArgs {
     float norm;                // 1/sqrt(rotation block)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+// K splits for the down projection on `cus` CUs; y = scale . sum of the splits' planes.
+int gemm_down_split(int N, int K, int T, int cus);
+hipError_t launch_split_reduce(int T, int N, int splits, const float* part, const uint16_t* sc,
+                               uint16_t* y, hipStream_t st);
 
 }  // namespace vqmlp

@@ -19,6 +19,8 @@
 #include "device.h"
 #include "internal.h"
 
+#include <cmath>
+
 namespace vqmlp {
 
 constexpr int kGK = 64;        // K tile
@@ -223,22 +225,25 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
 
     // Two raw tiles in flight in registers: tile kt + 2 is requested while tile kt is multiplied,
     // and decoded into LDS one step later, so its loads have two steps to arrive.
+    // this workgroup's K tiles: split blockIdx.z of a.ksplit equal ranges
+    const int nsplit = a.ksplit > 1 ? a.ksplit : 1;
+    const int kb = int(blockIdx.z) * KT / nsplit, nk = (int(blockIdx.z) + 1) * KT / nsplit - kb;
     __syncthreads();  // tables
-    fetch(0, 0);
-    fetch(min(1, KT - 1), 1);
+    fetch(kb, 0);
+    fetch(kb + min(1, nk - 1), 1);
     stage(0, 0);
     __syncthreads();
     // The fetches are unconditional (tiles past the end reload the last one): a conditional
     // load would make the wait before each stage count no younger loads and drain the queue.
-    for (int kt = 0; kt < KT; kt += 2) {
-        fetch(min(kt + 2, KT - 1), 0);
+    for (int r = 0; r < nk; r += 2) {
+        fetch(kb + min(r + 2, nk - 1), 0);
         compute(0);
-        if (kt + 1 < KT) stage(1, 1);
+        if (r + 1 < nk) stage(1, 1);
         __syncthreads();
-        if (kt + 1 >= KT) break;
-        fetch(min(kt + 3, KT - 1), 1);
+        if (r + 1 >= nk) break;
+        fetch(kb + min(r + 3, nk - 1), 1);
         compute(1);
-        if (kt + 2 < KT) stage(0, 0);
+        if (r + 2 < nk) stage(0, 0);
         __syncthreads();
     }
 
@@ -354,8 +359,8 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
                     a.out32[size_t(tok) * N + row] = neg ? -act : act;
                 } else if constexpr (EPI == kEgScale16 || EPI == kEgLUT) {
                     a.out16[size_t(tok) * N + row] = (uint16_t)f2h(v0 * s0);
-                } else {
-                    a.out32[size_t(tok) * N + row] = v0;
+                } else {  // split z of a K-split product writes its own [T][N] plane
+                    a.out32[(size_t(blockIdx.z) * T + tok) * N + row] = v0;
                 }
             }
     }
@@ -363,14 +368,53 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
 
 template <int BM, int BN, int NMAT, int DEC, int EPI>
 static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t st) {
-    const dim3 grid((a.N + BN - 1) / BN, (a.T + BM - 1) / BM);
+    const dim3 grid((a.N + BN - 1) / BN, (a.T + BM - 1) / BM, a.ksplit > 1 ? a.ksplit : 1);
     hipLaunchKernelGGL((k_gemm<BM, BN, NMAT, DEC, EPI>), grid, dim3(kGThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+int gemm_down_split(int N, int K, int T, int cus) {
+    // K splits of the down projection that fill the CUs with whole rounds of workgroups (the
+    // row count alone leaves a partial last round); every split keeps at least 8 K tiles
+    const int bm = T > 64 ? 128 : 64;
+    const long tiles = long((N + 63) / 64) * ((T + bm - 1) / bm);
+    int best = 1;
+    double best_waste = 1e9;
+    for (int s = 1; s <= 16; s *= 2) {
+        if (K / kGK < 8 * s) break;
+        const double rounds = double(tiles * s) / cus;
+        const double waste = std::ceil(rounds) / rounds;
+        if (waste < best_waste - 0.05) {
+            best = s;
+            best_waste = waste;
+        }
+    }
+    return best;
+}
+
+__global__ void __launch_bounds__(256) k_split_reduce(int T, int N, int splits, const float* part,
+                                                      const uint16_t* sc, uint16_t* y) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= T * N) return;
+    const int row = i % N;
+    float sum = 0.f;
+    for (int z = 0; z < splits; ++z) sum += part[size_t(z) * T * N + i];
+    y[i] = (uint16_t)f2h(sum * h2f(sc[row]));
+}
+
+hipError_t launch_split_reduce(int T, int N, int splits, const float* part, const uint16_t* sc,
+                               uint16_t* y, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_split_reduce, dim3((T * N + 255) / 256), dim3(256), 0, st, T, N, splits,
+                       part, sc, y);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     if (a.K % kGK || a.N <= 0) return hipErrorInvalidValue;
+    if (a.ksplit > 1 && (a.kind != kGemmVQ3DownSplit || (a.K / kGK) < a.ksplit))
+        return hipErrorInvalidValue;
     // only the dense decoder clamps its rows; the coded ones need whole 64-row tiles
     if (a.kind != kGemmDense32 && a.N % 64) return hipErrorInvalidValue;
     const bool big = a.T > 64;          // 128-token tiles beyond one 64-row chunk
@@ -397,6 +441,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
         case kGemmDense32:
             return big ? launch_gemm_t<128, 64, 1, kDecDense, kEgPlain32>(a, st)
                        : launch_gemm_t<64, 64, 1, kDecDense, kEgPlain32>(a, st);
+        case kGemmVQ3DownSplit:  // unscaled FP32 partial sums, one plane per K split
+            return big ? launch_gemm_t<128, 64, 1, kDecVQ3, kEgPlain32>(a, st)
+                       : launch_gemm_t<64, 64, 1, kDecVQ3, kEgPlain32>(a, st);
     }
 #undef VQ_BM_BN
     return hipErrorInvalidValue;

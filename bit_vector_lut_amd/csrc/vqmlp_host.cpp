@@ -241,6 +241,8 @@ struct Workspace {
     uint16_t* xt;     // [T][H]
     float* a_t;       // [T][I]
     uint16_t* at;     // [T][I]
+    float* dpart;     // [dsplit][T][H] partial sums of a K-split down projection
+    int dsplit;
     size_t bytes;
 };
 
@@ -270,8 +272,12 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
     const size_t o_xt = take(size_t(Tt) * H * 2);
     const size_t o_at32 = take(size_t(Tt) * I * 4);
     const size_t o_at = take(size_t(Tt) * I * 2);
+    const int dsplit = T > kSkinnyT ? gemm_down_split(H, I, T, p->cus) : 1;
+    const size_t o_dpart = take(dsplit > 1 ? size_t(dsplit) * Tt * H * 4 : 0);
     w.bytes = off;
+    w.dsplit = dsplit;
     if (b) {
+        w.dpart = reinterpret_cast<float*>(b + o_dpart);
         w.ctl = reinterpret_cast<uint32_t*>(b + o_ctl);
         w.fxb = reinterpret_cast<uint64_t*>(b + o_fxb);
         w.fact = reinterpret_cast<uint64_t*>(b + o_fact);
@@ -478,6 +484,17 @@ vqmlp_status run_tiled(const vqmlp_plan* p, int T, const void* x, void* y, const
     d.cb[0] = p->down.cb;
     d.sc[0] = p->down.sc;
     d.out16 = static_cast<uint16_t*>(y);
+    if (w.dsplit > 1) {
+        // too few row tiles to fill the CUs: split K, then sum the planes and scale
+        d.kind = kGemmVQ3DownSplit;
+        d.ksplit = w.dsplit;
+        d.out32 = w.dpart;
+        e = launch_gemm(d, st);
+        if (e != hipSuccess) return hip_fail(e, "tiled down (K split)");
+        e = launch_split_reduce(T, H, w.dsplit, w.dpart, p->down.sc, static_cast<uint16_t*>(y), st);
+        if (e != hipSuccess) return hip_fail(e, "down split reduction");
+        return ok();
+    }
     e = launch_gemm(d, st);
     if (e != hipSuccess) return hip_fail(e, "tiled down");
     return ok();
