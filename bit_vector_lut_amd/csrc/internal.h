@@ -114,7 +114,7 @@ enum {
 };
 struct GemmArgs {
     int kind, N, K, T;
-    int ksplit;                // K splits (blockIdx.z; kGemmVQ3DownSplit only), 0 or 1 = none
+    int ksplit;                // K splits (blockIdx.z): down-split and dense kinds; 0/1 = none
     const uint16_t* x;         // [T][K] binary16
     const uint8_t* codes[2];   // packed code sections
     const uint32_t* cb[2];     // VQ3 codebooks / LUT tables (binary16 pairs)
@@ -129,9 +129,11 @@ struct GemmArgs {
     float norm;                // 1/sqrt(rotation block)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
-// K splits for the down projection on `cus` CUs; y = scale . sum of the splits' planes.
-int gemm_down_split(int N, int K, int T, int cus);
+// K splits for a product of this kind and shape on `cus` CUs (1 = none).  A split product
+// writes unscaled FP32 planes [ksplit][T][N]; the reductions below finish it.
+int gemm_split(int kind, int N, int K, int T, int cus);
 hipError_t launch_split_reduce(int T, int N, int splits, const float* part, const uint16_t* sc,
-                               uint16_t* y, hipStream_t st);
+                               uint16_t* y, hipStream_t st);  // y = sc . sum
+hipError_t launch_split_sum(int n, int splits, const float* part, float* out, hipStream_t st);
 
 }  // namespace vqmlp

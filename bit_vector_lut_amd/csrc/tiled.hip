@@ -373,15 +373,23 @@ static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-int gemm_down_split(int N, int K, int T, int cus) {
-    // K splits of the down projection that fill the CUs with whole rounds of workgroups (the
-    // row count alone leaves a partial last round); every split keeps at least 8 K tiles
-    const int bm = T > 64 ? 128 : 64;
-    const long tiles = long((N + 63) / 64) * ((T + bm - 1) / bm);
+int gemm_split(int kind, int N, int K, int T, int cus) {
+    // K splits that fill the CUs with whole rounds of workgroups where the output tiles alone
+    // leave a partial last round.  The down projection keeps at least 8 K tiles per split
+    // (the partial planes cost traffic); the small dense projection goes down to 2.
+    if ((kind != kGemmVQ3DownSplit && kind != kGemmDense32) || T <= 0 || N <= 0 || cus <= 0)
+        return 1;
+    const int bm = T > 64 ? 128 : 64, bn = 64;
+    const long tiles = long((N + bn - 1) / bn) * ((T + bm - 1) / bm);
+    const int kt = K / kGK;
+    if (kind == kGemmDense32) {
+        const long want = (2L * cus + tiles - 1) / tiles;
+        return int(std::max(1L, std::min<long>(want, kt / 2)));
+    }
     int best = 1;
     double best_waste = 1e9;
     for (int s = 1; s <= 16; s *= 2) {
-        if (K / kGK < 8 * s) break;
+        if (kt < 8 * s) break;
         const double rounds = double(tiles * s) / cus;
         const double waste = std::ceil(rounds) / rounds;
         if (waste < best_waste - 0.05) {
@@ -410,10 +418,36 @@ hipError_t launch_split_reduce(int T, int N, int splits, const float* part, cons
     return hipGetLastError();
 }
 
+// out = sum of the planes (FP32).  A workgroup owns 32 outputs; its 8 thread groups sum
+// interleaved subsets of the planes, then the 8 partial sums add in a fixed order.
+__global__ void __launch_bounds__(256) k_split_sum(int n, int splits, const float* part,
+                                                   float* out) {
+    __shared__ float ps[8][32];
+    const int o = threadIdx.x & 31, g = threadIdx.x >> 5, i = blockIdx.x * 32 + o;
+    float sum = 0.f;
+    if (i < n)
+        for (int z = g; z < splits; z += 8) sum += part[size_t(z) * n + i];
+    ps[g][o] = sum;
+    __syncthreads();
+    if (g == 0 && i < n) {
+        float v = ps[0][o];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) v += ps[k][o];
+        out[i] = v;
+    }
+}
+
+hipError_t launch_split_sum(int n, int splits, const float* part, float* out, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_split_sum, dim3((n + 31) / 32), dim3(256), 0, st, n, splits, part, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     if (a.K % kGK || a.N <= 0) return hipErrorInvalidValue;
-    if (a.ksplit > 1 && (a.kind != kGemmVQ3DownSplit || (a.K / kGK) < a.ksplit))
+    if (a.ksplit > 1 && ((a.kind != kGemmVQ3DownSplit && a.kind != kGemmDense32) ||
+                         (a.K / kGK) < a.ksplit))
         return hipErrorInvalidValue;
     // only the dense decoder clamps its rows; the coded ones need whole 64-row tiles
     if (a.kind != kGemmDense32 && a.N % 64) return hipErrorInvalidValue;

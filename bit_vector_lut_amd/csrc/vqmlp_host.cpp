@@ -272,7 +272,7 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
     const size_t o_xt = take(size_t(Tt) * H * 2);
     const size_t o_at32 = take(size_t(Tt) * I * 4);
     const size_t o_at = take(size_t(Tt) * I * 2);
-    const int dsplit = T > kSkinnyT ? gemm_down_split(H, I, T, p->cus) : 1;
+    const int dsplit = T > kSkinnyT ? gemm_split(kGemmVQ3DownSplit, H, I, T, p->cus) : 1;
     const size_t o_dpart = take(dsplit > 1 ? size_t(dsplit) * Tt * H * 4 : 0);
     w.bytes = off;
     w.dsplit = dsplit;
@@ -831,11 +831,18 @@ vqmlp_status vqmlp_lut_unpack(int bits, int N, int K, const void* packed, size_t
     return ok();
 }
 
+// The scalar-LUT forward has no plan; its K splits assume this many CUs (MI355X), so that the
+// workspace size does not depend on the device.
+constexpr int kLutSplitCUs = 256;
+
 vqmlp_status vqmlp_lut_workspace_bytes(int N, int K, int T, int r, size_t* bytes) {
     if (!bytes) return fail(VQMLP_ERR_INVALID_ARG, "bytes is NULL");
     if (N <= 0 || K <= 0 || T < 0 || r < 0 || r > 256)
         return fail(VQMLP_ERR_INVALID_ARG, "bad LUT workspace query");
-    *bytes = align256(size_t(T ? T : 1) * K * 2) + align256(size_t(T ? T : 1) * (r ? r : 1) * 4) + 256;
+    const size_t Tt = T ? T : 1;
+    const int zs = gemm_split(kGemmDense32, r ? r : 1, K, T, kLutSplitCUs);
+    *bytes = align256(Tt * K * 2) + align256(Tt * (r ? r : 1) * 4) +
+             (zs > 1 ? align256(size_t(zs) * Tt * (r ? r : 1) * 4) : 0) + 256;
     return ok();
 }
 
@@ -876,6 +883,7 @@ vqmlp_status vqmlp_lut_forward(int bits, int N, int K, int T, const void* packed
     hipError_t e = launch_rotate(T, K, had_block ? had_block : 1, x, 0, s, sign, xt, 1, hs);
     if (e != hipSuccess) return hip_fail(e, "rotate (mixer input)");
     if (r > 0) {
+        // z = x~ V^T has few outputs: split K over the CUs, then sum the planes
         GemmArgs g;
         memset(&g, 0, sizeof g);
         g.kind = kGemmDense32;
@@ -884,9 +892,16 @@ vqmlp_status vqmlp_lut_forward(int bits, int N, int K, int T, const void* packed
         g.T = T;
         g.x = xt;
         g.dense = V;
-        g.out32 = z;
+        g.ksplit = gemm_split(kGemmDense32, r, K, T, kLutSplitCUs);
+        float* zp = reinterpret_cast<float*>(wb + align256(size_t(T) * K * 2) +
+                                             align256(size_t(T) * r * 4));
+        g.out32 = g.ksplit > 1 ? zp : z;
         e = launch_gemm(g, hs);
         if (e != hipSuccess) return hip_fail(e, "rank-r projection");
+        if (g.ksplit > 1) {
+            e = launch_split_sum(T * r, g.ksplit, zp, z, hs);
+            if (e != hipSuccess) return hip_fail(e, "rank-r projection (K split sum)");
+        }
     }
     GemmArgs g;
     memset(&g, 0, sizeof g);
