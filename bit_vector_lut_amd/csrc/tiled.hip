@@ -42,7 +42,7 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
     static_assert(TM >= 1 && TN >= 1, "tile too small");
     // One LDS block, the code tables first (address 0: a lookup address needs no base), then the
     // two activation and the two weight tile buffers.
-    constexpr int kTabWords = DEC == kDecVQ3 ? NMAT * (BN / 8) * 64 : (BN / 8) * 8;
+    constexpr int kTabWords = DEC == kDecVQ3 ? 0 : (BN / 8) * 8;
     constexpr int kOffX = (kTabWords * 4 + 255) / 256 * 256;
     constexpr int kOffW = kOffX + 2 * BM * LDK * 2;
     constexpr int kLds = kOffW + 2 * NMAT * BN * LDK * 2;
@@ -58,12 +58,18 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
     const int row0 = blockIdx.x * BN, tok0 = blockIdx.y * BM;
     const int wm = w >> 2, wn = w & 3;
 
-    // ---- tables
+    // ---- tables.  VQ3: wave w decodes the GPW 8-row groups w * GPW .. (of all NMAT x BN/8) and
+    // keeps each group's 64-entry codebook in one register (lane e holds entry e); a lookup is
+    // a cross-lane read of that register (ds_bpermute), which never meets a bank conflict.
+    constexpr int GPW = DEC == kDecVQ3 ? NMAT * BN / 64 : 1;  // groups per wave (8 waves)
+    static_assert(DEC != kDecVQ3 || (NMAT * BN) % 64 == 0, "whole groups per wave");
+    uint32_t cbr[GPW];
     if constexpr (DEC == kDecVQ3) {
-        for (int i = tid; i < NMAT * (BN / 8) * 64; i += kGThreads) {
-            const int m = i / ((BN / 8) * 64), r = i % ((BN / 8) * 64);
+#pragma unroll
+        for (int i = 0; i < GPW; ++i) {
+            const int G = w * GPW + i, m = G / (BN / 8), g = G % (BN / 8);
             const uint32_t* cb = (NMAT > 1 && m) ? a.cb[1] : a.cb[0];
-            tabs[i] = cb[size_t(row0 / 8) * 64 + r];
+            cbr[i] = cb[size_t(row0 / 8 + g) * 64 + l];
         }
     } else if constexpr (DEC == kDecLUT2 || DEC == kDecLUT4) {
         constexpr int E = 1 << DecTraits<DEC>::bits;
@@ -80,12 +86,13 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
     // weights: VQ3 -> NMAT*(BN/32) packed tiles x 64 lanes x 12 B (one lane record per thread);
     // LUT2 -> BN rows x 4 words (16 codes each); LUT4 -> BN rows x 8 words (2 per task);
     // DENSE -> BN rows x 64 halves (8 chunks of 16 B per row)
-    constexpr int WTASKS = DEC == kDecVQ3 ? NMAT * (BN / 32) * 64
+    constexpr int WTASKS = DEC == kDecVQ3 ? kGThreads * GPW  // one code record per group
                          : DEC == kDecLUT2 ? BN * 4
                          : DEC == kDecLUT4 ? BN * 4
                                            : BN * 8;
     constexpr int WPT = (WTASKS + kGThreads - 1) / kGThreads;
-    uint32_t wr[2][WPT][4];
+    constexpr int WW = DEC == kDecVQ3 ? 2 : DEC == kDecLUT2 ? 1 : DEC == kDecLUT4 ? 2 : 4;
+    uint32_t wr[2][WPT][WW];  // raw words per task
 
     auto fetch = [&](int kt, int set) {
 #pragma unroll
@@ -101,16 +108,20 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
             const int task = tid + i * kGThreads;
             if (task >= WTASKS) break;
             if constexpr (DEC == kDecVQ3) {
-                const int m = task / ((BN / 32) * 64), pt = (task / 64) % (BN / 32), ll = task & 63;
-                const int mt = row0 / 32 + pt;
+                // lane l decodes pair (l >> 4) of group G at columns 4 (l & 15) .. + 3: codes
+                // 4 S .. 4 S + 3 (S = (l & 15) >> 2) of the packed lane record that holds
+                // column group (l & 3) of the pair (record layout: see the skinny kernel)
+                const int G = w * GPW + i, m = G / (BN / 8), g = G % (BN / 8);
+                const int mt = row0 / 32 + g / 4, ll = ((l & 3) << 4) | (4 * (g % 4) + (l >> 4));
                 // select between the two (uniform) base pointers instead of indexing the
                 // argument array per lane, which would load the pointer and wait for it
                 const uint8_t* cbase = (NMAT > 1 && m) ? a.codes[1] : a.codes[0];
+                // the two record words that hold bits 24 S .. 24 S + 23: words 0, 1 for S < 2,
+                // words 1, 2 otherwise
                 const uint32_t* p = reinterpret_cast<const uint32_t*>(
-                    cbase + (size_t(mt) * KT + kt) * kTileBytes) + 3 * ll;
+                    cbase + (size_t(mt) * KT + kt) * kTileBytes) + 3 * ll + (((l & 15) >> 3) & 1);
                 wr[set][i][0] = p[0];
                 wr[set][i][1] = p[1];
-                wr[set][i][2] = p[2];
             } else if constexpr (DEC == kDecLUT2) {
                 const int r = task >> 2, q = task & 3;  // 16 codes per word
                 const uint32_t* p = reinterpret_cast<const uint32_t*>(a.codes[0]) +
@@ -148,28 +159,27 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
             const int task = tid + i * kGThreads;
             if (task >= WTASKS) break;
             if constexpr (DEC == kDecVQ3) {
-                const int m = task / ((BN / 32) * 64), pt = (task / 64) % (BN / 32), ll = task & 63;
-                const int pl = pt * 16 + (ll & 15);  // row pair within the block
-                const uint32_t* tg = &tabs[(m * (BN / 8) + (pl >> 2)) * 64];
-                const uint32_t d0 = wr[set][i][0], d1 = wr[set][i][1], d2 = wr[set][i][2];
-                uint16_t* re = &Ws[buf][m][2 * pl][0];
-                uint16_t* ro = &Ws[buf][m][2 * pl + 1][0];
-                const int cb4 = 4 * (ll >> 4);
-#define VQ_STEP(S)                                                                   \
-    {                                                                                \
-        const uint32_t e0 = tg[code_of<4 * S + 0>(d0, d1, d2)];                      \
-        const uint32_t e1 = tg[code_of<4 * S + 1>(d0, d1, d2)];                      \
-        const uint32_t e2 = tg[code_of<4 * S + 2>(d0, d1, d2)];                      \
-        const uint32_t e3 = tg[code_of<4 * S + 3>(d0, d1, d2)];                      \
-        const u32x2 ev = u32x2{__builtin_amdgcn_perm(e1, e0, 0x05040100u),           \
-                               __builtin_amdgcn_perm(e3, e2, 0x05040100u)};          \
-        const u32x2 ov = u32x2{__builtin_amdgcn_perm(e1, e0, 0x07060302u),           \
-                               __builtin_amdgcn_perm(e3, e2, 0x07060302u)};          \
-        *reinterpret_cast<u32x2*>(re + 16 * S + cb4) = ev;                           \
-        *reinterpret_cast<u32x2*>(ro + 16 * S + cb4) = ov;                           \
-    }
-                VQ_STEP(0) VQ_STEP(1) VQ_STEP(2) VQ_STEP(3)
-#undef VQ_STEP
+                const int G = w * GPW + i, m = G / (BN / 8), g = G % (BN / 8);
+                const int S = (l & 15) >> 2;
+                // this lane's four codes: bits 24 S .. 24 S + 23 of the 96-bit record, from
+                // its words (0, 1) when S < 2, else (1, 2)
+                const uint32_t x = wr[set][i][0], y = wr[set][i][1];
+                const uint32_t c4 = __builtin_amdgcn_alignbit(y, S == 3 ? y : x, (24 * S) & 31);
+                uint32_t e[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t addr = q ? (c4 >> (6 * q - 2)) & 0xFCu : (c4 << 2) & 0xFCu;
+                    e[q] = uint32_t(__builtin_amdgcn_ds_bpermute(int(addr), int(cbr[i])));
+                }
+                // rows 2p, 2p + 1 of pair p = 4 g + (l >> 4), columns 4 (l & 15) .. + 3: each
+                // 16-lane quarter writes one contiguous 128-byte row segment
+                const int r = 8 * g + 2 * (l >> 4), c = 4 * (l & 15);
+                *reinterpret_cast<u32x2*>(&Ws[buf][m][r][c]) =
+                    u32x2{__builtin_amdgcn_perm(e[1], e[0], 0x05040100u),
+                          __builtin_amdgcn_perm(e[3], e[2], 0x05040100u)};
+                *reinterpret_cast<u32x2*>(&Ws[buf][m][r + 1][c]) =
+                    u32x2{__builtin_amdgcn_perm(e[1], e[0], 0x07060302u),
+                          __builtin_amdgcn_perm(e[3], e[2], 0x07060302u)};
             } else if constexpr (DEC == kDecLUT2 || DEC == kDecLUT4) {
                 constexpr int B = DecTraits<DEC>::bits;
                 const int r = task >> 2, q = task & 3;
