@@ -216,7 +216,7 @@ def main():
                                "(H=5120, I=17408, one HIP graph, 6.50 GB of weights)",
                    "layers": len(layers), "T": 8, "H": H, "I": I,
                    "weight_bytes_per_layer": weight_bytes(H, I)},
-        "roofline": {"bound": "hbm", "kernel": "k_fused<5> (whole T=8 forward of one layer)",
+        "roofline": {"bound": "hbm", "kernel": "k_fused<5, false> (whole T=8 forward of one layer, one launch)",
                      "achieved": round(fw_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(fw_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": weight_bytes(H, I),
