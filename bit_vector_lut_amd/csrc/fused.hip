@@ -187,31 +187,35 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
     const int cb_m = (w >> 2) & 1, cb_g = w & 3, cb_c = l;  // slot and group uniform per wave
     // one register per thread: a codebook word (waves 0-7), a row scale (waves 8, 9) or a sign
     // (wave 10)
+    // One dword per thread, loaded with no branch around the load (a load under a branch makes
+    // the next one wait for every older load, the code prefetch included): waves 0-7 a codebook
+    // word, waves 8 and 9 the dword holding their lane's row scale, wave 10 the dword holding
+    // its lane's sign; the other waves load a codebook word they ignore.
     auto load_tab = [&](const Item& it) -> uint32_t {
-        uint32_t v = 0u;
-        if (it.kind == kKindNone) return v;
-        if (w < 8) {
-            const uint32_t* cb = it.kind == kKindD ? a.down.cb : (cb_m ? a.up.cb : a.gate.cb);
-            const int mt = cb_m ? it.t1 : it.t0;
-            v = cb[size_t(mt * 4 + cb_g) * 64 + cb_c];
-        } else if ((w == 8 || w == 9) && l < 32) {
-            const int m = w - 8;
-            const uint16_t* sc = it.kind == kKindD ? a.down.sc : (m ? a.up.sc : a.gate.sc);
-            v = sc[(m ? it.t1 : it.t0) * kTileRows + l];
-        } else if (w == 10 && l < 32 && it.kind == kKindG && a.sign_i) {
-            v = uint32_t(uint8_t(a.sign_i[it.t0 * kTileRows + l]));
-        }
-        return v;
+        const bool dn = it.kind == kKindD;
+        const int mt = cb_m ? it.t1 : it.t0, sm = w & 1, r32 = l & 31;
+        const uint32_t* cbp =
+            (dn ? a.down.cb : (cb_m ? a.up.cb : a.gate.cb)) + size_t(mt * 4 + cb_g) * 64 + cb_c;
+        const uint16_t* scb = dn ? a.down.sc : (sm ? a.up.sc : a.gate.sc);
+        const uint32_t* scp = reinterpret_cast<const uint32_t*>(
+            scb + (sm ? it.t1 : it.t0) * kTileRows + (r32 & ~1));
+        const int8_t* sgb = a.sign_i ? a.sign_i : reinterpret_cast<const int8_t*>(a.gate.sc);
+        const uint32_t* sgp =
+            reinterpret_cast<const uint32_t*>(sgb + it.t0 * kTileRows + (r32 & ~3));
+        const uint32_t* p = (w == 8 || w == 9) ? scp : (w == 10 ? sgp : cbp);
+        return *p;
     };
-    auto store_tab = [&](int buf, int eb, uint32_t v) {
+    // signed: the item is a gate/up item and the intermediate rotation has signs
+    auto store_tab = [&](int buf, int eb, uint32_t v, bool signed_) {
         if (w < 8) {
             const u32x4 q = u32x4{v, v, v, v};
             *reinterpret_cast<u32x4*>(&tab[buf][cb_m][cb_c * 32 + 4 * cb_g]) = q;
             *reinterpret_cast<u32x4*>(&tab[buf][cb_m][cb_c * 32 + 4 * (cb_g + 4)]) = q;
         } else if ((w == 8 || w == 9) && l < 32) {
-            esc[eb][w - 8][l] = h2f(v);
+            esc[eb][w - 8][l] = h2f(v >> (16 * (l & 1)));
         } else if (w == 10 && l < 32) {
-            esg[eb][l] = (v >> 7) << 31;
+            const uint32_t byte = (v >> (8 * (l & 3))) & 0xFFu;
+            esg[eb][l] = signed_ ? (byte >> 7) << 31 : 0u;
         }
     };
 
@@ -323,7 +327,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
     int cur_u = a.n_r + b;
     {
         const Item c = decode(cur_u);
-        store_tab(0, 0, load_tab(c));
+        store_tab(0, 0, load_tab(c), c.kind == kKindG && a.sign_i);
     }
     uint32_t ring[D][2][3];
     {
@@ -353,7 +357,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
     for (int j = 0;; ++j) {
         const int buf = j & 1;
         __syncthreads();  // (A) tables of cur and partials of prev are complete
-        if (j > 0) nxt_u = a.dyn ? qslot : cur_u + G;
+        if (j > 0) nxt_u = a.dyn ? min(a.n_r + 2 * G + qslot, a.total) : cur_u + G;
 
         // (C) epilogue of the previous item: reduce the 16 waves' partials
         int job = -1;  // F: rotation unit; Y: (1 << 30) | row pair
@@ -363,12 +367,17 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
             if (prev.kind == kKindG) {
                 const int o = tid >> 2, qq = tid & 3;  // output o, quarter of the waves
                 const int e_l = o & 63, e_r = o >> 6;
-                float g = 0.f, u = 0.f;
+                // one float per read (a register-indexed vector element would serialize the
+                // reads behind one another)
+                const float* rf = reinterpret_cast<const float*>(&red[0][0][0]) + e_l * 4 + e_r;
+                float gv[4], uv[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    g += red[4 * qq + i][0][e_l][e_r];
-                    u += red[4 * qq + i][1][e_l][e_r];
+                    gv[i] = rf[((4 * qq + i) * 2 + 0) * 256];
+                    uv[i] = rf[((4 * qq + i) * 2 + 1) * 256];
                 }
+                float g = (gv[0] + gv[1]) + (gv[2] + gv[3]);
+                float u = (uv[0] + uv[1]) + (uv[2] + uv[3]);
                 g += dpp_xor1(g);
                 u += dpp_xor1(u);
                 g += dpp_xor2(g);
@@ -397,9 +406,11 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
             } else {
                 const int o = tid >> 1, hh = tid & 1;  // output o of 512, half of the waves
                 const int mm = o >> 8, e_l = o & 63, e_r = (o >> 6) & 3;
-                float v = 0.f;
+                const float* rf = reinterpret_cast<const float*>(&red[0][0][0]) + e_l * 4 + e_r;
+                float vv[8];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) v += red[8 * hh + i][mm][e_l][e_r];
+                for (int i = 0; i < 8; ++i) vv[i] = rf[((8 * hh + i) * 2 + mm) * 256];
+                float v = ((vv[0] + vv[1]) + (vv[2] + vv[3])) + ((vv[4] + vv[5]) + (vv[6] + vv[7]));
                 v += dpp_xor1(v);
                 const int tile = 2 * prev.id + mm;
                 if (hh == 0 && tile < MTh) {
@@ -428,12 +439,15 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
         if (cur_u >= a.total) break;
 
         // (F) table operands of the next item (written after this item's products)
-        const uint32_t tv_next = load_tab(decode(nxt_u));
-        int nn = a.total;
+        const Item nit = decode(nxt_u);
+        const uint32_t tv_next = load_tab(nit);
+        const bool sg_next = nit.kind == kKindG && a.sign_i;
+        // the queue slot after next; its value is first used after this item's products, so the
+        // wait for it does not hold up their code loads
+        uint32_t qv = uint32_t(a.total - a.n_r - 2 * G);
         if (a.dyn && tid == 0 && nxt_u < a.total)
-            nn = a.n_r + 2 * G +
-                 int(__hip_atomic_fetch_add(ctl + kCtlQueue, 1u, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT));
+            qv = __hip_atomic_fetch_add(ctl + kCtlQueue, 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
 
         // (G) activation operand of this item: one K slice of x~ or of the rotated a, 8 rows
         {
@@ -591,10 +605,10 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                 }
             }
             // (I) next item's tables into the idle buffers, this item's partials
-            store_tab(buf ^ 1, (j + 1) & 3, tv_next);
+            store_tab(buf ^ 1, (j + 1) & 3, tv_next, sg_next);
             red[w][0][l] = acc[0];
             red[w][1][l] = acc[1];
-            if (tid == 0) qslot = nn;
+            if (tid == 0) qslot = int(qv);
         }
         prev_u = cur_u;
         cur_u = nxt_u;
