@@ -102,7 +102,7 @@ hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, bool phased, hipS
 
 // ---- tiled matrix-core path (T > 8): decoders, epilogues, kinds
 enum { kDecVQ3 = 0, kDecLUT2 = 1, kDecLUT4 = 2, kDecDense = 3 };
-enum { kEgGateUp32 = 0, kEgGateUpRot = 1, kEgScale16 = 2, kEgLUT = 3, kEgPlain32 = 4 };
+enum { kEgGateUp32 = 0, kEgGateUpRot = 1, kEgScale16 = 2, kEgLUT = 3, kEgPlain32 = 4, kEgPart2 = 5 };
 enum {
     kGemmVQ3GateUp = 0,     // gate+up -> a fp32 [T][N] (sign applied)
     kGemmVQ3GateUpRot = 1,  // gate+up -> rotated a binary16 [T][N] (128-wide blocks)
@@ -110,7 +110,8 @@ enum {
     kGemmLUT2 = 3,          // scalar LUT 2-bit + rank-r factors -> y binary16
     kGemmLUT4 = 4,          // scalar LUT 4-bit + rank-r factors -> y binary16
     kGemmDense32 = 5,       // dense binary16 rows -> fp32 [T][N]
-    kGemmVQ3DownSplit = 6   // down, K split -> unscaled fp32 partials [ksplit][T][N]
+    kGemmVQ3DownSplit = 6,  // down, K split -> unscaled fp32 partials [ksplit][T][N]
+    kGemmVQ3GateUpSplit = 7 // gate+up, K split -> unscaled fp32 g, u planes [ksplit][T][2][N]
 };
 struct GemmArgs {
     int kind, N, K, T;
@@ -127,6 +128,7 @@ struct GemmArgs {
     const uint16_t* U;         // rank-r factor [N][r]
     int r;
     float norm;                // 1/sqrt(rotation block)
+    int ldo;                   // output row stride (0 = N)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 // K splits for a product of this kind and shape on `cus` CUs (1 = none).  A split product
@@ -135,5 +137,11 @@ int gemm_split(int kind, int N, int K, int T, int cus);
 hipError_t launch_split_reduce(int T, int N, int splits, const float* part, const uint16_t* sc,
                                uint16_t* y, hipStream_t st);  // y = sc . sum
 hipError_t launch_split_sum(int n, int splits, const float* part, float* out, hipStream_t st);
+// a = silu(sc_g sum g) (sc_u sum u) sign from K-split gate/up planes [splits][T][2][N]; rotate:
+// 128-wide rotation to binary16 out16 [T][ldo], else FP32 out32 [T][ldo]
+hipError_t launch_gateup_combine(int T, int N, int splits, const float* part,
+                                 const uint16_t* scg, const uint16_t* scu, const int8_t* sign,
+                                 int rotate, float norm, int ldo, uint16_t* out16, float* out32,
+                                 hipStream_t st);
 
 }  // namespace vqmlp

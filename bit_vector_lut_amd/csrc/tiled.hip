@@ -56,6 +56,7 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
     const int N = a.N, K = a.K, T = a.T;
     const int KT = K / kGK;
     const int row0 = blockIdx.x * BN, tok0 = blockIdx.y * BM;
+    const int ldo = a.ldo > 0 ? a.ldo : N;  // output row stride
     const int wm = w >> 2, wn = w & 3;
 
     // ---- tables.  VQ3: wave w decodes the GPW 8-row groups w * GPW .. (of all NMAT x BN/8) and
@@ -337,7 +338,7 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
             if (tok < T) {
                 const uint32_t h = f2h(Ab[tl * (BN + 1) + cc] * a.norm) |
                                    (f2h(Ab[tl * (BN + 1) + cc + 1] * a.norm) << 16);
-                *reinterpret_cast<uint32_t*>(a.out16 + size_t(tok) * N + row0 + cc) = h;
+                *reinterpret_cast<uint32_t*>(a.out16 + size_t(tok) * ldo + row0 + cc) = h;
             }
         }
         return;
@@ -366,9 +367,14 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
                 if constexpr (EPI == kEgGateUp32) {
                     const float g = v0 * s0, u = acc[NMAT - 1][i][j][r] * s1;
                     const float act = g / (1.f + expf(-g)) * u;
-                    a.out32[size_t(tok) * N + row] = neg ? -act : act;
+                    a.out32[size_t(tok) * ldo + row] = neg ? -act : act;
                 } else if constexpr (EPI == kEgScale16 || EPI == kEgLUT) {
-                    a.out16[size_t(tok) * N + row] = (uint16_t)f2h(v0 * s0);
+                    a.out16[size_t(tok) * ldo + row] = (uint16_t)f2h(v0 * s0);
+                } else if constexpr (EPI == kEgPart2) {
+                    // split z of a K-split gate/up product: unscaled g and u planes
+                    float* o = a.out32 + (size_t(blockIdx.z) * T + tok) * 2 * N + row;
+                    o[0] = v0;
+                    o[N] = acc[NMAT - 1][i][j][r];
                 } else {  // split z of a K-split product writes its own [T][N] plane
                     a.out32[(size_t(blockIdx.z) * T + tok) * N + row] = v0;
                 }
@@ -453,10 +459,71 @@ hipError_t launch_split_sum(int n, int splits, const float* part, float* out, hi
     return hipGetLastError();
 }
 
+// Finish a K-split gate/up product: a = silu(sc_g . sum g) . (sc_u . sum u) . sign for rows
+// [0, N) of the split part, then either the 128-wide rotation (binary16 out) or FP32 out.
+// One wave per (token, 128-row block); value e of lane l is row 64 e + l of the block.
+__global__ void __launch_bounds__(256) k_gateup_combine(int T, int N, int splits,
+                                                        const float* part, const uint16_t* scg,
+                                                        const uint16_t* scu, const int8_t* sign,
+                                                        int rotate, float norm, int ldo,
+                                                        uint16_t* out16, float* out32) {
+    const int l = threadIdx.x & 63, wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int nb = N / 128;
+    if (wv >= T * nb) return;
+    const int t = wv / nb, r0 = (wv % nb) * 128;
+    float v[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int row = r0 + 64 * e + l;
+        float g = 0.f, u = 0.f;
+        for (int z = 0; z < splits; ++z) {
+            const float* p = part + (size_t(z) * T + t) * 2 * N + row;
+            g += p[0];
+            u += p[N];
+        }
+        g *= h2f(scg[row]);
+        u *= h2f(scu[row]);
+        const float act = g / (1.f + expf(-g)) * u;
+        v[e] = sign && sign[row] < 0 ? -act : act;
+    }
+    if (!rotate) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) out32[size_t(t) * ldo + r0 + 64 * e + l] = v[e];
+        return;
+    }
+    for (int h = 1; h < 64; h <<= 1) {
+        const bool upper = (l & h) != 0;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const float p = __shfl_xor(v[e], h);
+            v[e] = upper ? p - v[e] : v[e] + p;
+        }
+    }
+    const float x0 = v[0], x1 = v[1];
+    v[0] = x0 + x1;
+    v[1] = x0 - x1;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+        out16[size_t(t) * ldo + r0 + 64 * e + l] = (uint16_t)f2h(v[e] * norm);
+}
+
+hipError_t launch_gateup_combine(int T, int N, int splits, const float* part,
+                                 const uint16_t* scg, const uint16_t* scu, const int8_t* sign,
+                                 int rotate, float norm, int ldo, uint16_t* out16, float* out32,
+                                 hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (N % 128) return hipErrorInvalidValue;
+    const int waves = T * (N / 128);
+    hipLaunchKernelGGL(k_gateup_combine, dim3((waves + 3) / 4), dim3(256), 0, st, T, N, splits,
+                       part, scg, scu, sign, rotate, norm, ldo, out16, out32);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     if (a.K % kGK || a.N <= 0) return hipErrorInvalidValue;
-    if (a.ksplit > 1 && ((a.kind != kGemmVQ3DownSplit && a.kind != kGemmDense32) ||
+    if (a.ksplit > 1 && ((a.kind != kGemmVQ3DownSplit && a.kind != kGemmDense32 &&
+                          a.kind != kGemmVQ3GateUpSplit) ||
                          (a.K / kGK) < a.ksplit))
         return hipErrorInvalidValue;
     // only the dense decoder clamps its rows; the coded ones need whole 64-row tiles
@@ -485,6 +552,10 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
         case kGemmDense32:
             return big ? launch_gemm_t<128, 64, 1, kDecDense, kEgPlain32>(a, st)
                        : launch_gemm_t<64, 64, 1, kDecDense, kEgPlain32>(a, st);
+        case kGemmVQ3GateUpSplit:  // unscaled g and u planes, one pair per K split
+            if (!n128) return hipErrorInvalidValue;
+            return big ? launch_gemm_t<128, 128, 2, kDecVQ3, kEgPart2>(a, st)
+                       : launch_gemm_t<64, 128, 2, kDecVQ3, kEgPart2>(a, st);
         case kGemmVQ3DownSplit:  // unscaled FP32 partial sums, one plane per K split
             return big ? launch_gemm_t<128, 64, 1, kDecVQ3, kEgPlain32>(a, st)
                        : launch_gemm_t<64, 64, 1, kDecVQ3, kEgPlain32>(a, st);

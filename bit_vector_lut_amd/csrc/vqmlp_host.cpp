@@ -225,6 +225,29 @@ struct vqmlp_plan {
 
 namespace {
 
+// The gate/up product of the tiled path in 128-row by 128- (or 64-) token tiles: the first
+// rows_main rows take whole rounds of workgroups on the CUs; the last rows_split rows, which
+// would leave a partial round, are split along K into `splits` parts over the CUs.
+struct GateUpSplit {
+    int rows_main, rows_split, splits;
+};
+GateUpSplit gateup_split(int I, int H, int T, int cus) {
+    GateUpSplit g{I, 0, 1};
+    if (I % 128 || T <= kSkinnyT || cus <= 0) return g;
+    const int bm = T > 64 ? 128 : 64;
+    const int rt = I / 128, tt = (T + bm - 1) / bm, total = rt * tt;
+    if (total <= cus || total % cus == 0) return g;
+    const int main_rt = (total / cus) * cus / tt;
+    const int left = (rt - main_rt) * tt;  // leftover tiles
+    const int kt = H / 64;
+    const int s = std::min(kt / 8, std::max(1, cus / left));
+    if (main_rt <= 0 || s < 2) return g;
+    g.rows_main = main_rt * 128;
+    g.rows_split = I - g.rows_main;
+    g.splits = s;
+    return g;
+}
+
 struct Workspace {
     uint32_t* ctl;    // fused control block (zero before the first call, left zero by each)
     // fused region
@@ -243,6 +266,8 @@ struct Workspace {
     uint16_t* at;     // [T][I]
     float* dpart;     // [dsplit][T][H] partial sums of a K-split down projection
     int dsplit;
+    float* gpart;     // [splits][T][2][rows] g, u partial sums of the K-split gate/up rows
+    GateUpSplit gs;
     size_t bytes;
 };
 
@@ -274,10 +299,15 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
     const size_t o_at = take(size_t(Tt) * I * 2);
     const int dsplit = T > kSkinnyT ? gemm_split(kGemmVQ3DownSplit, H, I, T, p->cus) : 1;
     const size_t o_dpart = take(dsplit > 1 ? size_t(dsplit) * Tt * H * 4 : 0);
+    const GateUpSplit gs = T > kSkinnyT ? gateup_split(I, H, T, p->cus) : GateUpSplit{I, 0, 1};
+    const size_t o_gpart =
+        take(gs.rows_split ? size_t(gs.splits) * Tt * 2 * gs.rows_split * 4 : 0);
     w.bytes = off;
     w.dsplit = dsplit;
+    w.gs = gs;
     if (b) {
         w.dpart = reinterpret_cast<float*>(b + o_dpart);
+        w.gpart = reinterpret_cast<float*>(b + o_gpart);
         w.ctl = reinterpret_cast<uint32_t*>(b + o_ctl);
         w.fxb = reinterpret_cast<uint64_t*>(b + o_fxb);
         w.fact = reinterpret_cast<uint64_t*>(b + o_fact);
@@ -459,17 +489,39 @@ vqmlp_status run_tiled(const vqmlp_plan* p, int T, const void* x, void* y, const
     g.sign = p->d.sign_i;
     // the gate/up epilogue rotates a itself when a rotation block is one 128-row tile
     const bool fused_rot = p->bi == 128 && I % 128 == 0;
-    if (fused_rot) {
-        g.kind = kGemmVQ3GateUpRot;
-        g.out16 = w.at;
-        g.norm = float(1.0 / 11.313708498984761);  // 1/sqrt(128)
-        e = launch_gemm(g, st);
-        if (e != hipSuccess) return hip_fail(e, "tiled gate/up");
-    } else {
-        g.kind = kGemmVQ3GateUp;
-        g.out32 = w.a_t;
-        e = launch_gemm(g, st);
-        if (e != hipSuccess) return hip_fail(e, "tiled gate/up");
+    const GateUpSplit& gs = w.gs;
+    g.N = gs.rows_main;
+    g.ldo = I;
+    g.norm = float(1.0 / 11.313708498984761);  // 1/sqrt(128)
+    g.kind = fused_rot ? kGemmVQ3GateUpRot : kGemmVQ3GateUp;
+    g.out16 = w.at;
+    g.out32 = w.a_t;
+    e = launch_gemm(g, st);
+    if (e != hipSuccess) return hip_fail(e, "tiled gate/up");
+    if (gs.rows_split) {
+        // the rows that would leave a partial round of workgroups: K split over the CUs, then
+        // one pass that sums the parts and applies the same epilogue
+        const int r0 = gs.rows_main;
+        GemmArgs q = g;
+        q.kind = kGemmVQ3GateUpSplit;
+        q.N = gs.rows_split;
+        q.ldo = 0;
+        q.ksplit = gs.splits;
+        for (int m = 0; m < 2; ++m) {
+            q.codes[m] = g.codes[m] + size_t(r0 / kTileRows) * (H / kTileCols) * kTileBytes;
+            q.cb[m] = g.cb[m] + size_t(r0 / 8) * 64;
+            q.sc[m] = g.sc[m] + r0;
+        }
+        q.sign = nullptr;
+        q.out32 = w.gpart;
+        e = launch_gemm(q, st);
+        if (e != hipSuccess) return hip_fail(e, "tiled gate/up (K split)");
+        e = launch_gateup_combine(T, gs.rows_split, gs.splits, w.gpart, p->gate.sc + r0,
+                                  p->up.sc + r0, p->d.sign_i ? p->d.sign_i + r0 : nullptr,
+                                  fused_rot ? 1 : 0, g.norm, I, w.at + r0, w.a_t + r0, st);
+        if (e != hipSuccess) return hip_fail(e, "gate/up split combine");
+    }
+    if (!fused_rot) {
         e = launch_rotate(T, I, p->bi, w.a_t, 1, nullptr, nullptr, w.at, 1, st);
         if (e != hipSuccess) return hip_fail(e, "rotate (intermediate)");
     }

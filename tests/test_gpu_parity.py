@@ -241,6 +241,21 @@ def test_config5_mlp_sampled_tokens(vq, oracle_mod, torch_dev, config5):
     assert _report("config5 MLP", y[toks], ref) <= MLP_TOL
 
 
+@pytest.mark.parametrize("H,I,T,bi", [(1024, 4352, 1024, None), (1024, 4352, 1024, 64),
+                                       (5120, 17408, 130, None)])
+def test_gateup_leftover_split_sampled_tokens(vq, oracle_mod, torch_dev, H, I, T, bi):
+    """Shapes whose gate/up tiles leave a partial round on 256 CUs: the leftover rows go through
+    the K-split product and the combine pass (with the fused 128-row rotation, or with the
+    FP32 product and the separate 64-wide rotation)."""
+    L = synth.mlp_layer(H, I, T, seed=H + I + T, outliers=True, had_block_i=bi)
+    _say("gate/up leftover split H=%d I=%d T=%d bi=%s" % (H, I, T, bi))
+    mlp = vq.MLP.from_layer(L, t_max=T)
+    y = _run(vq, torch_dev, L, 0, mlp)
+    toks = [0, 1, T // 2, T - 1]
+    ref = oracle_mod.mlp_forward(L, tokens=toks)
+    assert _report("leftover split H=%d I=%d T=%d" % (H, I, T), y[toks], ref) <= MLP_TOL
+
+
 # ------------------------------------------------------------------ scalar-LUT projection
 
 LUT_CASES = [  # N, K, T, rank, Hadamard block (0 = none)
