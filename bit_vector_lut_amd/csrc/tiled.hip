@@ -246,15 +246,18 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
     __syncthreads();
     // The fetches are unconditional (tiles past the end reload the last one): a conditional
     // load would make the wait before each stage count no younger loads and drain the queue.
+    // Each half-step stages unconditionally (past the end it decodes the clamped last tile into
+    // a buffer nobody reads), so the products and the next tile's decode form one block of
+    // independent instructions that the scheduler can interleave.
     for (int r = 0; r < nk; r += 2) {
         fetch(kb + min(r + 2, nk - 1), 0);
         compute(0);
-        if (r + 1 < nk) stage(1, 1);
+        stage(1, 1);
         __syncthreads();
         if (r + 1 >= nk) break;
         fetch(kb + min(r + 3, nk - 1), 1);
         compute(1);
-        if (r + 2 < nk) stage(0, 0);
+        stage(0, 0);
         __syncthreads();
     }
 
