@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libvqmlp.so")
-SOURCES = ["vqmlp_host.cpp", "kernels.hip", "skinny.hip", "fused.hip", "tiled.hip"]
+SOURCES = ["vqmlp_host.cpp", "kernels.hip", "skinny.hip", "fused.hip", "tiled.hip", "vq3mm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-FP32 VALU forms are kept out of the generated code: hipcc -O3 would otherwise form
@@ -22,6 +22,12 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
              "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
 
 
+# Per-source flags.  The register-decode product is one wave per SIMD with long independent
+# chains (cross-lane reads, matrix-core steps): the ILP-first scheduler batches its LDS reads and
+# keeps the accumulators in place, where the default one serialises them to save registers.
+SOURCE_FLAGS = {"vq3mm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source and link libvqmlp.so; always recompiles."""
     objdir = os.path.join(PKG, "_build")
@@ -29,7 +35,7 @@ def build(verbose: bool = False) -> str:
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [HIPCC, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+        cmd = [HIPCC, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), "-I", os.path.join(ROOT, "include"), "-I", CSRC,
                "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".hip"):
             cmd[1:1] = ["-x", "hip"]

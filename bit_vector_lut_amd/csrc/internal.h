@@ -131,6 +131,14 @@ struct GemmArgs {
     int ldo;                   // output row stride (0 = N)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
+// VQ3 products for T > 64 rows with the weights decoded in registers (vq3mm.hip): gate/up kinds
+// (two matrices) and down kinds (one).  Tile of one workgroup: bm tokens x bn rows.
+struct Vq3Tile {
+    int bm, bn;
+};
+Vq3Tile vq3mm_tile(int nmat);
+hipError_t launch_vq3mm(const GemmArgs& a, hipStream_t st);
+constexpr int kVq3mmMinT = 65;  // launch_gemm sends VQ3 kinds with at least this many rows there
 // K splits for a product of this kind and shape on `cus` CUs (1 = none).  A split product
 // writes unscaled FP32 planes [ksplit][T][N]; the reductions below finish it.
 int gemm_split(int kind, int N, int K, int T, int cus);

@@ -398,9 +398,24 @@ int gemm_split(int kind, int N, int K, int T, int cus) {
     // (the partial planes cost traffic); the small dense projection goes down to 2.
     if ((kind != kGemmVQ3DownSplit && kind != kGemmDense32) || T <= 0 || N <= 0 || cus <= 0)
         return 1;
+    const int kt = K / kGK;
+    if (kind == kGemmVQ3DownSplit && T >= kVq3mmMinT) {
+        // whole rounds of workgroups, each extra plane priced at 3% of the product
+        const Vq3Tile t = vq3mm_tile(1);
+        const long tiles = long((N + t.bn - 1) / t.bn) * ((T + t.bm - 1) / t.bm);
+        int best = 1;
+        double best_cost = 1e9;
+        for (int s = 1; s <= 16 && kt >= 4 * s; ++s) {
+            const double cost = double((tiles * s + cus - 1) / cus) / s + 0.03 * (s - 1);
+            if (cost < best_cost - 1e-9) {
+                best = s;
+                best_cost = cost;
+            }
+        }
+        return best;
+    }
     const int bm = T > 64 ? 128 : 64, bn = 64;
     const long tiles = long((N + bn - 1) / bn) * ((T + bm - 1) / bm);
-    const int kt = K / kGK;
     if (kind == kGemmDense32) {
         const long want = (2L * cus + tiles - 1) / tiles;
         return int(std::max(1L, std::min<long>(want, kt / 2)));
@@ -524,6 +539,10 @@ hipError_t launch_gateup_combine(int T, int N, int splits, const float* part,
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
+    if (a.T >= kVq3mmMinT &&
+        (a.kind == kGemmVQ3GateUp || a.kind == kGemmVQ3GateUpRot || a.kind == kGemmVQ3Down ||
+         a.kind == kGemmVQ3GateUpSplit || a.kind == kGemmVQ3DownSplit))
+        return launch_vq3mm(a, st);
     if (a.K % kGK || a.N <= 0) return hipErrorInvalidValue;
     if (a.ksplit > 1 && ((a.kind != kGemmVQ3DownSplit && a.kind != kGemmDense32 &&
                           a.kind != kGemmVQ3GateUpSplit) ||

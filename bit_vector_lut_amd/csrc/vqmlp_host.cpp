@@ -234,15 +234,16 @@ struct GateUpSplit {
 GateUpSplit gateup_split(int I, int H, int T, int cus) {
     GateUpSplit g{I, 0, 1};
     if (I % 128 || T <= kSkinnyT || cus <= 0) return g;
-    const int bm = T > 64 ? 128 : 64;
-    const int rt = I / 128, tt = (T + bm - 1) / bm, total = rt * tt;
+    const Vq3Tile t = T >= kVq3mmMinT ? vq3mm_tile(2) : Vq3Tile{64, 128};
+    if (I % t.bn) return g;
+    const int rt = I / t.bn, tt = (T + t.bm - 1) / t.bm, total = rt * tt;
     if (total <= cus || total % cus == 0) return g;
     const int main_rt = (total / cus) * cus / tt;
     const int left = (rt - main_rt) * tt;  // leftover tiles
     const int kt = H / 64;
     const int s = std::min(kt / 8, std::max(1, cus / left));
     if (main_rt <= 0 || s < 2) return g;
-    g.rows_main = main_rt * 128;
+    g.rows_main = main_rt * t.bn;
     g.rows_split = I - g.rows_main;
     g.splits = s;
     return g;
