@@ -127,7 +127,7 @@ struct GemmArgs {
     const float* z;            // rank-r activations [T][r]
     const uint16_t* U;         // rank-r factor [N][r]
     int r;
-    float norm;                // 1/sqrt(rotation block)
+    float norm;                // 1/sqrt(rotation block); K-split planes of vq3mm: plane scale
     int ldo;                   // output row stride (0 = N)
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);

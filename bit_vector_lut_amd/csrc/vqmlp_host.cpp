@@ -514,6 +514,7 @@ vqmlp_status run_tiled(const vqmlp_plan* p, int T, const void* x, void* y, const
             q.sc[m] = g.sc[m] + r0;
         }
         q.sign = nullptr;
+        q.norm = 1.f;  // unscaled planes
         q.out32 = w.gpart;
         e = launch_gemm(q, st);
         if (e != hipSuccess) return hip_fail(e, "tiled gate/up (K split)");
@@ -541,6 +542,7 @@ vqmlp_status run_tiled(const vqmlp_plan* p, int T, const void* x, void* y, const
         // too few row tiles to fill the CUs: split K, then sum the planes and scale
         d.kind = kGemmVQ3DownSplit;
         d.ksplit = w.dsplit;
+        d.norm = 1.f;  // unscaled planes
         d.out32 = w.dpart;
         e = launch_gemm(d, st);
         if (e != hipSuccess) return hip_fail(e, "tiled down (K split)");
