@@ -46,19 +46,27 @@ __device__ __forceinline__ uint32_t from_xor1(uint32_t v) {
     return uint32_t(__builtin_amdgcn_mov_dpp(int(v), kDppXor1, 0xF, 0xF, false));
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a),
+                                                  __builtin_bit_cast(half8, b), c, 0, 0, 0);
+}
+
 template <int NW, int BM, int RW, int NMAT, int EPI>
 __global__ void __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_vq3mm(GemmArgs a) {
     constexpr int NT = NW * 64;
-    constexpr int RF = RW / 16;       // 16-row operands per wave per matrix
-    constexpr int TF = BM / 16;       // 16-token operands
+    constexpr int RF = RW / 32;       // 32-row B operands per wave per matrix
+    constexpr int TF = BM / 32;       // 32-token A operands
     constexpr int BNW = NW * RW;      // rows per workgroup
-    constexpr int NTAB = NMAT * RF;   // centroid tables per wave (one per 16-row operand)
+    constexpr int NB = NMAT * RF;     // B operands per K step (one centroid table each)
     constexpr int XCH = BM * 8 / NT;  // 16-byte activation chunks per thread per K tile
     static_assert(RW % 32 == 0 && XCH >= 1 && (BM * 8) % NT == 0, "shape");
-    constexpr int kTabBytes = 64 * 32 * 4;        // 64 centroids x 32 bank columns
-    constexpr int kOffX = NW * NTAB * kTabBytes;  // activation tiles after the tables
-    constexpr int kXBuf = BM * kXK * 2;           // one activation tile
+    constexpr int kTabBytes = 64 * 32 * 4;      // 64 centroids x 32 bank columns
+    constexpr int kOffX = NW * NB * kTabBytes;  // activation tiles after the tables
+    constexpr int kXBuf = BM * kXK * 2;         // one activation tile
     constexpr int kMain = kOffX + 2 * kXBuf;
     constexpr int kEpBytes = EPI == kEgGateUpRot ? BM * (BNW + 1) * 4 : 0;
     constexpr int kLds = kMain > kEpBytes ? kMain : kEpBytes;
@@ -66,81 +74,67 @@ k_vq3mm(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
 
     const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
-    const int n = l & 15, kg = l >> 4, c0 = n & 1, pr = n >> 1;
+    const int n = l & 31, kh = l >> 5, c0 = n & 1, pr = n >> 1;
     const int N = a.N, K = a.K, T = a.T, KT = K / kXK;
     const int row0 = blockIdx.x * BNW, tok0 = blockIdx.y * BM;
     const int wrow = row0 + w * RW;  // first row of this wave
     const int ldo = a.ldo > 0 ? a.ldo : N;
     const int mt_last = N / 32 - 1;
 
-    // ---- centroid tables.  Table (m, j) serves operand j of matrix m (rows wrow + 16 j ..,
-    // two 8-row groups): word (e, b) -- centroid e, bank column b -- holds centroid e of the
-    // first group for b % 16 < 8 and of the second group otherwise.  Lane l reads column l % 32
-    // only, which holds its own row's group, so a lookup never meets a bank conflict.
-    {
+    // ---- centroid tables.  Table (m, j) serves B operand j of matrix m (rows wrow + 32 j ..,
+    // four 8-row groups): word (e, b) -- centroid e, bank column b -- holds centroid e of group
+    // b / 8.  Lane l reads column l % 32 only, which holds its own row's group, so a lookup never
+    // meets a bank conflict.
 #pragma unroll
-        for (int m = 0; m < NMAT; ++m) {
-            const uint32_t* cb = (NMAT > 1 && m) ? a.cb[1] : a.cb[0];
+    for (int m = 0; m < NMAT; ++m) {
+        const uint32_t* cb = (NMAT > 1 && m) ? a.cb[1] : a.cb[0];
 #pragma unroll
-            for (int j = 0; j < RF; ++j) {
-                unsigned char* tb = lds + (w * NTAB + m * RF + j) * kTabBytes;
-                const int g0 = wrow / 8 + 2 * j;
+        for (int j = 0; j < RF; ++j) {
+            unsigned char* tb = lds + (w * NB + m * RF + j) * kTabBytes;
+            const int g0 = wrow / 8 + 4 * j;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const int idx = l + 64 * k, e = idx >> 3, bq = idx & 7;  // 4 columns per store
-                    const int grp = min(g0 + ((bq >> 1) & 1), N / 8 - 1);
-                    const uint32_t v = cb[size_t(grp) * 64 + e];
-                    *reinterpret_cast<u32x4*>(tb + e * 128 + bq * 16) = u32x4{v, v, v, v};
-                }
+            for (int k = 0; k < 8; ++k) {
+                const int idx = l + 64 * k, e = idx >> 3, bq = idx & 7;  // 4 columns per store
+                const int grp = min(g0 + (bq >> 1), N / 8 - 1);
+                const uint32_t v = cb[size_t(grp) * 64 + e];
+                *reinterpret_cast<u32x4*>(tb + e * 128 + bq * 16) = u32x4{v, v, v, v};
             }
         }
     }
-    const uint32_t tab_lane = uint32_t(w * NTAB * kTabBytes) + uint32_t(l & 31) * 4u;
+    const uint32_t tab_lane = uint32_t(w * NB * kTabBytes) + uint32_t(n) * 4u;
 
-    // ---- this lane's codes.  Lane (row n of an operand: pair pr, component c0) looks up the
-    // centroids of its own pair for operand columns 4 c0 .. 4 c0 + 3, i.e. record slots 2 c0 and
-    // 2 c0 + 1 of lane record (kg, pair) -- record bits 48 c0 .. 48 c0 + 47, inside the two words
-    // starting at word c0.
+    // ---- this lane's codes.  Lane l holds B rows n = l % 32 (pair pr, component c0) at K
+    // columns 16 ks + 8 kh .. + 7 of each 16-column K step ks.  It looks up its pair's centroids
+    // for columns 4 c0 .. 4 c0 + 3 of those eight: for all four K steps these are the 16 codes of
+    // lane record (2 kh + c0, pair) of the packed tile, K step ks in its 24-bit slot ks.
     uint32_t voff[RF];
 #pragma unroll
     for (int j = 0; j < RF; ++j) {
-        const int mt = min(wrow / 32 + j / 2, mt_last);
-        const int pp = 8 * (j & 1) + pr;
-        voff[j] = uint32_t(mt) * uint32_t(KT) * kTileBytes + 12u * uint32_t((kg << 4) | pp) +
-                  4u * uint32_t(c0);
+        const int mt = min(wrow / 32 + j, mt_last);
+        voff[j] = uint32_t(mt) * uint32_t(KT) * kTileBytes +
+                  12u * uint32_t(((2 * kh + c0) << 4) | pr);
     }
-    const uint32_t sh16 = 16u * uint32_t(c0);
     // v_perm selectors: this lane's component and the partner's
     const uint32_t sel_own = c0 ? 0x07060302u : 0x05040100u;
     const uint32_t sel_oth = c0 ? 0x05040100u : 0x07060302u;
 
-    // ---- activation tiles in LDS: row r (token), 16-byte chunk q (operand positions 8q ..
-    // 8q + 7, i.e. K step q / 4 and lane group q % 4) stored at chunk q ^ (r % 8), so that the
-    // eight rows read together hit eight different chunks.
-    const uint32_t aoff0 = kOffX + uint32_t(n) * 128u + (uint32_t(kg ^ (n & 7)) << 4);
-    const uint32_t aoff1 = kOffX + uint32_t(n) * 128u + (uint32_t((4 + kg) ^ (n & 7)) << 4);
-    // staging: this thread's chunk x holds token row c / 8, columns 8 (c % 8) .. + 7; its four
-    // words go to operand chunks 2 (u % 2) + {0, 4, 1, 5}, word u / 2 of each
-    // (chunk x is NT / 8 rows below chunk 0, with the same row % 8: a constant offset)
-    uint32_t xw[4];
-    uint32_t xoff[XCH];  // global byte offset of the chunk in K tile 0
-    static_assert((NT / 8) % 8 == 0, "chunks of one thread share the row swizzle");
-    {
-        const int tt = tid >> 3, u = tid & 7;
-        constexpr int qd[4] = {0, 4, 1, 5};
+    // ---- activation tiles in LDS: row r (token), 16-byte chunk q (columns 8q .. 8q + 7) stored
+    // at chunk q ^ (r % 8), so that the eight rows read together hit eight different chunks.
+    uint32_t aoff[4];  // A operand of K step ks: row n, chunk 2 ks + kh
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const int q = 2 * (u & 1) + qd[d];
-            xw[d] = kOffX + uint32_t(tt) * 128u + (uint32_t(q ^ (tt & 7)) << 4) + 4u * uint32_t(u >> 1);
-        }
-    }
+    for (int ks = 0; ks < 4; ++ks)
+        aoff[ks] = kOffX + uint32_t(n) * 128u + (uint32_t((2 * ks + kh) ^ (n & 7)) << 4);
+    // staging: chunk x of this thread is token row tid / 8 + x NT / 8, columns 8 (tid % 8) ..;
+    // all of a thread's chunks share row % 8, hence one address plus constant offsets
+    static_assert((NT / 8) % 8 == 0, "chunks of one thread share the row swizzle");
+    const uint32_t xw = kOffX + uint32_t(tid >> 3) * 128u + (uint32_t((tid & 7) ^ ((tid >> 3) & 7)) << 4);
+    uint32_t xoff[XCH];  // global byte offset of the chunk in K tile 0
 #pragma unroll
     for (int x = 0; x < XCH; ++x) {
         const int c = tid + x * NT;
-        const int tt = c >> 3, u = c & 7;
         // rows past T repeat row T - 1: their products are never stored
-        const int tok = min(tok0 + tt, T - 1);
-        xoff[x] = (uint32_t(tok) * uint32_t(K) + 8u * uint32_t(u)) * 2u;
+        const int tok = min(tok0 + (c >> 3), T - 1);
+        xoff[x] = (uint32_t(tok) * uint32_t(K) + 8u * uint32_t(c & 7)) * 2u;
     }
 
     // Loads go through buffer resources: the lane's offset is fixed for the whole K loop and the
@@ -154,9 +148,10 @@ k_vq3mm(GemmArgs a) {
     const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.x), 0, int(uint32_t(T) * uint32_t(K) * 2u), kRsrcWord3);
 
-    u32x4 xr[XCH];          // activation chunks of the next K tile
-    u32x2 cw[NMAT][RF];     // code windows of the next K tile
-    u32x4 Bf[2][NMAT][RF];  // B operands [ks][m][j]
+    u32x4 xr[XCH];            // activation chunks of the next K tile
+    u32x3 rn[NMAT][RF];       // code records of the next K tile
+    u32x3 rc[NMAT][RF];       // code records being decoded
+    u32x4 Bf[4][NMAT][RF];    // B operands [ks][m][j]
 
     auto load_x = [&](int kt) {
 #pragma unroll
@@ -169,59 +164,47 @@ k_vq3mm(GemmArgs a) {
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
             for (int j = 0; j < RF; ++j)
-                cw[m][j] = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs_code[m], int(voff[j]),
+                rn[m][j] = __builtin_bit_cast(
+                    u32x3, __builtin_amdgcn_raw_buffer_load_b96(rs_code[m], int(voff[j]),
                                                                 kt * kTileBytes, 0));
     };
     auto stage = [&](uint32_t bufoff) {
+        unsigned char* base = lds + (xw + bufoff);
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            unsigned char* base = lds + (xw[d] + bufoff);
-#pragma unroll
-            for (int x = 0; x < XCH; ++x)
-                *reinterpret_cast<uint32_t*>(base + x * (NT / 8) * 128) = xr[x][d];
-        }
+        for (int x = 0; x < XCH; ++x)
+            *reinterpret_cast<u32x4*>(base + x * (NT / 8) * 128) = xr[x];
     };
-
-    // the lane's 48-bit code field of every record of one K tile, as low word and high half-word
-    uint32_t flo[NMAT][RF], fhi[NMAT][RF];
-    auto extract = [&]() {
+    auto take_codes = [&]() {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int j = 0; j < RF; ++j) {
-                const u32x2 v = cw[m][j];
-                flo[m][j] = __builtin_amdgcn_alignbit(v[1], v[0], sh16);
-                fhi[m][j] = v[1] >> sh16;
-            }
+            for (int j = 0; j < RF; ++j) rc[m][j] = rn[m][j];
     };
 
-    // Decoding B operand (ks, m, j) from the current code fields, in two phases: the four table
-    // reads (centroids of columns 4 c0 .. 4 c0 + 3 of the lane's pair), then the exchange with
-    // lane n ^ 1 that gives each lane its own component at all eight columns.
-    constexpr int NB = NMAT * RF;  // B operands per K step
-    uint32_t ev[2][4];             // table reads of two operands in flight
+    // Decoding B operand (ks, b = (m, j)), in two phases: the four table reads (centroids of the
+    // lane's pair at its four columns), then the exchange with lane l ^ 1 that gives each lane its
+    // own row's halves at all eight columns.
+    uint32_t ev[2][4];  // table reads of two operands in flight
     auto dec_read = [&](int ks, int b) {
         const int m = b / RF, j = b % RF;
-        const uint32_t lo = flo[m][j], hi = fhi[m][j];
-        // code k of the operand at field bit 24 (k / 2) + 12 ks + 6 (k % 2), moved to bits 12:7
-        uint32_t x0, x1, x2, x3;
-        if (ks == 0) {
-            x0 = lo << 7;
-            x1 = lo << 1;
-            x2 = lo >> 17;
-            x3 = __builtin_amdgcn_alignbit(hi, lo, 23);
-        } else {
-            x0 = lo >> 5;
-            x1 = lo >> 11;
-            x2 = hi << 3;
-            x3 = hi >> 3;
+        const u32x3 r = rc[m][j];
+        // code k of K step ks at record bit 24 ks + 6 k, moved to bits 12:7
+        uint32_t x[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int bit = 24 * ks + 6 * k;
+            const int wd = bit / 32, sh = bit % 32;
+            if (sh <= 7)
+                x[k] = r[wd] << (7 - sh);
+            else if (sh <= 26)
+                x[k] = r[wd] >> (sh - 7);
+            else
+                x[k] = __builtin_amdgcn_alignbit(r[wd + 1], r[wd], sh - 7);
         }
         const unsigned char* tb = lds + b * kTabBytes;
-        ev[b & 1][0] = *reinterpret_cast<const uint32_t*>(tb + and_or(x0, 0x1F80u, tab_lane));
-        ev[b & 1][1] = *reinterpret_cast<const uint32_t*>(tb + and_or(x1, 0x1F80u, tab_lane));
-        ev[b & 1][2] = *reinterpret_cast<const uint32_t*>(tb + and_or(x2, 0x1F80u, tab_lane));
-        ev[b & 1][3] = *reinterpret_cast<const uint32_t*>(tb + and_or(x3, 0x1F80u, tab_lane));
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            ev[b & 1][k] = *reinterpret_cast<const uint32_t*>(tb + and_or(x[k], 0x1F80u, tab_lane));
     };
     auto dec_place = [&](int ks, int b) {
         const int m = b / RF, j = b % RF;
@@ -233,22 +216,24 @@ k_vq3mm(GemmArgs a) {
         Bf[ks][m][j] = c0 ? u32x4{r0, r1, y0, y1} : u32x4{y0, y1, r0, r1};
     };
 
-    f32x4 acc[NMAT][RF][TF];
+    f32x16 acc[NMAT][RF][TF];
 #pragma unroll
     for (int m = 0; m < NMAT; ++m)
 #pragma unroll
         for (int j = 0; j < RF; ++j)
 #pragma unroll
-            for (int i = 0; i < TF; ++i) acc[m][j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < TF; ++i)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[m][j][i][q] = 0.f;
 
     auto readA = [&](uint32_t bufoff, int ks, int i) {
-        return *reinterpret_cast<const u32x4*>(lds + (ks ? aoff1 : aoff0) + bufoff + i * 2048);
+        return *reinterpret_cast<const u32x4*>(lds + aoff[ks] + bufoff + i * 32 * 128);
     };
     auto mma_unit = [&](int ks, int i, const u32x4& A) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int j = 0; j < RF; ++j) acc[m][j][i] = mfma16x16x32(A, Bf[ks][m][j], acc[m][j][i]);
+            for (int j = 0; j < RF; ++j) acc[m][j][i] = mfma32x32x16(A, Bf[ks][m][j], acc[m][j][i]);
     };
 
     // this workgroup's K tiles: split blockIdx.z of a.ksplit equal ranges
@@ -256,57 +241,62 @@ k_vq3mm(GemmArgs a) {
     const int kb = int(blockIdx.z) * KT / nsplit, nk = (int(blockIdx.z) + 1) * KT / nsplit - kb;
     auto tile = [&](int t) { return kb + min(t, nk - 1); };  // loads past the end repeat the last
 
-    // Prologue: tables, tile 0's activations in buffer 0, its K step 0 operands decoded; the
-    // codes and activations of tile 1 requested.
+    // Prologue: tables, tile 0's activations in buffer 0, its K steps 0 and 1 decoded; the codes
+    // and activations of tile 1 requested.
     load_codes(tile(0));
     load_x(tile(0));
     __syncthreads();  // tables
-    extract();
+    take_codes();
     load_codes(tile(1));
     stage(0);
     load_x(tile(1));
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        dec_read(0, b);
-        dec_place(0, b);
-    }
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            dec_read(ks, b);
+            dec_place(ks, b);
+        }
     __syncthreads();
 
-    // One K step per iteration, hand-interleaved.  The products of tile t run in 2 TF units (one
-    // A operand, NB matrix-core steps each): the first TF (K step 0) beside the decoding of the
-    // tile's K step 1 operands, the last TF (K step 1) beside the decoding of tile t + 1's K step 0
-    // operands, each into the registers its products have just released.  Mid-step the code
-    // fields of tile t + 1 are taken (once the last read of tile t's has gone out) and tile t + 2's
-    // codes requested; at the end tile t + 1's
+    // One K tile per iteration, hand-interleaved.  The products of tile t run in 4 TF units (one
+    // A operand, NB matrix-core steps each): those of K steps 0 and 1 beside the decoding of the
+    // tile's K steps 2 and 3, those of K steps 2 and 3 beside the decoding of tile t + 1's K steps
+    // 0 and 1, each into the registers its products have just released.  Mid-tile the code
+    // records of tile t + 1 are taken and tile t + 2's requested; at the end tile t + 1's
     // activations are staged and tile t + 2's requested.  A operands are read two units ahead;
     // scheduling barriers keep this order.  Every load is unconditional, so each wait counts the
     // same loads on every path.
-    static_assert(TF == 2 * NB, "two product units per decoded operand");
+    constexpr int MU = 4 * TF;  // product units per K tile
+    constexpr int DU = 4 * NB;  // decoded operands per K tile
+    static_assert(MU % DU == 0 && MU / DU >= 1, "whole product units per decoded operand");
+    constexpr int PER = MU / DU;
     for (int t = 0; t < nk; ++t) {
         const uint32_t cur = uint32_t(t & 1) * kXBuf, nxt = uint32_t(kXBuf) - cur;
         u32x4 Ar[3];
         Ar[0] = readA(cur, 0, 0);
-        Ar[1] = readA(cur, 0, 1);
-        dec_read(1, 0);
+        Ar[1] = readA(cur, 0, 1 % TF);
+        dec_read(2, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < 2 * TF; ++c) {
+        for (int c = 0; c < MU; ++c) {
             const int ks = c / TF, i = c % TF;
-            if (c + 2 < 2 * TF) Ar[(c + 2) % 3] = readA(cur, (c + 2) / TF, (c + 2) % TF);
+            if (c + 2 < MU) Ar[(c + 2) % 3] = readA(cur, (c + 2) / TF, (c + 2) % TF);
             mma_unit(ks, i, Ar[c % 3]);
-            if (c == TF - 2) {  // tile t's codes are read: take tile t + 1's, request t + 2's
-                extract();
-                load_codes(tile(t + 2));
-            }
-            if (c % 2 == 0) {
-                // operand b of the K step being decoded: (tile t, ks 1) in the first half,
-                // (tile t + 1, ks 0) in the second
-                const int dk = ks == 0 ? 1 : 0, b = i / 2;
-                if (b + 1 < NB) dec_read(dk, b + 1);
-                else if (ks == 0) dec_read(0, 0);  // first operand of the second half
-            } else {
-                const int dk = ks == 0 ? 1 : 0, b = i / 2;
-                dec_place(dk, b);
+            // decoded operand d = c / PER of this tile's list: K steps 2, 3 of tile t, then K
+            // steps 0, 1 of tile t + 1 (its codes taken once the list reaches them)
+            if (c % PER == PER - 1 || PER == 1) {
+                const int d = c / PER;
+                const int dks = (d / NB + 2) % 4, db = d % NB;
+                dec_place(dks, db);
+                if (d + 1 < DU) {
+                    const int nks = ((d + 1) / NB + 2) % 4, nb = (d + 1) % NB;
+                    if (d + 1 == 2 * NB) {  // tile t's records are read: take tile t + 1's
+                        take_codes();
+                        load_codes(tile(t + 2));
+                    }
+                    dec_read(nks, nb);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -317,7 +307,7 @@ k_vq3mm(GemmArgs a) {
     if constexpr (EPI == kEgGateUpRot) __syncthreads();  // the epilogue reuses the LDS
 
     // ---- epilogues.  Lane l, register q of acc[m][j][i] holds D[token][row] with
-    // token = tok0 + 16 i + 4 kg + q and row = wrow + 16 j + n.
+    // token = tok0 + 32 i + 8 (q / 4) + 4 kh + q % 4 and row = wrow + 32 j + n.
     if constexpr (EPI == kEgGateUpRot) {
         // a = silu(g) u sign over BM tokens x BNW rows in LDS (fp32), then the Hadamard transform
         // of every 128-row block, then binary16 out
@@ -325,15 +315,15 @@ k_vq3mm(GemmArgs a) {
         float* Ab = reinterpret_cast<float*>(lds);  // [BM][BNW + 1]
 #pragma unroll
         for (int j = 0; j < RF; ++j) {
-            const int rl = w * RW + 16 * j + n;
+            const int rl = w * RW + 32 * j + n;
             const int row = min(row0 + rl, N - 1);
             const float sg = h2f(a.sc[0][row]), su = h2f(a.sc[1][row]);
             const bool neg = a.sign && a.sign[row] < 0;
 #pragma unroll
             for (int i = 0; i < TF; ++i)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int tl = 16 * i + 4 * kg + q;
+                for (int q = 0; q < 16; ++q) {
+                    const int tl = 32 * i + 8 * (q >> 2) + 4 * kh + (q & 3);
                     const float g = acc[0][j][i][q] * sg, u = acc[1][j][i][q] * su;
                     const float v = g / (1.f + expf(-g)) * u;
                     Ab[tl * (BNW + 1) + rl] = neg ? -v : v;
@@ -368,8 +358,8 @@ k_vq3mm(GemmArgs a) {
     float* const plane = a.out32 + size_t(blockIdx.z) * size_t(T) * size_t(EPI == kEgPart2 ? 2 * N : N);
 #pragma unroll
     for (int j = 0; j < RF; ++j) {
-        const int row = wrow + 16 * j + n;
-        if (wrow + 16 * j >= N) continue;  // whole 16-row operands (N is a multiple of 32)
+        const int row = wrow + 32 * j + n;
+        if (wrow + 32 * j >= N) continue;  // whole 32-row operands (N is a multiple of 32)
         float s0 = 1.f, s1 = 1.f;
         bool neg = false;
         if constexpr (EPI == kEgGateUp32) {
@@ -387,8 +377,8 @@ k_vq3mm(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < TF; ++i)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int tok = tok0 + 16 * i + 4 * kg + q;
+            for (int q = 0; q < 16; ++q) {
+                const int tok = tok0 + 32 * i + 8 * (q >> 2) + 4 * kh + (q & 3);
                 if (!full && tok >= T) continue;
                 const float v0 = acc[0][j][i][q];
                 if constexpr (EPI == kEgGateUp32) {
