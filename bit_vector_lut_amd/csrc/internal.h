@@ -102,7 +102,8 @@ hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, bool phased, hipS
 
 // ---- tiled matrix-core path (T > 8): decoders, epilogues, kinds
 enum { kDecVQ3 = 0, kDecLUT2 = 1, kDecLUT4 = 2, kDecDense = 3 };
-enum { kEgGateUp32 = 0, kEgGateUpRot = 1, kEgScale16 = 2, kEgLUT = 3, kEgPlain32 = 4, kEgPart2 = 5 };
+enum { kEgGateUp32 = 0, kEgGateUpRot = 1, kEgScale16 = 2, kEgLUT = 3, kEgPlain32 = 4, kEgPart2 = 5,
+       kEgLUTPlane = 6 };
 enum {
     kGemmVQ3GateUp = 0,     // gate+up -> a fp32 [T][N] (sign applied)
     kGemmVQ3GateUpRot = 1,  // gate+up -> rotated a binary16 [T][N] (128-wide blocks)
@@ -143,7 +144,7 @@ constexpr int kVq3mmMinT = 65;  // launch_gemm sends VQ3 kinds with at least thi
 // writes unscaled FP32 planes [ksplit][T][N]; the reductions below finish it.
 int gemm_split(int kind, int N, int K, int T, int cus);
 hipError_t launch_split_reduce(int T, int N, int splits, const float* part, const uint16_t* sc,
-                               uint16_t* y, hipStream_t st);  // y = sc . sum
+                               uint16_t* y, hipStream_t st);  // y = sc . sum (sc null: 1)
 hipError_t launch_split_sum(int n, int splits, const float* part, float* out, hipStream_t st);
 // a = silu(sc_g sum g) (sc_u sum u) sign from K-split gate/up planes [splits][T][2][N]; rotate:
 // 128-wide rotation to binary16 out16 [T][ldo], else FP32 out32 [T][ldo]

@@ -111,12 +111,123 @@ __global__ void __launch_bounds__(256) k_rotate(int T, int rows, int n, int b, c
     }
 }
 
+// The same rotation with V consecutive columns per lane (a wave covers 64 V columns of one row):
+// every load and store is a 16-byte vector access, butterflies of distance below V stay in the
+// lane and the others pair lane l with lane l ^ (h / V).  Needs n to be a multiple of 64 V.
+template <int V>
+__global__ void __launch_bounds__(256) k_rotate_v(int T, int rows, int n, int b, const void* x,
+                                                  int x_is_f32, const uint16_t* s,
+                                                  const int8_t* sign, void* out, int mode,
+                                                  float norm) {
+    static_assert(V == 8 || V == 16, "16-byte accesses");
+    const int l = threadIdx.x & 63;
+    const int chunks = n / (64 * V);
+    const int wv = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wv >= rows * chunks) return;
+    const int t = wv / chunks, col = (wv % chunks) * 64 * V + V * l;
+    float v[V];
+    if (t < T) {
+        const size_t idx = size_t(t) * n + col;
+        if (x_is_f32) {
+            const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(x) + idx);
+#pragma unroll
+            for (int q = 0; q < V / 4; ++q) {
+                const f32x4 u = p[q];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * q + e] = u[e];
+            }
+        } else {
+            const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + idx);
+#pragma unroll
+            for (int q = 0; q < V / 8; ++q) {
+                const u32x4 u = p[q];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[8 * q + e] = h2f(u[e / 2] >> (16 * (e & 1)));
+            }
+        }
+        if (s) {
+            const u32x4* p = reinterpret_cast<const u32x4*>(s + col);
+#pragma unroll
+            for (int q = 0; q < V / 8; ++q) {
+                const u32x4 u = p[q];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[8 * q + e] *= h2f(u[e / 2] >> (16 * (e & 1)));
+            }
+        }
+        if (sign) {
+            const uint32_t* p = reinterpret_cast<const uint32_t*>(sign + col);
+#pragma unroll
+            for (int q = 0; q < V / 4; ++q) {
+                const uint32_t u = p[q];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (int8_t(u >> (8 * e)) < 0) v[4 * q + e] = -v[4 * q + e];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[e] = 0.f;
+    }
+#pragma unroll
+    for (int h = 1; h < V; h <<= 1)
+        if (h < b) {
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                if (!(e & h)) {
+                    const float x0 = v[e], x1 = v[e | h];
+                    v[e] = x0 + x1;
+                    v[e | h] = x0 - x1;
+                }
+        }
+    for (int h = V; h < b; h <<= 1) {
+        const int d = h / V;
+        const bool upper = (l & d) != 0;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const float p = __shfl_xor(v[e], d);
+            v[e] = upper ? p - v[e] : v[e] + p;
+        }
+    }
+    const size_t idx = size_t(t) * n + col;
+    if (mode == 0) {
+        f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx);
+#pragma unroll
+        for (int q = 0; q < V / 4; ++q)
+            p[q] = f32x4{v[4 * q] * norm, v[4 * q + 1] * norm, v[4 * q + 2] * norm, v[4 * q + 3] * norm};
+    } else {
+        u32x4* p = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(out) + idx);
+#pragma unroll
+        for (int q = 0; q < V / 8; ++q) {
+            u32x4 u;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                u[k] = f2h(v[8 * q + 2 * k] * norm) | (f2h(v[8 * q + 2 * k + 1] * norm) << 16);
+            p[q] = u;
+        }
+    }
+}
+
 hipError_t launch_rotate(int T, int n, int b, const void* x, int x_is_f32, const uint16_t* s,
                          const int8_t* sign, void* out, int mode, hipStream_t st) {
     if (mode == 3 && T > kSkinnyT) return hipErrorInvalidValue;
     if (mode < 0 || mode == 2 || mode > 3 || b < 1 || b > 1024 || (b & (b - 1)) || n % b)
         return hipErrorInvalidValue;
     const int rows = mode == 3 ? kSkinnyT : T;  // mode 3 writes the zero rows past T too
+    const float vnorm = float(1.0 / __builtin_sqrt(double(b)));
+    auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    if (b <= 1024 && n % (64 * (b <= 512 ? 8 : 16)) == 0 && al16(x) && al16(out) && al16(s) &&
+        (reinterpret_cast<uintptr_t>(sign) & 3) == 0) {  // 16-byte accesses
+        const int V = b <= 512 ? 8 : 16;
+        const int waves = rows * (n / (64 * V));
+        const dim3 grid((waves + 3) / 4);
+        if (V == 8)
+            hipLaunchKernelGGL(k_rotate_v<8>, grid, dim3(256), 0, st, T, rows, n, b, x, x_is_f32, s,
+                               sign, out, mode, vnorm);
+        else
+            hipLaunchKernelGGL(k_rotate_v<16>, grid, dim3(256), 0, st, T, rows, n, b, x, x_is_f32,
+                               s, sign, out, mode, vnorm);
+        return hipGetLastError();
+    }
     const int ne = b <= 64 ? 1 : b / 64;
     const int chunks = (n + 64 * ne - 1) / (64 * ne);
     const int waves = rows * chunks;

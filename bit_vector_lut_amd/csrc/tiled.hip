@@ -396,10 +396,12 @@ int gemm_split(int kind, int N, int K, int T, int cus) {
     // K splits that fill the CUs with whole rounds of workgroups where the output tiles alone
     // leave a partial last round.  The down projection keeps at least 8 K tiles per split
     // (the partial planes cost traffic); the small dense projection goes down to 2.
-    if ((kind != kGemmVQ3DownSplit && kind != kGemmDense32) || T <= 0 || N <= 0 || cus <= 0)
+    const bool lut = kind == kGemmLUT2 || kind == kGemmLUT4;
+    if ((kind != kGemmVQ3DownSplit && kind != kGemmDense32 && !lut) || T <= 0 || N <= 0 || cus <= 0)
         return 1;
+    if (lut && T < kVq3mmMinT) return 1;
     const int kt = K / kGK;
-    if (kind == kGemmVQ3DownSplit && T >= kVq3mmMinT) {
+    if ((kind == kGemmVQ3DownSplit || lut) && T >= kVq3mmMinT) {
         // whole rounds of workgroups, each extra plane priced at 3% of the product
         const Vq3Tile t = vq3mm_tile(1);
         const long tiles = long((N + t.bn - 1) / t.bn) * ((T + t.bm - 1) / t.bm);
@@ -441,7 +443,7 @@ __global__ void __launch_bounds__(256) k_split_reduce(int T, int N, int splits, 
     const int row = i % N;
     float sum = 0.f;
     for (int z = 0; z < splits; ++z) sum += part[size_t(z) * T * N + i];
-    y[i] = (uint16_t)f2h(sum * h2f(sc[row]));
+    y[i] = (uint16_t)f2h(sc ? sum * h2f(sc[row]) : sum);
 }
 
 hipError_t launch_split_reduce(int T, int N, int splits, const float* part, const uint16_t* sc,
@@ -541,7 +543,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     if (a.T >= kVq3mmMinT &&
         (a.kind == kGemmVQ3GateUp || a.kind == kGemmVQ3GateUpRot || a.kind == kGemmVQ3Down ||
-         a.kind == kGemmVQ3GateUpSplit || a.kind == kGemmVQ3DownSplit))
+         a.kind == kGemmVQ3GateUpSplit || a.kind == kGemmVQ3DownSplit || a.kind == kGemmLUT2 ||
+         a.kind == kGemmLUT4))
         return launch_vq3mm(a, st);
     if (a.K % kGK || a.N <= 0) return hipErrorInvalidValue;
     if (a.ksplit > 1 && ((a.kind != kGemmVQ3DownSplit && a.kind != kGemmDense32 &&

@@ -54,9 +54,11 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                   __builtin_bit_cast(half8, b), c, 0, 0, 0);
 }
 
-template <int NW, int BM, int RW, int NMAT, int EPI>
+template <int NW, int BM, int RW, int NMAT, int DEC, int EPI>
 __global__ void __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_vq3mm(GemmArgs a) {
+    constexpr bool VQ = DEC == kDecVQ3;
+    constexpr int BITS = DEC == kDecLUT2 ? 2 : 4;  // scalar-LUT code width
     constexpr int NT = NW * 64;
     constexpr int RF = RW / 32;       // 32-row B operands per wave per matrix
     constexpr int TF = BM / 32;       // 32-token A operands
@@ -64,11 +66,13 @@ k_vq3mm(GemmArgs a) {
     constexpr int NB = NMAT * RF;     // B operands per K step (one centroid table each)
     constexpr int XCH = BM * 8 / NT;  // 16-byte activation chunks per thread per K tile
     static_assert(RW % 32 == 0 && XCH >= 1 && (BM * 8) % NT == 0, "shape");
-    constexpr int kTabBytes = 64 * 32 * 4;      // 64 centroids x 32 bank columns
+    constexpr int kEnt = VQ ? 64 : 16;           // table entries
+    constexpr int kTabBytes = kEnt * 32 * 4;     // entries x 32 bank columns
     constexpr int kOffX = NW * NB * kTabBytes;  // activation tiles after the tables
     constexpr int kXBuf = BM * kXK * 2;         // one activation tile
     constexpr int kMain = kOffX + 2 * kXBuf;
     constexpr int kEpBytes = EPI == kEgGateUpRot ? BM * (BNW + 1) * 4 : 0;
+    static_assert(VQ || (NMAT == 1 && (EPI == kEgLUT || EPI == kEgLUTPlane)), "LUT: one matrix");
     constexpr int kLds = kMain > kEpBytes ? kMain : kEpBytes;
     static_assert(kLds <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
@@ -81,22 +85,30 @@ k_vq3mm(GemmArgs a) {
     const int ldo = a.ldo > 0 ? a.ldo : N;
     const int mt_last = N / 32 - 1;
 
-    // ---- centroid tables.  Table (m, j) serves B operand j of matrix m (rows wrow + 32 j ..,
-    // four 8-row groups): word (e, b) -- centroid e, bank column b -- holds centroid e of group
-    // b / 8.  Lane l reads column l % 32 only, which holds its own row's group, so a lookup never
-    // meets a bank conflict.
+    // ---- lookup tables.  Table (m, j) serves B operand j of matrix m (rows wrow + 32 j ..,
+    // four 8-row groups): word (e, b) -- entry e, bank column b -- holds entry e of group b / 8.
+    // Lane l reads column l % 32 only, which holds its own row's group, so a lookup never meets a
+    // bank conflict.  Entries: VQ3, the 64 two-component centroids; LUT2, the 16 pairs
+    // (lut[e % 4], lut[e / 4]) of two neighbouring codes; LUT4, the 16 scalars (low half).
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
         const uint32_t* cb = (NMAT > 1 && m) ? a.cb[1] : a.cb[0];
+        const uint16_t* lut = reinterpret_cast<const uint16_t*>(a.cb[0]);
 #pragma unroll
         for (int j = 0; j < RF; ++j) {
             unsigned char* tb = lds + (w * NB + m * RF + j) * kTabBytes;
             const int g0 = wrow / 8 + 4 * j;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
+            for (int k = 0; k < kEnt * 8 / 64; ++k) {
                 const int idx = l + 64 * k, e = idx >> 3, bq = idx & 7;  // 4 columns per store
                 const int grp = min(g0 + (bq >> 1), N / 8 - 1);
-                const uint32_t v = cb[size_t(grp) * 64 + e];
+                uint32_t v;
+                if constexpr (VQ)
+                    v = cb[size_t(grp) * 64 + e];
+                else if constexpr (DEC == kDecLUT2)
+                    v = uint32_t(lut[size_t(grp) * 4 + (e & 3)]) | (uint32_t(lut[size_t(grp) * 4 + (e >> 2)]) << 16);
+                else
+                    v = lut[size_t(grp) * 16 + e];
                 *reinterpret_cast<u32x4*>(tb + e * 128 + bq * 16) = u32x4{v, v, v, v};
             }
         }
@@ -107,12 +119,21 @@ k_vq3mm(GemmArgs a) {
     // columns 16 ks + 8 kh .. + 7 of each 16-column K step ks.  It looks up its pair's centroids
     // for columns 4 c0 .. 4 c0 + 3 of those eight: for all four K steps these are the 16 codes of
     // lane record (2 kh + c0, pair) of the packed tile, K step ks in its 24-bit slot ks.
+    // Scalar LUTs are packed row by row (32 / BITS codes per word, low bits first): a K tile is
+    // 8 BITS bytes of each row, K step ks in word ks (LUT2, half kh) or word 2 ks + kh (LUT4).
+    constexpr int CW = VQ ? 3 : 2 * BITS;          // code words per lane per operand and K tile
+    constexpr int kTileCode = VQ ? kTileBytes : 8 * BITS;  // bytes a K tile advances the codes
     uint32_t voff[RF];
 #pragma unroll
     for (int j = 0; j < RF; ++j) {
-        const int mt = min(wrow / 32 + j, mt_last);
-        voff[j] = uint32_t(mt) * uint32_t(KT) * kTileBytes +
-                  12u * uint32_t(((2 * kh + c0) << 4) | pr);
+        if constexpr (VQ) {
+            const int mt = min(wrow / 32 + j, mt_last);
+            voff[j] = uint32_t(mt) * uint32_t(KT) * kTileBytes +
+                      12u * uint32_t(((2 * kh + c0) << 4) | pr);
+        } else {
+            const int row = min(wrow + 32 * j + n, N - 1);
+            voff[j] = uint32_t(row) * uint32_t(K / 8 * BITS);
+        }
     }
     // v_perm selectors: this lane's component and the partner's
     const uint32_t sel_own = c0 ? 0x07060302u : 0x05040100u;
@@ -144,13 +165,14 @@ k_vq3mm(GemmArgs a) {
     for (int m = 0; m < NMAT; ++m)
         rs_code[m] = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>((NMAT > 1 && m) ? a.codes[1] : a.codes[0]), 0,
-            int(uint32_t(N / 32) * uint32_t(KT) * kTileBytes), kRsrcWord3);
+            int(VQ ? uint32_t(N / 32) * uint32_t(KT) * kTileBytes : uint32_t(N) * uint32_t(K / 8 * BITS)),
+            kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.x), 0, int(uint32_t(T) * uint32_t(K) * 2u), kRsrcWord3);
 
     u32x4 xr[XCH];            // activation chunks of the next K tile
-    u32x3 rn[NMAT][RF];       // code records of the next K tile
-    u32x3 rc[NMAT][RF];       // code records being decoded
+    uint32_t rn[NMAT][RF][CW];  // code words of the next K tile
+    uint32_t rc[NMAT][RF][CW];  // code words being decoded
     u32x4 Bf[4][NMAT][RF];    // B operands [ks][m][j]
 
     auto load_x = [&](int kt) {
@@ -163,10 +185,24 @@ k_vq3mm(GemmArgs a) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int j = 0; j < RF; ++j)
-                rn[m][j] = __builtin_bit_cast(
-                    u32x3, __builtin_amdgcn_raw_buffer_load_b96(rs_code[m], int(voff[j]),
-                                                                kt * kTileBytes, 0));
+            for (int j = 0; j < RF; ++j) {
+                if constexpr (VQ) {
+                    const u32x3 v = __builtin_bit_cast(
+                        u32x3, __builtin_amdgcn_raw_buffer_load_b96(rs_code[m], int(voff[j]),
+                                                                    kt * kTileCode, 0));
+#pragma unroll
+                    for (int q = 0; q < 3; ++q) rn[m][j][q] = v[q];
+                } else {
+#pragma unroll
+                    for (int h = 0; h < CW / 4; ++h) {
+                        const u32x4 v = __builtin_bit_cast(
+                            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                       rs_code[m], int(voff[j]) + 16 * h, kt * kTileCode, 0));
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) rn[m][j][4 * h + q] = v[q];
+                    }
+                }
+            }
     };
     auto stage = [&](uint32_t bufoff) {
         unsigned char* base = lds + (xw + bufoff);
@@ -178,36 +214,66 @@ k_vq3mm(GemmArgs a) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
-            for (int j = 0; j < RF; ++j) rc[m][j] = rn[m][j];
+            for (int j = 0; j < RF; ++j)
+#pragma unroll
+                for (int q = 0; q < CW; ++q) rc[m][j][q] = rn[m][j][q];
     };
 
     // Decoding B operand (ks, b = (m, j)), in two phases: the four table reads (centroids of the
     // lane's pair at its four columns), then the exchange with lane l ^ 1 that gives each lane its
     // own row's halves at all eight columns.
-    uint32_t ev[2][4];  // table reads of two operands in flight
+    constexpr int NE = DEC == kDecLUT4 ? 8 : 4;  // table reads per operand and K step
+    uint32_t ev[2][NE];                          // table reads of two operands in flight
     auto dec_read = [&](int ks, int b) {
         const int m = b / RF, j = b % RF;
-        const u32x3 r = rc[m][j];
-        // code k of K step ks at record bit 24 ks + 6 k, moved to bits 12:7
-        uint32_t x[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int bit = 24 * ks + 6 * k;
-            const int wd = bit / 32, sh = bit % 32;
-            if (sh <= 7)
-                x[k] = r[wd] << (7 - sh);
-            else if (sh <= 26)
-                x[k] = r[wd] >> (sh - 7);
-            else
-                x[k] = __builtin_amdgcn_alignbit(r[wd + 1], r[wd], sh - 7);
-        }
         const unsigned char* tb = lds + b * kTabBytes;
+        if constexpr (VQ) {
+            const uint32_t* r = rc[m][j];
+            // code k of K step ks at record bit 24 ks + 6 k, moved to bits 12:7
+            uint32_t x[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            ev[b & 1][k] = *reinterpret_cast<const uint32_t*>(tb + and_or(x[k], 0x1F80u, tab_lane));
+            for (int k = 0; k < 4; ++k) {
+                const int bit = 24 * ks + 6 * k;
+                const int wd = bit / 32, sh = bit % 32;
+                if (sh <= 7)
+                    x[k] = r[wd] << (7 - sh);
+                else if (sh <= 26)
+                    x[k] = r[wd] >> (sh - 7);
+                else
+                    x[k] = __builtin_amdgcn_alignbit(r[wd + 1], r[wd], sh - 7);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                ev[b & 1][k] = *reinterpret_cast<const uint32_t*>(tb + and_or(x[k], 0x1F80u, tab_lane));
+        } else if constexpr (DEC == kDecLUT2) {
+            // the lane's 16 bits of word ks: code pair p (4 bits) at bit 4 p, moved to bits 10:7
+            const uint32_t wk = rc[m][j][ks] >> (16 * kh);
+            const uint32_t x[4] = {wk << 7, wk << 3, wk >> 1, wk >> 5};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                ev[b & 1][k] = *reinterpret_cast<const uint32_t*>(tb + and_or(x[k], 0x780u, tab_lane));
+        } else {
+            // word 2 ks + kh: code i (4 bits) at bit 4 i, moved to bits 10:7
+            const uint32_t wd = kh ? rc[m][j][2 * ks + 1] : rc[m][j][2 * ks];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t x = i < 2 ? wd << (7 - 4 * i) : wd >> (4 * i - 7);
+                ev[b & 1][i] = *reinterpret_cast<const uint16_t*>(tb + and_or(x, 0x780u, tab_lane));
+            }
+        }
     };
     auto dec_place = [&](int ks, int b) {
         const int m = b / RF, j = b % RF;
+        if constexpr (DEC == kDecLUT2) {
+            Bf[ks][m][j] = u32x4{ev[b & 1][0], ev[b & 1][1], ev[b & 1][2], ev[b & 1][3]};
+            return;
+        } else if constexpr (DEC == kDecLUT4) {
+            u32x4 v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = ev[b & 1][2 * q] | (ev[b & 1][2 * q + 1] << 16);
+            Bf[ks][m][j] = v;
+            return;
+        }
         const uint32_t e0 = ev[b & 1][0], e1 = ev[b & 1][1], e2 = ev[b & 1][2], e3 = ev[b & 1][3];
         const uint32_t y0 = __builtin_amdgcn_perm(e1, e0, sel_own);
         const uint32_t y1 = __builtin_amdgcn_perm(e3, e2, sel_own);
@@ -352,6 +418,50 @@ k_vq3mm(GemmArgs a) {
         return;
     }
 
+    if constexpr (!VQ) {
+        // scalar LUT: row scales, then the rank-r term z U^T (split 0 only) as r / 16 more K
+        // steps with both operands read straight from global memory (z rounded to binary16)
+#pragma unroll
+        for (int j = 0; j < RF; ++j) {
+            const float sr = h2f(a.sc[0][min(wrow + 32 * j + n, N - 1)]);
+#pragma unroll
+            for (int i = 0; i < TF; ++i) acc[0][j][i] *= sr;
+        }
+        if (a.r > 0 && blockIdx.z == 0) {
+            for (int kr = 0; kr < a.r; kr += 16) {
+                const int k0 = kr + 8 * kh;  // this lane's 8 columns of the step
+                u32x4 Bu[RF];
+#pragma unroll
+                for (int j = 0; j < RF; ++j) {
+                    const uint16_t* up = a.U + size_t(min(wrow + 32 * j + n, N - 1)) * a.r;
+                    uint32_t h[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t u0 = k0 + 2 * q < a.r ? up[k0 + 2 * q] : 0u;
+                        const uint32_t u1 = k0 + 2 * q + 1 < a.r ? up[k0 + 2 * q + 1] : 0u;
+                        h[q] = u0 | (u1 << 16);
+                    }
+                    Bu[j] = u32x4{h[0], h[1], h[2], h[3]};
+                }
+#pragma unroll
+                for (int i = 0; i < TF; ++i) {
+                    const int tok = tok0 + 32 * i + n;
+                    const float* zp = a.z + size_t(min(tok, T - 1)) * a.r;
+                    uint32_t h[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float z0 = tok < T && k0 + 2 * q < a.r ? zp[k0 + 2 * q] : 0.f;
+                        const float z1 = tok < T && k0 + 2 * q + 1 < a.r ? zp[k0 + 2 * q + 1] : 0.f;
+                        h[q] = f2h(z0) | (f2h(z1) << 16);
+                    }
+                    const u32x4 Az = u32x4{h[0], h[1], h[2], h[3]};
+#pragma unroll
+                    for (int j = 0; j < RF; ++j) acc[0][j][i] = mfma32x32x16(Az, Bu[j], acc[0][j][i]);
+                }
+            }
+        }
+    }
+
     // whole token tiles store without a check per element
     const bool full = tok0 + BM <= T;
     // K-split planes: this split's plane ([T][N], or [T][2][N] for g and u)
@@ -368,6 +478,8 @@ k_vq3mm(GemmArgs a) {
             neg = a.sign && a.sign[row] < 0;
         } else if constexpr (EPI == kEgScale16) {
             s0 = h2f(a.sc[0][row]);
+        } else if constexpr (EPI == kEgLUT || EPI == kEgLUTPlane) {
+            // scaled above
         } else {
             // planes carry a scale (1 for plain partial sums): a product on the accumulators
             // here keeps them in place through the K loop, where plain stores had the register
@@ -387,6 +499,8 @@ k_vq3mm(GemmArgs a) {
                     a.out32[size_t(tok) * ldo + row] = neg ? -act : act;
                 } else if constexpr (EPI == kEgScale16) {
                     a.out16[size_t(tok) * ldo + row] = (uint16_t)f2h(v0 * s0);
+                } else if constexpr (EPI == kEgLUT) {
+                    a.out16[size_t(tok) * ldo + row] = (uint16_t)f2h(v0);
                 } else if constexpr (EPI == kEgPart2) {
                     // split z of a K-split gate/up product: unscaled g and u planes
                     float* o = plane + uint32_t(tok * 2 * N + row);
@@ -399,11 +513,11 @@ k_vq3mm(GemmArgs a) {
     }
 }
 
-template <int NW, int BM, int RW, int NMAT, int EPI>
+template <int NW, int BM, int RW, int NMAT, int EPI, int DEC = kDecVQ3>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
     constexpr int BNW = NW * RW;
     const dim3 grid((a.N + BNW - 1) / BNW, (a.T + BM - 1) / BM, a.ksplit > 1 ? a.ksplit : 1);
-    hipLaunchKernelGGL((k_vq3mm<NW, BM, RW, NMAT, EPI>), grid, dim3(NW * 64), 0, st, a);
+    hipLaunchKernelGGL((k_vq3mm<NW, BM, RW, NMAT, DEC, EPI>), grid, dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }
 
@@ -446,6 +560,12 @@ hipError_t launch_vq3mm(const GemmArgs& a, hipStream_t st) {
             return launch_t<kDnNW, kDnBM, kDnRW, 1, kEgScale16>(a, st);
         case kGemmVQ3DownSplit:
             return launch_t<kDnNW, kDnBM, kDnRW, 1, kEgPlain32>(a, st);
+        case kGemmLUT2:  // scalar LUT + rank-r term: binary16 y, or scaled FP32 planes per K split
+            return a.ksplit > 1 ? launch_t<kDnNW, kDnBM, kDnRW, 1, kEgLUTPlane, kDecLUT2>(a, st)
+                                : launch_t<kDnNW, kDnBM, kDnRW, 1, kEgLUT, kDecLUT2>(a, st);
+        case kGemmLUT4:
+            return a.ksplit > 1 ? launch_t<kDnNW, kDnBM, kDnRW, 1, kEgLUTPlane, kDecLUT4>(a, st)
+                                : launch_t<kDnNW, kDnBM, kDnRW, 1, kEgLUT, kDecLUT4>(a, st);
     }
     return hipErrorInvalidValue;
 }

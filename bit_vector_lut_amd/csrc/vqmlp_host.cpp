@@ -896,46 +896,89 @@ vqmlp_status vqmlp_lut_workspace_bytes(int N, int K, int T, int r, size_t* bytes
         return fail(VQMLP_ERR_INVALID_ARG, "bad LUT workspace query");
     const size_t Tt = T ? T : 1;
     const int zs = gemm_split(kGemmDense32, r ? r : 1, K, T, kLutSplitCUs);
+    const int ls = gemm_split(kGemmLUT2, N, K, T, kLutSplitCUs);  // same split for both widths
     *bytes = align256(Tt * K * 2) + align256(Tt * (r ? r : 1) * 4) +
-             (zs > 1 ? align256(size_t(zs) * Tt * (r ? r : 1) * 4) : 0) + 256;
+             (zs > 1 ? align256(size_t(zs) * Tt * (r ? r : 1) * 4) : 0) +
+             (ls > 1 ? align256(size_t(ls) * Tt * N * 4) : 0) + 256;
     return ok();
 }
 
-vqmlp_status vqmlp_lut_forward(int bits, int N, int K, int T, const void* packed,
-                               const uint16_t* U, const uint16_t* V, int r, const uint16_t* s,
-                               const int8_t* sign, int had_block, const void* x, void* y,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// A validated scalar-LUT projection: everything a forward needs but its rows.
+struct vqmlp_lut_plan {
+    int bits, N, K, r, had_block;
+    const uint8_t* base;
+    Layout L;
+    const uint16_t *U, *V, *s;
+    const int8_t* sign;
+};
+
+namespace {
+
+// shapes, rank and block: the checks that need no device
+vqmlp_status lut_args(int bits, int N, int K, int r, int had_block) {
     vqmlp_status st = lut_shape(bits, N, K);
     if (st) return st;
-    if (T < 0 || r < 0 || r > 256)
-        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_forward: T=%d r=%d", T, r);
+    if (r < 0 || r > 256) return fail(VQMLP_ERR_INVALID_ARG, "scalar-LUT projection: r=%d", r);
     if (had_block && (!is_pow2(had_block) || had_block < 2 || had_block > 1024 || K % had_block))
         return fail(VQMLP_ERR_INVALID_ARG, "Hadamard block %d does not divide K=%d", had_block, K);
-    if (T == 0) return ok();
-    if (!packed || !x || !y || !workspace)
-        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_forward: null pointer");
+    return VQMLP_OK;
+}
+
+vqmlp_status lut_validate(int bits, int N, int K, const void* packed, const uint16_t* U,
+                          const uint16_t* V, int r, const uint16_t* s, const int8_t* sign,
+                          int had_block, vqmlp_lut_plan* p) {
+    vqmlp_status st = lut_args(bits, N, K, r, had_block);
+    if (st) return st;
+    if (!packed) return fail(VQMLP_ERR_INVALID_ARG, "scalar-LUT projection: null packed buffer");
     if (r > 0 && (!U || !V))
-        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_forward: r=%d needs U and V", r);
-    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256) ||
-        (U && !aligned(U, 16)) || (V && !aligned(V, 16)))
-        return fail(VQMLP_ERR_INVALID_ARG, "x, y, U, V must be 16-byte aligned, the workspace 256");
-    size_t need = 0;
-    vqmlp_lut_workspace_bytes(N, K, T, r, &need);
-    if (workspace_bytes < need)
-        return fail(VQMLP_ERR_WORKSPACE, "workspace holds %zu bytes, this forward needs %zu",
-                    workspace_bytes, need);
+        return fail(VQMLP_ERR_INVALID_ARG, "scalar-LUT projection: r=%d needs U and V", r);
+    if ((U && !aligned(U, 16)) || (V && !aligned(V, 16)))
+        return fail(VQMLP_ERR_INVALID_ARG, "U, V must be 16-byte aligned");
     if ((st = check_device())) return st;
     const Layout L = lut_layout(bits, N, K);
     PackedHeader h;
     if ((st = read_device_header(packed, &h, "lut"))) return st;
     if ((st = check_header(h, N, K, uint32_t(bits), 1u << bits, L, "lut"))) return st;
+    p->bits = bits;
+    p->N = N;
+    p->K = K;
+    p->r = r;
+    p->had_block = had_block;
+    p->base = static_cast<const uint8_t*>(packed);
+    p->L = L;
+    p->U = U;
+    p->V = V;
+    p->s = s;
+    p->sign = sign;
+    return VQMLP_OK;
+}
+
+vqmlp_status lut_run(const vqmlp_lut_plan& p, int T, const void* x, void* y, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    const int N = p.N, K = p.K, r = p.r;
+    if (T < 0) return fail(VQMLP_ERR_INVALID_ARG, "scalar-LUT projection: T=%d", T);
+    if (T == 0) return ok();
+    if (!x || !y || !workspace)
+        return fail(VQMLP_ERR_INVALID_ARG, "scalar-LUT projection: null pointer");
+    if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256))
+        return fail(VQMLP_ERR_INVALID_ARG, "x, y must be 16-byte aligned, the workspace 256");
+    size_t need = 0;
+    vqmlp_lut_workspace_bytes(N, K, T, r, &need);
+    if (workspace_bytes < need)
+        return fail(VQMLP_ERR_WORKSPACE, "workspace holds %zu bytes, this forward needs %zu",
+                    workspace_bytes, need);
+    const Layout& L = p.L;
     uint8_t* wb = static_cast<uint8_t*>(workspace) + 256;
     uint16_t* xt = reinterpret_cast<uint16_t*>(wb);
     float* z = reinterpret_cast<float*>(wb + align256(size_t(T) * K * 2));
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    const uint8_t* base = static_cast<const uint8_t*>(packed);
+    const uint8_t* base = p.base;
+    const uint16_t *U = p.U, *V = p.V;
+    const int bits = p.bits;
     // x~ = R(x . s): the rotation kernel with a 1-wide block is the plain scale and sign
-    hipError_t e = launch_rotate(T, K, had_block ? had_block : 1, x, 0, s, sign, xt, 1, hs);
+    hipError_t e = launch_rotate(T, K, p.had_block ? p.had_block : 1, x, 0, p.s, p.sign, xt, 1, hs);
     if (e != hipSuccess) return hip_fail(e, "rotate (mixer input)");
     if (r > 0) {
         // z = x~ V^T has few outputs: split K over the CUs, then sum the planes
@@ -972,9 +1015,68 @@ vqmlp_status vqmlp_lut_forward(int bits, int N, int K, int T, const void* packed
     g.U = U;
     g.r = r;
     g.out16 = static_cast<uint16_t*>(y);
+    // too few row tiles to fill the CUs: split K into scaled FP32 planes, then sum them
+    const int ls = gemm_split(g.kind, N, K, T, kLutSplitCUs);
+    if (ls > 1) {
+        const int zs = gemm_split(kGemmDense32, r ? r : 1, K, T, kLutSplitCUs);
+        float* lp = reinterpret_cast<float*>(wb + align256(size_t(T) * K * 2) +
+                                             align256(size_t(T) * (r ? r : 1) * 4) +
+                                             (zs > 1 ? align256(size_t(zs) * T * (r ? r : 1) * 4) : 0));
+        g.ksplit = ls;
+        g.out32 = lp;
+        e = launch_gemm(g, hs);
+        if (e != hipSuccess) return hip_fail(e, "scalar-LUT projection (K split)");
+        e = launch_split_reduce(T, N, ls, lp, nullptr, static_cast<uint16_t*>(y), hs);
+        if (e != hipSuccess) return hip_fail(e, "scalar-LUT projection (K split sum)");
+        return ok();
+    }
     e = launch_gemm(g, hs);
     if (e != hipSuccess) return hip_fail(e, "scalar-LUT projection");
     return ok();
+}
+
+
+}  // namespace
+
+extern "C" {
+
+vqmlp_status vqmlp_lut_forward(int bits, int N, int K, int T, const void* packed,
+                               const uint16_t* U, const uint16_t* V, int r, const uint16_t* s,
+                               const int8_t* sign, int had_block, const void* x, void* y,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    if (T < 0) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_forward: T=%d", T);
+    vqmlp_status st = lut_args(bits, N, K, r, had_block);
+    if (st) return st;
+    if (T == 0) return ok();
+    vqmlp_lut_plan p;
+    st = lut_validate(bits, N, K, packed, U, V, r, s, sign, had_block, &p);
+    if (st) return st;
+    return lut_run(p, T, x, y, workspace, workspace_bytes, stream);
+}
+
+vqmlp_status vqmlp_lut_create(int bits, int N, int K, const void* packed, const uint16_t* U,
+                              const uint16_t* V, int r, const uint16_t* s, const int8_t* sign,
+                              int had_block, vqmlp_lut_plan** out) {
+    if (!out) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_create: null pointer");
+    *out = nullptr;
+    vqmlp_lut_plan tmp;
+    vqmlp_status st = lut_validate(bits, N, K, packed, U, V, r, s, sign, had_block, &tmp);
+    if (st) return st;
+    vqmlp_lut_plan* p = new (std::nothrow) vqmlp_lut_plan(tmp);
+    if (!p) return fail(VQMLP_ERR_INVALID_ARG, "out of host memory");
+    *out = p;
+    return ok();
+}
+
+vqmlp_status vqmlp_lut_destroy(vqmlp_lut_plan* plan) {
+    delete plan;
+    return ok();
+}
+
+vqmlp_status vqmlp_lut_plan_forward(const vqmlp_lut_plan* plan, int T, const void* x, void* y,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+    if (!plan) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_plan_forward: null plan");
+    return lut_run(*plan, T, x, y, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -60,6 +60,9 @@ def lib():
             "vqmlp_lut_unpack": [I, I, I, P, S, P, P, P],
             "vqmlp_lut_workspace_bytes": [I, I, I, I, C.POINTER(S)],
             "vqmlp_lut_forward": [I, I, I, I, P, P, P, I, P, P, I, P, P, P, S, P],
+            "vqmlp_lut_create": [I, I, I, P, P, P, I, P, P, I, C.POINTER(P)],
+            "vqmlp_lut_destroy": [P],
+            "vqmlp_lut_plan_forward": [P, I, P, P, P, S, P],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -246,6 +249,9 @@ class LUTProjection:
         self.had_block = had_block
         self.packed, self.U, self.V, self.s, self.sign = packed, U, V, s, sign
         self.device = packed.device
+        self._plan = C.c_void_p()
+        _check(lib().vqmlp_lut_create(bits, N, K, _dptr(packed), _dptr(U), _dptr(V), self.r,
+                                      _dptr(s), _dptr(sign), had_block, C.byref(self._plan)))
 
     @classmethod
     def from_proj(cls, proj, device="cuda"):
@@ -274,8 +280,26 @@ class LUTProjection:
             y = torch.empty((T, self.N), dtype=x.dtype, device=x.device)
         if workspace is None:
             workspace = self.workspace(T)
+        _check(lib().vqmlp_lut_plan_forward(self._plan, T, _dptr(x), _dptr(y), _dptr(workspace),
+                                            workspace.numel(), _stream(stream)))
+        return y
+
+    def forward_stateless(self, x, y=None, workspace=None, stream=None):
+        """The same through vqmlp_lut_forward (validates the packed buffer on every call)."""
+        import torch
+
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.N), dtype=x.dtype, device=x.device)
+        if workspace is None:
+            workspace = self.workspace(T)
         _check(lib().vqmlp_lut_forward(self.bits, self.N, self.K, T, _dptr(self.packed),
                                        _dptr(self.U), _dptr(self.V), self.r, _dptr(self.s),
                                        _dptr(self.sign), self.had_block, _dptr(x), _dptr(y),
                                        _dptr(workspace), workspace.numel(), _stream(stream)))
         return y
+
+    def __del__(self):
+        if getattr(self, "_plan", None) and _lib is not None:
+            _lib.vqmlp_lut_destroy(self._plan)
+            self._plan = None

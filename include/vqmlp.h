@@ -162,6 +162,20 @@ vqmlp_status vqmlp_lut_forward(int bits, int N, int K, int T, const void *packed
                                const int8_t *sign, int had_block, const void *x, void *y,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* The same projection with its validation done once.  vqmlp_lut_forward checks the device and
+ * reads the packed header through a synchronous device-to-host copy on every call, which stalls
+ * the host until earlier work has drained; a plan does those checks at creation (same
+ * arguments and errors as vqmlp_lut_forward) and keeps the pointers only (no device memory;
+ * the caller keeps every buffer alive).  vqmlp_lut_plan_forward then issues no host-device
+ * synchronisation: same x, y, workspace rules and errors as vqmlp_lut_forward. */
+typedef struct vqmlp_lut_plan vqmlp_lut_plan;
+vqmlp_status vqmlp_lut_create(int bits, int N, int K, const void *packed, const uint16_t *U,
+                              const uint16_t *V, int r, const uint16_t *s, const int8_t *sign,
+                              int had_block, vqmlp_lut_plan **out);
+vqmlp_status vqmlp_lut_destroy(vqmlp_lut_plan *plan);
+vqmlp_status vqmlp_lut_plan_forward(const vqmlp_lut_plan *plan, int T, const void *x, void *y,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -300,18 +300,26 @@ def test_lut_errors_on_device(vq, torch_dev):
     proj = vq.LUTProjection.from_proj(p)
     x = vq.to_device(rng.standard_normal((4, 128)).astype(np.float16))
     small = torch_dev.zeros(256, dtype=torch_dev.uint8, device="cuda")
-    with pytest.raises(vq.VqmlpError) as e:
-        proj.forward(x, workspace=small)
-    assert e.value.status == vq.ERR_WORKSPACE
-    proj.bits = 4  # header says 2-bit
-    with pytest.raises(vq.VqmlpError) as e:
-        proj.forward(x)
-    assert e.value.status == vq.ERR_INVALID_ARG
-    proj.bits = 2
-    proj.had_block = 96
-    with pytest.raises(vq.VqmlpError) as e:
-        proj.forward(x)
-    assert e.value.status == vq.ERR_INVALID_ARG
-    proj.had_block = 128
+    for fwd in (proj.forward, proj.forward_stateless):
+        with pytest.raises(vq.VqmlpError) as e:
+            fwd(x, workspace=small)
+        assert e.value.status == vq.ERR_WORKSPACE
+    # a header that does not match (bits) and a block that does not divide K: rejected by the
+    # stateless call and by plan creation alike
+    args = (proj.packed, proj.U, proj.V, proj.s, proj.sign)
+    for bits, hb in ((4, 128), (2, 96)):
+        with pytest.raises(vq.VqmlpError) as e:
+            vq.LUTProjection(bits, p.N, p.K, *args, had_block=hb)
+        assert e.value.status == vq.ERR_INVALID_ARG
+        proj.bits, proj.had_block = bits, hb
+        with pytest.raises(vq.VqmlpError) as e:
+            proj.forward_stateless(x)
+        assert e.value.status == vq.ERR_INVALID_ARG
+    proj.bits, proj.had_block = 2, 128
     empty = vq.to_device(np.zeros((0, 128), np.float16))
     assert proj.forward(empty).shape == (0, 64)
+    assert proj.forward_stateless(empty).shape == (0, 64)
+    # the plan and the stateless call give the same bits
+    y1, y2 = proj.forward(x), proj.forward_stateless(x)
+    torch_dev.cuda.synchronize()
+    assert torch_dev.equal(y1, y2)

@@ -158,4 +158,13 @@ def test_null_arguments_are_rejected_without_device(vq):
     assert lf(2, 64, 64, 2, None, None, None, 0, None, None, 0, None, None, None, 0,
               None) == vq.ERR_INVALID_ARG  # null buffers
     assert L.vqmlp_lut_workspace_bytes(64, 64, 1, 257, C.byref(n)) == vq.ERR_INVALID_ARG
+    lp = C.c_void_p()
+    lc = L.vqmlp_lut_create
+    assert lc(3, 64, 64, None, None, None, 0, None, None, 0, C.byref(lp)) == vq.ERR_INVALID_ARG
+    assert lc(2, 64, 192, None, None, None, 0, None, None, 128, C.byref(lp)) == vq.ERR_INVALID_ARG
+    assert lc(2, 64, 64, None, None, None, 0, None, None, 0, C.byref(lp)) == vq.ERR_INVALID_ARG
+    assert lc(2, 64, 64, None, None, None, 0, None, None, 0, None) == vq.ERR_INVALID_ARG
+    assert not lp.value  # no plan on failure
+    assert L.vqmlp_lut_plan_forward(None, 1, None, None, None, 0, None) == vq.ERR_INVALID_ARG
     assert L.vqmlp_last_error() != b""
+    assert L.vqmlp_lut_destroy(None) == vq.OK
