@@ -42,9 +42,18 @@ hipError_t launch_dequant(const VQ3View& m, float* w, hipStream_t s);
 
 // out[t][.] = R(x . s . sign) for a binary16 or float input, Hadamard blocks of b (a power of
 // two up to 1024; 1 = no rotation).  mode: 0 = FP32 row-major [T][n], 1 = binary16 row-major
-// [T][n], 3 = binary16 row-major [8][n] with the rows past T zero (T <= 8).
+// [T][n], 3 = binary16 row-major [8][n] with the rows past T zero (T <= 8), 4 = as 3 in the
+// unit-major layout below (n a multiple of 64).
 hipError_t launch_rotate(int T, int n, int b, const void* x, int x_is_f32, const uint16_t* s,
                          const int8_t* sign, void* out, int mode, hipStream_t st);
+// Unit-major activation operand of the T <= 8 stream-K kernels: the 8 rows x 64 columns of
+// K tile kt are 1 KB at kt * 512 halves, ordered [g][t][s][i] for column 16 s + 4 g + i, so
+// the matrix-core B words of one lane (token t, column group g, all 4 steps) are 32
+// contiguous bytes.
+__host__ __device__ __forceinline__ size_t unit_major_index(int t, int col) {
+    const int kt = col >> 6, w = col & 63, s = w >> 4, g = (w >> 2) & 3, i = w & 3;
+    return size_t(kt) * 512 + ((g * 8 + t) * 4 + s) * 4 + i;
+}
 
 struct SkinnyArgs {
     VQ3View mat[2];
@@ -63,6 +72,23 @@ struct SkinnyArgs {
 hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st);
 hipError_t launch_reduce_down(int T, int N, int slices, const float* part, const uint16_t* sc,
                               uint16_t* y, hipStream_t st);
+
+// ---- stream-K skinny path (T <= 8): the weight stream cut into equal contiguous ranges
+constexpr int kStreamKMaxQ = 4;  // row-tile pairs one workgroup range may touch
+struct StreamKArgs {
+    VQ3View mat[2];        // gate, up (nmat 2) or down (nmat 1: tiles 2q and 2q + 1)
+    int nmat;
+    int MT, KT, NQ, U;     // row tiles, K tiles, row-tile pairs, units (set by the launcher)
+    const uint16_t* bx;    // activation operand, 8 rows of K in the unit-major layout
+    float* part;           // partial-sum slots [NQ + grid][2][64][4]
+    const int8_t* sign_i;  // gate+up: sign of the intermediate rotation (NULL = +1)
+};
+int streamk_grid(int nmat, int N, int K, int cus);
+size_t streamk_part_floats(int nmat, int N, int K, int cus);
+// the projection and its epilogue: nmat 2 writes a [8][I] fp32 (SiLU(g) u, signed), nmat 1
+// writes y [T][H] binary16
+hipError_t launch_streamk(const StreamKArgs& a, int cus, int T, float* a_out, uint16_t* y,
+                          hipStream_t st);
 
 // ---- fused persistent forward (T <= 8): the whole MLP in one launch
 // Control block (kCtlHdr 32-bit words, zero before the first call): word 0 is the item queue

@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(256) k_rotate(int T, int rows, int n, int b, c
     for (int e = 0; e < NE; ++e) {
         const int col = c0 + 64 * e + l;
         if (col >= n) continue;
-        const size_t idx = size_t(t) * n + col;
+        const size_t idx = mode == 4 ? unit_major_index(t, col) : size_t(t) * n + col;
         const float r = v[e] * norm;
         if (mode == 0)
             static_cast<float*>(out)[idx] = r;
@@ -189,7 +189,17 @@ __global__ void __launch_bounds__(256) k_rotate_v(int T, int rows, int n, int b,
         }
     }
     const size_t idx = size_t(t) * n + col;
-    if (mode == 0) {
+    if (mode == 4) {
+        // 8 consecutive columns: two runs of 4 of the unit-major layout
+#pragma unroll
+        for (int q = 0; q < V / 4; ++q) {
+            u32x2 u;
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                u[k] = f2h(v[4 * q + 2 * k] * norm) | (f2h(v[4 * q + 2 * k + 1] * norm) << 16);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + unit_major_index(t, col + 4 * q)) = u;
+        }
+    } else if (mode == 0) {
         f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx);
 #pragma unroll
         for (int q = 0; q < V / 4; ++q)
@@ -209,10 +219,11 @@ __global__ void __launch_bounds__(256) k_rotate_v(int T, int rows, int n, int b,
 
 hipError_t launch_rotate(int T, int n, int b, const void* x, int x_is_f32, const uint16_t* s,
                          const int8_t* sign, void* out, int mode, hipStream_t st) {
-    if (mode == 3 && T > kSkinnyT) return hipErrorInvalidValue;
-    if (mode < 0 || mode == 2 || mode > 3 || b < 1 || b > 1024 || (b & (b - 1)) || n % b)
+    if ((mode == 3 || mode == 4) && T > kSkinnyT) return hipErrorInvalidValue;
+    if (mode < 0 || mode == 2 || mode > 4 || b < 1 || b > 1024 || (b & (b - 1)) || n % b ||
+        (mode == 4 && n % kTileCols))
         return hipErrorInvalidValue;
-    const int rows = mode == 3 ? kSkinnyT : T;  // mode 3 writes the zero rows past T too
+    const int rows = mode >= 3 ? kSkinnyT : T;  // modes 3 and 4 write the zero rows past T too
     const float vnorm = float(1.0 / __builtin_sqrt(double(b)));
     auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
     if (b <= 1024 && n % (64 * (b <= 512 ? 8 : 16)) == 0 && al16(x) && al16(out) && al16(s) &&

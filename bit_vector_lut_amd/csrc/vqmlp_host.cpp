@@ -261,6 +261,7 @@ struct Workspace {
     float* a;         // [8][I]
     uint16_t* ab;     // [8][I] binary16 rotated intermediate
     float* part;      // [slices][8][H]
+    float* skp;       // stream-K partial-sum slots (gate/up, then reused by down)
     // tiled region
     uint16_t* xt;     // [T][H]
     float* a_t;       // [T][I]
@@ -294,6 +295,8 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
     const size_t o_a = take(size_t(kSkinnyT) * I * 4);
     const size_t o_ab = take(size_t(kSkinnyT) * I * 2);
     const size_t o_part = take(size_t(p->g_dn.slices) * kSkinnyT * H * 4);
+    const size_t o_skp = take(std::max(streamk_part_floats(2, I, H, p->cus),
+                                       streamk_part_floats(1, H, I, p->cus)) * 4);
     const int Tt = T > 0 ? T : 1;
     const size_t o_xt = take(size_t(Tt) * H * 2);
     const size_t o_at32 = take(size_t(Tt) * I * 4);
@@ -318,6 +321,7 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
         w.a = reinterpret_cast<float*>(b + o_a);
         w.ab = reinterpret_cast<uint16_t*>(b + o_ab);
         w.part = reinterpret_cast<float*>(b + o_part);
+        w.skp = reinterpret_cast<float*>(b + o_skp);
         w.xt = reinterpret_cast<uint16_t*>(b + o_xt);
         w.a_t = reinterpret_cast<float*>(b + o_at32);
         w.at = reinterpret_cast<uint16_t*>(b + o_at);
@@ -384,6 +388,35 @@ vqmlp_status run_skinny(const vqmlp_plan* p, int T, const void* x, void* y, cons
         e = launch_reduce_down(T, H, d.slices, w.part, p->down.sc, static_cast<uint16_t*>(y), st);
         if (e != hipSuccess) return hip_fail(e, "down reduction");
     }
+    return ok();
+}
+
+// The stream-K kernels: rotate x, gate/up (+ SiLU epilogue), rotate a, down (+ y epilogue).
+vqmlp_status run_streamk(const vqmlp_plan* p, int T, const void* x, void* y, const Workspace& w,
+                         hipStream_t st) {
+    const int H = p->d.H, I = p->d.I;
+    hipError_t e = launch_rotate(T, H, p->bh, x, 0, p->d.s_in, p->d.sign_h, w.xb, 4, st);
+    if (e != hipSuccess) return hip_fail(e, "rotate (input)");
+    StreamKArgs a;
+    memset(&a, 0, sizeof a);
+    a.mat[0] = p->gate;
+    a.mat[1] = p->up;
+    a.nmat = 2;
+    a.bx = w.xb;
+    a.part = w.skp;
+    a.sign_i = p->d.sign_i;
+    e = launch_streamk(a, p->cus, T, w.a, nullptr, st);
+    if (e != hipSuccess) return hip_fail(e, "stream-K gate/up");
+    e = launch_rotate(T, I, p->bi, w.a, 1, nullptr, nullptr, w.ab, 4, st);
+    if (e != hipSuccess) return hip_fail(e, "rotate (intermediate)");
+    StreamKArgs d;
+    memset(&d, 0, sizeof d);
+    d.mat[0] = p->down;
+    d.nmat = 1;
+    d.bx = w.ab;
+    d.part = w.skp;
+    e = launch_streamk(d, p->cus, T, nullptr, static_cast<uint16_t*>(y), st);
+    if (e != hipSuccess) return hip_fail(e, "stream-K down");
     return ok();
 }
 
@@ -759,7 +792,7 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
     if (!p) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_forward: null plan");
     if (T < 0 || T > p->d.t_max)
         return fail(VQMLP_ERR_INVALID_ARG, "T=%d outside [0, t_max=%d]", T, p->d.t_max);
-    if (path < 0 || path > 4) return fail(VQMLP_ERR_INVALID_ARG, "unknown path %d", path);
+    if (path < 0 || path > 5) return fail(VQMLP_ERR_INVALID_ARG, "unknown path %d", path);
     if (T == 0) return ok();
     if (!x || !y || !workspace) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_forward: null pointer");
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256))
@@ -775,13 +808,19 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
     const size_t xy = size_t(T) * p->d.H * 2;
     if ((xb < wb + w.bytes && wb < xb + xy) || (yb < wb + w.bytes && wb < yb + xy))
         return fail(VQMLP_ERR_INVALID_ARG, "x or y overlaps the workspace");
-    // 1: the fused single-launch kernel, 3: the per-phase skinny kernels, 2: tiled; 0 picks
-    // the fused kernel for T <= 8 where it applies, else the per-phase kernels, else tiled
+    // 1: the fused single-launch kernel, 3: the per-phase skinny kernels, 4: the fused kernel's
+    // phases as separate launches, 5: the stream-K kernels, 2: tiled; 0 picks the fused kernel
+    // for T <= 8 where it applies, else the per-phase kernels, else tiled
     const bool fused_ok = p->fz.tpw > 0;
-    if (path == 1 || path == 3 || path == 4) {
+    const bool streamk_ok = streamk_grid(2, p->d.I, p->d.H, p->cus) > 0 &&
+                            streamk_grid(1, p->d.H, p->d.I, p->cus) > 0;
+    if (path == 1 || path == 3 || path == 4 || path == 5) {
         if (T > kSkinnyT)
             return fail(VQMLP_ERR_UNSUPPORTED, "the skinny path takes T <= %d (T=%d)", kSkinnyT, T);
-        if (!(path == 3 ? p->skinny_ok : fused_ok))
+        if (path == 5 && !streamk_ok)
+            return fail(VQMLP_ERR_UNSUPPORTED, "the stream-K path does not take H=%d I=%d",
+                        p->d.H, p->d.I);
+        if (path != 5 && !(path == 3 ? p->skinny_ok : fused_ok))
             return fail(VQMLP_ERR_UNSUPPORTED, "the skinny path takes H <= %d (H=%d)",
                         kSkinnyWaves * kSkinnyMaxTPW * kTileCols, p->d.H);
     }
@@ -790,6 +829,7 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
     if (use == 2 && !p->tiled_ok)
         return fail(VQMLP_ERR_UNSUPPORTED, "the tiled path takes H and I multiples of 64");
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (use == 5) return run_streamk(p, T, x, y, w, st);
     if (use == 1) return run_fused(p, T, x, y, w, st);
     if (use == 4) return run_fused_phased(p, T, x, y, w, st);
     if (use == 3) return run_skinny(p, T, x, y, w, st);

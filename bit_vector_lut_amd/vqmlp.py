@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libvqmlp.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_PHASED = 0, 1, 2, 3
+PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_PHASED, PATH_FUSED_PHASED, PATH_STREAMK = 0, 1, 2, 3, 4, 5
 
 
 class VqmlpError(RuntimeError):

@@ -113,7 +113,7 @@ def _run(vq, torch_dev, layer, path=0, mlp=None):
     return _f64(y)
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("path", [0, 1, 2, 3, 4, 5])
 def test_config1_tiny(vq, oracle_mod, torch_dev, path):
     L = synth.config1()
     _say("config1 path=%d" % path)
@@ -132,7 +132,7 @@ def test_mlp_small_shapes(vq, oracle_mod, torch_dev, H, I, T):
     _say("small H=%d I=%d T=%d" % (H, I, T))
     mlp = vq.MLP.from_layer(L, t_max=max(T, 8))
     ref = oracle_mod.mlp_forward(L)
-    for path in ([0, 1, 2, 3, 4] if T <= 8 else [0]):
+    for path in ([0, 1, 2, 3, 4, 5] if T <= 8 else [0]):
         y = _run(vq, torch_dev, L, path, mlp)
         assert _report("H=%d I=%d T=%d path %d" % (H, I, T, path), y, ref) <= MLP_TOL
 
@@ -159,11 +159,36 @@ def test_config2_tiled_path(vq, oracle_mod, torch_dev, config2, config2_ref):
     assert _report("config2 tiled", y, config2_ref) <= MLP_TOL
 
 
-@pytest.mark.parametrize("path", [1, 4])
-def test_config2_fused_path(vq, oracle_mod, torch_dev, config2, config2_ref, path):
-    _say("config2 fused kernel path %d" % path)
+@pytest.mark.parametrize("path", [1, 3, 4, 5])
+def test_config2_t8_paths(vq, oracle_mod, torch_dev, config2, config2_ref, path):
+    _say("config2 T=8 path %d" % path)
     y = _run(vq, torch_dev, config2, path)
-    assert _report("config2 fused path %d" % path, y, config2_ref) <= MLP_TOL
+    assert _report("config2 path %d" % path, y, config2_ref) <= MLP_TOL
+
+
+@pytest.mark.parametrize("H,I,T", [(256, 17408, 8), (5120, 1024, 3), (64, 65536, 8), (1024, 4352, 1)])
+def test_streamk_range_shapes(vq, oracle_mod, torch_dev, H, I, T):
+    """Stream-K ranges that cross up to four row-tile pairs (short K), ranges inside one pair
+    (long K), more workgroups than compute units (K = 64: ranges are capped), and T = 1."""
+    L = synth.mlp_layer(H, I, T, seed=H + 3 * I + T, outliers=True)
+    _say("stream-K H=%d I=%d T=%d" % (H, I, T))
+    y = _run(vq, torch_dev, L, 5)
+    ref = oracle_mod.mlp_forward(L)
+    assert _report("stream-K H=%d I=%d T=%d" % (H, I, T), y, ref) <= MLP_TOL
+
+
+@pytest.mark.parametrize("H,I,T,bh", [(512, 1024, 8, 32), (512, 1024, 3, 64), (512, 1024, 8, 256),
+                                       (320, 640, 5, 64), (1024, 2048, 8, 128)])
+def test_fused_input_rotation_blocks(vq, oracle_mod, torch_dev, H, I, T, bh):
+    """The fused kernel rotates x inside every workgroup, one 64-, 128- or 256-column chunk of
+    all 8 operand rows per wave: Hadamard blocks smaller than, and as wide as, the chunk."""
+    L = synth.mlp_layer(H, I, T, seed=H + 7 * bh + T, outliers=True, had_block_h=bh)
+    _say("fused input rotation H=%d I=%d T=%d bh=%d" % (H, I, T, bh))
+    mlp = vq.MLP.from_layer(L, t_max=8)
+    ref = oracle_mod.mlp_forward(L)
+    for path in (1, 4):
+        y = _run(vq, torch_dev, L, path, mlp)
+        assert _report("bh=%d path %d" % (bh, path), y, ref) <= MLP_TOL
 
 
 def test_fused_control_block_is_left_ready(vq, oracle_mod, torch_dev):
@@ -188,7 +213,7 @@ def test_fused_control_block_is_left_ready(vq, oracle_mod, torch_dev):
     assert ctl[3] == fused_calls
 
 
-@pytest.mark.parametrize("path", [1, 3, 4])
+@pytest.mark.parametrize("path", [1, 3, 4, 5])
 def test_config2_deterministic(vq, torch_dev, config2, path):
     mlp = vq.MLP.from_layer(config2)
     x = vq.to_device(config2.x)
