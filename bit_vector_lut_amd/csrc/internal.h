@@ -79,16 +79,21 @@ struct StreamKArgs {
     VQ3View mat[2];        // gate, up (nmat 2) or down (nmat 1: tiles 2q and 2q + 1)
     int nmat;
     int MT, KT, NQ, U;     // row tiles, K tiles, row-tile pairs, units (set by the launcher)
+    int T;
     const uint16_t* bx;    // activation operand, 8 rows of K in the unit-major layout
     float* part;           // partial-sum slots [NQ + grid][2][64][4]
-    const int8_t* sign_i;  // gate+up: sign of the intermediate rotation (NULL = +1)
+    // gate/up finish: a = SiLU(g) u . sign, rotated per span into the down operand
+    const int8_t* sign_i;  // sign of the intermediate rotation (NULL = +1)
+    int span, bi;          // span rows = max(bi, 32) (set by the launcher); Hadamard block of I
+    float norm_i;          // 1 / sqrt(bi)
+    uint16_t* ab_out;      // rotated a, 8 rows of I, unit-major binary16
+    // down finish
+    uint16_t* y;           // y [T][H] binary16
 };
 int streamk_grid(int nmat, int N, int K, int cus);
 size_t streamk_part_floats(int nmat, int N, int K, int cus);
-// the projection and its epilogue: nmat 2 writes a [8][I] fp32 (SiLU(g) u, signed), nmat 1
-// writes y [T][H] binary16
-hipError_t launch_streamk(const StreamKArgs& a, int cus, int T, float* a_out, uint16_t* y,
-                          hipStream_t st);
+// One projection and its finishing pass: nmat 2 writes the rotated a, nmat 1 writes y.
+hipError_t launch_streamk(const StreamKArgs& a, int cus, hipStream_t st);
 
 // ---- fused persistent forward (T <= 8): the whole MLP in one launch
 // Control block (kCtlHdr 32-bit words, zero before the first call): word 0 is the item queue

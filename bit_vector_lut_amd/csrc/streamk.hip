@@ -45,9 +45,13 @@ typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
 __host__ __device__ __forceinline__ int sk_start(int b, int U, int G) {
     return int((long long)b * U / G);
 }
-// the workgroup whose range holds unit u
+// the workgroup whose range holds unit u (U G < 2^31, checked by the launcher)
 __device__ __forceinline__ int sk_owner(int u, int U, int G) {
-    return int(((long long)(u + 1) * G + U - 1) / U) - 1;
+    return int((uint32_t(u + 1) * uint32_t(G) + uint32_t(U) - 1u) / uint32_t(U)) - 1;
+}
+// first unit of workgroup b's range, 32-bit form of sk_start for the combine passes
+__device__ __forceinline__ int sk_start32(int b, int U, int G) {
+    return int(uint32_t(b) * uint32_t(U) / uint32_t(G));
 }
 }  // namespace
 
@@ -64,9 +68,11 @@ template <int NMAT>
 __global__ void __launch_bounds__(kW * 64, 1) k_streamk(StreamKArgs a) {
     // one LDS block with the tables at address 0: a lookup address is then the code and lane
     // bits alone (a base of 64 KB would not fit the 16-bit offset field and cost an add each)
-    __shared__ __attribute__((aligned(16))) unsigned char lds[kMaxQ * 2 * kTabDw * 4 + kW * 2 * 2 * 64 * 16];
-    auto& tab = *reinterpret_cast<uint32_t (*)[kMaxQ][2][kTabDw]>(lds);                      // 64 KB
-    auto& red = *reinterpret_cast<f32x4 (*)[kW][2][2][64]>(lds + kMaxQ * 2 * kTabDw * 4);    // 64 KB
+    constexpr int kOffRed = kMaxQ * 2 * kTabDw * 4, kOffMeta = kOffRed + kW * 2 * 2 * 64 * 16;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kOffMeta + kW * 8];
+    auto& tab = *reinterpret_cast<uint32_t (*)[kMaxQ][2][kTabDw]>(lds);      // 64 KB
+    auto& red = *reinterpret_cast<f32x4 (*)[kW][2][2][64]>(lds + kOffRed);  // 64 KB
+    auto& meta = *reinterpret_cast<int (*)[kW][2]>(lds + kOffMeta);         // wave's first, last pair
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int KT = a.KT, U = a.U, MT = a.MT, G = gridDim.x, b = blockIdx.x;
@@ -110,6 +116,18 @@ __global__ void __launch_bounds__(kW * 64, 1) k_streamk(StreamKArgs a) {
     const int voff_c = 12 * l;                              // the lane's 12 code bytes
     const int voff_b = ((l >> 4) * 8 + tok) * 32;           // the lane's 32 activation bytes
 
+    // table words of this thread (loaded first: they are small and the ring waits on nothing)
+    constexpr int kTabPer = (kMaxQ * 512 + kW * 64 - 1) / (kW * 64);
+    uint32_t tv[kTabPer];
+#pragma unroll
+    for (int k = 0; k < kTabPer; ++k) {
+        const int i = tid + k * kW * 64;
+        const int c = i & 63, g = (i >> 6) & 3, m = (i >> 8) & 1, r = i >> 9;
+        // (a select of the two pointers: indexing the argument array by a lane's m would load it)
+        const uint32_t* cbm = m ? a.mat[1].cb : a.mat[0].cb;
+        tv[k] = i < nq * 512 ? cbm[size_t(tile_of(q0 + r, m) * 4 + g) * 64 + c] : 0u;
+    }
+
     // ring: code words of both tiles and the activation words of kRing units
     uint32_t rc[kRing][2][3];
     u32x4 rb[kRing][2];
@@ -150,13 +168,21 @@ __global__ void __launch_bounds__(kW * 64, 1) k_streamk(StreamKArgs a) {
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- tables of the range's row-tile pairs (thread i: pair r, matrix m, group g, entry c)
-    for (int i = tid; i < nq * 512; i += kW * 64) {
-        const int c = i & 63, g = (i >> 6) & 3, m = (i >> 8) & 1, r = i >> 9;
-        const uint32_t v = a.mat[m].cb[size_t(tile_of(q0 + r, m) * 4 + g) * 64 + c];
-        const u32x4 q4 = u32x4{v, v, v, v};
-        *reinterpret_cast<u32x4*>(&tab[r][m][c * 32 + 4 * g]) = q4;
-        *reinterpret_cast<u32x4*>(&tab[r][m][c * 32 + 4 * (g + 4)]) = q4;
+    // ---- tables of the range's row-tile pairs (thread i: pair r, matrix m, group g, entry c),
+    // stored once the loads (issued before the ring's) are in
+#pragma unroll
+    for (int k = 0; k < kTabPer; ++k) {
+        const int i = tid + k * kW * 64;
+        if (i < nq * 512) {
+            const int c = i & 63, g = (i >> 6) & 3, m = (i >> 8) & 1, r = i >> 9;
+            const u32x4 q4 = u32x4{tv[k], tv[k], tv[k], tv[k]};
+            *reinterpret_cast<u32x4*>(&tab[r][m][c * 32 + 4 * g]) = q4;
+            *reinterpret_cast<u32x4*>(&tab[r][m][c * 32 + 4 * (g + 4)]) = q4;
+        }
+    }
+    if (l == 0) {
+        meta[w][0] = nw > 0 ? qa : -1;
+        meta[w][1] = nw > 0 ? qa + (na < nw ? 1 : 0) : -1;
     }
 
     __syncthreads();  // tables written
@@ -234,9 +260,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_streamk(StreamKArgs a) {
         const int r = tid >> 7, m = (tid >> 6) & 1, ln = tid & 63, q = q0 + r;
         f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int v = 0; v < kW; ++v) {
-            const int vu0 = u0 + (v * n) / kW, vn = u0 + ((v + 1) * n) / kW - vu0;
-            if (vn <= 0) continue;
-            const int va = vu0 / KT, vb = (vu0 + vn - 1) / KT;
+            const int va = meta[v][0], vb = meta[v][1];  // -1: no units
             if (q < va || q > vb) continue;
             sum += red[v][q == va ? 0 : 1][m][ln];
         }
@@ -244,42 +268,62 @@ __global__ void __launch_bounds__(kW * 64, 1) k_streamk(StreamKArgs a) {
     }
 }
 
-// gate/up epilogue: thread (q, lane, reg) sums the slots of q, scales, a = SiLU(g) u, sign
-__global__ void __launch_bounds__(256) k_streamk_gu_fin(StreamKArgs a, int G, float* a_out) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= a.NQ * 256) return;
-    const int q = i >> 8, ln = (i >> 2) & 63, rg = i & 3;
-    const int b0 = sk_owner(q * a.KT, a.U, G), b1 = sk_owner((q + 1) * a.KT - 1, a.U, G);
-    float g = 0.f, u = 0.f;
-    for (int bb = b0; bb <= b1; ++bb) {
-        if (sk_start(bb, a.U, G) == sk_start(bb + 1, a.U, G)) continue;  // empty range: no slot
-        const float* s = a.part + size_t(q + bb) * kSlot + ln * 4 + rg;
-        g += s[0];
-        u += s[256];
-    }
-    const int row = q * kTileRows + 2 * (4 * (ln >> 4) + rg) + (ln & 1), t = (ln & 15) >> 1;
-    g *= h2f(a.mat[0].sc[row]);
-    u *= h2f(a.mat[1].sc[row]);
-    const float act = g / (1.f + expf(-g)) * u;
-    const uint32_t sbit = a.sign_i && a.sign_i[row] < 0 ? 0x80000000u : 0u;
-    a_out[size_t(t) * a.mat[0].N + row] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, act) ^ sbit);
-}
+// ---- finishing passes (after the projection's launch, so its slots are plain reads)
 
-// down epilogue: thread (q, tile m, lane, reg) sums the slots of q and scales into y
-__global__ void __launch_bounds__(256) k_streamk_dn_fin(StreamKArgs a, int G, int T, uint16_t* y) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= a.NQ * 512) return;
-    const int q = i >> 9, m = (i >> 8) & 1, ln = (i >> 2) & 63, rg = i & 3;
-    const int tile = 2 * q + m;
-    const int t = (ln & 15) >> 1;
-    if (tile >= a.MT || t >= T) return;
+// sum of the slots of row-tile pair q, in workgroup order (empty ranges have no slot); w is the
+// slot-relative word (tile m, lane, reg)
+__device__ __forceinline__ float sk_slot_sum(const StreamKArgs& a, int G, int q, int w) {
     const int b0 = sk_owner(q * a.KT, a.U, G), b1 = sk_owner((q + 1) * a.KT - 1, a.U, G);
     float v = 0.f;
     for (int bb = b0; bb <= b1; ++bb)
-        if (sk_start(bb, a.U, G) != sk_start(bb + 1, a.U, G))  // empty ranges have no slot
-            v += a.part[size_t(q + bb) * kSlot + (m * 64 + ln) * 4 + rg];
+        if (sk_start32(bb, a.U, G) != sk_start32(bb + 1, a.U, G)) v += a.part[size_t(q + bb) * kSlot + w];
+    return v;
+}
+
+// gate/up: workgroup s finishes rotation span s (R = max(bi, 32) rows of the intermediate):
+// a = SiLU(g s_g) (u s_u) . sign for the 8 operand rows, then x~ = H_bi(a) / sqrt(bi) in LDS
+// (distances 1 .. bi/2 in that order, each pair (lo, hi) -> (lo + hi, lo - hi)), written in
+// the unit-major binary16 layout the down projection reads.
+__global__ void __launch_bounds__(1024) k_streamk_gu_fin(StreamKArgs a, int G) {
+    __shared__ float buf[kSkinnyT * 1024];
+    const int R = a.span, r0 = blockIdx.x * R, tid = threadIdx.x;
+    // thread i < 8 R: pair q = (r0 + 32 j) / 32 with j = i / 256, lane ln, reg rg of its tile
+    for (int i = tid; i < kSkinnyT * R; i += 1024) {
+        const int q = r0 / kTileRows + (i >> 8), ln = (i >> 2) & 63, rg = i & 3;
+        float g = sk_slot_sum(a, G, q, ln * 4 + rg);
+        float u = sk_slot_sum(a, G, q, 256 + ln * 4 + rg);
+        const int row = q * kTileRows + 2 * (4 * (ln >> 4) + rg) + (ln & 1), t = (ln & 15) >> 1;
+        g *= h2f(a.mat[0].sc[row]);
+        u *= h2f(a.mat[1].sc[row]);
+        const float act = g / (1.f + expf(-g)) * u;
+        const uint32_t sbit = a.sign_i && a.sign_i[row] < 0 ? 0x80000000u : 0u;
+        buf[t * R + row - r0] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, act) ^ sbit);
+    }
+    __syncthreads();
+    for (int h = 1; h < a.bi; h <<= 1) {
+        for (int p = tid; p < kSkinnyT * R / 2; p += 1024) {
+            const int t = p / (R / 2), k = p % (R / 2);
+            const int i0 = t * R + (k / h) * 2 * h + k % h, i1 = i0 + h;
+            const float x0 = buf[i0], x1 = buf[i1];
+            buf[i0] = x0 + x1;
+            buf[i1] = x0 - x1;
+        }
+        __syncthreads();
+    }
+    for (int i = tid; i < kSkinnyT * R; i += 1024)
+        a.ab_out[unit_major_index(i / R, r0 + i % R)] = uint16_t(f2h(buf[i] * a.norm_i));
+}
+
+// down: thread (q, tile m, lane, reg) sums the slots of q and scales into y
+__global__ void __launch_bounds__(256) k_streamk_dn_fin(StreamKArgs a, int G) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.NQ * 512) return;
+    const int q = i >> 9, m = (i >> 8) & 1, ln = (i >> 2) & 63, rg = i & 3;
+    const int tile = 2 * q + m, t = (ln & 15) >> 1;
+    if (tile >= a.MT || t >= a.T) return;
+    const float v = sk_slot_sum(a, G, q, (m * 64 + ln) * 4 + rg);
     const int row = tile * kTileRows + 2 * (4 * (ln >> 4) + rg) + (ln & 1);
-    y[size_t(t) * a.mat[0].N + row] = uint16_t(f2h(v * h2f(a.mat[0].sc[row])));
+    a.y[size_t(t) * a.mat[0].N + row] = uint16_t(f2h(v * h2f(a.mat[0].sc[row])));
 }
 
 int streamk_grid(int nmat, int N, int K, int cus) {
@@ -292,7 +336,8 @@ int streamk_grid(int nmat, int N, int K, int cus) {
     const long long cap = (long long)(kMaxQ - 1) * KT + 1;
     long long g = cus > 0 ? cus : 1;
     if ((U + g - 1) / g > cap) g = (U + cap - 1) / cap;
-    return g > (1 << 20) ? 0 : int(g);
+    // (the combine passes index in 32 bits)
+    return g > (1 << 20) || U * g >= (1ll << 31) ? 0 : int(g);
 }
 
 size_t streamk_part_floats(int nmat, int N, int K, int cus) {
@@ -300,8 +345,7 @@ size_t streamk_part_floats(int nmat, int N, int K, int cus) {
     return size_t(NQ + streamk_grid(nmat, N, K, cus)) * kSlot;
 }
 
-hipError_t launch_streamk(const StreamKArgs& in, int cus, int T, float* a_out, uint16_t* y,
-                          hipStream_t st) {
+hipError_t launch_streamk(const StreamKArgs& in, int cus, hipStream_t st) {
     StreamKArgs a = in;
     const int nmat = a.nmat;
     if (nmat == 1) a.mat[1] = a.mat[0];
@@ -309,23 +353,29 @@ hipError_t launch_streamk(const StreamKArgs& in, int cus, int T, float* a_out, u
     for (int m = 0; m < 2; ++m)
         if (!a.mat[m].codes || !a.mat[m].cb || !a.mat[m].sc || a.mat[m].N != N || a.mat[m].K != K)
             return hipErrorInvalidValue;
-    if (!a.bx || !a.part || N % kTileRows || K % kTileCols || (nmat == 2 ? !a_out : !y) ||
-        T < 1 || T > kSkinnyT)
+    if (!a.bx || !a.part || N % kTileRows || K % kTileCols || a.T < 1 || a.T > kSkinnyT)
         return hipErrorInvalidValue;
+    if (nmat == 2) {
+        // spans of max(bi, 32) rows (at most 1024: the finishing pass holds 8 x span floats)
+        if (!a.ab_out || a.bi < 1 || a.bi > 1024 || (a.bi & (a.bi - 1)))
+            return hipErrorInvalidValue;
+        a.span = a.bi > kTileRows ? a.bi : kTileRows;
+        if (N % a.span) return hipErrorInvalidValue;
+    } else if (nmat != 1 || !a.y) {
+        return hipErrorInvalidValue;
+    }
     a.MT = N / kTileRows;
     a.KT = K / kTileCols;
     a.NQ = nmat == 2 ? a.MT : (a.MT + 1) / 2;
     a.U = a.NQ * a.KT;
     const int G = streamk_grid(nmat, N, K, cus);
-    if (G < 1) return hipErrorInvalidValue;
+    if (G < 1 || (long long)a.U * G >= (1ll << 31)) return hipErrorInvalidValue;
     if (nmat == 2) {
         hipLaunchKernelGGL(k_streamk<2>, dim3(G), dim3(kW * 64), 0, st, a);
-        hipLaunchKernelGGL(k_streamk_gu_fin, dim3((a.NQ * 256 + 255) / 256), dim3(256), 0, st, a, G,
-                           a_out);
+        hipLaunchKernelGGL(k_streamk_gu_fin, dim3(N / a.span), dim3(1024), 0, st, a, G);
     } else {
         hipLaunchKernelGGL(k_streamk<1>, dim3(G), dim3(kW * 64), 0, st, a);
-        hipLaunchKernelGGL(k_streamk_dn_fin, dim3((a.NQ * 512 + 255) / 256), dim3(256), 0, st, a, G,
-                           T, y);
+        hipLaunchKernelGGL(k_streamk_dn_fin, dim3((a.NQ * 512 + 255) / 256), dim3(256), 0, st, a, G);
     }
     return hipGetLastError();
 }

@@ -391,7 +391,8 @@ vqmlp_status run_skinny(const vqmlp_plan* p, int T, const void* x, void* y, cons
     return ok();
 }
 
-// The stream-K kernels: rotate x, gate/up (+ SiLU epilogue), rotate a, down (+ y epilogue).
+// The stream-K kernels: rotate x, gate/up and its finishing pass (a and its rotation), down and
+// its finishing pass (y).
 vqmlp_status run_streamk(const vqmlp_plan* p, int T, const void* x, void* y, const Workspace& w,
                          hipStream_t st) {
     const int H = p->d.H, I = p->d.I;
@@ -402,20 +403,24 @@ vqmlp_status run_streamk(const vqmlp_plan* p, int T, const void* x, void* y, con
     a.mat[0] = p->gate;
     a.mat[1] = p->up;
     a.nmat = 2;
+    a.T = T;
     a.bx = w.xb;
     a.part = w.skp;
     a.sign_i = p->d.sign_i;
-    e = launch_streamk(a, p->cus, T, w.a, nullptr, st);
+    a.bi = p->bi;
+    a.norm_i = float(1.0 / std::sqrt(double(p->bi)));
+    a.ab_out = w.ab;
+    e = launch_streamk(a, p->cus, st);
     if (e != hipSuccess) return hip_fail(e, "stream-K gate/up");
-    e = launch_rotate(T, I, p->bi, w.a, 1, nullptr, nullptr, w.ab, 4, st);
-    if (e != hipSuccess) return hip_fail(e, "rotate (intermediate)");
     StreamKArgs d;
     memset(&d, 0, sizeof d);
     d.mat[0] = p->down;
     d.nmat = 1;
+    d.T = T;
     d.bx = w.ab;
     d.part = w.skp;
-    e = launch_streamk(d, p->cus, T, nullptr, static_cast<uint16_t*>(y), st);
+    d.y = static_cast<uint16_t*>(y);
+    e = launch_streamk(d, p->cus, st);
     if (e != hipSuccess) return hip_fail(e, "stream-K down");
     return ok();
 }

@@ -192,15 +192,16 @@ def test_fused_input_rotation_blocks(vq, oracle_mod, torch_dev, H, I, T, bh):
 
 
 def test_fused_control_block_is_left_ready(vq, oracle_mod, torch_dev):
-    """Several fused calls on one workspace (mixed with the other paths): every call is right,
-    the queue and counters are back at zero, the error word stays clear, the epoch counts calls."""
+    """Several fused calls on one workspace (mixed with the other paths, stream-K included):
+    every call is right, the queue and counters are back at zero, the error word stays clear,
+    the epoch counts calls."""
     L = synth.mlp_layer(512, 1024, 8, seed=11, outliers=True)
     mlp = vq.MLP.from_layer(L, t_max=8)
     x = vq.to_device(L.x)
     ws = mlp.workspace(8)
     ref = oracle_mod.mlp_forward(L)
     fused_calls = 0
-    for path in (1, 0, 2, 1, 3, 4, 1, 1):
+    for path in (1, 0, 5, 2, 1, 3, 5, 4, 1, 5, 1):
         _say("control block: path %d" % path)
         y = _f64(mlp.forward(x, workspace=ws, path=path))
         torch_dev.cuda.synchronize()
@@ -211,6 +212,7 @@ def test_fused_control_block_is_left_ready(vq, oracle_mod, torch_dev):
     assert ctl[0] == 0 and ctl[1] == 0, ctl[:4]  # queue head, exit count
     assert ctl[2] == 0, "a bounded wait ran out: error bits %#x" % ctl[2]
     assert ctl[3] == fused_calls
+    assert not ctl[4:].any(), ctl  # the rest of the block is never written
 
 
 @pytest.mark.parametrize("path", [1, 3, 4, 5])
