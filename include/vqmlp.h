@@ -125,9 +125,9 @@ vqmlp_status vqmlp_forward(const vqmlp_plan *plan, int T, const void *x, void *y
  * matrix-core kernels, 3 = the T <= 8 kernels as separate per-phase launches, 4 = the fused
  * kernel's phases as separate launches, 5 = the T <= 8 stream-K kernels (the weight stream cut
  * into equal contiguous ranges, one per workgroup; any H and I that are multiples of 64).
- * Paths 1, 3, 4 and 5 take T <= 8; paths 1, 3 and 4 take H <= 5120.  Paths 1, 4 and 5 keep
- * queues, counters or an epoch in the workspace: the caller zero-fills the workspace once, and
- * every call leaves that state ready for the next call. */
+ * Paths 1, 3, 4 and 5 take T <= 8; paths 1, 3 and 4 take H <= 5120.  Paths 1 and 4 keep their
+ * queue, counters and epoch in the first bytes of the workspace: the caller zero-fills the
+ * workspace once, and every call leaves that control block ready for the next call. */
 vqmlp_status vqmlp_forward_path(const vqmlp_plan *plan, int T, const void *x, void *y,
                                 void *workspace, size_t workspace_bytes, int path, void *stream);
 
