@@ -73,6 +73,20 @@ hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st);
 hipError_t launch_reduce_down(int T, int N, int slices, const float* part, const uint16_t* sc,
                               uint16_t* y, hipStream_t st);
 
+// ---- scalar-LUT projection for T <= 8 (K <= kLut8MaxK): y = sc . (W_lut x~) + U z
+constexpr int kLut8MaxK = 5120;
+struct Lut8Args {
+    const uint32_t* codes;  // [N][K * bits / 32] row-major code words
+    const uint16_t* lut;    // [N / 8][2^bits] binary16
+    const uint16_t* sc;     // [N] binary16 row scales
+    const uint16_t* x;      // x~ [T][K] binary16
+    uint16_t* y;            // [T][N] binary16
+    const uint16_t* U;      // [N][r] binary16 (r > 0)
+    const float* z;         // [T][r] fp32 (r > 0)
+    int bits, N, K, T, r;
+};
+hipError_t launch_lut8(const Lut8Args& a, hipStream_t st);
+
 // ---- stream-K skinny path (T <= 8): the weight stream cut into equal contiguous ranges
 constexpr int kStreamKMaxQ = 4;  // row-tile pairs one workgroup range may touch
 struct StreamKArgs {

@@ -1,0 +1,197 @@
+// lut8.hip -- scalar-LUT projection for T <= 8 rows (token mixers at decode size), gfx950.
+//
+// Format (model card "anemll/anemll-forge-qwen3.8-27B", format table, "Token mixers" row): 2- or
+// 4-bit codes, one table of 2^bits binary16 scalars per 8 output rows, a binary16 scale per row,
+// rank-r binary16 factors U [N][r], V [r][K]:  y = sc . (W_lut x~) + U z,  z = V x~.
+//
+// At T <= 8 the projection streams each code once and multiplies it by at most 8 tokens, so the
+// layout is chosen for the code stream: a workgroup of 16 waves owns 32 output rows (two 16-row
+// tiles) and splits K in 8 slices; every lane issues all of its code loads (one 32-bit word per
+// 64-column unit for 2-bit codes, two for 4-bit) before anything else, x~ (at most 8 x 5120
+// binary16) is staged once per workgroup in LDS, and the 16 waves' partial sums meet in LDS.
+//
+// Product: v_mfma_f32_16x16x32_f16 with A = the decoded weights of 16 rows and B = x~ (column n =
+// token n, zero for n >= 8).  A wave's K slice of nus 64-column units is cut into four runs of
+// 16 nus columns, one per lane group g = l / 16; MFMA step (u, s) takes columns 16 u + 8 s + 0 .. 7
+// of each group's run in both operands, so a lane's codes for the whole slice are one contiguous
+// run of 16 nus codes in the row-major packing (nus or 2 nus consecutive words).  Lookups go to tables replicated over the 32 bank
+// columns (column c serves the lanes with l % 32 == c, whose row lies in group (c % 16) / 8):
+// 2-bit codes are looked up in pairs (16 entries, each the two binary16 weights of a code pair,
+// so the 32-bit read is the operand word), 4-bit codes one by one (16 entries).
+#include "device.h"
+#include "internal.h"
+
+namespace vqmlp {
+
+namespace {
+constexpr int kW = 16;                  // waves per workgroup: 2 row tiles x 8 K slices
+constexpr int kKS = 8;                  // K slices
+constexpr int kMaxK = kLut8MaxK;        // x~ rows staged in LDS
+constexpr int kXRow = kMaxK + 8;        // LDS row of x~ in halves (padded against bank conflicts)
+constexpr int kMaxU = (kMaxK / 64 + kKS - 1) / kKS;  // units per slice
+constexpr int kTabDw = 16 * 32;         // one table: 16 entries x 32 bank columns
+constexpr int kMaxR = 256;              // rank of the low-rank term
+constexpr int kUPre = 8;                // 16-byte chunks of a U row held from the start (r <= 64)
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));  // 4-byte aligned
+}  // namespace
+
+template <int BITS>
+__global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
+    constexpr int CW = BITS == 2 ? 1 : 2;  // code words per lane and unit
+    // one LDS block with the tables at address 0 (a lookup address is the entry and lane bits)
+    constexpr int kOffX = 2 * kTabDw * 4, kOffRed = kOffX + kSkinnyT * kXRow * 2;
+    constexpr int kOffZ = kOffRed + kW * 64 * 16;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kOffZ + kSkinnyT * kMaxR * 4];
+    auto& tab = *reinterpret_cast<uint32_t (*)[2][kTabDw]>(lds);
+    auto& xs = *reinterpret_cast<uint16_t (*)[kSkinnyT][kXRow]>(lds + kOffX);
+    auto& red = *reinterpret_cast<f32x4 (*)[kW][64]>(lds + kOffRed);
+    float* zs = reinterpret_cast<float*>(lds + kOffZ);  // z [8][r] (rows past T zero)
+
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int K = a.K, T = a.T, N = a.N;
+    const int row0 = blockIdx.x * 32;
+    const int rt = w / kKS, ks = w % kKS;  // row tile, K slice (uniform)
+    const int nu = K / 64, u0 = ks * nu / kKS, nus = (ks + 1) * nu / kKS - u0;
+
+    // ---- the code stream first: lane (row i, column group g) of its row tile
+    const int i = l & 15, g = l >> 4;
+    // The lane's run is kMaxU * CW words read as 16-byte loads whatever nus is: words past the
+    // run are never used, and past the last row they fall in the table section that follows
+    // the codes in the packed buffer.
+    const uint32_t* crun = a.codes + size_t(row0 + rt * 16 + i) * (K * BITS / 32) +
+                           u0 * (64 * BITS / 32) + g * nus * (16 * BITS / 32);
+    constexpr int kRunW = kMaxU * CW, kRunV = (kRunW + 3) / 4;
+    uint32_t cw[kRunV * 4];
+#pragma unroll
+    for (int v = 0; v < kRunV; ++v) {
+        const u32x4a q = *reinterpret_cast<const u32x4a*>(crun + 4 * v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cw[4 * v + e] = q[e];
+    }
+
+    // ---- the epilogue's U row (threads 0 .. 255 own one output row each), requested now
+    const int ert = tid >> 7, ej = tid & 127, ell = ej >> 2, eq = ej & 3;
+    const int el = (ell >> 3) * 16 + (ell & 7);  // lanes holding tokens 0 .. 7
+    const int erow = row0 + ert * 16 + 4 * (el >> 4) + eq;
+    const float esc = tid < 256 ? h2f(a.sc[erow]) : 0.f;
+    u32x4 upre[kUPre];
+#pragma unroll
+    for (int c = 0; c < kUPre; ++c)
+        upre[c] = tid < 256 && 8 * c < a.r
+                      ? *reinterpret_cast<const u32x4*>(a.U + size_t(erow) * a.r + 8 * c)
+                      : u32x4{0u, 0u, 0u, 0u};
+
+    // ---- every other global load before the first LDS store (a store that needs a loaded value
+    // waits for every older load, so one round trip covers them all): table entries (thread: row
+    // tile, entry e, bank column c), z, x~
+    const int trt = tid >> 9, te = (tid >> 5) & 15, tc = tid & 31;
+    const int grp = (row0 + trt * 16) / 8 + ((tc & 15) >> 3);
+    const uint32_t t0 = a.lut[BITS == 2 ? grp * 4 + (te & 3) : grp * 16 + te];
+    const uint32_t t1 = BITS == 2 ? a.lut[grp * 4 + (te >> 2)] : 0u;
+    constexpr int kZPer = kSkinnyT * kMaxR / (kW * 64);
+    float zv[kZPer];
+#pragma unroll
+    for (int k = 0; k < kZPer; ++k) {
+        const int q = tid + k * kW * 64;
+        zv[k] = q < kSkinnyT * a.r && q / a.r < T ? a.z[q] : 0.f;
+    }
+    constexpr int kXPer = kSkinnyT * kMaxK / 8 / (kW * 64);  // 16-byte chunks per thread at most
+    const int c8n = K / 8;
+    u32x4 xv[kXPer];
+#pragma unroll
+    for (int k = 0; k < kXPer; ++k) {
+        const int q = tid + k * kW * 64, t = q / c8n, c8 = (q % c8n) * 8;
+        xv[k] = q < kSkinnyT * c8n && t < T ? *reinterpret_cast<const u32x4*>(a.x + size_t(t) * K + c8)
+                                           : u32x4{0u, 0u, 0u, 0u};
+    }
+    tab[trt][te * 32 + tc] = BITS == 2 ? (t0 | (t1 << 16)) : t0;
+#pragma unroll
+    for (int k = 0; k < kZPer; ++k) {
+        const int q = tid + k * kW * 64;
+        if (q < kSkinnyT * a.r) zs[q] = zv[k];
+    }
+#pragma unroll
+    for (int k = 0; k < kXPer; ++k) {
+        const int q = tid + k * kW * 64, t = q / c8n, c8 = (q % c8n) * 8;
+        if (q < kSkinnyT * c8n) *reinterpret_cast<u32x4*>(&xs[t][c8]) = xv[k];
+    }
+    __syncthreads();
+
+    // ---- products
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    const char* tbase = reinterpret_cast<const char*>(&tab[0][0]);
+    const uint32_t lb = (uint32_t(l & 31) << 2) | uint32_t(rt * kTabDw * 4);
+    const int n = l & 15;  // B column: token n
+    auto look = [&](uint32_t e) -> uint32_t {
+        return *reinterpret_cast<const uint32_t*>(tbase + ((e << 7) | lb));
+    };
+#pragma unroll
+    for (int u = 0; u < kMaxU; ++u) {
+        if (u < nus) {  // uniform
+            const int kb = u0 * 64 + 16 * (g * nus + u);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 A;
+                if constexpr (BITS == 2) {
+                    const uint32_t d = cw[u] >> (16 * s);
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) A[p] = look((d >> (4 * p)) & 15u);
+                } else {
+                    const uint32_t d = cw[2 * u + s];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        A[p] = (look((d >> (8 * p)) & 15u) & 0xFFFFu) | (look((d >> (8 * p + 4)) & 15u) << 16);
+                }
+                const u32x4 B = n < kSkinnyT ? *reinterpret_cast<const u32x4*>(&xs[n < kSkinnyT ? n : 0][kb + 8 * s])
+                                             : u32x4{0u, 0u, 0u, 0u};
+                acc = mfma16x16x32(A, B, acc);
+            }
+        }
+    }
+    red[w][l] = acc;
+    __syncthreads();
+
+    // ---- epilogue: thread (row tile, lane with token < 8, reg) sums the 8 slices, scales, adds
+    // the rank-r term in FP32
+    if (tid < 256) {
+        float v = 0.f;
+#pragma unroll
+        for (int s = 0; s < kKS; ++s) v += red[ert * kKS + s][el][eq];
+        const int t = el & 15;
+        if (t < T) {
+            v *= esc;
+            // rank-r term in FP32: U row chunks of 8 (the first kUPre held since the start)
+            float rs = 0.f;
+            const float* zt = zs + t * a.r;
+            auto chunk = [&](const u32x4& uv, int c) {
+                const f32x4 z0 = *reinterpret_cast<const f32x4*>(zt + 8 * c);
+                const f32x4 z1 = *reinterpret_cast<const f32x4*>(zt + 8 * c + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    rs += h2f(uint16_t(uv[e / 2] >> (16 * (e & 1)))) * (e < 4 ? z0[e] : z1[e - 4]);
+            };
+#pragma unroll
+            for (int c = 0; c < kUPre; ++c)
+                if (8 * c < a.r) chunk(upre[c], c);
+            for (int c = kUPre; 8 * c < a.r; ++c)
+                chunk(*reinterpret_cast<const u32x4*>(a.U + size_t(erow) * a.r + 8 * c), c);
+            v += rs;
+            a.y[size_t(t) * N + erow] = uint16_t(f2h(v));
+        }
+    }
+}
+
+hipError_t launch_lut8(const Lut8Args& a, hipStream_t st) {
+    if (!a.codes || !a.lut || !a.sc || !a.x || !a.y || (a.bits != 2 && a.bits != 4) || a.N < 32 ||
+        a.N % 32 || a.K < 64 || a.K % 64 || a.K > kMaxK || a.T < 1 || a.T > kSkinnyT || a.r < 0 ||
+        a.r > kMaxR || a.r % 8 || (a.r > 0 && (!a.U || !a.z)))
+        return hipErrorInvalidValue;
+    if (a.bits == 2)
+        hipLaunchKernelGGL(k_lut8<2>, dim3(a.N / 32), dim3(kW * 64), 0, st, a);
+    else
+        hipLaunchKernelGGL(k_lut8<4>, dim3(a.N / 32), dim3(kW * 64), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace vqmlp

@@ -1046,6 +1046,26 @@ vqmlp_status lut_run(const vqmlp_lut_plan& p, int T, const void* x, void* y, voi
             if (e != hipSuccess) return hip_fail(e, "rank-r projection (K split sum)");
         }
     }
+    if (T <= kSkinnyT && K <= kLut8MaxK && r % 8 == 0) {
+        // decode-size T: the code-stream kernel (rank-r term in its epilogue, in FP32)
+        Lut8Args q;
+        memset(&q, 0, sizeof q);
+        q.codes = reinterpret_cast<const uint32_t*>(base + L.codes_off);
+        q.lut = reinterpret_cast<const uint16_t*>(base + L.cb_off);
+        q.sc = reinterpret_cast<const uint16_t*>(base + L.sc_off);
+        q.x = xt;
+        q.y = static_cast<uint16_t*>(y);
+        q.U = U;
+        q.z = z;
+        q.bits = bits;
+        q.N = N;
+        q.K = K;
+        q.T = T;
+        q.r = r;
+        e = launch_lut8(q, hs);
+        if (e != hipSuccess) return hip_fail(e, "scalar-LUT projection (T <= 8)");
+        return ok();
+    }
     GemmArgs g;
     memset(&g, 0, sizeof g);
     g.kind = bits == 2 ? kGemmLUT2 : kGemmLUT4;

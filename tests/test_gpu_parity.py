@@ -295,6 +295,31 @@ LUT_CASES = [  # N, K, T, rank, Hadamard block (0 = none)
 ]
 
 
+LUT8_CASES = [  # decode-size T: the code-stream kernel (K <= 5120), and K past it (tiled)
+    (5120, 5120, 8, 64, 1024),  # the token-mixer shape at T = 8
+    (192, 320, 5, 0, 64),       # fewer 64-column units than K slices
+    (256, 2048, 2, 128, 512),
+    (64, 5184, 8, 64, 64),      # K > 5120: tiled kernels
+    (128, 1024, 4, 20, 1024),   # rank not a multiple of 8: tiled kernels
+    (64, 1024, 7, 256, 256),    # largest rank
+]
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("N,K,T,rank,hb", LUT8_CASES)
+def test_lut_decode_shapes(vq, oracle_mod, torch_dev, bits, N, K, T, rank, hb):
+    """Scalar-LUT projections at T <= 8 against the oracle, every output."""
+    rng = np.random.default_rng(N + 5 * K + 11 * T + bits)
+    p = synth.lut_projection(rng, bits, N, K, rank, hb)
+    x = synth.activations(rng, T, K, outliers=True)
+    _say("LUT T<=8 bits=%d N=%d K=%d T=%d r=%d hb=%d" % (bits, N, K, T, rank, hb))
+    proj = vq.LUTProjection.from_proj(p)
+    y = _f64(proj.forward(vq.to_device(x)))
+    torch_dev.cuda.synchronize()
+    ref = oracle_mod.lut_forward(p, x)
+    assert _report("LUT T<=8 %d-bit %dx%d T=%d" % (bits, N, K, T), y, ref) <= MLP_TOL
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 @pytest.mark.parametrize("N,K,T,rank,hb", LUT_CASES)
 def test_lut_small_shapes(vq, oracle_mod, torch_dev, bits, N, K, T, rank, hb):
