@@ -82,10 +82,17 @@ struct Lut8Args {
     const uint16_t* x;      // x~ [T][K] binary16
     uint16_t* y;            // [T][N] binary16
     const uint16_t* U;      // [N][r] binary16 (r > 0)
-    const float* z;         // [T][r] fp32 (r > 0)
-    int bits, N, K, T, r;
+    const float* zp;        // [nch][8][r] fp32 partial sums of z = V x~ (r > 0), summed in order
+    int bits, N, K, T, r, nch;
 };
 hipError_t launch_lut8(const Lut8Args& a, hipStream_t st);
+// Pre-pass of the T <= 8 projection: x~ = R_K(x . s . sign) ([T][K] binary16, Hadamard block hb,
+// 1 = none) and, for r > 0, the partial sums zp[c][t][j] = sum over chunk c of V[j][k] x~[t][k]
+// (chunks of lut8_chunk(K, hb) columns; x~ rounded to binary16 first).
+int lut8_chunk(int K, int hb);
+hipError_t launch_lut8_pre(int T, int K, int hb, const uint16_t* x, const uint16_t* s,
+                           const int8_t* sign, const uint16_t* V, int r, uint16_t* xt, float* zp,
+                           hipStream_t st);
 
 // ---- stream-K skinny path (T <= 8): the weight stream cut into equal contiguous ranges
 constexpr int kStreamKMaxQ = 4;  // row-tile pairs one workgroup range may touch

@@ -94,7 +94,10 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
 #pragma unroll
     for (int k = 0; k < kZPer; ++k) {
         const int q = tid + k * kW * 64;
-        zv[k] = q < kSkinnyT * a.r && q / a.r < T ? a.z[q] : 0.f;
+        float zsum = 0.f;
+        if (q < kSkinnyT * a.r && q / a.r < T)
+            for (int c = 0; c < a.nch; ++c) zsum += a.zp[size_t(c) * kSkinnyT * a.r + q];
+        zv[k] = zsum;
     }
     constexpr int kXPer = kSkinnyT * kMaxK / 8 / (kW * 64);  // 16-byte chunks per thread at most
     const int c8n = K / 8;
@@ -182,10 +185,157 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
     }
 }
 
+// ---- pre-pass: workgroup (chunk c of C = 64 V columns, group of 16 rows of V); wave t < 8 holds
+// token row t of the chunk, V consecutive columns per lane (16-byte loads of x, s, sign).  The
+// Walsh-Hadamard butterflies (blocks of hb, distances 1 .. hb/2 in that order, each pair (lo, hi)
+// -> (lo + hi, lo - hi)) run in registers below V and across lanes above, as the rotation
+// kernels do; x~ = . / sqrt(hb) is rounded to binary16, written out by group 0 and kept in LDS,
+// where the group's 16 rows of V (loaded up front) meet it on the matrix cores: wave w takes the
+// 32-column steps w, w + 8, ... (A = 16 rows of V, B = x~, column n = token n, zero for n >= 8).
+template <int V>
+__global__ void __launch_bounds__(512) k_lut8_pre(int T, int K, int hb, const uint16_t* x,
+                                                  const uint16_t* s, const int8_t* sign,
+                                                  const uint16_t* Vm, int r, uint16_t* xt,
+                                                  float* zp, float norm) {
+    constexpr int C = 64 * V, XR = C + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t vs[16 * C];
+    __shared__ __attribute__((aligned(16))) uint16_t xh[kSkinnyT * XR];
+    __shared__ f32x4 zred[8][64];
+    const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, c = blockIdx.x, rg = blockIdx.y;
+    const int c0 = c * C, col = c0 + V * l;
+    // the group's V rows: 16 x C in 16-byte chunks, issued first
+    constexpr int kVPer = (16 * C / 8 + 511) / 512;
+    u32x4 vv[kVPer];
+#pragma unroll
+    for (int k = 0; k < kVPer; ++k) {
+        const int q = tid + 512 * k, jr = q / (C / 8), cc = (q % (C / 8)) * 8;
+        vv[k] = r > 0 && q < 16 * C / 8 ? *reinterpret_cast<const u32x4*>(Vm + size_t(rg * 16 + jr) * K + c0 + cc)
+                                        : u32x4{0u, 0u, 0u, 0u};
+    }
+    // row w of x . s . sign
+    float v[V];
+    {
+        const int t = w;
+#pragma unroll
+        for (int q = 0; q < (V + 7) / 8; ++q) {
+            constexpr int kE = V < 8 ? V : 8;
+            uint32_t xw[4] = {0u, 0u, 0u, 0u}, sw[4] = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+            uint64_t gw = 0;
+            if (t < T) {
+                if constexpr (kE == 8) {
+                    const u32x4 a4 = *reinterpret_cast<const u32x4*>(x + size_t(t) * K + col + 8 * q);
+                    for (int e = 0; e < 4; ++e) xw[e] = a4[e];
+                    if (s) {
+                        const u32x4 s4 = *reinterpret_cast<const u32x4*>(s + col + 8 * q);
+                        for (int e = 0; e < 4; ++e) sw[e] = s4[e];
+                    }
+                    if (sign) gw = *reinterpret_cast<const uint64_t*>(sign + col + 8 * q);
+                } else {
+                    for (int e = 0; e < kE; ++e) {
+                        xw[e / 2] |= uint32_t(x[size_t(t) * K + col + e]) << (16 * (e & 1));
+                        if (s) sw[e / 2] = (sw[e / 2] & ~(0xFFFFu << (16 * (e & 1)))) |
+                                           (uint32_t(s[col + e]) << (16 * (e & 1)));
+                        if (sign) gw |= uint64_t(uint8_t(sign[col + e])) << (8 * e);
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < kE; ++e) {
+                float u = h2f(uint16_t(xw[e / 2] >> (16 * (e & 1)))) * h2f(uint16_t(sw[e / 2] >> (16 * (e & 1))));
+                if (int8_t(gw >> (8 * e)) < 0) u = -u;
+                v[8 * q + e] = t < T ? u : 0.f;
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 1; h < V; h <<= 1)
+        if (h < hb) {
+#pragma unroll
+            for (int e = 0; e < V; ++e)
+                if (!(e & h)) {
+                    const float x0 = v[e], x1 = v[e | h];
+                    v[e] = x0 + x1;
+                    v[e | h] = x0 - x1;
+                }
+        }
+    for (int h = V; h < hb; h <<= 1) {
+        const int d = h / V;
+        const bool upper = (l & d) != 0;
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+            const float p = __shfl_xor(v[e], d);
+            v[e] = upper ? p - v[e] : v[e] + p;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+        const uint16_t hv = uint16_t(f2h(v[e] * norm));
+        if (rg == 0 && w < T) xt[size_t(w) * K + col + e] = hv;
+        xh[w * XR + V * l + e] = hv;  // z is formed from the rounded x~, as the product reads it
+    }
+#pragma unroll
+    for (int k = 0; k < kVPer; ++k) {
+        const int q = tid + 512 * k;
+        if (q < 16 * C / 8) *reinterpret_cast<u32x4*>(&vs[(q / (C / 8)) * C + (q % (C / 8)) * 8]) = vv[k];
+    }
+    if (r == 0) return;
+    __syncthreads();
+    const int i = l & 15, g = l >> 4;
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kk = 32 * w; kk < C; kk += 256) {
+        const u32x4 A = *reinterpret_cast<const u32x4*>(&vs[i * C + kk + 8 * g]);
+        const u32x4 B = i < kSkinnyT ? *reinterpret_cast<const u32x4*>(&xh[(i < kSkinnyT ? i : 0) * XR + kk + 8 * g])
+                                     : u32x4{0u, 0u, 0u, 0u};
+        acc = mfma16x16x32(A, B, acc);
+    }
+    zred[w][l] = acc;
+    __syncthreads();
+    if (tid < 256) {
+        // lane ll holds rows 4 (ll / 16) + q of the block, token ll % 16
+        const int ll = tid >> 2, q = tid & 3, t = ll & 15, jl = 4 * (ll >> 4) + q;
+        if (t < kSkinnyT) {
+            float sum = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < 8; ++ww) sum += zred[ww][ll][q];
+            zp[(size_t(c) * kSkinnyT + t) * r + rg * 16 + jl] = sum;
+        }
+    }
+}
+
+int lut8_chunk(int K, int hb) {
+    // the widest power-of-two chunk of 64 .. 1024 columns that is a whole number of Hadamard
+    // blocks and divides K (0: none)
+    const int b = hb > 1 ? hb : 1;
+    int best = 0;
+    for (int c = 64; c <= 1024; c *= 2)
+        if (K % c == 0 && c % b == 0) best = c;
+    return best;
+}
+
+hipError_t launch_lut8_pre(int T, int K, int hb, const uint16_t* x, const uint16_t* s,
+                           const int8_t* sign, const uint16_t* V, int r, uint16_t* xt, float* zp,
+                           hipStream_t st) {
+    const int C = lut8_chunk(K, hb);
+    if (!x || !xt || C < 64 || T < 1 || T > kSkinnyT || r < 0 || r % 16 || (r > 0 && (!V || !zp)) ||
+        hb < 1 || hb > 1024 || (hb & (hb - 1)))
+        return hipErrorInvalidValue;
+    const float norm = float(1.0 / __builtin_sqrt(double(hb)));
+    const dim3 grid(K / C, r > 0 ? r / 16 : 1);
+#define VQ_PRE(VV)                                                                                \
+    if (C == 64 * VV) {                                                                           \
+        hipLaunchKernelGGL(k_lut8_pre<VV>, grid, dim3(512), 0, st, T, K, hb, x, s, sign, V, r, xt, \
+                           zp, norm);                                                             \
+        return hipGetLastError();                                                                 \
+    }
+    VQ_PRE(1) VQ_PRE(2) VQ_PRE(4) VQ_PRE(8) VQ_PRE(16)
+#undef VQ_PRE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_lut8(const Lut8Args& a, hipStream_t st) {
     if (!a.codes || !a.lut || !a.sc || !a.x || !a.y || (a.bits != 2 && a.bits != 4) || a.N < 32 ||
         a.N % 32 || a.K < 64 || a.K % 64 || a.K > kMaxK || a.T < 1 || a.T > kSkinnyT || a.r < 0 ||
-        a.r > kMaxR || a.r % 8 || (a.r > 0 && (!a.U || !a.z)))
+        a.r > kMaxR || a.r % 8 || (a.r > 0 && (!a.U || !a.zp || a.nch < 1)))
         return hipErrorInvalidValue;
     if (a.bits == 2)
         hipLaunchKernelGGL(k_lut8<2>, dim3(a.N / 32), dim3(kW * 64), 0, st, a);

@@ -300,10 +300,12 @@ __global__ void __launch_bounds__(1024) k_streamk_gu_fin(StreamKArgs a, int G) {
         buf[t * R + row - r0] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, act) ^ sbit);
     }
     __syncthreads();
-    for (int h = 1; h < a.bi; h <<= 1) {
+    // (R and h are powers of two: shifts, no integer division)
+    const int lr = 31 - __builtin_clz(R);
+    for (int h = 1, lh = 0; h < a.bi; h <<= 1, ++lh) {
         for (int p = tid; p < kSkinnyT * R / 2; p += 1024) {
-            const int t = p / (R / 2), k = p % (R / 2);
-            const int i0 = t * R + (k / h) * 2 * h + k % h, i1 = i0 + h;
+            const int t = p >> (lr - 1), k = p & (R / 2 - 1);
+            const int i0 = (t << lr) + (((k >> lh) << (lh + 1)) | (k & (h - 1))), i1 = i0 + h;
             const float x0 = buf[i0], x1 = buf[i1];
             buf[i0] = x0 + x1;
             buf[i1] = x0 - x1;
@@ -311,7 +313,7 @@ __global__ void __launch_bounds__(1024) k_streamk_gu_fin(StreamKArgs a, int G) {
         __syncthreads();
     }
     for (int i = tid; i < kSkinnyT * R; i += 1024)
-        a.ab_out[unit_major_index(i / R, r0 + i % R)] = uint16_t(f2h(buf[i] * a.norm_i));
+        a.ab_out[unit_major_index(i >> lr, r0 + (i & (R - 1)))] = uint16_t(f2h(buf[i] * a.norm_i));
 }
 
 // down: thread (q, tile m, lane, reg) sums the slots of q and scales into y

@@ -945,6 +945,10 @@ vqmlp_status vqmlp_lut_workspace_bytes(int N, int K, int T, int r, size_t* bytes
     *bytes = align256(Tt * K * 2) + align256(Tt * (r ? r : 1) * 4) +
              (zs > 1 ? align256(size_t(zs) * Tt * (r ? r : 1) * 4) : 0) +
              (ls > 1 ? align256(size_t(ls) * Tt * N * 4) : 0) + 256;
+    // T <= 8: x~ and the per-chunk partial sums of z (at most K / 64 chunks of 8 rows)
+    if (T <= kSkinnyT)
+        *bytes = std::max(*bytes, align256(Tt * K * 2) +
+                                      align256(size_t(K / 64 + 1) * kSkinnyT * (r ? r : 1) * 4) + 256);
     return ok();
 }
 
@@ -1022,8 +1026,36 @@ vqmlp_status lut_run(const vqmlp_lut_plan& p, int T, const void* x, void* y, voi
     const uint8_t* base = p.base;
     const uint16_t *U = p.U, *V = p.V;
     const int bits = p.bits;
+    const int hb = p.had_block ? p.had_block : 1;
+    if (T <= kSkinnyT && K <= kLut8MaxK && r % 16 == 0 && lut8_chunk(K, hb) >= 64 &&
+        aligned(p.s, 16) && aligned(p.sign, 8)) {  // (the pre-pass reads s and sign in vectors)
+        // decode-size T: one pre-pass (rotation and per-chunk partial sums of z), then the
+        // code-stream kernel (its epilogue adds U z in FP32)
+        float* zp = reinterpret_cast<float*>(wb + align256(size_t(T) * K * 2));
+        hipError_t e = launch_lut8_pre(T, K, hb, static_cast<const uint16_t*>(x), p.s, p.sign, V, r,
+                                       xt, zp, hs);
+        if (e != hipSuccess) return hip_fail(e, "scalar-LUT pre-pass (T <= 8)");
+        Lut8Args q;
+        memset(&q, 0, sizeof q);
+        q.codes = reinterpret_cast<const uint32_t*>(base + L.codes_off);
+        q.lut = reinterpret_cast<const uint16_t*>(base + L.cb_off);
+        q.sc = reinterpret_cast<const uint16_t*>(base + L.sc_off);
+        q.x = xt;
+        q.y = static_cast<uint16_t*>(y);
+        q.U = U;
+        q.zp = zp;
+        q.nch = K / lut8_chunk(K, hb);
+        q.bits = bits;
+        q.N = N;
+        q.K = K;
+        q.T = T;
+        q.r = r;
+        e = launch_lut8(q, hs);
+        if (e != hipSuccess) return hip_fail(e, "scalar-LUT projection (T <= 8)");
+        return ok();
+    }
     // x~ = R(x . s): the rotation kernel with a 1-wide block is the plain scale and sign
-    hipError_t e = launch_rotate(T, K, p.had_block ? p.had_block : 1, x, 0, p.s, p.sign, xt, 1, hs);
+    hipError_t e = launch_rotate(T, K, hb, x, 0, p.s, p.sign, xt, 1, hs);
     if (e != hipSuccess) return hip_fail(e, "rotate (mixer input)");
     if (r > 0) {
         // z = x~ V^T has few outputs: split K over the CUs, then sum the planes
@@ -1045,26 +1077,6 @@ vqmlp_status lut_run(const vqmlp_lut_plan& p, int T, const void* x, void* y, voi
             e = launch_split_sum(T * r, g.ksplit, zp, z, hs);
             if (e != hipSuccess) return hip_fail(e, "rank-r projection (K split sum)");
         }
-    }
-    if (T <= kSkinnyT && K <= kLut8MaxK && r % 8 == 0) {
-        // decode-size T: the code-stream kernel (rank-r term in its epilogue, in FP32)
-        Lut8Args q;
-        memset(&q, 0, sizeof q);
-        q.codes = reinterpret_cast<const uint32_t*>(base + L.codes_off);
-        q.lut = reinterpret_cast<const uint16_t*>(base + L.cb_off);
-        q.sc = reinterpret_cast<const uint16_t*>(base + L.sc_off);
-        q.x = xt;
-        q.y = static_cast<uint16_t*>(y);
-        q.U = U;
-        q.z = z;
-        q.bits = bits;
-        q.N = N;
-        q.K = K;
-        q.T = T;
-        q.r = r;
-        e = launch_lut8(q, hs);
-        if (e != hipSuccess) return hip_fail(e, "scalar-LUT projection (T <= 8)");
-        return ok();
     }
     GemmArgs g;
     memset(&g, 0, sizeof g);

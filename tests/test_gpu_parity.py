@@ -302,6 +302,7 @@ LUT8_CASES = [  # decode-size T: the code-stream kernel (K <= 5120), and K past 
     (64, 5184, 8, 64, 64),      # K > 5120: tiled kernels
     (128, 1024, 4, 20, 1024),   # rank not a multiple of 8: tiled kernels
     (64, 1024, 7, 256, 256),    # largest rank
+    (128, 512, 6, 32, 0),       # no rotation
 ]
 
 
