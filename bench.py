@@ -119,6 +119,57 @@ def build_stream(n_layers, device):
     return layers
 
 
+def lut_weight_bytes(bits, N, K, r):
+    """Bytes one scalar-LUT projection reads from its weights: codes, tables, scales, U and V."""
+    return N * K * bits // 8 + (N // 8) * (1 << bits) * 2 + N * 2 + 2 * r * (N + K) * 2
+
+
+def t8_mixers(device, stream, n_proj=16):
+    """The token-mixer projections at T = 8 (5120 x 5120, rank 64, 1024-wide rotation): one HIP
+    graph of n_proj distinct seeded projections per code width (more bytes than the on-die cache
+    holds), timed over replays; effective weight GB/s against the HBM peak."""
+    import numpy as np
+    import torch
+
+    from bit_vector_lut_amd import synth, vqmlp
+
+    out = []
+    for bits in (2, 4):
+        projs = [vqmlp.LUTProjection.from_proj(
+            synth.lut_projection(np.random.default_rng(9000 + 100 * bits + i), bits, 5120, 5120, 64, 1024),
+            device) for i in range(n_proj)]
+        x = vqmlp.to_device(synth.activations(np.random.default_rng(bits), 8, 5120, True), device)
+        ys = [torch.empty((8, 5120), dtype=x.dtype, device=device) for _ in projs]
+        ws = projs[0].workspace(8)
+        with torch.cuda.stream(stream):
+            for m, y in zip(projs, ys):
+                m.forward(x, y, ws, stream=stream)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for m, y in zip(projs, ys):
+                m.forward(x, y, ws, stream=stream)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            with torch.cuda.stream(stream):
+                g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * n_proj)
+        wb = lut_weight_bytes(bits, 5120, 5120, 64)
+        gbs = wb / (us * 1e-6) / 1e9
+        log("T=8 %d-bit mixer 5120x5120 r=64: %.2f us per forward, %.1f GB/s of weights" % (bits, us, gbs))
+        out.append({"bits": bits, "N": 5120, "K": 5120, "rank": 64, "T": 8, "us": round(us, 2),
+                    "weight_bytes": wb, "gbps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+        del g, projs, ys
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +178,7 @@ def main():
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-t512", action="store_true")
+    ap.add_argument("--no-mixers8", action="store_true")
     ap.add_argument("--probe", action="store_true",
                     help="counter run only: a known-size copy and 4 forwards, no timing")
     args = ap.parse_args()
@@ -224,6 +276,10 @@ def main():
     }
     del graph
     layers_keep = layers  # noqa: F841
+
+    # ---------------------------------------------------------------- T = 8 token mixers
+    if not args.no_mixers8:
+        result["t8_token_mixers"] = t8_mixers(device, stream)
 
     # ---------------------------------------------------------------- T = 512 prefill MLP
     if not args.no_t512:
