@@ -191,6 +191,17 @@ def lut_forward(proj, x, tokens=None, with_xt: bool = False):
     return (y, xt) if with_xt else y
 
 
+def lut_argmax(proj, x, tokens=None):
+    """Greedy next token of a scalar-LUT output head: per row of x, the index of the largest FP64
+    logit of ``lut_forward`` (the lowest index among equal logits) and that logit.  In-model argmax
+    ("ANEMLL ANE LLM conversion pipeline", section "Facts", in-model argmax item: the head returns
+    an index and its value instead of the vocabulary's logits; the four-bit LUT head of the model
+    card's format table)."""
+    y = lut_forward(proj, x, tokens)
+    idx = np.argmax(y, axis=1)  # first occurrence of the maximum
+    return idx.astype(np.int64), y[np.arange(y.shape[0]), idx]
+
+
 def num_threads() -> int:
     return lib().orc_num_threads()
 

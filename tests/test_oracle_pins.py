@@ -363,3 +363,38 @@ def test_lut_low_rank_only(oracle_mod):
     y = oracle_mod.lut_forward(p, x)
     ref = (x.astype(np.float64) @ p.V.astype(np.float64).T) @ p.U.astype(np.float64).T
     assert np.allclose(y, ref, rtol=1e-13, atol=1e-16)
+
+
+# ------------------------------------------------------------------------------ output head argmax
+
+
+def _head(N, K, seed):
+    """A 4-bit LUT output head with no rotation or factors (the head's own form)."""
+    return synth.lut_projection(np.random.default_rng(seed), 4, N, K, 0, 0)
+
+
+def test_lut_argmax_planted_maximum_and_ties(oracle_mod):
+    p = _head(256, 64, 3)
+    p.lut = np.zeros_like(p.lut)
+    p.codes = np.zeros_like(p.codes)
+    p.s, p.sign = None, None
+    p.sc = np.ones_like(p.sc)
+    # rows 77 and 140 share the largest logit (their tables' entry 15 = 1, all codes 15); row 13 is
+    # half as large; every other logit is 0
+    for j, v in ((77, 1.0), (140, 1.0), (13, 0.5)):
+        p.lut[j // 8, 15] = v
+        p.codes[j, :] = 15
+    x = np.ones((3, 64), np.float16)
+    x[2] = -1  # all planted logits negative: the largest is 0, first at row 0
+    idx, val = oracle_mod.lut_argmax(p, x)
+    assert list(idx) == [77, 77, 0]
+    assert val[0] == 64.0 and val[2] == 0.0
+
+
+def test_lut_argmax_equals_brute_force(oracle_mod):
+    p = _head(512, 128, 4)
+    x = np.random.default_rng(5).standard_normal((8, 128)).astype(np.float16)
+    idx, val = oracle_mod.lut_argmax(p, x)
+    ref = _lut_library(p, x)
+    assert np.array_equal(idx, np.argmax(ref, axis=1))
+    assert np.allclose(val, ref.max(axis=1), rtol=1e-12)
