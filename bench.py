@@ -170,6 +170,45 @@ def t8_mixers(device, stream, n_proj=16):
     return out
 
 
+def t8_lm_head(device, stream):
+    """The four-bit LUT output head (248,320 x 5120) with in-model argmax at T = 8: one seeded
+    head (636 MB of codes, more than the on-die cache), timed over back-to-back calls with
+    events on the stream they run on; effective weight GB/s against the HBM peak."""
+    import numpy as np
+    import torch
+
+    from bit_vector_lut_amd import synth, vqmlp
+
+    N, K, T = 248320, 5120, 8
+    rng = np.random.default_rng(11)
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    lut = (rng.standard_normal((N // 8, 16)) * 0.02).astype(np.float16)
+    sc = rng.uniform(0.5, 1.5, N).astype(np.float16)
+    packed = vqmlp.to_device(vqmlp.lut_pack(4, codes, lut, sc), device)
+    del codes
+    head = vqmlp.LUTProjection(4, N, K, packed, None, None, None, None, 0)
+    x = vqmlp.to_device(synth.activations(rng, T, K, True), device)
+    ws = head.workspace(T)
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            head.argmax(x, ws, stream=stream)
+    stream.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            head.argmax(x, ws, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    wb = lut_weight_bytes(4, N, K, 0)
+    gbs = wb / (us * 1e-6) / 1e9
+    log("T=8 LM head 4-bit %dx%d + argmax: %.1f us, %.1f GB/s of weights" % (N, K, us, gbs))
+    return {"bits": 4, "N": N, "K": K, "T": T, "us": round(us, 1), "weight_bytes": wb,
+            "gbps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +319,7 @@ def main():
     # ---------------------------------------------------------------- T = 8 token mixers
     if not args.no_mixers8:
         result["t8_token_mixers"] = t8_mixers(device, stream)
+        result["t8_lm_head_argmax"] = t8_lm_head(device, stream)
 
     # ---------------------------------------------------------------- T = 512 prefill MLP
     if not args.no_t512:

@@ -185,6 +185,200 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
     }
 }
 
+// ---- greedy argmax of a scalar-LUT output head (no rotation, no factors): y = sc . (W_lut x~)
+// is never written; the largest logit of each token and its row are.  Persistent workgroups of
+// the same shape as k_lut8 stage x~ once and walk the 32-row blocks b, b + G, ...; a block's code
+// runs and table words are requested one block ahead (tables double-buffered in LDS).  The
+// epilogue keeps, per output thread, the best (value, row) seen (rows only grow, so a strictly
+// larger value is needed to replace: the lowest row wins ties); at the end the workgroup's
+// threads of a token are merged into part[b][t], and k_argmax_merge merges the workgroups.
+template <int BITS>
+__global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* pval, int* pidx) {
+    constexpr int CW = BITS == 2 ? 1 : 2;
+    constexpr int kOffX = 2 * 2 * kTabDw * 4, kOffRed = kOffX + kSkinnyT * kXRow * 2;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kOffRed + kW * 64 * 16];
+    auto& tab = *reinterpret_cast<uint32_t (*)[2][2][kTabDw]>(lds);  // [buffer][row tile][.]
+    auto& xs = *reinterpret_cast<uint16_t (*)[kSkinnyT][kXRow]>(lds + kOffX);
+    auto& red = *reinterpret_cast<f32x4 (*)[kW][64]>(lds + kOffRed);
+    float* mval = reinterpret_cast<float*>(lds + kOffRed);       // final merge (reuses red)
+    int* midx = reinterpret_cast<int*>(lds + kOffRed + 256 * 4);
+
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int K = a.K, T = a.T, nb = a.N / 32, G = gridDim.x;
+    const int rt = w / kKS, ks = w % kKS;
+    const int nu = K / 64, u0 = ks * nu / kKS, nus = (ks + 1) * nu / kKS - u0;
+    const int i = l & 15, g = l >> 4;
+    constexpr int kRunW = kMaxU * CW, kRunV = (kRunW + 3) / 4;
+    auto load_codes = [&](int blk, uint32_t (&cw)[kRunV * 4]) {
+        const uint32_t* crun = a.codes + size_t(blk * 32 + rt * 16 + i) * (K * BITS / 32) +
+                               u0 * (64 * BITS / 32) + g * nus * (16 * BITS / 32);
+#pragma unroll
+        for (int v = 0; v < kRunV; ++v) {
+            const u32x4a q = *reinterpret_cast<const u32x4a*>(crun + 4 * v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) cw[4 * v + e] = q[e];
+        }
+    };
+    const int trt = tid >> 9, te = (tid >> 5) & 15, tc = tid & 31;
+    auto load_tab = [&](int blk) -> uint32_t {
+        const int grp = (blk * 32 + trt * 16) / 8 + ((tc & 15) >> 3);
+        if constexpr (BITS == 2)
+            return uint32_t(a.lut[grp * 4 + (te & 3)]) | (uint32_t(a.lut[grp * 4 + (te >> 2)]) << 16);
+        else
+            return a.lut[grp * 16 + te];
+    };
+    // epilogue thread: row tile, lane holding a token < 8, reg
+    const int ert = tid >> 7, ej = tid & 127, ell = ej >> 2, eq = ej & 3;
+    const int el = (ell >> 3) * 16 + (ell & 7), et = el & 15;
+    const int erl = ert * 16 + 4 * (el >> 4) + eq;  // row within the block
+
+    int blk = blockIdx.x;
+    uint32_t cw[kRunV * 4];
+    load_codes(blk, cw);
+    uint32_t tv = load_tab(blk);
+    float esc = tid < 256 ? h2f(a.sc[blk * 32 + erl]) : 0.f;
+    // x~ (rows past T zero), all loads before the stores
+    constexpr int kXPer = kSkinnyT * kMaxK / 8 / (kW * 64);
+    const int c8n = K / 8;
+    {
+        u32x4 xv[kXPer];
+#pragma unroll
+        for (int k = 0; k < kXPer; ++k) {
+            const int q = tid + k * kW * 64, t = q / c8n, c8 = (q % c8n) * 8;
+            xv[k] = q < kSkinnyT * c8n && t < T ? *reinterpret_cast<const u32x4*>(a.x + size_t(t) * K + c8)
+                                               : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int k = 0; k < kXPer; ++k) {
+            const int q = tid + k * kW * 64, t = q / c8n, c8 = (q % c8n) * 8;
+            if (q < kSkinnyT * c8n) *reinterpret_cast<u32x4*>(&xs[t][c8]) = xv[k];
+        }
+    }
+    const char* tb0 = reinterpret_cast<const char*>(&tab[0][0][0]);
+    const int n = l & 15;
+    float best = -__builtin_inff();
+    int bidx = 0x7fffffff;
+    for (int it = 0; blk < nb; ++it, blk += G) {
+        const int par = it & 1;
+        tab[par][trt][te * 32 + tc] = tv;
+        // the next block's words, requested now (the last block repeats itself)
+        const int nxt = blk + G < nb ? blk + G : blk;
+        uint32_t cn[kRunV * 4];
+        load_codes(nxt, cn);
+        const uint32_t tvn = load_tab(nxt);
+        const float escn = tid < 256 ? h2f(a.sc[nxt * 32 + erl]) : 0.f;
+        __syncthreads();  // tables of this block written; red of the last block consumed
+        const uint32_t lb = (uint32_t(l & 31) << 2) | uint32_t(((par * 2 + rt) * kTabDw) * 4);
+        auto look = [&](uint32_t e) -> uint32_t {
+            return *reinterpret_cast<const uint32_t*>(tb0 + ((e << 7) + lb));
+        };
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < kMaxU; ++u) {
+            if (u < nus) {  // uniform
+                const int kb = u0 * 64 + 16 * (g * nus + u);
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    u32x4 A;
+                    if constexpr (BITS == 2) {
+                        const uint32_t d = cw[u] >> (16 * s);
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) A[p] = look((d >> (4 * p)) & 15u);
+                    } else {
+                        const uint32_t d = cw[2 * u + s];
+#pragma unroll
+                        for (int p = 0; p < 4; ++p)
+                            A[p] = (look((d >> (8 * p)) & 15u) & 0xFFFFu) | (look((d >> (8 * p + 4)) & 15u) << 16);
+                    }
+                    const u32x4 B = n < kSkinnyT ? *reinterpret_cast<const u32x4*>(&xs[n < kSkinnyT ? n : 0][kb + 8 * s])
+                                                 : u32x4{0u, 0u, 0u, 0u};
+                    acc = mfma16x16x32(A, B, acc);
+                }
+            }
+        }
+        red[w][l] = acc;
+        __syncthreads();
+        if (tid < 256) {
+            float v = 0.f;
+#pragma unroll
+            for (int s = 0; s < kKS; ++s) v += red[ert * kKS + s][el][eq];
+            v *= esc;
+            if (v > best) {
+                best = v;
+                bidx = blk * 32 + erl;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kRunV * 4; ++k) cw[k] = cn[k];
+        tv = tvn;
+        esc = escn;
+    }
+    // merge the 32 threads of each token (2 row tiles x 4 lane groups x 4 regs): larger value,
+    // then lower row
+    __syncthreads();
+    if (tid < 256) {
+        mval[tid] = best;
+        midx[tid] = bidx;
+    }
+    __syncthreads();
+    if (tid < kSkinnyT) {
+        float bv = -__builtin_inff();
+        int bi = 0x7fffffff;
+        for (int q = 0; q < 256; ++q) {
+            const int qj = q & 127, qll = qj >> 2, qel = (qll >> 3) * 16 + (qll & 7);
+            if ((qel & 15) != tid) continue;
+            const float v = mval[q];
+            const int ix = midx[q];
+            if (v > bv || (v == bv && ix < bi)) {
+                bv = v;
+                bi = ix;
+            }
+        }
+        pval[blockIdx.x * kSkinnyT + tid] = bv;
+        pidx[blockIdx.x * kSkinnyT + tid] = bi;
+    }
+}
+
+// merge of the workgroups' bests: token t (thread t < T) scans them in order
+__global__ void __launch_bounds__(64) k_argmax_merge(int G, int T, const float* pval, const int* pidx,
+                                                     int* out_idx, float* out_val) {
+    const int t = threadIdx.x;
+    if (t >= T) return;
+    float bv = -__builtin_inff();
+    int bi = 0x7fffffff;
+    for (int b = 0; b < G; ++b) {
+        const float v = pval[b * kSkinnyT + t];
+        const int ix = pidx[b * kSkinnyT + t];
+        if (v > bv || (v == bv && ix < bi)) {
+            bv = v;
+            bi = ix;
+        }
+    }
+    out_idx[t] = bi;
+    if (out_val) out_val[t] = bv;
+}
+
+int lut8_argmax_grid(int N, int cus) {
+    const int nb = N / 32;
+    return nb < cus ? nb : cus;
+}
+
+hipError_t launch_lut8_argmax(const Lut8Args& a, int cus, float* pval, int* pidx, int* out_idx,
+                              float* out_val, hipStream_t st) {
+    if (!a.codes || !a.lut || !a.sc || !a.x || !pval || !pidx || !out_idx ||
+        (a.bits != 2 && a.bits != 4) || a.N < 32 || a.N % 32 || a.K < 64 || a.K % 64 ||
+        a.K > kMaxK || a.T < 1 || a.T > kSkinnyT || a.r != 0 || cus < 1)
+        return hipErrorInvalidValue;
+    const int G = lut8_argmax_grid(a.N, cus);
+    if (a.bits == 2)
+        hipLaunchKernelGGL(k_lut8_argmax<2>, dim3(G), dim3(kW * 64), 0, st, a, pval, pidx);
+    else
+        hipLaunchKernelGGL(k_lut8_argmax<4>, dim3(G), dim3(kW * 64), 0, st, a, pval, pidx);
+    hipLaunchKernelGGL(k_argmax_merge, dim3(1), dim3(64), 0, st, G, a.T, pval, pidx, out_idx, out_val);
+    return hipGetLastError();
+}
+
 // ---- pre-pass: workgroup (chunk c of C = 64 V columns, group of 16 rows of V); wave t < 8 holds
 // token row t of the chunk, V consecutive columns per lane (16-byte loads of x, s, sign).  The
 // Walsh-Hadamard butterflies (blocks of hb, distances 1 .. hb/2 in that order, each pair (lo, hi)

@@ -945,10 +945,13 @@ vqmlp_status vqmlp_lut_workspace_bytes(int N, int K, int T, int r, size_t* bytes
     *bytes = align256(Tt * K * 2) + align256(Tt * (r ? r : 1) * 4) +
              (zs > 1 ? align256(size_t(zs) * Tt * (r ? r : 1) * 4) : 0) +
              (ls > 1 ? align256(size_t(ls) * Tt * N * 4) : 0) + 256;
-    // T <= 8: x~ and the per-chunk partial sums of z (at most K / 64 chunks of 8 rows)
+    // T <= 8: x~ and the per-chunk partial sums of z (at most K / 64 chunks of 8 rows), or the
+    // argmax head's per-workgroup bests
     if (T <= kSkinnyT)
         *bytes = std::max(*bytes, align256(Tt * K * 2) +
-                                      align256(size_t(K / 64 + 1) * kSkinnyT * (r ? r : 1) * 4) + 256);
+                                      std::max(align256(size_t(K / 64 + 1) * kSkinnyT * (r ? r : 1) * 4),
+                                               align256(size_t(kArgmaxMaxGroups) * kSkinnyT * 8)) +
+                                      256);
     return ok();
 }
 
@@ -957,6 +960,7 @@ vqmlp_status vqmlp_lut_workspace_bytes(int N, int K, int T, int r, size_t* bytes
 // A validated scalar-LUT projection: everything a forward needs but its rows.
 struct vqmlp_lut_plan {
     int bits, N, K, r, had_block;
+    int cus;  // compute units of the device at creation (workgroups of the argmax head)
     const uint8_t* base;
     Layout L;
     const uint16_t *U, *V, *s;
@@ -1139,6 +1143,14 @@ vqmlp_status vqmlp_lut_create(int bits, int N, int K, const void* packed, const 
     vqmlp_lut_plan tmp;
     vqmlp_status st = lut_validate(bits, N, K, packed, U, V, r, s, sign, had_block, &tmp);
     if (st) return st;
+    {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1)
+            cus = 256;
+        tmp.cus = std::min(cus, kArgmaxMaxGroups);
+    }
     vqmlp_lut_plan* p = new (std::nothrow) vqmlp_lut_plan(tmp);
     if (!p) return fail(VQMLP_ERR_INVALID_ARG, "out of host memory");
     *out = p;
@@ -1154,6 +1166,53 @@ vqmlp_status vqmlp_lut_plan_forward(const vqmlp_lut_plan* plan, int T, const voi
                                     void* workspace, size_t workspace_bytes, void* stream) {
     if (!plan) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_plan_forward: null plan");
     return lut_run(*plan, T, x, y, workspace, workspace_bytes, stream);
+}
+
+vqmlp_status vqmlp_lut_plan_argmax(const vqmlp_lut_plan* plan, int T, const void* x,
+                                   int32_t* index, float* value, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (!plan) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_plan_argmax: null plan");
+    const vqmlp_lut_plan& p = *plan;
+    const int N = p.N, K = p.K;
+    if (T < 0 || T > kSkinnyT)
+        return fail(VQMLP_ERR_UNSUPPORTED, "the argmax head takes T <= %d (T=%d)", kSkinnyT, T);
+    if (T == 0) return ok();
+    if (p.r != 0) return fail(VQMLP_ERR_UNSUPPORTED, "the argmax head takes no low-rank factors");
+    const int hb = p.had_block ? p.had_block : 1;
+    if (K > kLut8MaxK || lut8_chunk(K, hb) < 64 || !aligned(p.s, 16) || !aligned(p.sign, 8))
+        return fail(VQMLP_ERR_UNSUPPORTED,
+                    "the argmax head takes K <= %d, power-of-two column chunks, s 16- and sign "
+                    "8-byte aligned (K=%d)", kLut8MaxK, K);
+    if (!x || !index || !workspace)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_lut_plan_argmax: null pointer");
+    if (!aligned(x, 16) || !aligned(workspace, 256) || !aligned(index, 4) || !aligned(value, 4))
+        return fail(VQMLP_ERR_INVALID_ARG, "x must be 16-byte aligned, the workspace 256");
+    size_t need = 0;
+    vqmlp_lut_workspace_bytes(N, K, T, 0, &need);
+    if (workspace_bytes < need)
+        return fail(VQMLP_ERR_WORKSPACE, "workspace holds %zu bytes, this call needs %zu",
+                    workspace_bytes, need);
+    uint8_t* wb = static_cast<uint8_t*>(workspace) + 256;
+    uint16_t* xt = reinterpret_cast<uint16_t*>(wb);
+    float* pval = reinterpret_cast<float*>(wb + align256(size_t(T) * K * 2));
+    int* pidx = reinterpret_cast<int*>(pval + kArgmaxMaxGroups * kSkinnyT);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e = launch_lut8_pre(T, K, hb, static_cast<const uint16_t*>(x), p.s, p.sign, nullptr, 0,
+                                   xt, nullptr, hs);
+    if (e != hipSuccess) return hip_fail(e, "argmax head: input scale and rotation");
+    Lut8Args q;
+    memset(&q, 0, sizeof q);
+    q.codes = reinterpret_cast<const uint32_t*>(p.base + p.L.codes_off);
+    q.lut = reinterpret_cast<const uint16_t*>(p.base + p.L.cb_off);
+    q.sc = reinterpret_cast<const uint16_t*>(p.base + p.L.sc_off);
+    q.x = xt;
+    q.bits = p.bits;
+    q.N = N;
+    q.K = K;
+    q.T = T;
+    e = launch_lut8_argmax(q, p.cus, pval, pidx, index, value, hs);
+    if (e != hipSuccess) return hip_fail(e, "argmax head");
+    return ok();
 }
 
 }  // extern "C"

@@ -63,6 +63,7 @@ def lib():
             "vqmlp_lut_create": [I, I, I, P, P, P, I, P, P, I, C.POINTER(P)],
             "vqmlp_lut_destroy": [P],
             "vqmlp_lut_plan_forward": [P, I, P, P, P, S, P],
+            "vqmlp_lut_plan_argmax": [P, I, P, P, P, P, S, P],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -283,6 +284,20 @@ class LUTProjection:
         _check(lib().vqmlp_lut_plan_forward(self._plan, T, _dptr(x), _dptr(y), _dptr(workspace),
                                             workspace.numel(), _stream(stream)))
         return y
+
+    def argmax(self, x, workspace=None, stream=None):
+        """Greedy argmax head: x [T, K] float16 device tensor (T <= 8) -> (index int32 [T],
+        value float32 [T]): per token the lowest row of the largest logit, and that logit."""
+        import torch
+
+        T = x.shape[0]
+        index = torch.empty(T, dtype=torch.int32, device=x.device)
+        value = torch.empty(T, dtype=torch.float32, device=x.device)
+        if workspace is None:
+            workspace = self.workspace(T)
+        _check(lib().vqmlp_lut_plan_argmax(self._plan, T, _dptr(x), _dptr(index), _dptr(value),
+                                           _dptr(workspace), workspace.numel(), _stream(stream)))
+        return index, value
 
     def forward_stateless(self, x, y=None, workspace=None, stream=None):
         """The same through vqmlp_lut_forward (validates the packed buffer on every call)."""

@@ -179,6 +179,21 @@ vqmlp_status vqmlp_lut_destroy(vqmlp_lut_plan *plan);
 vqmlp_status vqmlp_lut_plan_forward(const vqmlp_lut_plan *plan, int T, const void *x, void *y,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* Greedy next token from a scalar-LUT output head (the model card's four-bit LUT head; in-model
+ * argmax of the conversion pipeline page, "Facts": the head returns, per token, the index of the
+ * largest logit and its value instead of the vocabulary's logits).  plan: a vqmlp_lut_create plan
+ * with r == 0 (no factors), K <= 5120, s 16-byte and sign 8-byte aligned (the head's norm gain
+ * goes in s; had_block 0: no rotation).  For T <= 8 rows of x (DEVICE binary16 [T][K], 16-byte
+ * aligned) writes index[t] (DEVICE int32) = the lowest row n among the largest logits
+ * sc[n] * (W_lut x~)[t][n] (FP32 accumulation, no rank term) and, when value is not NULL,
+ * value[t] (DEVICE float) = that logit.  Workspace: vqmlp_lut_workspace_bytes(N, K, T, 0), 256-byte
+ * aligned, no zero fill.  Errors: VQMLP_ERR_UNSUPPORTED for T > 8, r != 0, K > 5120 or unaligned
+ * s / sign; VQMLP_ERR_INVALID_ARG, VQMLP_ERR_WORKSPACE, VQMLP_ERR_HIP as vqmlp_lut_forward.
+ * T == 0 is a no-op. */
+vqmlp_status vqmlp_lut_plan_argmax(const vqmlp_lut_plan *plan, int T, const void *x,
+                                   int32_t *index, float *value, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

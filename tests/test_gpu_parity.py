@@ -321,6 +321,68 @@ def test_lut_decode_shapes(vq, oracle_mod, torch_dev, bits, N, K, T, rank, hb):
     assert _report("LUT T<=8 %d-bit %dx%d T=%d" % (bits, N, K, T), y, ref) <= MLP_TOL
 
 
+HEAD_CASES = [  # N, K, T, Hadamard block (0 = none), bits
+    (4096, 5120, 8, 0, 4),
+    (1024, 5120, 3, 1024, 4),
+    (2048, 512, 1, 0, 2),
+    (64, 128, 8, 64, 4),  # fewer 32-row blocks than workgroups
+]
+
+
+@pytest.mark.parametrize("N,K,T,hb,bits", HEAD_CASES)
+def test_lut_argmax_head(vq, oracle_mod, torch_dev, N, K, T, hb, bits):
+    """Greedy argmax head against the oracle's FP64 logits: the returned row holds the largest
+    logit up to the FP32-versus-FP64 accumulation difference (rows whose logits differ by less
+    may be ordered either way), and its value is that row's logit."""
+    rng = np.random.default_rng(N + K + T + hb + bits)
+    p = synth.lut_projection(rng, bits, N, K, 0, hb)
+    x = synth.activations(rng, T, K, outliers=True)
+    _say("argmax head N=%d K=%d T=%d hb=%d bits=%d" % (N, K, T, hb, bits))
+    proj = vq.LUTProjection.from_proj(p)
+    idx, val = proj.argmax(vq.to_device(x))
+    torch_dev.cuda.synchronize()
+    idx, val = idx.cpu().numpy(), val.cpu().numpy().astype(np.float64)
+    y = oracle_mod.lut_forward(p, x)
+    ref_idx, ref_val = oracle_mod.lut_argmax(p, x)
+    tol = 2e-3 * np.abs(y).max(axis=1)
+    for t in range(T):
+        assert y[t, idx[t]] >= ref_val[t] - tol[t], (t, idx[t], ref_idx[t])
+        assert abs(val[t] - y[t, idx[t]]) <= tol[t]
+
+
+def test_lut_argmax_full_head_planted(vq, torch_dev):
+    """The 248,320-row four-bit output head at T = 8 (property test: no oracle pass over 1.3 G
+    weights).  Token t's x is positive on its own 640 columns and zero elsewhere; row planted[t]
+    takes its table's entry 15 (= 1) on those columns and entry 0 (= 0) elsewhere, so its logit
+    for token t is about 640 x sc while every random row stays near 0.02 sqrt(640) and the other
+    planted rows give 0: the head must return planted[t] for token t, with that logit."""
+    N, K, T = 248320, 5120, 8
+    span = K // T
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    lut = (rng.standard_normal((N // 8, 16)) * 0.02).astype(np.float16)
+    sc = rng.uniform(0.5, 1.5, N).astype(np.float16)
+    planted = rng.choice(N, T, replace=False)
+    x = np.zeros((T, K), np.float16)
+    for t, j in enumerate(planted):
+        cols = slice(t * span, (t + 1) * span)
+        x[t, cols] = (np.abs(rng.standard_normal(span)) + 0.1).astype(np.float16)
+        lut[j // 8, 15], lut[j // 8, 0] = np.float16(1.0), np.float16(0.0)
+        codes[j, :] = 0
+        codes[j, cols] = 15
+    packed = vq.to_device(vq.lut_pack(4, codes, lut, sc))
+    del codes
+    proj = vq.LUTProjection(4, N, K, packed, None, None, None, None, 0)
+    _say("argmax head full 248320 x 5120 T=8")
+    idx, val = proj.argmax(vq.to_device(x))
+    torch_dev.cuda.synchronize()
+    idx, val = idx.cpu().numpy(), val.cpu().numpy().astype(np.float64)
+    assert list(idx) == [int(j) for j in planted]
+    for t, j in enumerate(planted):
+        want = float(sc[j]) * float(x[t].astype(np.float64).sum())
+        assert abs(val[t] - want) <= 1e-3 * want
+
+
 @pytest.mark.parametrize("bits", [2, 4])
 @pytest.mark.parametrize("N,K,T,rank,hb", LUT_CASES)
 def test_lut_small_shapes(vq, oracle_mod, torch_dev, bits, N, K, T, rank, hb):

@@ -168,3 +168,9 @@ def test_null_arguments_are_rejected_without_device(vq):
     assert L.vqmlp_lut_plan_forward(None, 1, None, None, None, 0, None) == vq.ERR_INVALID_ARG
     assert L.vqmlp_last_error() != b""
     assert L.vqmlp_lut_destroy(None) == vq.OK
+
+
+def test_lut_argmax_rejects_null_plan(vq):
+    L = vq.lib()
+    assert L.vqmlp_lut_plan_argmax(None, 1, None, None, None, None, 0, None) == vq.ERR_INVALID_ARG
+    assert b"null plan" in L.vqmlp_last_error()
