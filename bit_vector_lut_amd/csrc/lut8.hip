@@ -30,6 +30,28 @@ constexpr int kMaxK = kLut8MaxK;        // x~ rows staged in LDS
 constexpr int kXRow = kMaxK + 8;        // LDS row of x~ in halves (padded against bank conflicts)
 constexpr int kMaxU = (kMaxK / 64 + kKS - 1) / kKS;  // units per slice
 constexpr int kTabDw = 16 * 32;         // one table: 16 entries x 32 bank columns
+
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+// The table words of two 4-bit codes (bits sh..sh+3 and sh+4..sh+7 of d) as one binary16 pair:
+// each entry is read with a 16-bit LDS load straight into its half of the result, so the pair
+// costs two field extracts and two address merges and no packing.
+// LDS byte address of the entry that bits sh..sh+3 of d select, in the table column lb: a field
+// extract and a shift-or (the compiler would otherwise emit shift, mask and add).
+__device__ __forceinline__ uint32_t lut_addr(uint32_t d, uint32_t sh, uint32_t lb) {
+    uint32_t a;
+    asm("v_bfe_u32 %0, %1, %2, 4\n\tv_lshl_or_b32 %0, %0, 7, %3" : "=&v"(a) : "v"(d), "s"(sh), "v"(lb));
+    return a;
+}
+__device__ __forceinline__ uint32_t look_pair4(const char* tb, uint32_t lb, uint32_t d, int sh) {
+    h2v v;
+    v.x = *reinterpret_cast<const _Float16*>(tb + lut_addr(d, sh, lb));
+    v.y = *reinterpret_cast<const _Float16*>(tb + lut_addr(d, sh + 4, lb));
+    return __builtin_bit_cast(uint32_t, v);
+}
+// the half2 table word of the 2-bit code pair in bits sh..sh+3 of d
+__device__ __forceinline__ uint32_t look_pair2(const char* tb, uint32_t lb, uint32_t d, int sh) {
+    return *reinterpret_cast<const uint32_t*>(tb + lut_addr(d, sh, lb));
+}
 constexpr int kMaxR = 256;              // rank of the low-rank term
 constexpr int kUPre = 8;                // 16-byte chunks of a U row held from the start (r <= 64)
 typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));  // 4-byte aligned
@@ -126,9 +148,6 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
     const char* tbase = reinterpret_cast<const char*>(&tab[0][0]);
     const uint32_t lb = (uint32_t(l & 31) << 2) | uint32_t(rt * kTabDw * 4);
     const int n = l & 15;  // B column: token n
-    auto look = [&](uint32_t e) -> uint32_t {
-        return *reinterpret_cast<const uint32_t*>(tbase + ((e << 7) | lb));
-    };
 #pragma unroll
     for (int u = 0; u < kMaxU; ++u) {
         if (u < nus) {  // uniform
@@ -137,17 +156,15 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
             for (int s = 0; s < 2; ++s) {
                 u32x4 A;
                 if constexpr (BITS == 2) {
-                    const uint32_t d = cw[u] >> (16 * s);
 #pragma unroll
-                    for (int p = 0; p < 4; ++p) A[p] = look((d >> (4 * p)) & 15u);
+                    for (int p = 0; p < 4; ++p) A[p] = look_pair2(tbase, lb, cw[u], 16 * s + 4 * p);
                 } else {
                     const uint32_t d = cw[2 * u + s];
 #pragma unroll
-                    for (int p = 0; p < 4; ++p)
-                        A[p] = (look((d >> (8 * p)) & 15u) & 0xFFFFu) | (look((d >> (8 * p + 4)) & 15u) << 16);
+                    for (int p = 0; p < 4; ++p) A[p] = look_pair4(tbase, lb, d, 8 * p);
                 }
-                const u32x4 B = n < kSkinnyT ? *reinterpret_cast<const u32x4*>(&xs[n < kSkinnyT ? n : 0][kb + 8 * s])
-                                             : u32x4{0u, 0u, 0u, 0u};
+                // columns 8..15 repeat tokens 0..7: those outputs are never read, so no masking
+                const u32x4 B = *reinterpret_cast<const u32x4*>(&xs[n & (kSkinnyT - 1)][kb + 8 * s]);
                 acc = mfma16x16x32(A, B, acc);
             }
         }
@@ -233,11 +250,15 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* p
     const int el = (ell >> 3) * 16 + (ell & 7), et = el & 15;
     const int erl = ert * 16 + 4 * (el >> 4) + eq;  // row within the block
 
+    // every thread loads a scale (threads past the epilogue's 256 a harmless duplicate): a load
+    // under a branch would have to complete inside it, and with in-order returns that wait
+    // would also cover the code words requested before it
+    const int erw = erl & 31;
     int blk = blockIdx.x;
+    uint32_t tv = load_tab(blk);
+    uint16_t esc = a.sc[blk * 32 + erw];
     uint32_t cw[kRunV * 4];
     load_codes(blk, cw);
-    uint32_t tv = load_tab(blk);
-    float esc = tid < 256 ? h2f(a.sc[blk * 32 + erl]) : 0.f;
     // x~ (rows past T zero), all loads before the stores
     constexpr int kXPer = kSkinnyT * kMaxK / 8 / (kW * 64);
     const int c8n = K / 8;
@@ -264,15 +285,12 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* p
         tab[par][trt][te * 32 + tc] = tv;
         // the next block's words, requested now (the last block repeats itself)
         const int nxt = blk + G < nb ? blk + G : blk;
+        const uint32_t tvn = load_tab(nxt);
+        const uint16_t escn = a.sc[nxt * 32 + erw];
         uint32_t cn[kRunV * 4];
         load_codes(nxt, cn);
-        const uint32_t tvn = load_tab(nxt);
-        const float escn = tid < 256 ? h2f(a.sc[nxt * 32 + erl]) : 0.f;
         __syncthreads();  // tables of this block written; red of the last block consumed
         const uint32_t lb = (uint32_t(l & 31) << 2) | uint32_t(((par * 2 + rt) * kTabDw) * 4);
-        auto look = [&](uint32_t e) -> uint32_t {
-            return *reinterpret_cast<const uint32_t*>(tb0 + ((e << 7) + lb));
-        };
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < kMaxU; ++u) {
@@ -282,17 +300,15 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* p
                 for (int s = 0; s < 2; ++s) {
                     u32x4 A;
                     if constexpr (BITS == 2) {
-                        const uint32_t d = cw[u] >> (16 * s);
 #pragma unroll
-                        for (int p = 0; p < 4; ++p) A[p] = look((d >> (4 * p)) & 15u);
+                        for (int p = 0; p < 4; ++p) A[p] = look_pair2(tb0, lb, cw[u], 16 * s + 4 * p);
                     } else {
                         const uint32_t d = cw[2 * u + s];
 #pragma unroll
-                        for (int p = 0; p < 4; ++p)
-                            A[p] = (look((d >> (8 * p)) & 15u) & 0xFFFFu) | (look((d >> (8 * p + 4)) & 15u) << 16);
+                        for (int p = 0; p < 4; ++p) A[p] = look_pair4(tb0, lb, d, 8 * p);
                     }
-                    const u32x4 B = n < kSkinnyT ? *reinterpret_cast<const u32x4*>(&xs[n < kSkinnyT ? n : 0][kb + 8 * s])
-                                                 : u32x4{0u, 0u, 0u, 0u};
+                    // columns 8..15 repeat tokens 0..7: those outputs are never read, so no masking
+                    const u32x4 B = *reinterpret_cast<const u32x4*>(&xs[n & (kSkinnyT - 1)][kb + 8 * s]);
                     acc = mfma16x16x32(A, B, acc);
                 }
             }
@@ -303,7 +319,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* p
             float v = 0.f;
 #pragma unroll
             for (int s = 0; s < kKS; ++s) v += red[ert * kKS + s][el][eq];
-            v *= esc;
+            v *= h2f(esc);
             if (v > best) {
                 best = v;
                 bidx = blk * 32 + erl;
