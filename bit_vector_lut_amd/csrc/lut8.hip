@@ -356,23 +356,61 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* p
     }
 }
 
-// merge of the workgroups' bests: token t (thread t < T) scans them in order
-__global__ void __launch_bounds__(64) k_argmax_merge(int G, int T, const float* pval, const int* pidx,
-                                                     int* out_idx, float* out_val) {
-    const int t = threadIdx.x;
-    if (t >= T) return;
-    float bv = -__builtin_inff();
-    int bi = 0x7fffffff;
-    for (int b = 0; b < G; ++b) {
-        const float v = pval[b * kSkinnyT + t];
-        const int ix = pidx[b * kSkinnyT + t];
-        if (v > bv || (v == bv && ix < bi)) {
-            bv = v;
-            bi = ix;
+// merge of the workgroups' bests: 256 threads take candidates b = tid, tid + 256, ... (8 tokens
+// each, two 16-byte loads), then a tree in LDS.  The order "larger value, then lower row" is a
+// total order, so the winner does not depend on how the candidates are grouped.
+__device__ __forceinline__ void argmax_take(float& bv, int& bi, float v, int ix) {
+    if (v > bv || (v == bv && ix < bi)) {
+        bv = v;
+        bi = ix;
+    }
+}
+__global__ void __launch_bounds__(256) k_argmax_merge(int G, int T, const float* pval, const int* pidx,
+                                                      int* out_idx, float* out_val) {
+    __shared__ float sv[kSkinnyT][256];
+    __shared__ int si[kSkinnyT][256];
+    const int tid = threadIdx.x;
+    float bv[kSkinnyT];
+    int bi[kSkinnyT];
+#pragma unroll
+    for (int t = 0; t < kSkinnyT; ++t) {
+        bv[t] = -__builtin_inff();
+        bi[t] = 0x7fffffff;
+    }
+    for (int b = tid; b < G; b += 256) {
+        const f32x4 v0 = *reinterpret_cast<const f32x4*>(pval + b * kSkinnyT);
+        const f32x4 v1 = *reinterpret_cast<const f32x4*>(pval + b * kSkinnyT + 4);
+        const u32x4 i0 = *reinterpret_cast<const u32x4*>(pidx + b * kSkinnyT);
+        const u32x4 i1 = *reinterpret_cast<const u32x4*>(pidx + b * kSkinnyT + 4);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            argmax_take(bv[t], bi[t], v0[t], int(i0[t]));
+            argmax_take(bv[t + 4], bi[t + 4], v1[t], int(i1[t]));
         }
     }
-    out_idx[t] = bi;
-    if (out_val) out_val[t] = bv;
+#pragma unroll
+    for (int t = 0; t < kSkinnyT; ++t) {
+        sv[t][tid] = bv[t];
+        si[t][tid] = bi[t];
+    }
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (tid < h) {
+#pragma unroll
+            for (int t = 0; t < kSkinnyT; ++t) {
+                float v = sv[t][tid];
+                int ix = si[t][tid];
+                argmax_take(v, ix, sv[t][tid + h], si[t][tid + h]);
+                sv[t][tid] = v;
+                si[t][tid] = ix;
+            }
+        }
+        __syncthreads();
+    }
+    if (tid < T) {
+        out_idx[tid] = si[tid][0];
+        if (out_val) out_val[tid] = sv[tid][0];
+    }
 }
 
 int lut8_argmax_grid(int N, int cus) {
@@ -391,7 +429,7 @@ hipError_t launch_lut8_argmax(const Lut8Args& a, int cus, float* pval, int* pidx
         hipLaunchKernelGGL(k_lut8_argmax<2>, dim3(G), dim3(kW * 64), 0, st, a, pval, pidx);
     else
         hipLaunchKernelGGL(k_lut8_argmax<4>, dim3(G), dim3(kW * 64), 0, st, a, pval, pidx);
-    hipLaunchKernelGGL(k_argmax_merge, dim3(1), dim3(64), 0, st, G, a.T, pval, pidx, out_idx, out_val);
+    hipLaunchKernelGGL(k_argmax_merge, dim3(1), dim3(256), 0, st, G, a.T, pval, pidx, out_idx, out_val);
     return hipGetLastError();
 }
 
