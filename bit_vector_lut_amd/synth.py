@@ -95,6 +95,21 @@ def vq3_matrix(rng: np.random.Generator, N: int, K: int) -> VQ3Matrix:
     return VQ3Matrix(codes, cb, sc)
 
 
+class VQ2Matrix(VQ3Matrix):
+    """One 2x16 matrix W[N, K]: codes uint8 [N/2, K] with values 0..15, cb float16 [N/8, 16, 2]
+    (same component and group conventions as VQ3Matrix), sc float16 [N]."""
+
+
+def vq2_matrix(rng: np.random.Generator, N: int, K: int) -> VQ2Matrix:
+    """Draw order: codes, codebook, scales (the distributions of vq3_matrix)."""
+    if N % 8:
+        raise ValueError("N must be a multiple of 8")
+    codes = rng.integers(0, 16, size=(N // 2, K), dtype=np.uint8)
+    cb = rng.normal(0.0, 0.02, size=(N // 8, 16, 2)).astype(F16)
+    sc = rng.uniform(0.5, 1.5, size=N).astype(F16)
+    return VQ2Matrix(codes, cb, sc)
+
+
 def signs(rng: np.random.Generator, n: int) -> np.ndarray:
     return (2 * rng.integers(0, 2, size=n) - 1).astype(np.int8)
 

@@ -5,7 +5,8 @@ leg, never by the HIP library or its binding.  Arguments are the unpacked arrays
 ``bit_vector_lut_amd.synth`` (plain numpy), so nothing here depends on the GPU path.
 
 The arithmetic lives in vqmlp_oracle.c, whose header gives the definitions and the passages of
-the pages they follow.
+the pages they follow, except the 2x16 vector-LUT decode (``vq2_weight``, plain numpy; its
+docstring cites its passage) and the argmax over ``lut_forward``.
 """
 from __future__ import annotations
 
@@ -200,6 +201,39 @@ def lut_argmax(proj, x, tokens=None):
     y = lut_forward(proj, x, tokens)
     idx = np.argmax(y, axis=1)  # first occurrence of the maximum
     return idx.astype(np.int64), y[np.arange(y.shape[0]), idx]
+
+
+def vq2_weight(codes, cb, sc) -> np.ndarray:
+    """Decoded 2x16 matrix in FP64: W[r][j] = cb[r // 8][codes[r // 2][j]][r % 2] * sc[r].
+
+    The two-bit vector lookup table "2x16" of the MLP in the previous packages (model card
+    "anemll/anemll-forge-qwen3.8-27B", section "Release 0.2: three-bit MLP, token-mixer
+    rotations, distilled weights", format table, "Previous packages" column): 16 two-component
+    centroids, one four-bit index per pair of output channels, per-channel scales.  The vector
+    axis, component order, group of 8 output rows per codebook and scale placement are the
+    readings of the three-bit 2x64 form (vqmlp_oracle.c header) with 16 entries instead of 64.
+    Written in numpy on its own: one row at a time, the centroid component times the scale."""
+    codes = np.asarray(codes)
+    if codes.size and int(codes.max()) > 15:
+        raise OracleError("vq2_weight: code above 15")
+    cbv = f16_to_f64(cb)
+    scv = f16_to_f64(sc)
+    N, K = scv.shape[0], codes.shape[1]
+    if codes.shape[0] * 2 != N or cbv.shape != (N // 8, 16, 2) or N % 8:
+        raise OracleError("vq2_weight: inconsistent shapes")
+    W = np.empty((N, K), np.float64)
+    for r in range(N):
+        W[r] = cbv[r // 8][codes[r // 2].astype(np.int64), r % 2] * scv[r]
+    return W
+
+
+def vq2_matmul(codes, cb, sc, xin) -> np.ndarray:
+    """out[t][r] = sum_j W[r][j] xin[t][j] for the 2x16 matrix (FP64; the operand is used as
+    given: any input scale or rotation is the caller's)."""
+    W = vq2_weight(codes, cb, sc)
+    x = np.asarray(np.atleast_2d(xin))
+    x = f16_to_f64(x) if x.dtype in (np.float16, np.uint16) else x.astype(np.float64)
+    return x @ W.T
 
 
 def num_threads() -> int:

@@ -398,3 +398,54 @@ def test_lut_argmax_equals_brute_force(oracle_mod):
     ref = _lut_library(p, x)
     assert np.array_equal(idx, np.argmax(ref, axis=1))
     assert np.allclose(val, ref.max(axis=1), rtol=1e-12)
+
+
+# ---- 2x16 vector LUT (model card, Release 0.2 format table, previous packages' MLP format)
+
+def test_vq2_weight_hand_example(oracle_mod):
+    """16 rows (two codebook groups), 2 columns, worked by hand: row r takes component r % 2 of
+    centroid codes[r // 2][j] from group r // 8, times sc[r]."""
+    cb = np.zeros((2, 16, 2), np.float16)
+    cb[0, 3] = (0.5, -1.0)
+    cb[0, 15] = (2.0, 0.25)
+    cb[1, 3] = (-4.0, 8.0)
+    cb[1, 0] = (1.5, -0.5)
+    sc = np.ones(16, np.float16)
+    sc[1], sc[9], sc[14] = 2.0, 0.5, -1.0
+    codes = np.zeros((8, 2), np.uint8)
+    codes[0] = (3, 15)   # rows 0, 1 (group 0)
+    codes[4] = (3, 0)    # rows 8, 9 (group 1)
+    codes[7] = (0, 3)    # rows 14, 15 (group 1)
+    W = oracle_mod.vq2_weight(codes, cb, sc)
+    assert W[0].tolist() == [0.5, 2.0]
+    assert W[1].tolist() == [-2.0, 0.5]          # component 1, scale 2
+    assert W[8].tolist() == [-4.0, 1.5]
+    assert W[9].tolist() == [4.0, -0.25]         # component 1, scale 0.5
+    assert W[14].tolist() == [-1.5, 4.0]         # component 0, scale -1
+    assert W[15].tolist() == [-0.5, 8.0]
+    assert not W[2:8].any()                      # group 0, centroid 0 is zero
+    assert W[10:14].tolist() == [[1.5, 1.5], [-0.5, -0.5]] * 2  # group 1, centroid 0
+    with pytest.raises(oracle_mod.OracleError):
+        oracle_mod.vq2_weight(np.full((8, 2), 16, np.uint8), cb, sc)
+
+
+def test_vq2_is_vq3_with_a_padded_codebook(oracle_mod):
+    """With its 16 centroids placed first in a 64-entry codebook, a 2x16 matrix is a three-bit
+    matrix with codes below 16: the numpy decode equals the C oracle's VQ3 decode exactly."""
+    m = synth.vq2_matrix(np.random.default_rng(5), 48, 37)
+    cb64 = np.zeros((6, 64, 2), np.float16)
+    cb64[:, :16] = m.cb
+    assert np.array_equal(oracle_mod.vq2_weight(m.codes, m.cb, m.sc),
+                          oracle_mod.vq3_weight(m.codes, cb64.view(np.uint16), m.sc.view(np.uint16)))
+
+
+def test_vq2_matmul_brute_force(oracle_mod):
+    m = synth.vq2_matrix(np.random.default_rng(6), 16, 5)
+    x = np.random.default_rng(7).standard_normal((3, 5)).astype(np.float16)
+    cb, sc, xv = m.cb.astype(np.float64), m.sc.astype(np.float64), x.astype(np.float64)
+    want = np.zeros((3, 16))
+    for t in range(3):
+        for r in range(16):
+            for j in range(5):
+                want[t, r] += cb[r // 8, m.codes[r // 2, j], r % 2] * sc[r] * xv[t, j]
+    np.testing.assert_allclose(oracle_mod.vq2_matmul(m.codes, m.cb, m.sc, x), want, rtol=1e-13, atol=1e-15)
