@@ -170,6 +170,50 @@ def t8_mixers(device, stream, n_proj=16):
     return out
 
 
+def t8_vq2(device, stream, n_proj=16):
+    """The 2x16 vector-LUT projection at T = 8 (5120 x 5120 and the 17408 x 5120 gate / up shape):
+    one HIP graph of n_proj distinct seeded matrices per shape, timed over replays; weight GB/s
+    (codes, centroids, scales) against the HBM peak."""
+    import numpy as np
+    import torch
+
+    from bit_vector_lut_amd import synth, vqmlp
+
+    out = []
+    for N, K in ((5120, 5120), (17408, 5120)):
+        projs = [vqmlp.VQ2Projection.from_matrix(
+            synth.vq2_matrix(np.random.default_rng(7000 + i), N, K), device) for i in range(n_proj)]
+        x = vqmlp.to_device(synth.activations(np.random.default_rng(N), 8, K, True), device)
+        ys = [torch.empty((8, N), dtype=x.dtype, device=device) for _ in projs]
+        with torch.cuda.stream(stream):
+            for m, y in zip(projs, ys):
+                m.forward(x, y, stream=stream)
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for m, y in zip(projs, ys):
+                m.forward(x, y, stream=stream)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            with torch.cuda.stream(stream):
+                g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * n_proj)
+        wb = N * K // 4 + (N // 8) * 16 * 4 + N * 2
+        gbs = wb / (us * 1e-6) / 1e9
+        log("T=8 2x16 projection %dx%d: %.2f us per forward, %.1f GB/s of weights" % (N, K, us, gbs))
+        out.append({"N": N, "K": K, "T": 8, "us": round(us, 2), "weight_bytes": wb,
+                    "gbps": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)})
+        del g, projs, ys
+    return out
+
+
 def t8_lm_head(device, stream):
     """The four-bit LUT output head (248,320 x 5120) with in-model argmax at T = 8: one seeded
     head (636 MB of codes, more than the on-die cache), timed over back-to-back calls with
@@ -218,6 +262,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-t512", action="store_true")
     ap.add_argument("--no-mixers8", action="store_true")
+    ap.add_argument("--no-vq2", action="store_true")
     ap.add_argument("--probe", action="store_true",
                     help="counter run only: a known-size copy and 4 forwards, no timing")
     args = ap.parse_args()
@@ -319,6 +364,8 @@ def main():
     # ---------------------------------------------------------------- T = 8 token mixers
     if not args.no_mixers8:
         result["t8_token_mixers"] = t8_mixers(device, stream)
+    if not args.no_vq2:
+        result["t8_vq2x16"] = t8_vq2(device, stream)
         result["t8_lm_head_argmax"] = t8_lm_head(device, stream)
 
     # ---------------------------------------------------------------- T = 512 prefill MLP

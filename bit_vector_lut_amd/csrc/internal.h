@@ -86,6 +86,18 @@ struct Lut8Args {
     int bits, N, K, T, r, nch;
 };
 hipError_t launch_lut8(const Lut8Args& a, hipStream_t st);
+// 2x16 vector-LUT projection at T <= 8: y[t][r] = sc[r] * sum_j cb[r/8][code[r/2][j]][r%2] x[t][j]
+// (x as given; FP32 accumulation, one rounding).  N % 32 == 0, K % 32 == 0, K <= kVq2MaxK.
+constexpr int kVq2MaxK = 5120;
+struct Vq2Args {
+    const uint32_t* codes;  // [N/2][K/8] words, code j of a pair row at bits 4 (j % 8) of word j / 8
+    const uint32_t* cb;     // [N/8][16] centroids, binary16 (component 0) | (component 1) << 16
+    const uint16_t* sc;     // [N] binary16 row scales
+    const uint16_t* x;      // [T][K] binary16
+    uint16_t* y;            // [T][N] binary16
+    int N, K, T;
+};
+hipError_t launch_vq2_8(const Vq2Args& a, hipStream_t st);
 // Pre-pass of the T <= 8 projection: x~ = R_K(x . s . sign) ([T][K] binary16, Hadamard block hb,
 // 1 = none) and, for r > 0, the partial sums zp[c][t][j] = sum over chunk c of V[j][k] x~[t][k]
 // (chunks of lut8_chunk(K, hb) columns; x~ rounded to binary16 first).

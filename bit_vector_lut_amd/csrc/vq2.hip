@@ -1,0 +1,139 @@
+// 2x16 vector-LUT projection at T <= 8 tokens: y[t][r] = sc[r] * sum_j cb[r/8][code[r/2][j]][r%2] x[t][j]
+// (the two-bit vector LUT of the model card's previous packages, section "Release 0.2",
+// format table: 16 two-component centroids per group of 8 output rows, one four-bit index per
+// pair of output channels, per-channel scales).
+//
+// Workgroup: one tile of 16 row pairs (32 output rows) x 16 K slices, one wave per slice.  Lane
+// (pair i = l mod 16, group g = l / 16) of a wave streams one contiguous run of code words (8
+// codes per word, code j at bits 4 (j mod 8) of word j / 8 of its pair row), g taking a quarter
+// of the slice.  A code is looked up in LDS as the half2 (component 0, component 1) of its
+// centroid, which is the A operand of v_mfma_f32_16x16x32_f16 when the contraction index is
+// (column, component): A[i][(j, c)] = cb[code[i][j]][c].  The token operand then carries the
+// component as well: B[(j, c)][n] = x[n mod 8][j] if c == n / 8, else 0, so output column n
+// holds row 2 i + n / 8 of token n mod 8, and all 16 columns are used.
+#include "device.h"
+#include "internal.h"
+
+namespace vqmlp {
+namespace {
+
+constexpr int kVW = 16;                    // waves: 16 K slices
+constexpr int kVMaxK = kVq2MaxK;           // x rows staged in LDS
+constexpr int kVXRow = kVMaxK + 8;         // LDS row of x in halves (padded against bank conflicts)
+constexpr int kVMaxU = (kVMaxK / 32 + kVW - 1) / kVW;  // units (32 columns, one word per lane) per slice
+constexpr int kVRunV = (kVMaxU + 3) / 4;   // 16-byte loads per lane
+constexpr int kVTab = 16 * 32;             // 16 centroids x 32 bank columns
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+
+// LDS byte address of the centroid that bits sh..sh+3 of d select, in table column lb
+__device__ __forceinline__ uint32_t vq2_addr(uint32_t d, uint32_t sh, uint32_t lb) {
+    uint32_t a;
+    asm("v_bfe_u32 %0, %1, %2, 4\n\tv_lshl_or_b32 %0, %0, 7, %3" : "=&v"(a) : "v"(d), "s"(sh), "v"(lb));
+    return a;
+}
+
+}  // namespace
+
+__global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
+    constexpr int kOffX = kVTab * 4, kOffRed = kOffX + kSkinnyT * kVXRow * 2;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kOffRed + kVW * 64 * 16];
+    auto& tab = *reinterpret_cast<uint32_t (*)[kVTab]>(lds);
+    auto& xs = *reinterpret_cast<uint16_t (*)[kSkinnyT][kVXRow]>(lds + kOffX);
+    auto& red = *reinterpret_cast<f32x4 (*)[kVW][64]>(lds + kOffRed);
+
+    const int tid = threadIdx.x, l = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int K = a.K, T = a.T, N = a.N;
+    const int pair0 = blockIdx.x * 16;
+    const int nu = K / 32, u0 = w * nu / kVW, nus = (w + 1) * nu / kVW - u0;
+
+    // ---- code run first: kVRunV 16-byte loads whatever nus is; words past the run are unused
+    // and past the last pair row they fall in the codebook section that follows the codes
+    const int i = l & 15, g = l >> 4;
+    const uint32_t* crun = a.codes + size_t(pair0 + i) * (K / 8) + u0 * 4 + g * nus;
+    uint32_t cw[kVRunV * 4];
+#pragma unroll
+    for (int v = 0; v < kVRunV; ++v) {
+        const u32x4a q = *reinterpret_cast<const u32x4a*>(crun + 4 * v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cw[4 * v + e] = q[e];
+    }
+    // epilogue thread (pair ei, column en) of the tile: every thread loads a scale (threads
+    // past 256 a duplicate) so that no load sits under a branch
+    const int ei = (tid >> 4) & 15, en = tid & 15;
+    const int erow = 2 * (pair0 + ei) + (en >> 3);
+    const uint16_t esc = a.sc[erow];
+    // centroid words: thread (entry te, bank column tc) for tid < 512, column tc serving pair
+    // row tc mod 16 (group of 4 pairs = 8 output rows)
+    const int te = (tid >> 5) & 15, tc = tid & 31;
+    const uint32_t tw = a.cb[size_t((pair0 + (tc & 15)) >> 2) * 16 + te];
+    // x rows (past T zero), all loads before the stores
+    constexpr int kXPer = kSkinnyT * kVMaxK / 8 / (kVW * 64);
+    const int c8n = K / 8;
+    u32x4 xv[kXPer];
+#pragma unroll
+    for (int k = 0; k < kXPer; ++k) {
+        const int q = tid + k * kVW * 64, t = q / c8n, c8 = (q % c8n) * 8;
+        xv[k] = q < kSkinnyT * c8n && t < T ? *reinterpret_cast<const u32x4*>(a.x + size_t(t) * K + c8)
+                                           : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < kVTab) tab[te * 32 + tc] = tw;
+#pragma unroll
+    for (int k = 0; k < kXPer; ++k) {
+        const int q = tid + k * kVW * 64, t = q / c8n, c8 = (q % c8n) * 8;
+        if (q < kSkinnyT * c8n) *reinterpret_cast<u32x4*>(&xs[t][c8]) = xv[k];
+    }
+    __syncthreads();
+
+    // ---- products.  Lane column n: token n mod 8, component n / 8; its B word for column j
+    // keeps x in the half of its component and zero in the other (byte selectors of v_perm:
+    // 4..7 pick the source word, 12 gives zero)
+    const char* tbase = reinterpret_cast<const char*>(&tab[0]);
+    const uint32_t lb = uint32_t(l & 31) << 2;
+    const int n = l & 15, tok = n & 7;
+    const uint32_t selE = n < 8 ? 0x0C0C0504u : 0x05040C0Cu;  // low half of the word
+    const uint32_t selO = n < 8 ? 0x0C0C0706u : 0x07060C0Cu;  // high half
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kVMaxU; ++u) {
+        if (u < nus) {  // uniform
+            const int jb = 32 * u0 + 8 * (g * nus + u);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 A, B;
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    A[p] = *reinterpret_cast<const uint32_t*>(tbase + vq2_addr(cw[u], 16 * s + 4 * p, lb));
+                const u32x2 xw = *reinterpret_cast<const u32x2*>(&xs[tok][jb + 4 * s]);
+                B[0] = __builtin_amdgcn_perm(xw[0], 0u, selE);
+                B[1] = __builtin_amdgcn_perm(xw[0], 0u, selO);
+                B[2] = __builtin_amdgcn_perm(xw[1], 0u, selE);
+                B[3] = __builtin_amdgcn_perm(xw[1], 0u, selO);
+                acc = mfma16x16x32(A, B, acc);
+            }
+        }
+    }
+    red[w][l] = acc;
+    __syncthreads();
+
+    // ---- epilogue: output (pair ei, column en) is register ei mod 4 of lane 16 (ei / 4) + en;
+    // sum the 16 slices in order, scale in FP32, round once
+    if (tid < 256) {
+        const int el = 16 * (ei >> 2) + en, eq = ei & 3;
+        float v = 0.f;
+#pragma unroll
+        for (int s = 0; s < kVW; ++s) v += red[s][el][eq];
+        const int t = en & 7;
+        if (t < T) a.y[size_t(t) * N + erow] = uint16_t(f2h(v * h2f(esc)));
+    }
+}
+
+hipError_t launch_vq2_8(const Vq2Args& a, hipStream_t st) {
+    if (!a.codes || !a.cb || !a.sc || !a.x || !a.y || a.N < 32 || a.N % 32 || a.K < 32 || a.K % 32 ||
+        a.K > kVMaxK || a.T < 1 || a.T > kSkinnyT)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_vq2_8, dim3(a.N / 32), dim3(kVW * 64), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace vqmlp

@@ -1216,3 +1216,140 @@ vqmlp_status vqmlp_lut_plan_argmax(const vqmlp_lut_plan* plan, int T, const void
 }
 
 }  // extern "C"
+
+// ==================================================================== 2x16 vector LUT
+namespace {
+
+constexpr uint32_t kKindVq2 = 216;  // packed-header kind of the 2x16 format (16 entries)
+
+vqmlp_status vq2_shape(int N, int K) {
+    if (N <= 0 || K <= 0 || N > (1 << 20) || K > (1 << 20) || N % 32 || K % 32)
+        return fail(VQMLP_ERR_INVALID_ARG, "2x16 matrix %dx%d: both must be multiples of 32", N, K);
+    return VQMLP_OK;
+}
+
+Layout vq2_layout(int N, int K) {
+    Layout L;
+    L.codes_off = kHeaderBytes;
+    L.codes_bytes = size_t(N / 2) * K / 2;  // 4 bits per code, [N/2][K/8] words
+    L.cb_off = align256(L.codes_off + L.codes_bytes);
+    L.cb_bytes = size_t(N / 8) * 16 * 4;
+    L.sc_off = align256(L.cb_off + L.cb_bytes);
+    L.sc_bytes = size_t(N) * 2;
+    L.total = align256(L.sc_off + L.sc_bytes);
+    return L;
+}
+
+}  // namespace
+
+struct vqmlp_vq2_plan {
+    int N, K;
+    const uint8_t* base;
+    Layout L;
+};
+
+extern "C" {
+
+vqmlp_status vqmlp_vq2_packed_bytes(int N, int K, size_t* bytes) {
+    if (!bytes) return fail(VQMLP_ERR_INVALID_ARG, "bytes is NULL");
+    vqmlp_status st = vq2_shape(N, K);
+    if (st) return st;
+    *bytes = vq2_layout(N, K).total;
+    return ok();
+}
+
+vqmlp_status vqmlp_vq2_pack(int N, int K, const uint8_t* codes, const uint16_t* codebook,
+                            const uint16_t* row_scale, void* packed, size_t bytes) {
+    vqmlp_status st = vq2_shape(N, K);
+    if (st) return st;
+    if (!codes || !codebook || !row_scale || !packed)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_vq2_pack: null pointer");
+    const Layout L = vq2_layout(N, K);
+    if (bytes < L.total)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_vq2_pack: buffer holds %zu bytes, needs %zu",
+                    bytes, L.total);
+    const size_t nc = size_t(N / 2) * K;
+    for (size_t i = 0; i < nc; ++i)
+        if (codes[i] > 15)
+            return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_vq2_pack: code %u > 15 at %zu", codes[i], i);
+    uint8_t* out = static_cast<uint8_t*>(packed);
+    memset(out, 0, L.total);
+    PackedHeader h = header_of(N, K, kKindVq2, 16, L);
+    memcpy(out, &h, sizeof h);
+    uint32_t* words = reinterpret_cast<uint32_t*>(out + L.codes_off);
+    for (size_t i = 0; i < nc; ++i) words[i / 8] |= uint32_t(codes[i]) << (4 * (i % 8));
+    memcpy(out + L.cb_off, codebook, L.cb_bytes);
+    memcpy(out + L.sc_off, row_scale, L.sc_bytes);
+    return ok();
+}
+
+vqmlp_status vqmlp_vq2_unpack(int N, int K, const void* packed, size_t bytes, uint8_t* codes,
+                              uint16_t* codebook, uint16_t* row_scale) {
+    vqmlp_status st = vq2_shape(N, K);
+    if (st) return st;
+    if (!packed || !codes || !codebook || !row_scale)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_vq2_unpack: null pointer");
+    const Layout L = vq2_layout(N, K);
+    if (bytes < L.total)
+        return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_vq2_unpack: buffer holds %zu bytes, needs %zu",
+                    bytes, L.total);
+    const uint8_t* in = static_cast<const uint8_t*>(packed);
+    PackedHeader h;
+    memcpy(&h, in, sizeof h);
+    if ((st = check_header(h, N, K, kKindVq2, 16, L, "vqmlp_vq2_unpack"))) return st;
+    const uint32_t* words = reinterpret_cast<const uint32_t*>(in + L.codes_off);
+    const size_t nc = size_t(N / 2) * K;
+    for (size_t i = 0; i < nc; ++i) codes[i] = uint8_t((words[i / 8] >> (4 * (i % 8))) & 15u);
+    memcpy(codebook, in + L.cb_off, L.cb_bytes);
+    memcpy(row_scale, in + L.sc_off, L.sc_bytes);
+    return ok();
+}
+
+vqmlp_status vqmlp_vq2_create(int N, int K, const void* packed, vqmlp_vq2_plan** out) {
+    if (!out) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_vq2_create: null pointer");
+    *out = nullptr;
+    vqmlp_status st = vq2_shape(N, K);
+    if (st) return st;
+    if (K > kVq2MaxK)
+        return fail(VQMLP_ERR_UNSUPPORTED, "2x16 projection: K=%d above %d", K, kVq2MaxK);
+    if (!packed) return fail(VQMLP_ERR_INVALID_ARG, "2x16 projection: null packed buffer");
+    if ((st = check_device())) return st;
+    const Layout L = vq2_layout(N, K);
+    PackedHeader h;
+    if ((st = read_device_header(packed, &h, "vq2"))) return st;
+    if ((st = check_header(h, N, K, kKindVq2, 16, L, "vq2"))) return st;
+    vqmlp_vq2_plan* p = new (std::nothrow) vqmlp_vq2_plan{N, K, static_cast<const uint8_t*>(packed), L};
+    if (!p) return fail(VQMLP_ERR_INVALID_ARG, "out of host memory");
+    *out = p;
+    return ok();
+}
+
+vqmlp_status vqmlp_vq2_destroy(vqmlp_vq2_plan* plan) {
+    delete plan;
+    return ok();
+}
+
+vqmlp_status vqmlp_vq2_plan_forward(const vqmlp_vq2_plan* plan, int T, const void* x, void* y,
+                                    void* stream) {
+    if (!plan) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_vq2_plan_forward: null plan");
+    if (T < 0 || T > kSkinnyT)
+        return fail(VQMLP_ERR_UNSUPPORTED, "the 2x16 projection takes T <= %d (T=%d)", kSkinnyT, T);
+    if (T == 0) return ok();
+    if (!x || !y) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_vq2_plan_forward: null x or y");
+    if (!aligned(x, 16)) return fail(VQMLP_ERR_INVALID_ARG, "x must be 16-byte aligned");
+    const vqmlp_vq2_plan& p = *plan;
+    Vq2Args a;
+    a.codes = reinterpret_cast<const uint32_t*>(p.base + p.L.codes_off);
+    a.cb = reinterpret_cast<const uint32_t*>(p.base + p.L.cb_off);
+    a.sc = reinterpret_cast<const uint16_t*>(p.base + p.L.sc_off);
+    a.x = static_cast<const uint16_t*>(x);
+    a.y = static_cast<uint16_t*>(y);
+    a.N = p.N;
+    a.K = p.K;
+    a.T = T;
+    const hipError_t e = launch_vq2_8(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "2x16 projection");
+    return ok();
+}
+
+}  // extern "C"

@@ -64,6 +64,12 @@ def lib():
             "vqmlp_lut_destroy": [P],
             "vqmlp_lut_plan_forward": [P, I, P, P, P, S, P],
             "vqmlp_lut_plan_argmax": [P, I, P, P, P, P, S, P],
+            "vqmlp_vq2_packed_bytes": [I, I, C.POINTER(S)],
+            "vqmlp_vq2_pack": [I, I, P, P, P, P, S],
+            "vqmlp_vq2_unpack": [I, I, P, S, P, P, P],
+            "vqmlp_vq2_create": [I, I, P, C.POINTER(P)],
+            "vqmlp_vq2_destroy": [P],
+            "vqmlp_vq2_plan_forward": [P, I, P, P, P],
         }
         for name, args in sigs.items():
             f = getattr(L, name)
@@ -155,6 +161,33 @@ def lut_unpack(bits: int, N: int, K: int, packed):
 
 
 # ------------------------------------------------------------------ device side (torch)
+
+
+def vq2_packed_bytes(N: int, K: int) -> int:
+    n = C.c_size_t()
+    _check(lib().vqmlp_vq2_packed_bytes(N, K, C.byref(n)))
+    return n.value
+
+
+def vq2_pack(codes, cb, sc) -> np.ndarray:
+    """2x16 matrix: codes uint8 [N/2, K] (0..15), cb [N/8, 16, 2] and sc [N] binary16."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    cb, sc = _u16(cb), _u16(sc)
+    N, K = sc.shape[0], codes.shape[1]
+    out = np.empty(vq2_packed_bytes(N, K), np.uint8)
+    _check(lib().vqmlp_vq2_pack(N, K, _np_ptr(codes), _np_ptr(cb), _np_ptr(sc), _np_ptr(out),
+                                out.size))
+    return out
+
+
+def vq2_unpack(N: int, K: int, packed):
+    packed = np.ascontiguousarray(packed, np.uint8)
+    codes = np.empty((N // 2, K), np.uint8)
+    cb = np.empty((N // 8, 16, 2), np.uint16)
+    sc = np.empty(N, np.uint16)
+    _check(lib().vqmlp_vq2_unpack(N, K, _np_ptr(packed), packed.size, _np_ptr(codes),
+                                  _np_ptr(cb), _np_ptr(sc)))
+    return codes, cb, sc
 
 
 def to_device(a, device="cuda"):
@@ -318,3 +351,33 @@ class LUTProjection:
         if getattr(self, "_plan", None) and _lib is not None:
             _lib.vqmlp_lut_destroy(self._plan)
             self._plan = None
+
+
+class VQ2Projection:
+    """Device-resident 2x16 vector-LUT projection for T <= 8 tokens (x used as given)."""
+
+    def __init__(self, N, K, packed):
+        self.N, self.K, self.packed = N, K, packed
+        self._plan = C.c_void_p()
+        _check(lib().vqmlp_vq2_create(N, K, _dptr(packed), C.byref(self._plan)))
+
+    @classmethod
+    def from_matrix(cls, m, device="cuda"):
+        """Pack a ``synth.VQ2Matrix`` on the host and upload it."""
+        return cls(m.N, m.K, to_device(vq2_pack(m.codes, m.cb, m.sc), device))
+
+    def forward(self, x, y=None, stream=None):
+        """x: [T, K] binary16 device tensor (T <= 8) -> y [T, N] (same dtype)."""
+        import torch
+
+        if y is None:
+            y = torch.empty((x.shape[0], self.N), dtype=x.dtype, device=x.device)
+        _check(lib().vqmlp_vq2_plan_forward(self._plan, x.shape[0], _dptr(x), _dptr(y),
+                                            _stream(stream)))
+        return y
+
+    def __del__(self):
+        if getattr(self, "_plan", None) and _lib is not None:
+            _lib.vqmlp_vq2_destroy(self._plan)
+            self._plan = None
+

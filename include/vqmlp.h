@@ -194,6 +194,41 @@ vqmlp_status vqmlp_lut_plan_argmax(const vqmlp_lut_plan *plan, int T, const void
                                    int32_t *index, float *value, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------------------ 2x16 vector LUT
+ * The two-bit vector lookup table "2x16" of the previous packages' MLP (model card, section
+ * "Release 0.2: three-bit MLP, token-mixer rotations, distilled weights", format table): 16
+ * two-component centroids per group of 8 output rows, one four-bit index per pair of output
+ * channels, per-channel scales.  W[r][j] = cb[r/8][code[r/2][j]][r%2] * sc[r], the conventions
+ * of the three-bit form with 16 entries.  N and K multiples of 32.
+ *
+ * vqmlp_vq2_packed_bytes: size of the packed buffer (header, codes [N/2][K/8] words with code j
+ * at bits 4 (j % 8) of word j / 8, centroids [N/8][16] words (component 0 in the low half), row
+ * scales [N]; sections 256-byte aligned).
+ * vqmlp_vq2_pack / vqmlp_vq2_unpack: HOST to HOST; codes [N/2][K] uint8 (0..15, INVALID_ARG
+ * above), codebook [N/8][16][2] binary16 bits, row_scale [N] binary16 bits; unpack validates
+ * the header first. */
+vqmlp_status vqmlp_vq2_packed_bytes(int N, int K, size_t *bytes);
+vqmlp_status vqmlp_vq2_pack(int N, int K, const uint8_t *codes, const uint16_t *codebook,
+                            const uint16_t *row_scale, void *packed, size_t packed_bytes);
+vqmlp_status vqmlp_vq2_unpack(int N, int K, const void *packed, size_t packed_bytes,
+                              uint8_t *codes, uint16_t *codebook, uint16_t *row_scale);
+
+/* Projection plan at T <= 8 tokens: y[t][r] = sum_j W[r][j] x[t][j] (x used as given: an input
+ * scale or rotation is the caller's), FP32 accumulation, one rounding to binary16.
+ * vqmlp_vq2_create: packed is a DEVICE buffer written by vqmlp_vq2_pack (256-byte aligned; its
+ * header is read once here, so create synchronises); the plan keeps the pointer only.  Errors:
+ * VQMLP_ERR_INVALID_ARG for a bad shape, null or mismatched buffer; VQMLP_ERR_UNSUPPORTED for
+ * K > 5120 or a device other than gfx950.
+ * vqmlp_vq2_plan_forward: x DEVICE binary16 [T][K] (16-byte aligned), y DEVICE binary16 [T][N];
+ * no workspace, no allocation, no host-device synchronisation (stream: a hipStream_t, NULL =
+ * default).  Errors: VQMLP_ERR_UNSUPPORTED for T > 8; VQMLP_ERR_INVALID_ARG for null or
+ * unaligned pointers; VQMLP_ERR_HIP if the launch fails.  T == 0 is a no-op. */
+typedef struct vqmlp_vq2_plan vqmlp_vq2_plan;
+vqmlp_status vqmlp_vq2_create(int N, int K, const void *packed, vqmlp_vq2_plan **out);
+vqmlp_status vqmlp_vq2_destroy(vqmlp_vq2_plan *plan);
+vqmlp_status vqmlp_vq2_plan_forward(const vqmlp_vq2_plan *plan, int T, const void *x, void *y,
+                                    void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -438,3 +438,39 @@ def test_lut_errors_on_device(vq, torch_dev):
     y1, y2 = proj.forward(x), proj.forward_stateless(x)
     torch_dev.cuda.synchronize()
     assert torch_dev.equal(y1, y2)
+
+
+VQ2_CASES = [  # N, K, T
+    (32, 32, 1),        # one tile, one 32-column unit: 15 of 16 slices empty
+    (64, 96, 5),        # ragged slices
+    (160, 320, 8),
+    (5120, 5120, 8),    # the previous format's down-projection output width
+    (17408, 5120, 7),   # gate / up shape
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("N,K,T", VQ2_CASES)
+def test_vq2_projection(vq, oracle_mod, torch_dev, N, K, T):
+    """2x16 vector-LUT projection at T <= 8 against the oracle's FP64 product, every output."""
+    rng = np.random.default_rng(N + 3 * K + T)
+    m = synth.vq2_matrix(rng, N, K)
+    x = synth.activations(rng, T, K, outliers=True)
+    _say("2x16 projection N=%d K=%d T=%d" % (N, K, T))
+    proj = vq.VQ2Projection.from_matrix(m)
+    y = _f64(proj.forward(vq.to_device(x)))
+    torch_dev.cuda.synchronize()
+    ref = oracle_mod.vq2_matmul(m.codes, m.cb, m.sc, x)
+    assert _report("2x16 %dx%d T=%d" % (N, K, T), y, ref) <= MLP_TOL
+
+
+@pytest.mark.gpu
+def test_vq2_projection_limits(vq, torch_dev):
+    m = synth.vq2_matrix(np.random.default_rng(9), 64, 64)
+    proj = vq.VQ2Projection.from_matrix(m)
+    x = vq.to_device(np.zeros((9, 64), np.float16))
+    with pytest.raises(vq.VqmlpError, match="T <= 8"):
+        proj.forward(x)
+    big = synth.vq2_matrix(np.random.default_rng(10), 32, 5152)
+    with pytest.raises(vq.VqmlpError, match="above 5120"):
+        vq.VQ2Projection.from_matrix(big)

@@ -174,3 +174,29 @@ def test_lut_argmax_rejects_null_plan(vq):
     L = vq.lib()
     assert L.vqmlp_lut_plan_argmax(None, 1, None, None, None, None, 0, None) == vq.ERR_INVALID_ARG
     assert b"null plan" in L.vqmlp_last_error()
+
+
+def test_vq2_pack_round_trip(vq):
+    m = synth.vq2_matrix(np.random.default_rng(3), 64, 96)
+    packed = vq.vq2_pack(m.codes, m.cb, m.sc)
+    assert packed.size == vq.vq2_packed_bytes(64, 96) and packed.size % 256 == 0
+    codes, cb, sc = vq.vq2_unpack(64, 96, packed)
+    assert np.array_equal(codes, m.codes)
+    assert np.array_equal(cb, m.cb.view(np.uint16))
+    assert np.array_equal(sc, m.sc.view(np.uint16))
+
+
+def test_vq2_pack_rejects_bad_codes_and_shapes(vq):
+    m = synth.vq2_matrix(np.random.default_rng(4), 32, 32)
+    codes = m.codes.copy()
+    codes[3, 5] = 16
+    with pytest.raises(vq.VqmlpError, match="code 16 > 15"):
+        vq.vq2_pack(codes, m.cb, m.sc)
+    with pytest.raises(vq.VqmlpError, match="multiples of 32"):
+        vq.vq2_packed_bytes(40, 32)
+    # a scalar-LUT buffer of the same shape is refused by its header kind
+    lut = vq.lut_pack(2, np.zeros((64, 64), np.uint8), np.zeros((8, 4), np.float16),
+                      np.ones(64, np.float16))
+    lut = np.concatenate([lut, np.zeros(vq.vq2_packed_bytes(64, 64), np.uint8)])
+    with pytest.raises(vq.VqmlpError, match="packed kind"):
+        vq.vq2_unpack(64, 64, lut)
