@@ -283,12 +283,15 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* p
     for (int it = 0; blk < nb; ++it, blk += G) {
         const int par = it & 1;
         tab[par][trt][te * 32 + tc] = tv;
-        // the next block's words, requested now (the last block repeats itself)
-        const int nxt = blk + G < nb ? blk + G : blk;
-        const uint32_t tvn = load_tab(nxt);
-        const uint16_t escn = a.sc[nxt * 32 + erw];
-        uint32_t cn[kRunV * 4];
-        load_codes(nxt, cn);
+        // the next block's words, requested now (none after the workgroup's last block)
+        const bool more = blk + G < nb;  // uniform
+        uint32_t tvn = 0, cn[kRunV * 4];
+        uint16_t escn = 0;
+        if (more) {
+            tvn = load_tab(blk + G);
+            escn = a.sc[(blk + G) * 32 + erw];
+            load_codes(blk + G, cn);
+        }
         __syncthreads();  // tables of this block written; red of the last block consumed
         const uint32_t lb = (uint32_t(l & 31) << 2) | uint32_t(((par * 2 + rt) * kTabDw) * 4);
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -325,10 +328,12 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* p
                 bidx = blk * 32 + erl;
             }
         }
+        if (more) {
 #pragma unroll
-        for (int k = 0; k < kRunV * 4; ++k) cw[k] = cn[k];
-        tv = tvn;
-        esc = escn;
+            for (int k = 0; k < kRunV * 4; ++k) cw[k] = cn[k];
+            tv = tvn;
+            esc = escn;
+        }
     }
     // merge the 32 threads of each token (2 row tiles x 4 lane groups x 4 regs): larger value,
     // then lower row

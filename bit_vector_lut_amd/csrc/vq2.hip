@@ -34,105 +34,150 @@ __device__ __forceinline__ uint32_t vq2_addr(uint32_t d, uint32_t sh, uint32_t l
 
 }  // namespace
 
+// Persistent: workgroup b takes the tiles b, b + G, ...; x is staged once, and while a tile's
+// lookups run, the next tile's code runs, centroid words and row scales are already in flight
+// (centroid tables double-buffered in LDS).
 __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
-    constexpr int kOffX = kVTab * 4, kOffRed = kOffX + kSkinnyT * kVXRow * 2;
+    constexpr int kOffX = 2 * kVTab * 4, kOffRed = kOffX + kSkinnyT * kVXRow * 2;
     __shared__ __attribute__((aligned(16))) unsigned char lds[kOffRed + kVW * 64 * 16];
-    auto& tab = *reinterpret_cast<uint32_t (*)[kVTab]>(lds);
+    auto& tab = *reinterpret_cast<uint32_t (*)[2][kVTab]>(lds);
     auto& xs = *reinterpret_cast<uint16_t (*)[kSkinnyT][kVXRow]>(lds + kOffX);
     auto& red = *reinterpret_cast<f32x4 (*)[kVW][64]>(lds + kOffRed);
 
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int K = a.K, T = a.T, N = a.N;
-    const int pair0 = blockIdx.x * 16;
+    const int K = a.K, T = a.T, N = a.N, ntile = a.N / 32, G = gridDim.x;
     const int nu = K / 32, u0 = w * nu / kVW, nus = (w + 1) * nu / kVW - u0;
 
-    // ---- code run first: kVRunV 16-byte loads whatever nus is; words past the run are unused
-    // and past the last pair row they fall in the codebook section that follows the codes
+    // lane (pair i, group g): kVRunV 16-byte loads of its code run whatever nus is; words past
+    // the run are unused and past the last pair row they fall in the codebook section
     const int i = l & 15, g = l >> 4;
-    const uint32_t* crun = a.codes + size_t(pair0 + i) * (K / 8) + u0 * 4 + g * nus;
-    uint32_t cw[kVRunV * 4];
+    auto load_codes = [&](int b, uint32_t (&c)[kVRunV * 4]) {
+        const uint32_t* crun = a.codes + size_t(b * 16 + i) * (K / 8) + u0 * 4 + g * nus;
 #pragma unroll
-    for (int v = 0; v < kVRunV; ++v) {
-        const u32x4a q = *reinterpret_cast<const u32x4a*>(crun + 4 * v);
+        for (int v = 0; v < kVRunV; ++v) {
+            const u32x4a q = *reinterpret_cast<const u32x4a*>(crun + 4 * v);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cw[4 * v + e] = q[e];
-    }
-    // epilogue thread (pair ei, column en) of the tile: every thread loads a scale (threads
-    // past 256 a duplicate) so that no load sits under a branch
-    const int ei = (tid >> 4) & 15, en = tid & 15;
-    const int erow = 2 * (pair0 + ei) + (en >> 3);
-    const uint16_t esc = a.sc[erow];
-    // centroid words: thread (entry te, bank column tc) for tid < 512, column tc serving pair
-    // row tc mod 16 (group of 4 pairs = 8 output rows)
+            for (int e = 0; e < 4; ++e) c[4 * v + e] = q[e];
+        }
+    };
+    // centroid words: thread (entry te, bank column tc), column tc serving pair row tc mod 16
+    // (a group of 4 pairs = 8 output rows); stored by threads below kVTab
     const int te = (tid >> 5) & 15, tc = tid & 31;
-    const uint32_t tw = a.cb[size_t((pair0 + (tc & 15)) >> 2) * 16 + te];
+    auto load_tw = [&](int b) { return a.cb[size_t((b * 16 + (tc & 15)) >> 2) * 16 + te]; };
+    // epilogue thread (pair ei, column en): every thread loads a scale (past 256 a duplicate), so
+    // no load sits under a branch
+    const int ei = (tid >> 4) & 15, en = tid & 15;
+    auto load_sc = [&](int b) { return a.sc[2 * (b * 16 + ei) + (en >> 3)]; };
+
+    int blk = blockIdx.x;
+    uint32_t tw = load_tw(blk);
+    uint16_t esc = load_sc(blk);
+    uint32_t cw[kVRunV * 4];
+    load_codes(blk, cw);
     // x rows (past T zero), all loads before the stores
     constexpr int kXPer = kSkinnyT * kVMaxK / 8 / (kVW * 64);
     const int c8n = K / 8;
-    u32x4 xv[kXPer];
+    {
+        u32x4 xv[kXPer];
 #pragma unroll
-    for (int k = 0; k < kXPer; ++k) {
-        const int q = tid + k * kVW * 64, t = q / c8n, c8 = (q % c8n) * 8;
-        xv[k] = q < kSkinnyT * c8n && t < T ? *reinterpret_cast<const u32x4*>(a.x + size_t(t) * K + c8)
-                                           : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < kVTab) tab[te * 32 + tc] = tw;
+        for (int k = 0; k < kXPer; ++k) {
+            const int q = tid + k * kVW * 64, t = q / c8n, c8 = (q % c8n) * 8;
+            xv[k] = q < kSkinnyT * c8n && t < T ? *reinterpret_cast<const u32x4*>(a.x + size_t(t) * K + c8)
+                                               : u32x4{0u, 0u, 0u, 0u};
+        }
 #pragma unroll
-    for (int k = 0; k < kXPer; ++k) {
-        const int q = tid + k * kVW * 64, t = q / c8n, c8 = (q % c8n) * 8;
-        if (q < kSkinnyT * c8n) *reinterpret_cast<u32x4*>(&xs[t][c8]) = xv[k];
+        for (int k = 0; k < kXPer; ++k) {
+            const int q = tid + k * kVW * 64, t = q / c8n, c8 = (q % c8n) * 8;
+            if (q < kSkinnyT * c8n) *reinterpret_cast<u32x4*>(&xs[t][c8]) = xv[k];
+        }
     }
-    __syncthreads();
 
-    // ---- products.  Lane column n: token n mod 8, component n / 8; its B word for column j
-    // keeps x in the half of its component and zero in the other (byte selectors of v_perm:
-    // 4..7 pick the source word, 12 gives zero)
-    const char* tbase = reinterpret_cast<const char*>(&tab[0]);
-    const uint32_t lb = uint32_t(l & 31) << 2;
+    // Lane column n: token n mod 8, component n / 8; its B word for column j keeps x in the half
+    // of its component and zero in the other (v_perm byte selectors: 4..7 pick the source word,
+    // 12 gives zero)
+    const char* tb0 = reinterpret_cast<const char*>(&tab[0][0]);
     const int n = l & 15, tok = n & 7;
     const uint32_t selE = n < 8 ? 0x0C0C0504u : 0x05040C0Cu;  // low half of the word
     const uint32_t selO = n < 8 ? 0x0C0C0706u : 0x07060C0Cu;  // high half
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; blk < ntile; ++it, blk += G) {
+        const int par = it & 1;
+        if (tid < kVTab) tab[par][te * 32 + tc] = tw;
+        // the next tile's words, requested now (none after the workgroup's last tile)
+        const bool more = blk + G < ntile;  // uniform
+        uint32_t twn = 0, cn[kVRunV * 4];
+        uint16_t escn = 0;
+        if (more) {
+            twn = load_tw(blk + G);
+            escn = load_sc(blk + G);
+            load_codes(blk + G, cn);
+        }
+        __syncthreads();  // this tile's table (and x) written; red of the last tile consumed
+        const uint32_t lb = (uint32_t(l & 31) << 2) | uint32_t(par * kVTab * 4);
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < kVMaxU; ++u) {
-        if (u < nus) {  // uniform
-            const int jb = 32 * u0 + 8 * (g * nus + u);
+        for (int u = 0; u < kVMaxU; ++u) {
+            if (u < nus) {  // uniform
+                const int jb = 32 * u0 + 8 * (g * nus + u);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                u32x4 A, B;
+                for (int s = 0; s < 2; ++s) {
+                    u32x4 A, B;
 #pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    A[p] = *reinterpret_cast<const uint32_t*>(tbase + vq2_addr(cw[u], 16 * s + 4 * p, lb));
-                const u32x2 xw = *reinterpret_cast<const u32x2*>(&xs[tok][jb + 4 * s]);
-                B[0] = __builtin_amdgcn_perm(xw[0], 0u, selE);
-                B[1] = __builtin_amdgcn_perm(xw[0], 0u, selO);
-                B[2] = __builtin_amdgcn_perm(xw[1], 0u, selE);
-                B[3] = __builtin_amdgcn_perm(xw[1], 0u, selO);
-                acc = mfma16x16x32(A, B, acc);
+                    for (int p = 0; p < 4; ++p)
+                        A[p] = *reinterpret_cast<const uint32_t*>(tb0 + vq2_addr(cw[u], 16 * s + 4 * p, lb));
+                    const u32x2 xw = *reinterpret_cast<const u32x2*>(&xs[tok][jb + 4 * s]);
+                    B[0] = __builtin_amdgcn_perm(xw[0], 0u, selE);
+                    B[1] = __builtin_amdgcn_perm(xw[0], 0u, selO);
+                    B[2] = __builtin_amdgcn_perm(xw[1], 0u, selE);
+                    B[3] = __builtin_amdgcn_perm(xw[1], 0u, selO);
+                    acc = mfma16x16x32(A, B, acc);
+                }
             }
         }
-    }
-    red[w][l] = acc;
-    __syncthreads();
-
-    // ---- epilogue: output (pair ei, column en) is register ei mod 4 of lane 16 (ei / 4) + en;
-    // sum the 16 slices in order, scale in FP32, round once
-    if (tid < 256) {
-        const int el = 16 * (ei >> 2) + en, eq = ei & 3;
-        float v = 0.f;
+        red[w][l] = acc;
+        __syncthreads();
+        // output (pair ei, column en) is register ei mod 4 of lane 16 (ei / 4) + en: sum the 16
+        // slices in order, scale in FP32, round once
+        if (tid < 256) {
+            const int el = 16 * (ei >> 2) + en, eq = ei & 3;
+            float v = 0.f;
 #pragma unroll
-        for (int s = 0; s < kVW; ++s) v += red[s][el][eq];
-        const int t = en & 7;
-        if (t < T) a.y[size_t(t) * N + erow] = uint16_t(f2h(v * h2f(esc)));
+            for (int s = 0; s < kVW; ++s) v += red[s][el][eq];
+            const int t = en & 7;
+            if (t < T) a.y[size_t(t) * N + 2 * (blk * 16 + ei) + (en >> 3)] = uint16_t(f2h(v * h2f(esc)));
+        }
+        if (more) {
+#pragma unroll
+            for (int k = 0; k < kVRunV * 4; ++k) cw[k] = cn[k];
+            tw = twn;
+            esc = escn;
+        }
     }
 }
+
+namespace {
+// compute units of the current device (cached per device; workgroups of the persistent grid)
+int vq2_cus() {
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int c = 0;
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c < 1)
+            c = 256;
+        cache[dev] = c;
+    }
+    return cache[dev];
+}
+}  // namespace
 
 hipError_t launch_vq2_8(const Vq2Args& a, hipStream_t st) {
     if (!a.codes || !a.cb || !a.sc || !a.x || !a.y || a.N < 32 || a.N % 32 || a.K < 32 || a.K % 32 ||
         a.K > kVMaxK || a.T < 1 || a.T > kSkinnyT)
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_vq2_8, dim3(a.N / 32), dim3(kVW * 64), 0, st, a);
+    const int ntile = a.N / 32, cus = vq2_cus();
+    const int G = ntile < cus ? ntile : cus;
+    hipLaunchKernelGGL(k_vq2_8, dim3(G), dim3(kVW * 64), 0, st, a);
     return hipGetLastError();
 }
 
