@@ -474,3 +474,49 @@ def test_vq2_projection_limits(vq, torch_dev):
     big = synth.vq2_matrix(np.random.default_rng(10), 32, 5152)
     with pytest.raises(vq.VqmlpError, match="above 5120"):
         vq.VQ2Projection.from_matrix(big)
+
+
+@pytest.mark.gpu
+def test_vq2_and_argmax_t0_noop(vq, torch_dev):
+    """T == 0 launches nothing and leaves the outputs untouched."""
+    torch = torch_dev
+    m = synth.vq2_matrix(np.random.default_rng(21), 64, 64)
+    proj = vq.VQ2Projection.from_matrix(m)
+    y = torch.full((0, 64), 7, dtype=torch.int16, device="cuda")
+    proj.forward(vq.to_device(np.zeros((0, 64), np.float16)), y)
+    head = vq.LUTProjection.from_proj(synth.lut_projection(np.random.default_rng(22), 4, 64, 64, 0, 0))
+    idx, val = head.argmax(vq.to_device(np.zeros((0, 64), np.float16)), head.workspace(8))
+    torch.cuda.synchronize()
+    assert idx.numel() == 0 and val.numel() == 0
+
+
+@pytest.mark.gpu
+def test_vq2_and_argmax_graph_replays_match_eager(vq, torch_dev):
+    """The 2x16 projection and the argmax head captured in one HIP graph: every replay (with
+    eager work and synchronisations between them) reproduces the eager results bit for bit."""
+    torch = torch_dev
+    rng = np.random.default_rng(23)
+    proj = vq.VQ2Projection.from_matrix(synth.vq2_matrix(rng, 1024, 512))
+    head = vq.LUTProjection.from_proj(synth.lut_projection(rng, 4, 2048, 512, 0, 0))
+    x = vq.to_device(synth.activations(rng, 8, 512, True))
+    ws = head.workspace(8)
+    st = torch.cuda.Stream()
+    y = torch.empty((8, 1024), dtype=x.dtype, device="cuda")
+    with torch.cuda.stream(st):
+        proj.forward(x, y, stream=st)
+        idx, val = head.argmax(x, ws, stream=st)
+    st.synchronize()
+    ref = (y.clone(), idx.clone(), val.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=st):
+        proj.forward(x, y, stream=st)
+        gi, gv = head.argmax(x, ws, stream=st)
+    for rep in range(3):
+        y.zero_()
+        gi.fill_(-1)
+        gv.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref[0]), "replay %d: 2x16 output" % rep
+        assert torch.equal(gi, ref[1]) and torch.equal(gv, ref[2]), "replay %d: argmax" % rep
