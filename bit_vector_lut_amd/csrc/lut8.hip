@@ -11,13 +11,16 @@
 // binary16) is staged once per workgroup in LDS, and the 16 waves' partial sums meet in LDS.
 //
 // Product: v_mfma_f32_16x16x32_f16 with A = the decoded weights of 16 rows and B = x~ (column n =
-// token n, zero for n >= 8).  A wave's K slice of nus 64-column units is cut into four runs of
+// token n mod 8; columns 8..15 repeat tokens 0..7 and their outputs are never read).  A wave's K slice of nus 64-column units is cut into four runs of
 // 16 nus columns, one per lane group g = l / 16; MFMA step (u, s) takes columns 16 u + 8 s + 0 .. 7
 // of each group's run in both operands, so a lane's codes for the whole slice are one contiguous
 // run of 16 nus codes in the row-major packing (nus or 2 nus consecutive words).  Lookups go to tables replicated over the 32 bank
 // columns (column c serves the lanes with l % 32 == c, whose row lies in group (c % 16) / 8):
 // 2-bit codes are looked up in pairs (16 entries, each the two binary16 weights of a code pair,
-// so the 32-bit read is the operand word), 4-bit codes one by one (16 entries).
+// so the 32-bit read is the operand word), 4-bit codes one by one (16 entries, 16-bit reads).
+//
+// The output head (k_lut8_argmax) runs the same product persistently over 32-row blocks and keeps a
+// running per-token argmax instead of writing logits.
 #include "device.h"
 #include "internal.h"
 
@@ -33,8 +36,7 @@ constexpr int kTabDw = 16 * 32;         // one table: 16 entries x 32 bank colum
 
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
 // The table words of two 4-bit codes (bits sh..sh+3 and sh+4..sh+7 of d) as one binary16 pair:
-// each entry is read with a 16-bit LDS load straight into its half of the result, so the pair
-// costs two field extracts and two address merges and no packing.
+// two 16-bit LDS reads joined by one byte permute (two field extracts, two address merges).
 // LDS byte address of the entry that bits sh..sh+3 of d select, in the table column lb: a field
 // extract and a shift-or (the compiler would otherwise emit shift, mask and add).
 __device__ __forceinline__ uint32_t lut_addr(uint32_t d, uint32_t sh, uint32_t lb) {
