@@ -57,6 +57,7 @@ def lib():
         L.orc_lut_weight.argtypes = [I, I, I, P, P, P, P]
         L.orc_lut_forward.argtypes = [I] * 6 + [P] * 3 + [P] * 5 + [P, P]
         L.orc_num_threads.restype = I
+        L.orc_set_num_threads.argtypes = [I]
         _lib = L
     return _lib
 
@@ -238,6 +239,11 @@ def vq2_matmul(codes, cb, sc, xin) -> np.ndarray:
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP loops (for timing it on one core)."""
+    lib().orc_set_num_threads(int(n))
 
 
 if __name__ == "__main__":

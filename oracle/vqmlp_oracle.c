@@ -156,21 +156,35 @@ int orc_vq3_weight(int N, int K, const uint8_t *codes, const uint16_t *cb, const
     return 0;
 }
 
-/* out[t][r] = sum_j W[r][j] * in[t][j], W decoded on the fly, j in index order. */
-static void orc_vq3_apply(int T, int N, int K, const uint8_t *codes, const uint16_t *cb,
-                          const uint16_t *sc, const double *in, double *out)
+/* out[t][r] = sum_j W[r][j] * in[t][j], j in index order.  Row r of W is decoded once into a
+ * buffer (the definition of W above, entry by entry) and then used for every token: the terms
+ * and their order are those of decoding each weight where it is used. */
+static int orc_vq3_apply(int T, int N, int K, const uint8_t *codes, const uint16_t *cb,
+                         const uint16_t *sc, const double *in, double *out)
 {
-    for (int t = 0; t < T; ++t) {
-        const double *it = in + (size_t)t * K;
-        double *ot = out + (size_t)t * N;
-#pragma omp parallel for schedule(static)
+    int bad = 0;
+#pragma omp parallel reduction(| : bad)
+    {
+        double *wr = malloc(sizeof(double) * (size_t)K);
+        if (!wr)
+            bad = 1;
+#pragma omp for schedule(static)
         for (int r = 0; r < N; ++r) {
-            double acc = 0.0;
+            if (!wr)
+                continue;
             for (int j = 0; j < K; ++j)
-                acc += orc_vq3_w(K, codes, cb, sc, r, j) * it[j];
-            ot[r] = acc;
+                wr[j] = orc_vq3_w(K, codes, cb, sc, r, j);
+            for (int t = 0; t < T; ++t) {
+                const double *it = in + (size_t)t * K;
+                double acc = 0.0;
+                for (int j = 0; j < K; ++j)
+                    acc += wr[j] * it[j];
+                out[(size_t)t * N + r] = acc;
+            }
         }
+        free(wr);
     }
+    return bad;
 }
 
 /* Public form of the product above (used by the dequantisation pins). */
@@ -179,8 +193,7 @@ int orc_vq3_matmul(int T, int N, int K, const uint8_t *codes, const uint16_t *cb
 {
     if (N <= 0 || K <= 0 || N % 8 || T < 0)
         return 1;
-    orc_vq3_apply(T, N, K, codes, cb, sc, in, out);
-    return 0;
+    return orc_vq3_apply(T, N, K, codes, cb, sc, in, out);
 }
 
 /* ---------------------------------------------------------------- the MLP forward */
@@ -221,8 +234,9 @@ int orc_mlp_forward(int T, int H, int I, int bh, int bi,
     if (orc_rotate(T, H, bh, u, sign_h, xt))
         goto done;
     /* 3. gate and up projections */
-    orc_vq3_apply(T, I, H, c_gate, cb_gate, sc_gate, xt, g);
-    orc_vq3_apply(T, I, H, c_up, cb_up, sc_up, xt, v);
+    if (orc_vq3_apply(T, I, H, c_gate, cb_gate, sc_gate, xt, g) ||
+        orc_vq3_apply(T, I, H, c_up, cb_up, sc_up, xt, v))
+        goto done;
     /* 4. gated product */
     for (size_t i = 0; i < (size_t)T * I; ++i)
         a[i] = orc_silu_1(g[i]) * v[i];
@@ -230,7 +244,8 @@ int orc_mlp_forward(int T, int H, int I, int bh, int bi,
     if (orc_rotate(T, I, bi, a, sign_i, at))
         goto done;
     /* 6. down projection */
-    orc_vq3_apply(T, H, I, c_down, cb_down, sc_down, at, y);
+    if (orc_vq3_apply(T, H, I, c_down, cb_down, sc_down, at, y))
+        goto done;
 
     if (xt_out)
         for (size_t i = 0; i < (size_t)T * H; ++i) xt_out[i] = xt[i];
@@ -322,21 +337,36 @@ int orc_lut_forward(int bits, int N, int K, int T, int b, int rank,
                     acc += orc_f16_to_f64(V[(size_t)q * K + j]) * xt[(size_t)t * K + j];
                 z[(size_t)t * rank + q] = acc;
             }
-    for (int t = 0; t < T; ++t) {
-#pragma omp parallel for schedule(static)
+    /* row n of W decoded once, then used for every token (same terms, same order) */
+    int bad = 0;
+#pragma omp parallel reduction(| : bad)
+    {
+        double *wr = malloc(sizeof(double) * (size_t)K);
+        if (!wr)
+            bad = 1;
+#pragma omp for schedule(static)
         for (int n = 0; n < N; ++n) {
-            double acc = 0.0;
+            if (!wr)
+                continue;
             for (int j = 0; j < K; ++j)
-                acc += orc_lut_w(bits, K, codes, lut, sc, n, j) * xt[(size_t)t * K + j];
-            if (use_lr) {
-                double lr = 0.0;
-                for (int q = 0; q < rank; ++q)
-                    lr += orc_f16_to_f64(U[(size_t)n * rank + q]) * z[(size_t)t * rank + q];
-                acc += lr;
+                wr[j] = orc_lut_w(bits, K, codes, lut, sc, n, j);
+            for (int t = 0; t < T; ++t) {
+                double acc = 0.0;
+                for (int j = 0; j < K; ++j)
+                    acc += wr[j] * xt[(size_t)t * K + j];
+                if (use_lr) {
+                    double lr = 0.0;
+                    for (int q = 0; q < rank; ++q)
+                        lr += orc_f16_to_f64(U[(size_t)n * rank + q]) * z[(size_t)t * rank + q];
+                    acc += lr;
+                }
+                y[(size_t)t * N + n] = acc;
             }
-            y[(size_t)t * N + n] = acc;
         }
+        free(wr);
     }
+    if (bad)
+        goto done;
     if (xt_out)
         for (size_t i = 0; i < (size_t)T * K; ++i) xt_out[i] = xt[i];
     rc = 0;
@@ -345,6 +375,18 @@ done:
     free(xt);
     free(z);
     return rc;
+}
+
+/* Thread count of the OpenMP loops (for timing the oracle on one core and on all of them). */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
 }
 
 int orc_num_threads(void)
