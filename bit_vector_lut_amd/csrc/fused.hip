@@ -103,11 +103,7 @@ struct Item {
 
 }  // namespace
 
-// PH = false: the whole forward in one launch.  PH = true: one phase per launch (the gate/up
-// items, or the down items), with the operands written by an earlier launch as plain binary16
-// rows (a.xb16 / a.ab16) and a written as plain FP32 (a.act32): the launch boundary orders
-// them, so they are read through the caches with no tags.
-template <int TPW, bool PH>
+template <int TPW>
 __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
     constexpr int D = TPW;  // ring slots: slot t always holds tile t of some item
     // Prefetch distance in tiles.  Code words are requested P tiles before their use, not a whole
@@ -199,9 +195,12 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
         const uint16_t* scb = dn ? a.down.sc : (sm ? a.up.sc : a.gate.sc);
         const uint32_t* scp = reinterpret_cast<const uint32_t*>(
             scb + (sm ? it.t1 : it.t0) * kTileRows + (r32 & ~1));
+        // the sign belongs to rows of I: only a gate/up item's row tile indexes it (a down
+        // item's tiles are rows of H, which may run past I; it reads tile 0 and ignores it)
         const int8_t* sgb = a.sign_i ? a.sign_i : reinterpret_cast<const int8_t*>(a.gate.sc);
+        const int sgt = it.kind == kKindG ? it.t0 : 0;
         const uint32_t* sgp =
-            reinterpret_cast<const uint32_t*>(sgb + it.t0 * kTileRows + (r32 & ~3));
+            reinterpret_cast<const uint32_t*>(sgb + sgt * kTileRows + (r32 & ~3));
         const uint32_t* p = (w == 8 || w == 9) ? scp : (w == 10 ? sgp : cbp);
         return *p;
     };
@@ -388,11 +387,8 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                     u *= esc[eb][1][rl];
                     const float act = g / (1.f + expf(-g)) * u;
                     const uint32_t bits = __builtin_bit_cast(uint32_t, act) ^ esg[eb][rl];
-                    if constexpr (PH)
-                        reinterpret_cast<uint32_t*>(a.act32)[size_t(t) * I + prev.id * kTileRows + rl] = bits;
-                    else
-                        st_relaxed64(a.act + size_t(t) * I + prev.id * kTileRows + rl,
-                                     (uint64_t(tag) << 32) | bits);
+                    st_relaxed64(a.act + size_t(t) * I + prev.id * kTileRows + rl,
+                                 (uint64_t(tag) << 32) | bits);
                 }
                 // One tile of each rotation unit rotates the whole unit once the others' values
                 // are in; which tile is hashed from the unit, so that round-robin assignment does
@@ -402,7 +398,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                 // rotation only ever waits for tiles handed out before it.
                 const int unit = prev.id / tpu;
                 const int owner = a.dyn ? tpu - 1 : int((unit ^ (unit >> 2) ^ (unit >> 5)) % tpu);
-                if (!PH && prev.id % tpu == owner) job = unit;
+                if (prev.id % tpu == owner) job = unit;
             } else {
                 const int o = tid >> 1, hh = tid & 1;  // output o of 512, half of the waves
                 const int mm = o >> 8, e_l = o & 63, e_r = (o >> 6) & 3;
@@ -458,25 +454,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                 // inputs are ready starts while the others still wait.  The operand words carry
                 // the call's tag; a word whose tag is not yet this call's is read again.
                 constexpr int wcols = TPW * kTileCols;
-                if constexpr (PH) {
-                    const int c0 = cur.sl * SWT * kTileCols + w * wcols;
-                    const int K = cur.kind == kKindG ? H : I;
-                    const uint16_t* src = cur.kind == kKindG ? a.xb16 : a.ab16;
-                    constexpr int kPer = kSkinnyT * wcols / 8 / 64;  // 16-byte chunks per lane
-                    u32x4 v[kPer];
-#pragma unroll
-                    for (int k = 0; k < kPer; ++k) {
-                        const int i = l + 64 * k, t = i / (wcols / 8), c8 = (i % (wcols / 8)) * 8;
-                        v[k] = c0 + c8 < K ? *reinterpret_cast<const u32x4*>(src + size_t(t) * K + c0 + c8)
-                                           : u32x4{0u, 0u, 0u, 0u};
-                    }
-#pragma unroll
-                    for (int k = 0; k < kPer; ++k) {
-                        const int i = l + 64 * k;
-                        *reinterpret_cast<u32x4*>(
-                            &bsh[i / (wcols / 8)][w * wcols + (i % (wcols / 8)) * 8]) = v[k];
-                    }
-                } else {
+                {
                     constexpr int kPairs = wcols / 2;                 // pairs per operand row
                     constexpr int kM = (kPairs + 63) / 64;            // pairs per lane and row
                     const int c0 = cur.sl * SWT * kTileCols + w * wcols;
@@ -634,21 +612,16 @@ int fused_tpw(int H) {
     return tpw >= 1 && tpw <= kSkinnyMaxTPW ? tpw : 0;
 }
 
-hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, bool phased, hipStream_t st) {
+hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, hipStream_t st) {
     if (!a.y || !a.ctl || grid < 1 || (a.nsl > 1 && !a.part) || a.fu < kTileRows ||
         a.fu > 64 * kRotVals || a.rc > 64 * kRotVals || a.n_r > kW * 64 || a.T < 1 ||
         a.T > kSkinnyT)
         return hipErrorInvalidValue;
-    if (phased ? (a.n_r != 0 || !a.xb16 || !a.ab16 || !a.act32)
-               : (!a.x || !a.s || !a.xb || !a.act || !a.ab))
-        return hipErrorInvalidValue;
-#define VQ_CASE(TP)                                                                  \
-    if (tpw == TP) {                                                                 \
-        if (phased)                                                                  \
-            hipLaunchKernelGGL((k_fused<TP, true>), dim3(grid), dim3(kW * 64), 0, st, a); \
-        else                                                                         \
-            hipLaunchKernelGGL((k_fused<TP, false>), dim3(grid), dim3(kW * 64), 0, st, a); \
-        return hipGetLastError();                                                    \
+    if (!a.x || !a.s || !a.xb || !a.act || !a.ab) return hipErrorInvalidValue;
+#define VQ_CASE(TP)                                                               \
+    if (tpw == TP) {                                                              \
+        hipLaunchKernelGGL((k_fused<TP>), dim3(grid), dim3(kW * 64), 0, st, a);   \
+        return hipGetLastError();                                                 \
     }
     VQ_CASE(1) VQ_CASE(2) VQ_CASE(3) VQ_CASE(4) VQ_CASE(5)
 #undef VQ_CASE

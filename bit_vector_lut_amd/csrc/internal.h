@@ -35,43 +35,18 @@ struct VQ3View {          // device pointers into one packed buffer
 constexpr int kSkinnyT = 8;            // rows of the matrix-core operand (8 tokens x 2 components)
 constexpr int kSkinnyWaves = 16;       // waves per workgroup, each owning a K range
 constexpr int kSkinnyMaxTPW = 5;       // 64-column tiles per wave held in registers
-enum { kEpiGateUp = 0, kEpiDownFinal = 1, kEpiDownPart = 2 };
 
 // ---- launchers (kernels.hip).  All return hipError_t of the launch.
 hipError_t launch_dequant(const VQ3View& m, float* w, hipStream_t s);
 
 // out[t][.] = R(x . s . sign) for a binary16 or float input, Hadamard blocks of b (a power of
 // two up to 1024; 1 = no rotation).  mode: 0 = FP32 row-major [T][n], 1 = binary16 row-major
-// [T][n], 3 = binary16 row-major [8][n] with the rows past T zero (T <= 8), 4 = as 3 in the
-// unit-major layout below (n a multiple of 64).
+// [T][n].
 hipError_t launch_rotate(int T, int n, int b, const void* x, int x_is_f32, const uint16_t* s,
                          const int8_t* sign, void* out, int mode, hipStream_t st);
-// Unit-major activation operand of the T <= 8 stream-K kernels: the 8 rows x 64 columns of
-// K tile kt are 1 KB at kt * 512 halves, ordered [g][t][s][i] for column 16 s + 4 g + i, so
-// the matrix-core B words of one lane (token t, column group g, all 4 steps) are 32
-// contiguous bytes.
-__host__ __device__ __forceinline__ size_t unit_major_index(int t, int col) {
-    const int kt = col >> 6, w = col & 63, s = w >> 4, g = (w >> 2) & 3, i = w & 3;
-    return size_t(kt) * 512 + ((g * 8 + t) * 4 + s) * 4 + i;
-}
-
-struct SkinnyArgs {
-    VQ3View mat[2];
-    int nmat;              // 2 = gate+up (shared operand), 1 = down
-    int T;
-    int slices;            // K split into this many slices of 8*tpw tiles
-    int tpw;               // tiles per wave
-    int contig;            // 1: each workgroup takes a contiguous item range; 0: round robin
-    const uint16_t* bx;    // activation operand, binary16 [8][K] (rows past T zero)
-    // epilogues
-    const int8_t* sign_i;  // gate+up: sign of the intermediate rotation (NULL = +1)
-    float* a_out;          // gate+up: a [8][I] fp32
-    float* part;           // down, slices > 1: [slices][8][N] fp32
-    uint16_t* y;           // down, slices == 1: y [T][N] binary16
-};
-hipError_t launch_skinny(const SkinnyArgs& a, hipStream_t st);
-hipError_t launch_reduce_down(int T, int N, int slices, const float* part, const uint16_t* sc,
-                              uint16_t* y, hipStream_t st);
+// Reads bytes (a multiple of 16) of buf once, 16-byte loads, contiguous share per workgroup.
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int cus,
+                              hipStream_t st);
 
 // ---- scalar-LUT projection for T <= 8 (K <= kLut8MaxK): y = sc . (W_lut x~) + U z
 constexpr int kLut8MaxK = 5120;
@@ -113,28 +88,6 @@ hipError_t launch_lut8_pre(int T, int K, int hb, const uint16_t* x, const uint16
                            const int8_t* sign, const uint16_t* V, int r, uint16_t* xt, float* zp,
                            hipStream_t st);
 
-// ---- stream-K skinny path (T <= 8): the weight stream cut into equal contiguous ranges
-constexpr int kStreamKMaxQ = 4;  // row-tile pairs one workgroup range may touch
-struct StreamKArgs {
-    VQ3View mat[2];        // gate, up (nmat 2) or down (nmat 1: tiles 2q and 2q + 1)
-    int nmat;
-    int MT, KT, NQ, U;     // row tiles, K tiles, row-tile pairs, units (set by the launcher)
-    int T;
-    const uint16_t* bx;    // activation operand, 8 rows of K in the unit-major layout
-    float* part;           // partial-sum slots [NQ + grid][2][64][4]
-    // gate/up finish: a = SiLU(g) u . sign, rotated per span into the down operand
-    const int8_t* sign_i;  // sign of the intermediate rotation (NULL = +1)
-    int span, bi;          // span rows = max(bi, 32) (set by the launcher); Hadamard block of I
-    float norm_i;          // 1 / sqrt(bi)
-    uint16_t* ab_out;      // rotated a, 8 rows of I, unit-major binary16
-    // down finish
-    uint16_t* y;           // y [T][H] binary16
-};
-int streamk_grid(int nmat, int N, int K, int cus);
-size_t streamk_part_floats(int nmat, int N, int K, int cus);
-// One projection and its finishing pass: nmat 2 writes the rotated a, nmat 1 writes y.
-hipError_t launch_streamk(const StreamKArgs& a, int cus, hipStream_t st);
-
 // ---- fused persistent forward (T <= 8): the whole MLP in one launch
 // Control block (kCtlHdr 32-bit words, zero before the first call): word 0 is the item queue
 // head and word 1 counts finished workgroups (both back to zero after each call), word 2
@@ -160,16 +113,12 @@ struct FusedArgs {
     uint64_t* act;           // [8][I] silu(g) u sign, FP32 bits, tagged
     uint64_t* ab;            // [2][8][I/2] rotated intermediate, binary16 pairs, tagged
     uint64_t* part;          // [nsl][8][H] tagged FP32 partial sums of the down projection
-    // one-phase launches: operands and a written by the launches before, untagged
-    const uint16_t* xb16;    // [8][H] rotated input, binary16, rows past T zero
-    const uint16_t* ab16;    // [8][I] rotated intermediate, binary16
-    float* act32;            // [8][I] silu(g) u sign
     unsigned spin_limit;     // bound of every wait (then the error word records it)
     int dyn;                 // items after the first two rounds from the queue (else round-robin)
 };
 inline size_t fused_ctl_words() { return size_t(kCtlHdr); }
 int fused_tpw(int H);  // tiles per wave of the fused kernel for hidden size H (0 = unsupported)
-hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, bool phased, hipStream_t st);
+hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, hipStream_t st);
 
 // ---- tiled matrix-core path (T > 8): decoders, epilogues, kinds
 enum { kDecVQ3 = 0, kDecLUT2 = 1, kDecLUT4 = 2, kDecDense = 3 };

@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(256) k_rotate(int T, int rows, int n, int b, c
     for (int e = 0; e < NE; ++e) {
         const int col = c0 + 64 * e + l;
         if (col >= n) continue;
-        const size_t idx = mode == 4 ? unit_major_index(t, col) : size_t(t) * n + col;
+        const size_t idx = size_t(t) * n + col;
         const float r = v[e] * norm;
         if (mode == 0)
             static_cast<float*>(out)[idx] = r;
@@ -189,17 +189,7 @@ __global__ void __launch_bounds__(256) k_rotate_v(int T, int rows, int n, int b,
         }
     }
     const size_t idx = size_t(t) * n + col;
-    if (mode == 4) {
-        // 8 consecutive columns: two runs of 4 of the unit-major layout
-#pragma unroll
-        for (int q = 0; q < V / 4; ++q) {
-            u32x2 u;
-#pragma unroll
-            for (int k = 0; k < 2; ++k)
-                u[k] = f2h(v[4 * q + 2 * k] * norm) | (f2h(v[4 * q + 2 * k + 1] * norm) << 16);
-            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + unit_major_index(t, col + 4 * q)) = u;
-        }
-    } else if (mode == 0) {
+    if (mode == 0) {
         f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx);
 #pragma unroll
         for (int q = 0; q < V / 4; ++q)
@@ -219,11 +209,9 @@ __global__ void __launch_bounds__(256) k_rotate_v(int T, int rows, int n, int b,
 
 hipError_t launch_rotate(int T, int n, int b, const void* x, int x_is_f32, const uint16_t* s,
                          const int8_t* sign, void* out, int mode, hipStream_t st) {
-    if ((mode == 3 || mode == 4) && T > kSkinnyT) return hipErrorInvalidValue;
-    if (mode < 0 || mode == 2 || mode > 4 || b < 1 || b > 1024 || (b & (b - 1)) || n % b ||
-        (mode == 4 && n % kTileCols))
+    if (mode < 0 || mode > 1 || b < 1 || b > 1024 || (b & (b - 1)) || n % b)
         return hipErrorInvalidValue;
-    const int rows = mode >= 3 ? kSkinnyT : T;  // modes 3 and 4 write the zero rows past T too
+    const int rows = T;
     const float vnorm = float(1.0 / __builtin_sqrt(double(b)));
     auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
     if (b <= 1024 && n % (64 * (b <= 512 ? 8 : 16)) == 0 && al16(x) && al16(out) && al16(s) &&
@@ -253,6 +241,41 @@ hipError_t launch_rotate(int T, int n, int b, const void* x, int x_is_f32, const
     VQ_ROT(1) VQ_ROT(2) VQ_ROT(4) VQ_ROT(8) VQ_ROT(16)
 #undef VQ_ROT
     return hipErrorInvalidValue;
+}
+
+// Streaming read of a buffer (measurement hook): workgroup b reads its own contiguous share of
+// the 16-byte words, 256 threads x 16 bytes per step, and folds them into a XOR the compiler
+// cannot drop (the word is stored only when the fold hits one particular value).
+__global__ void __launch_bounds__(256) k_stream_read(const u32x4* __restrict__ buf, size_t n16,
+                                                     size_t per_wg, uint32_t* sink) {
+    const size_t b0 = size_t(blockIdx.x) * per_wg;
+    const size_t b1 = b0 + per_wg < n16 ? b0 + per_wg : n16;
+    u32x4 acc = u32x4{0u, 0u, 0u, 0u};
+    size_t i = b0 + threadIdx.x;
+    for (; i + 3 * 256 < b1; i += 4 * 256) {
+        const u32x4 v0 = __builtin_nontemporal_load(buf + i);
+        const u32x4 v1 = __builtin_nontemporal_load(buf + i + 256);
+        const u32x4 v2 = __builtin_nontemporal_load(buf + i + 512);
+        const u32x4 v3 = __builtin_nontemporal_load(buf + i + 768);
+        acc ^= (v0 ^ v1) ^ (v2 ^ v3);
+    }
+    for (; i < b1; i += 256) acc ^= buf[i];
+    const uint32_t r = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (r == 0x9E3779B9u) sink[0] = r;
+}
+
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int cus,
+                              hipStream_t st) {
+    if (!buf || !sink || bytes % 16 || cus < 1) return hipErrorInvalidValue;
+    const size_t n16 = bytes / 16;
+    if (n16 == 0) return hipSuccess;
+    size_t grid = size_t(cus) * 8;  // 8 workgroups of 4 waves per CU
+    size_t per = (n16 + grid - 1) / grid;
+    per = (per + 1023) & ~size_t(1023);  // whole 16 KB steps
+    grid = (n16 + per - 1) / per;
+    hipLaunchKernelGGL(k_stream_read, dim3(unsigned(grid)), dim3(256), 0, st,
+                       static_cast<const u32x4*>(buf), n16, per, sink);
+    return hipGetLastError();
 }
 
 }  // namespace vqmlp

@@ -167,42 +167,6 @@ vqmlp_status check_device() {
     return VQMLP_OK;
 }
 
-// ---------------------------------------------------------------- skinny path geometry
-
-struct SkinnyGeom {
-    int tpw, slices;
-};
-
-// Tiles per wave and slices of the K range for a matrix with K columns on the skinny path.
-// need_single: the epilogue needs whole sums (gate+up), so K must fit in one slice.
-bool skinny_geom(int K, bool need_single, SkinnyGeom* g) {
-    const int KT = K / kTileCols;
-    if (need_single) {
-        const int tpw = (KT + kSkinnyWaves - 1) / kSkinnyWaves;
-        if (tpw > kSkinnyMaxTPW) return false;
-        g->tpw = tpw;
-        g->slices = 1;
-        return true;
-    }
-    // down: K in slices of the waves x tpw tiles (the operand stays in registers);
-    // pick the largest tpw that wastes at most 1/16 of the tile slots past K (long work
-    // items amortise the per-item table build and reduction), else the least wasteful one
-    int best_tpw = 0, least_tpw = 1, least_waste = 1 << 30;
-    for (int tpw = 1; tpw <= kSkinnyMaxTPW; ++tpw) {
-        const int slices = (KT + kSkinnyWaves * tpw - 1) / (kSkinnyWaves * tpw);
-        const int waste = slices * kSkinnyWaves * tpw - KT;
-        if (16 * waste <= slices * kSkinnyWaves * tpw) best_tpw = tpw;
-        if (waste < least_waste) {
-            least_waste = waste;
-            least_tpw = tpw;
-        }
-    }
-    if (!best_tpw) best_tpw = least_tpw;
-    g->tpw = best_tpw;
-    g->slices = (KT + kSkinnyWaves * best_tpw - 1) / (kSkinnyWaves * best_tpw);
-    return true;
-}
-
 }  // namespace
 
 // ==================================================================== plan
@@ -217,10 +181,9 @@ struct vqmlp_plan {
     vqmlp_desc d;
     int bh, bi;
     VQ3View gate, up, down;
-    SkinnyGeom g_gu, g_dn;
     FusedGeom fz;
     int cus;                              // compute units: workgroups of the fused kernel
-    bool skinny_ok, tiled_ok;
+    bool tiled_ok;
 };
 
 namespace {
@@ -256,12 +219,6 @@ struct Workspace {
     uint64_t* fact;   // [8][I] tagged
     uint64_t* fab;    // [2][8][I/2] tagged binary16 pairs
     uint64_t* fpart;  // [nsl][8][H] tagged
-    // per-phase skinny region
-    uint16_t* xb;     // [8][H] binary16 rotated input
-    float* a;         // [8][I]
-    uint16_t* ab;     // [8][I] binary16 rotated intermediate
-    float* part;      // [slices][8][H]
-    float* skp;       // stream-K partial-sum slots (gate/up, then reused by down)
     // tiled region
     uint16_t* xt;     // [T][H]
     float* a_t;       // [T][I]
@@ -291,12 +248,6 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
     const size_t o_fact = take(size_t(kSkinnyT) * I * 8);
     const size_t o_fab = take(2 * size_t(kSkinnyT) * I * 4);
     const size_t o_fpart = take(size_t(std::max(p->fz.nsl, 1)) * kSkinnyT * H * 8);
-    const size_t o_xb = take(size_t(kSkinnyT) * H * 2);
-    const size_t o_a = take(size_t(kSkinnyT) * I * 4);
-    const size_t o_ab = take(size_t(kSkinnyT) * I * 2);
-    const size_t o_part = take(size_t(p->g_dn.slices) * kSkinnyT * H * 4);
-    const size_t o_skp = take(std::max(streamk_part_floats(2, I, H, p->cus),
-                                       streamk_part_floats(1, H, I, p->cus)) * 4);
     const int Tt = T > 0 ? T : 1;
     const size_t o_xt = take(size_t(Tt) * H * 2);
     const size_t o_at32 = take(size_t(Tt) * I * 4);
@@ -317,11 +268,6 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
         w.fact = reinterpret_cast<uint64_t*>(b + o_fact);
         w.fab = reinterpret_cast<uint64_t*>(b + o_fab);
         w.fpart = reinterpret_cast<uint64_t*>(b + o_fpart);
-        w.xb = reinterpret_cast<uint16_t*>(b + o_xb);
-        w.a = reinterpret_cast<float*>(b + o_a);
-        w.ab = reinterpret_cast<uint16_t*>(b + o_ab);
-        w.part = reinterpret_cast<float*>(b + o_part);
-        w.skp = reinterpret_cast<float*>(b + o_skp);
         w.xt = reinterpret_cast<uint16_t*>(b + o_xt);
         w.a_t = reinterpret_cast<float*>(b + o_at32);
         w.at = reinterpret_cast<uint16_t*>(b + o_at);
@@ -348,81 +294,6 @@ FusedGeom fused_geom(int H, int I, int bh, int bi) {
     // the kernel rotates rows of up to 256 columns in registers
     if (g.n_r > 1024 || g.rc > 256 || g.fu > 256) g.tpw = 0;
     return g;
-}
-
-vqmlp_status run_skinny(const vqmlp_plan* p, int T, const void* x, void* y, const Workspace& w,
-                        hipStream_t st) {
-    const int H = p->d.H, I = p->d.I;
-    hipError_t e = launch_rotate(T, H, p->bh, x, 0, p->d.s_in, p->d.sign_h, w.xb, 3, st);
-    if (e != hipSuccess) return hip_fail(e, "rotate (input)");
-    SkinnyArgs a;
-    memset(&a, 0, sizeof a);
-    a.mat[0] = p->gate;
-    a.mat[1] = p->up;
-    a.nmat = 2;
-    a.T = T;
-    a.slices = 1;
-    a.tpw = p->g_gu.tpw;
-    a.contig = 0;
-    a.bx = w.xb;
-    a.sign_i = p->d.sign_i;
-    a.a_out = w.a;
-    e = launch_skinny(a, st);
-    if (e != hipSuccess) return hip_fail(e, "skinny gate/up");
-    e = launch_rotate(T, I, p->bi, w.a, 1, nullptr, nullptr, w.ab, 3, st);
-    if (e != hipSuccess) return hip_fail(e, "rotate (intermediate)");
-    SkinnyArgs d;
-    memset(&d, 0, sizeof d);
-    d.mat[0] = p->down;
-    d.nmat = 1;
-    d.T = T;
-    d.slices = p->g_dn.slices;
-    d.tpw = p->g_dn.tpw;
-    d.contig = 1;
-    d.bx = w.ab;
-    d.part = w.part;
-    d.y = static_cast<uint16_t*>(y);
-    e = launch_skinny(d, st);
-    if (e != hipSuccess) return hip_fail(e, "skinny down");
-    if (d.slices > 1) {
-        e = launch_reduce_down(T, H, d.slices, w.part, p->down.sc, static_cast<uint16_t*>(y), st);
-        if (e != hipSuccess) return hip_fail(e, "down reduction");
-    }
-    return ok();
-}
-
-// The stream-K kernels: rotate x, gate/up and its finishing pass (a and its rotation), down and
-// its finishing pass (y).
-vqmlp_status run_streamk(const vqmlp_plan* p, int T, const void* x, void* y, const Workspace& w,
-                         hipStream_t st) {
-    const int H = p->d.H, I = p->d.I;
-    hipError_t e = launch_rotate(T, H, p->bh, x, 0, p->d.s_in, p->d.sign_h, w.xb, 4, st);
-    if (e != hipSuccess) return hip_fail(e, "rotate (input)");
-    StreamKArgs a;
-    memset(&a, 0, sizeof a);
-    a.mat[0] = p->gate;
-    a.mat[1] = p->up;
-    a.nmat = 2;
-    a.T = T;
-    a.bx = w.xb;
-    a.part = w.skp;
-    a.sign_i = p->d.sign_i;
-    a.bi = p->bi;
-    a.norm_i = float(1.0 / std::sqrt(double(p->bi)));
-    a.ab_out = w.ab;
-    e = launch_streamk(a, p->cus, st);
-    if (e != hipSuccess) return hip_fail(e, "stream-K gate/up");
-    StreamKArgs d;
-    memset(&d, 0, sizeof d);
-    d.mat[0] = p->down;
-    d.nmat = 1;
-    d.T = T;
-    d.bx = w.ab;
-    d.part = w.skp;
-    d.y = static_cast<uint16_t*>(y);
-    e = launch_streamk(d, p->cus, st);
-    if (e != hipSuccess) return hip_fail(e, "stream-K down");
-    return ok();
 }
 
 vqmlp_status run_fused(const vqmlp_plan* p, int T, const void* x, void* y, const Workspace& w,
@@ -460,51 +331,8 @@ vqmlp_status run_fused(const vqmlp_plan* p, int T, const void* x, void* y, const
     a.part = w.fpart;
     a.spin_limit = 1u << 18;
     a.dyn = 1;
-    const hipError_t e = launch_fused(a, g.tpw, p->cus, false, st);
+    const hipError_t e = launch_fused(a, g.tpw, p->cus, st);
     if (e != hipSuccess) return hip_fail(e, "fused forward");
-    return ok();
-}
-
-// The same items as four launches: rotate x, the gate/up items, rotate a, the down items.
-vqmlp_status run_fused_phased(const vqmlp_plan* p, int T, const void* x, void* y,
-                              const Workspace& w, hipStream_t st) {
-    const FusedGeom& g = p->fz;
-    const int H = p->d.H, I = p->d.I;
-    hipError_t e = launch_rotate(T, H, p->bh, x, 0, p->d.s_in, p->d.sign_h, w.xb, 3, st);
-    if (e != hipSuccess) return hip_fail(e, "rotate (input)");
-    FusedArgs a;
-    memset(&a, 0, sizeof a);
-    a.gate = p->gate;
-    a.up = p->up;
-    a.down = p->down;
-    a.H = H;
-    a.I = I;
-    a.T = T;
-    a.bh = p->bh;
-    a.bi = p->bi;
-    a.rc = g.rc;
-    a.fu = g.fu;
-    a.nsl = g.nsl;
-    a.nqd = g.nqd;
-    a.n_fu = g.n_fu;
-    a.sign_i = p->d.sign_i;
-    a.y = static_cast<uint16_t*>(y);
-    a.ctl = w.ctl;
-    a.part = w.fpart;
-    a.xb16 = w.xb;
-    a.ab16 = w.ab;
-    a.act32 = w.a;
-    a.spin_limit = 1u << 18;
-    a.n_g = g.n_g;  // gate/up items only
-    a.total = g.n_g;
-    e = launch_fused(a, g.tpw, std::min(p->cus, a.total), true, st);
-    if (e != hipSuccess) return hip_fail(e, "gate/up phase");
-    e = launch_rotate(T, I, p->bi, w.a, 1, nullptr, nullptr, w.ab, 3, st);
-    if (e != hipSuccess) return hip_fail(e, "rotate (intermediate)");
-    a.n_g = 0;  // down items only
-    a.total = g.nsl * g.nqd;
-    e = launch_fused(a, g.tpw, std::min(p->cus, a.total), true, st);
-    if (e != hipSuccess) return hip_fail(e, "down phase");
     return ok();
 }
 
@@ -767,13 +595,7 @@ vqmlp_status vqmlp_create(const vqmlp_desc* desc, vqmlp_plan** out) {
             cus = 256;
         p->cus = cus;
     }
-    p->skinny_ok = skinny_geom(d.H, true, &p->g_gu);
     p->tiled_ok = d.H % 64 == 0 && d.I % 64 == 0;
-    skinny_geom(d.I, false, &p->g_dn);
-    if (!p->skinny_ok) {
-        p->g_gu.tpw = 0;
-        p->g_gu.slices = 0;
-    }
     *out = p;
     return ok();
 }
@@ -797,7 +619,7 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
     if (!p) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_forward: null plan");
     if (T < 0 || T > p->d.t_max)
         return fail(VQMLP_ERR_INVALID_ARG, "T=%d outside [0, t_max=%d]", T, p->d.t_max);
-    if (path < 0 || path > 5) return fail(VQMLP_ERR_INVALID_ARG, "unknown path %d", path);
+    if (path < 0 || path > 2) return fail(VQMLP_ERR_INVALID_ARG, "unknown path %d", path);
     if (T == 0) return ok();
     if (!x || !y || !workspace) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_forward: null pointer");
     if (!aligned(x, 16) || !aligned(y, 16) || !aligned(workspace, 256))
@@ -813,37 +635,67 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
     const size_t xy = size_t(T) * p->d.H * 2;
     if ((xb < wb + w.bytes && wb < xb + xy) || (yb < wb + w.bytes && wb < yb + xy))
         return fail(VQMLP_ERR_INVALID_ARG, "x or y overlaps the workspace");
-    // 1: the fused single-launch kernel, 3: the per-phase skinny kernels, 4: the fused kernel's
-    // phases as separate launches, 5: the stream-K kernels, 2: tiled; 0 picks the fused kernel
-    // for T <= 8 where it applies, else the per-phase kernels, else tiled
+    // 1: the fused single-launch kernel (T <= 8), 2: the tiled kernels; 0 picks the fused
+    // kernel for T <= 8 where it applies, else the tiled kernels
     const bool fused_ok = p->fz.tpw > 0;
-    const bool streamk_ok = streamk_grid(2, p->d.I, p->d.H, p->cus) > 0 &&
-                            streamk_grid(1, p->d.H, p->d.I, p->cus) > 0;
-    if (path == 1 || path == 3 || path == 4 || path == 5) {
+    if (path == 1) {
         if (T > kSkinnyT)
-            return fail(VQMLP_ERR_UNSUPPORTED, "the skinny path takes T <= %d (T=%d)", kSkinnyT, T);
-        if (path == 5 && !streamk_ok)
-            return fail(VQMLP_ERR_UNSUPPORTED, "the stream-K path does not take H=%d I=%d",
-                        p->d.H, p->d.I);
-        if (path != 5 && !(path == 3 ? p->skinny_ok : fused_ok))
-            return fail(VQMLP_ERR_UNSUPPORTED, "the skinny path takes H <= %d (H=%d)",
+            return fail(VQMLP_ERR_UNSUPPORTED, "the fused kernel takes T <= %d (T=%d)", kSkinnyT, T);
+        if (!fused_ok)
+            return fail(VQMLP_ERR_UNSUPPORTED, "the fused kernel takes H <= %d (H=%d)",
                         kSkinnyWaves * kSkinnyMaxTPW * kTileCols, p->d.H);
     }
-    int use = path;
-    if (path == 0) use = T <= kSkinnyT ? (fused_ok ? 1 : (p->skinny_ok ? 3 : 2)) : 2;
+    const int use = path == 0 ? (T <= kSkinnyT && fused_ok ? 1 : 2) : path;
     if (use == 2 && !p->tiled_ok)
         return fail(VQMLP_ERR_UNSUPPORTED, "the tiled path takes H and I multiples of 64");
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (use == 5) return run_streamk(p, T, x, y, w, st);
     if (use == 1) return run_fused(p, T, x, y, w, st);
-    if (use == 4) return run_fused_phased(p, T, x, y, w, st);
-    if (use == 3) return run_skinny(p, T, x, y, w, st);
     return run_tiled(p, T, x, y, w, st);
 }
 
 vqmlp_status vqmlp_forward(const vqmlp_plan* p, int T, const void* x, void* y, void* workspace,
                            size_t workspace_bytes, void* stream) {
     return vqmlp_forward_path(p, T, x, y, workspace, workspace_bytes, 0, stream);
+}
+
+vqmlp_status vqmlp_workspace_errors(void* workspace, size_t workspace_bytes, int clear,
+                                    uint32_t* bits, void* stream) {
+    if (!workspace || !bits) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_workspace_errors: null pointer");
+    if (!aligned(workspace, 256) || workspace_bytes < kCtlHdr * 4)
+        return fail(VQMLP_ERR_INVALID_ARG,
+                    "vqmlp_workspace_errors: the workspace must be 256-byte aligned and hold "
+                    "at least %d bytes", int(kCtlHdr * 4));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint32_t* err = static_cast<uint32_t*>(workspace) + kCtlError;  // control block at offset 0
+    hipError_t e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, "vqmlp_workspace_errors: stream synchronisation");
+    uint32_t v = 0;
+    e = hipMemcpy(&v, err, sizeof v, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "vqmlp_workspace_errors: reading the error word");
+    if (clear && v) {
+        e = hipMemsetAsync(err, 0, sizeof v, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+        if (e != hipSuccess) return hip_fail(e, "vqmlp_workspace_errors: clearing the error word");
+    }
+    *bits = v;
+    return ok();
+}
+
+vqmlp_status vqmlp_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_stream_read: null pointer");
+    if (!aligned(buf, 16) || bytes % 16)
+        return fail(VQMLP_ERR_INVALID_ARG,
+                    "vqmlp_stream_read: buf must be 16-byte aligned and bytes a multiple of 16");
+    vqmlp_status st = check_device();
+    if (st) return st;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        cus = 256;
+    hipError_t e = launch_stream_read(buf, bytes, sink, cus, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "stream read launch");
+    return ok();
 }
 
 // ------------------------------------------------------------------ scalar-LUT projection

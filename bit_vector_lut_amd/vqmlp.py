@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libvqmlp.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
-PATH_AUTO, PATH_SKINNY, PATH_TILED, PATH_PHASED, PATH_FUSED_PHASED, PATH_STREAMK = 0, 1, 2, 3, 4, 5
+PATH_AUTO, PATH_FUSED, PATH_TILED = 0, 1, 2
 
 
 class VqmlpError(RuntimeError):
@@ -54,6 +54,8 @@ def lib():
             "vqmlp_workspace_bytes": [P, I, C.POINTER(S)],
             "vqmlp_forward": [P, I, P, P, P, S, P],
             "vqmlp_forward_path": [P, I, P, P, P, S, I, P],
+            "vqmlp_workspace_errors": [P, S, I, C.POINTER(C.c_uint32), P],
+            "vqmlp_stream_read": [P, S, P, P],
             "vqmlp_rotate": [I, I, I, P, P, P, P, P],
             "vqmlp_lut_packed_bytes": [I, I, I, C.POINTER(S)],
             "vqmlp_lut_pack": [I, I, I, P, P, P, P, S],
@@ -198,6 +200,21 @@ def to_device(a, device="cuda"):
     if a.dtype == np.float16:
         a = a.view(np.int16)
     return torch.from_numpy(a).to(device)
+
+
+def workspace_errors(workspace, clear: bool = True, stream=None) -> int:
+    """Error bits of the fused kernel's bounded waits in a forward workspace (0 = none); waits
+    for the stream and, with clear, zeroes the word."""
+    bits = C.c_uint32()
+    _check(lib().vqmlp_workspace_errors(_dptr(workspace), workspace.numel(), int(clear),
+                                        C.byref(bits), _stream(stream)))
+    return bits.value
+
+
+def stream_read(buf, sink, stream=None):
+    """Measurement hook: one streaming read of the device tensor buf (bytes a multiple of 16)."""
+    _check(lib().vqmlp_stream_read(_dptr(buf), buf.numel() * buf.element_size(), _dptr(sink),
+                                   _stream(stream)))
 
 
 def dequant(N: int, K: int, packed_dev, stream=None):

@@ -115,27 +115,53 @@ vqmlp_status vqmlp_destroy(vqmlp_plan *plan);
 vqmlp_status vqmlp_workspace_bytes(const vqmlp_plan *plan, int T, size_t *bytes);
 
 /* y = MLP(x).  x, y: DEVICE binary16 [T][H], 16-byte aligned, may not overlap the workspace.
- * T == 0 is a no-op.  T <= 8 runs the bandwidth-bound skinny kernels, T > 8 the matrix-core
- * tiled kernels.  Calls that share a workspace must not overlap in time. */
+ * T == 0 is a no-op.  T <= 8 runs the bandwidth-bound fused kernel (H <= 5120; larger H takes
+ * the tiled kernels), T > 8 the matrix-core tiled kernels.  Calls that share a workspace must
+ * not overlap in time.
+ *
+ * The fused T <= 8 kernel is persistent: one workgroup per compute unit, handing operands and
+ * partial sums to one another through the workspace.  It needs all of its workgroups resident
+ * at once, i.e. no other kernel holding compute units for long while it runs.  Every wait for a
+ * hand-off is bounded (about 2^18 short sleeps, milliseconds); a wait that runs out sets a bit
+ * in the workspace's error word and the call completes with wrong values in y instead of
+ * hanging.  vqmlp_workspace_errors reads (and clears) that word. */
 vqmlp_status vqmlp_forward(const vqmlp_plan *plan, int T, const void *x, void *y, void *workspace,
                            size_t workspace_bytes, void *stream);
 
 /* Same as vqmlp_forward with the kernel family chosen by the caller: path 0 = automatic
- * (T <= 8: path 1; larger T: path 2), 1 = the fused single-launch T <= 8 kernel, 2 = tiled
- * matrix-core kernels, 3 = the T <= 8 kernels as separate per-phase launches, 4 = the fused
- * kernel's phases as separate launches, 5 = the T <= 8 stream-K kernels (the weight stream cut
- * into equal contiguous ranges, one per workgroup; any H and I that are multiples of 64).
- * Paths 1, 3, 4 and 5 take T <= 8; paths 1, 3 and 4 take H <= 5120.  Paths 1 and 4 keep their
- * queue, counters and epoch in the first bytes of the workspace: the caller zero-fills the
- * workspace once, and every call leaves that control block ready for the next call. */
+ * (T <= 8 and H <= 5120: path 1; otherwise path 2), 1 = the fused single-launch T <= 8 kernel
+ * (T <= 8, H <= 5120), 2 = the tiled matrix-core kernels (any T; H and I multiples of 64).
+ * Path 1 keeps its queue, counters, error word and epoch in the first 64 bytes of the
+ * workspace: the caller zero-fills the workspace once, and every call leaves that control block
+ * ready for the next call.  VQMLP_ERR_INVALID_ARG for another path number,
+ * VQMLP_ERR_UNSUPPORTED when the chosen path does not take the shape or T. */
 vqmlp_status vqmlp_forward_path(const vqmlp_plan *plan, int T, const void *x, void *y,
                                 void *workspace, size_t workspace_bytes, int path, void *stream);
+
+/* Error bits that the fused kernel's bounded waits left in a workspace (see vqmlp_forward):
+ * 1 = a projection's operand never arrived, 2 = a rotation block of the gated intermediate never
+ * completed, 4 = a partial sum of the down projection never arrived.  0 means every wait of
+ * every call since the last clear ended normally.  Waits for `stream` (a host-device
+ * synchronisation: not for use inside graph capture), copies the word to *bits and, when
+ * clear != 0, zeroes it on `stream` and waits again.  workspace: the DEVICE workspace of
+ * vqmlp_forward (256-byte aligned, workspace_bytes >= 64).  VQMLP_ERR_INVALID_ARG for null or
+ * unaligned pointers or a short workspace, VQMLP_ERR_HIP when a HIP call fails. */
+vqmlp_status vqmlp_workspace_errors(void *workspace, size_t workspace_bytes, int clear,
+                                    uint32_t *bits, void *stream);
 
 /* Test hook for the rotation kernels: out[t][.] = R_n(x[t][.] . s) with block b (power of two,
  * 2..1024), FP32 output.  x DEVICE binary16 [T][n]; s DEVICE binary16 [n] or NULL (all 1);
  * sign DEVICE int8 [n] or NULL; out DEVICE float [T][n]. */
 vqmlp_status vqmlp_rotate(int T, int n, int b, const uint16_t *x, const uint16_t *s,
                           const int8_t *sign, float *out, void *stream);
+
+/* Measurement hook: reads `bytes` of the DEVICE buffer buf once (16-byte loads, each workgroup a
+ * contiguous share, one pass), the plainest weight stream there is: its rate is the HBM read
+ * rate that the weight-streaming kernels above can be compared with.  buf 16-byte aligned,
+ * bytes a multiple of 16; sink: DEVICE uint32, written only in the unlikely case that the XOR of
+ * all words equals one fixed value (so the loads cannot be dropped).  Asynchronous on stream.
+ * VQMLP_ERR_INVALID_ARG for null or unaligned arguments, VQMLP_ERR_HIP for a failed launch. */
+vqmlp_status vqmlp_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
 /* ------------------------------------------------------------------ scalar-LUT projection
  * Token-mixer format of the same model card (format table, "Token mixers" row; rotation bullet):
