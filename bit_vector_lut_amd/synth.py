@@ -195,32 +195,32 @@ def lut_projection(rng: np.random.Generator, bits: int, N: int, K: int, rank: in
 H27, I27 = 5120, 17408  # 27B-like MLP shape
 
 
-def config1() -> MLPLayer:
+def tiny_layer() -> MLPLayer:
     """Tiny single MLP: H=256, I=704, T=1, seed 0 (rotation blocks 128 and 64)."""
     return mlp_layer(256, 704, 1, seed=0, outliers=False)
 
 
-def config2() -> MLPLayer:
+def layer27b_t8() -> MLPLayer:
     """One 27B-like MLP at T=8 (anchor + 7 drafts), 1% outlier channels x20, seed 0."""
     return mlp_layer(H27, I27, 8, seed=0, outliers=True)
 
 
-def config3() -> MLPLayer:
+def layer27b_t64() -> MLPLayer:
     """The same shape at T=64 (fixed-size prefill chunk), no outliers, seed 0."""
     return mlp_layer(H27, I27, 64, seed=0, outliers=False)
 
 
-def config4_seeds(n_layers: int = 64):
+def stream_seeds(n_layers: int = 64):
     """Per-layer generators of the 64-layer T=8 stream."""
     return [np.random.default_rng(c) for c in np.random.SeedSequence(0).spawn(n_layers)]
 
 
-def config4_layer(i: int, n_layers: int = 64) -> MLPLayer:
+def stream_layer(i: int, n_layers: int = 64) -> MLPLayer:
     child = np.random.SeedSequence(0).spawn(n_layers)[i]
     return mlp_layer(H27, I27, 8, seed=np.random.default_rng(child), outliers=True)
 
 
-def config5():
+def prefill512():
     """T=512 prefill: one 27B-like MLP, then a 2-bit and a 4-bit 5120x5120 scalar-LUT projection
     with rank-64 factors, all from one generator (MLP first, then 2-bit, then 4-bit).  The
     projections take the MLP's input x."""

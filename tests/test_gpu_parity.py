@@ -46,11 +46,30 @@ def _rel_fro(y, ref):
     return np.linalg.norm(y - ref) / np.linalg.norm(ref)
 
 
-def _report(name, y, ref):
+ROW_TOL = 1e-2   # worst row (token): relative error of that row
+ELEM_TOL = 1e-2  # worst element, relative to the largest |reference| of its row
+
+
+def _report(name, y, ref, row_scale="own"):
+    """Relative Frobenius error (returned), after asserting the local bounds: no row of y and no
+    single element may be off by more than 1% of its row's scale, so an error confined to a few
+    rows or one tile cannot hide under the whole-matrix norm.  row_scale="global" measures every
+    row against the largest row norm instead (for closed forms whose rows can cancel to nearly
+    zero, where a row's own norm says nothing about the kernel's accuracy)."""
+    assert y.shape == ref.shape, (y.shape, ref.shape)
+    assert np.isfinite(y).all(), "%s: non-finite outputs" % name
     err = _rel_fro(y, ref)
-    row = np.linalg.norm(y - ref, axis=1) / np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
-    _say("%s: rel_fro=%.3e max_abs=%.3e worst_row=%.3e" % (name, err, np.abs(y - ref).max(),
-                                                          row.max()))
+    rnorm = np.maximum(np.linalg.norm(ref, axis=1), 1e-30)
+    rmax = np.maximum(np.abs(ref).max(axis=1, keepdims=True), 1e-30)
+    if row_scale == "global":
+        rnorm = np.full_like(rnorm, rnorm.max())
+        rmax = np.full_like(rmax, rmax.max())
+    row = np.linalg.norm(y - ref, axis=1) / rnorm
+    elem = (np.abs(y - ref) / rmax).max()
+    _say("%s: rel_fro=%.3e max_abs=%.3e worst_row=%.3e worst_elem=%.3e" % (
+        name, err, np.abs(y - ref).max(), row.max(), elem))
+    assert row.max() <= ROW_TOL, "%s: worst row %.3e (row %d)" % (name, row.max(), row.argmax())
+    assert elem <= ELEM_TOL, "%s: worst element %.3e of its row's scale" % (name, elem)
     return err
 
 
@@ -113,13 +132,13 @@ def _run(vq, torch_dev, layer, path=0, mlp=None):
     return _f64(y)
 
 
-@pytest.mark.parametrize("path", [0, 1, 2, 3, 4, 5])
-def test_config1_tiny(vq, oracle_mod, torch_dev, path):
-    L = synth.config1()
-    _say("config1 path=%d" % path)
+@pytest.mark.parametrize("path", [0, 1, 2])
+def test_tiny_layer(vq, oracle_mod, torch_dev, path):
+    L = synth.tiny_layer()
+    _say("tiny_layer path=%d" % path)
     y = _run(vq, torch_dev, L, path)
     ref = oracle_mod.mlp_forward(L)
-    assert _report("config1 path %d" % path, y, ref) <= MLP_TOL
+    assert _report("tiny_layer path %d" % path, y, ref) <= MLP_TOL
 
 
 SMALL = [(256, 704), (128, 192), (512, 1024), (320, 640)]
@@ -132,49 +151,46 @@ def test_mlp_small_shapes(vq, oracle_mod, torch_dev, H, I, T):
     _say("small H=%d I=%d T=%d" % (H, I, T))
     mlp = vq.MLP.from_layer(L, t_max=max(T, 8))
     ref = oracle_mod.mlp_forward(L)
-    for path in ([0, 1, 2, 3, 4, 5] if T <= 8 else [0]):
+    for path in ([0, 1, 2] if T <= 8 else [0]):
         y = _run(vq, torch_dev, L, path, mlp)
         assert _report("H=%d I=%d T=%d path %d" % (H, I, T, path), y, ref) <= MLP_TOL
 
 
 @pytest.fixture(scope="module")
-def config2():
-    return synth.config2()
+def layer27b_t8():
+    return synth.layer27b_t8()
 
 
 @pytest.fixture(scope="module")
-def config2_ref(oracle_mod, config2):
-    return oracle_mod.mlp_forward(config2)
+def layer27b_t8_ref(oracle_mod, layer27b_t8):
+    return oracle_mod.mlp_forward(layer27b_t8)
 
 
-def test_config2_full(vq, oracle_mod, torch_dev, config2, config2_ref):
-    _say("config2 skinny")
-    y = _run(vq, torch_dev, config2, 0)
-    assert _report("config2", y, config2_ref) <= MLP_TOL
+def test_layer27b_t8_full(vq, oracle_mod, torch_dev, layer27b_t8, layer27b_t8_ref):
+    _say("layer27b_t8 fused")
+    y = _run(vq, torch_dev, layer27b_t8, 0)
+    assert _report("layer27b_t8", y, layer27b_t8_ref) <= MLP_TOL
 
 
-def test_config2_tiled_path(vq, oracle_mod, torch_dev, config2, config2_ref):
-    _say("config2 tiled")
-    y = _run(vq, torch_dev, config2, 2)
-    assert _report("config2 tiled", y, config2_ref) <= MLP_TOL
+def test_layer27b_t8_tiled_path(vq, oracle_mod, torch_dev, layer27b_t8, layer27b_t8_ref):
+    _say("layer27b_t8 tiled")
+    y = _run(vq, torch_dev, layer27b_t8, 2)
+    assert _report("layer27b_t8 tiled", y, layer27b_t8_ref) <= MLP_TOL
 
 
-@pytest.mark.parametrize("path", [1, 3, 4, 5])
-def test_config2_t8_paths(vq, oracle_mod, torch_dev, config2, config2_ref, path):
-    _say("config2 T=8 path %d" % path)
-    y = _run(vq, torch_dev, config2, path)
-    assert _report("config2 path %d" % path, y, config2_ref) <= MLP_TOL
-
-
-@pytest.mark.parametrize("H,I,T", [(256, 17408, 8), (5120, 1024, 3), (64, 65536, 8), (1024, 4352, 1)])
-def test_streamk_range_shapes(vq, oracle_mod, torch_dev, H, I, T):
-    """Stream-K ranges that cross up to four row-tile pairs (short K), ranges inside one pair
-    (long K), more workgroups than compute units (K = 64: ranges are capped), and T = 1."""
+@pytest.mark.parametrize("H,I,T", [(256, 17408, 8), (5120, 1024, 3), (512, 256, 8), (64, 65536, 8),
+                                   (1024, 4352, 1), (4096, 1024, 8)])
+def test_fused_unusual_shapes(vq, oracle_mod, torch_dev, H, I, T):
+    """The fused kernel on shapes far from the 27B-like one: long K with few rows, H larger than
+    I (down items then cover more row tiles than I has: nothing of theirs may index I-sized
+    arrays by an H row tile), K = 64 with more row tiles than compute units, and T = 1."""
     L = synth.mlp_layer(H, I, T, seed=H + 3 * I + T, outliers=True)
-    _say("stream-K H=%d I=%d T=%d" % (H, I, T))
-    y = _run(vq, torch_dev, L, 5)
+    _say("fused H=%d I=%d T=%d" % (H, I, T))
+    mlp = vq.MLP.from_layer(L, t_max=8)
     ref = oracle_mod.mlp_forward(L)
-    assert _report("stream-K H=%d I=%d T=%d" % (H, I, T), y, ref) <= MLP_TOL
+    for path in (0, 1):
+        y = _run(vq, torch_dev, L, path, mlp)
+        assert _report("fused H=%d I=%d T=%d path %d" % (H, I, T, path), y, ref) <= MLP_TOL
 
 
 @pytest.mark.parametrize("H,I,T,bh", [(512, 1024, 8, 32), (512, 1024, 3, 64), (512, 1024, 8, 256),
@@ -186,14 +202,13 @@ def test_fused_input_rotation_blocks(vq, oracle_mod, torch_dev, H, I, T, bh):
     _say("fused input rotation H=%d I=%d T=%d bh=%d" % (H, I, T, bh))
     mlp = vq.MLP.from_layer(L, t_max=8)
     ref = oracle_mod.mlp_forward(L)
-    for path in (1, 4):
-        y = _run(vq, torch_dev, L, path, mlp)
-        assert _report("bh=%d path %d" % (bh, path), y, ref) <= MLP_TOL
+    y = _run(vq, torch_dev, L, 1, mlp)
+    assert _report("bh=%d" % bh, y, ref) <= MLP_TOL
 
 
 def test_fused_control_block_is_left_ready(vq, oracle_mod, torch_dev):
-    """Several fused calls on one workspace (mixed with the other paths, stream-K included):
-    every call is right, the queue and counters are back at zero, the error word stays clear,
+    """Several fused calls on one workspace (mixed with tiled calls): every call is right, the
+    queue and counters are back at zero, the error word stays clear (read through the C ABI),
     the epoch counts calls."""
     L = synth.mlp_layer(512, 1024, 8, seed=11, outliers=True)
     mlp = vq.MLP.from_layer(L, t_max=8)
@@ -201,13 +216,13 @@ def test_fused_control_block_is_left_ready(vq, oracle_mod, torch_dev):
     ws = mlp.workspace(8)
     ref = oracle_mod.mlp_forward(L)
     fused_calls = 0
-    for path in (1, 0, 5, 2, 1, 3, 5, 4, 1, 5, 1):
+    for path in (1, 0, 2, 1, 2, 2, 1, 0, 1):
         _say("control block: path %d" % path)
         y = _f64(mlp.forward(x, workspace=ws, path=path))
         torch_dev.cuda.synchronize()
         assert _report("path %d" % path, y, ref) <= MLP_TOL
         fused_calls += path in (0, 1)  # path 0 takes the fused kernel at T <= 8
-        fused_calls += 2 * (path == 4)  # one launch per phase
+    assert vq.workspace_errors(ws, clear=False) == 0
     ctl = ws[:64].cpu().numpy().view(np.uint32)
     assert ctl[0] == 0 and ctl[1] == 0, ctl[:4]  # queue head, exit count
     assert ctl[2] == 0, "a bounded wait ran out: error bits %#x" % ctl[2]
@@ -215,25 +230,51 @@ def test_fused_control_block_is_left_ready(vq, oracle_mod, torch_dev):
     assert not ctl[4:].any(), ctl  # the rest of the block is never written
 
 
-@pytest.mark.parametrize("path", [1, 3, 4, 5])
-def test_config2_deterministic(vq, torch_dev, config2, path):
-    mlp = vq.MLP.from_layer(config2)
-    x = vq.to_device(config2.x)
+def test_workspace_errors_reads_and_clears(vq, torch_dev):
+    """The error word is the third word of the control block: what the call reports is that
+    word, and clearing zeroes only that word (written here from the host: a kernel never sets
+    it when its waits end normally)."""
+    L = synth.mlp_layer(256, 704, 4, seed=2)
+    mlp = vq.MLP.from_layer(L, t_max=8)
     ws = mlp.workspace(8)
-    _say("config2 determinism path %d" % path)
+    mlp.forward(vq.to_device(L.x), workspace=ws)
+    assert vq.workspace_errors(ws) == 0
+    ws[8:12] = torch_dev.tensor([5, 0, 0, 0], dtype=torch_dev.uint8)
+    epoch = ws[12:16].clone()
+    assert vq.workspace_errors(ws, clear=False) == 5
+    assert vq.workspace_errors(ws) == 5
+    assert vq.workspace_errors(ws) == 0
+    assert torch_dev.equal(ws[12:16], epoch)
+    with pytest.raises(vq.VqmlpError) as e:
+        vq.workspace_errors(ws[:32])
+    assert e.value.status == vq.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("path", [1, 2])
+def test_layer27b_t8_deterministic(vq, torch_dev, layer27b_t8, path):
+    mlp = vq.MLP.from_layer(layer27b_t8)
+    x = vq.to_device(layer27b_t8.x)
+    ws = mlp.workspace(8)
+    _say("layer27b_t8 determinism path %d" % path)
     y1 = mlp.forward(x, workspace=ws, path=path).clone()
     y2 = mlp.forward(x, workspace=ws, path=path).clone()
     torch_dev.cuda.synchronize()
     assert torch_dev.equal(y1, y2)
 
 
-def test_config3_sampled_tokens(vq, oracle_mod, torch_dev):
-    L = synth.config3()
-    _say("config3 T=64")
-    y = _run(vq, torch_dev, L, 0)
-    toks = [0, 17, 42, 63]
-    ref = oracle_mod.mlp_forward(L, tokens=toks)
-    assert _report("config3", y[toks], ref) <= MLP_TOL
+def test_layer27b_t64_all_tokens(vq, oracle_mod, torch_dev):
+    """The 27B-like layer at T = 64 (the fixed prefill chunk), every output."""
+    L = synth.layer27b_t64()
+    _say("layer27b_t64 T=64")
+    mlp = vq.MLP.from_layer(L, t_max=64)
+    x = vq.to_device(L.x)
+    ws = mlp.workspace(64)
+    y1 = mlp.forward(x, workspace=ws)
+    y2 = mlp.forward(x, workspace=ws).clone()
+    torch_dev.cuda.synchronize()
+    assert torch_dev.equal(y1, y2), "T=64 forward is not bitwise repeatable"
+    ref = oracle_mod.mlp_forward(L)
+    assert _report("layer27b_t64", _f64(y1), ref) <= MLP_TOL
 
 
 def test_errors_on_device(vq, torch_dev):
@@ -250,27 +291,38 @@ def test_errors_on_device(vq, torch_dev):
     assert e.value.status == vq.ERR_INVALID_ARG
     with pytest.raises(vq.VqmlpError) as e:
         mlp.forward(vq.to_device(np.zeros((9, 256), np.float16)), path=1)
+    for bad in (3, 4, 5, -1):
+        with pytest.raises(vq.VqmlpError) as e:
+            mlp.forward(x, path=bad)
+        assert e.value.status == vq.ERR_INVALID_ARG
     empty = vq.to_device(np.zeros((0, 256), np.float16))
     assert mlp.forward(empty).shape == (0, 256)
 
 
 @pytest.fixture(scope="module")
-def config5():
-    return synth.config5()
+def prefill512():
+    return synth.prefill512()
 
 
-def test_config5_mlp_sampled_tokens(vq, oracle_mod, torch_dev, config5):
-    L = config5[0]
-    _say("config5 MLP T=512")
-    y = _run(vq, torch_dev, L, 0)
-    toks = [0, 1, 127, 128, 300, 511]
-    ref = oracle_mod.mlp_forward(L, tokens=toks)
-    assert _report("config5 MLP", y[toks], ref) <= MLP_TOL
+def test_prefill512_mlp_all_tokens(vq, oracle_mod, torch_dev, prefill512):
+    """The 27B-like layer at T = 512 (register-decode matrix-core products, K-split down
+    projection), every output; a second call is bitwise identical."""
+    L = prefill512[0]
+    _say("prefill512 MLP T=512")
+    mlp = vq.MLP.from_layer(L, t_max=512)
+    x = vq.to_device(L.x)
+    ws = mlp.workspace(512)
+    y1 = mlp.forward(x, workspace=ws)
+    y2 = mlp.forward(x, workspace=ws).clone()
+    torch_dev.cuda.synchronize()
+    assert torch_dev.equal(y1, y2), "T=512 forward is not bitwise repeatable"
+    ref = oracle_mod.mlp_forward(L)
+    assert _report("prefill512 MLP", _f64(y1), ref) <= MLP_TOL
 
 
 @pytest.mark.parametrize("H,I,T,bi", [(1024, 4352, 1024, None), (1024, 4352, 1024, 64),
                                        (5120, 17408, 130, None)])
-def test_gateup_leftover_split_sampled_tokens(vq, oracle_mod, torch_dev, H, I, T, bi):
+def test_gateup_leftover_split(vq, oracle_mod, torch_dev, H, I, T, bi):
     """Shapes whose gate/up tiles leave a partial round on 256 CUs: the leftover rows go through
     the K-split product and the combine pass (with the fused 128-row rotation, or with the
     FP32 product and the separate 64-wide rotation)."""
@@ -278,9 +330,8 @@ def test_gateup_leftover_split_sampled_tokens(vq, oracle_mod, torch_dev, H, I, T
     _say("gate/up leftover split H=%d I=%d T=%d bi=%s" % (H, I, T, bi))
     mlp = vq.MLP.from_layer(L, t_max=T)
     y = _run(vq, torch_dev, L, 0, mlp)
-    toks = [0, 1, T // 2, T - 1]
-    ref = oracle_mod.mlp_forward(L, tokens=toks)
-    assert _report("leftover split H=%d I=%d T=%d" % (H, I, T), y[toks], ref) <= MLP_TOL
+    ref = oracle_mod.mlp_forward(L)
+    assert _report("leftover split H=%d I=%d T=%d" % (H, I, T), y, ref) <= MLP_TOL
 
 
 # ------------------------------------------------------------------ scalar-LUT projection
@@ -315,10 +366,14 @@ def test_lut_decode_shapes(vq, oracle_mod, torch_dev, bits, N, K, T, rank, hb):
     x = synth.activations(rng, T, K, outliers=True)
     _say("LUT T<=8 bits=%d N=%d K=%d T=%d r=%d hb=%d" % (bits, N, K, T, rank, hb))
     proj = vq.LUTProjection.from_proj(p)
-    y = _f64(proj.forward(vq.to_device(x)))
+    xd = vq.to_device(x)
+    ws = proj.workspace(T)
+    y1 = proj.forward(xd, workspace=ws)
+    y2 = proj.forward(xd, workspace=ws).clone()
     torch_dev.cuda.synchronize()
+    assert torch_dev.equal(y1, y2), "not bitwise repeatable"
     ref = oracle_mod.lut_forward(p, x)
-    assert _report("LUT T<=8 %d-bit %dx%d T=%d" % (bits, N, K, T), y, ref) <= MLP_TOL
+    assert _report("LUT T<=8 %d-bit %dx%d T=%d" % (bits, N, K, T), _f64(y1), ref) <= MLP_TOL
 
 
 HEAD_CASES = [  # N, K, T, Hadamard block (0 = none), bits
@@ -339,9 +394,14 @@ def test_lut_argmax_head(vq, oracle_mod, torch_dev, N, K, T, hb, bits):
     x = synth.activations(rng, T, K, outliers=True)
     _say("argmax head N=%d K=%d T=%d hb=%d bits=%d" % (N, K, T, hb, bits))
     proj = vq.LUTProjection.from_proj(p)
-    idx, val = proj.argmax(vq.to_device(x))
+    xd = vq.to_device(x)
+    ws = proj.workspace(T)
+    idx, val = proj.argmax(xd, ws)
+    idx2, val2 = proj.argmax(xd, ws)
     torch_dev.cuda.synchronize()
+    assert torch_dev.equal(idx, idx2) and torch_dev.equal(val, val2), "not bitwise repeatable"
     idx, val = idx.cpu().numpy(), val.cpu().numpy().astype(np.float64)
+    assert idx.shape == (T,) and ((idx >= 0) & (idx < N)).all(), idx
     y = oracle_mod.lut_forward(p, x)
     ref_idx, ref_val = oracle_mod.lut_argmax(p, x)
     tol = 2e-3 * np.abs(y).max(axis=1)
@@ -377,6 +437,7 @@ def test_lut_argmax_full_head_planted(vq, torch_dev):
     idx, val = proj.argmax(vq.to_device(x))
     torch_dev.cuda.synchronize()
     idx, val = idx.cpu().numpy(), val.cpu().numpy().astype(np.float64)
+    assert ((idx >= 0) & (idx < N)).all(), idx
     assert list(idx) == [int(j) for j in planted]
     for t, j in enumerate(planted):
         want = float(sc[j]) * float(x[t].astype(np.float64).sum())
@@ -398,15 +459,18 @@ def test_lut_small_shapes(vq, oracle_mod, torch_dev, bits, N, K, T, rank, hb):
 
 
 @pytest.mark.parametrize("which", [1, 2])
-def test_config5_lut_sampled_tokens(vq, oracle_mod, torch_dev, config5, which):
-    L, p = config5[0], config5[which]
-    _say("config5 lut%d T=512" % p.bits)
+def test_prefill512_lut_all_tokens(vq, oracle_mod, torch_dev, prefill512, which):
+    L, p = prefill512[0], prefill512[which]
+    _say("prefill512 lut%d T=512" % p.bits)
     proj = vq.LUTProjection.from_proj(p)
-    y = _f64(proj.forward(vq.to_device(L.x)))
+    xd = vq.to_device(L.x)
+    ws = proj.workspace(512)
+    y1 = proj.forward(xd, workspace=ws)
+    y2 = proj.forward(xd, workspace=ws).clone()
     torch_dev.cuda.synchronize()
-    toks = [0, 5, 255, 256, 511]
-    ref = oracle_mod.lut_forward(p, L.x, tokens=toks)
-    assert _report("config5 lut%d" % p.bits, y[toks], ref) <= MLP_TOL
+    assert torch_dev.equal(y1, y2), "not bitwise repeatable"
+    ref = oracle_mod.lut_forward(p, L.x)
+    assert _report("prefill512 lut%d" % p.bits, _f64(y1), ref) <= MLP_TOL
 
 
 def test_lut_errors_on_device(vq, torch_dev):
@@ -458,8 +522,12 @@ def test_vq2_projection(vq, oracle_mod, torch_dev, N, K, T):
     x = synth.activations(rng, T, K, outliers=True)
     _say("2x16 projection N=%d K=%d T=%d" % (N, K, T))
     proj = vq.VQ2Projection.from_matrix(m)
-    y = _f64(proj.forward(vq.to_device(x)))
+    xd = vq.to_device(x)
+    y1 = proj.forward(xd)
+    y2 = proj.forward(xd)
     torch_dev.cuda.synchronize()
+    assert torch_dev.equal(y1, y2), "not bitwise repeatable"
+    y = _f64(y1)
     ref = oracle_mod.vq2_matmul(m.codes, m.cb, m.sc, x)
     assert _report("2x16 %dx%d T=%d" % (N, K, T), y, ref) <= MLP_TOL
 
@@ -520,3 +588,112 @@ def test_vq2_and_argmax_graph_replays_match_eager(vq, torch_dev):
         torch.cuda.synchronize()
         assert torch.equal(y, ref[0]), "replay %d: 2x16 output" % rep
         assert torch.equal(gi, ref[1]) and torch.equal(gv, ref[2]), "replay %d: argmax" % rep
+
+
+# ------------------------------------------------------------------ closed forms on the GPU
+
+
+def _blockdiag_rotation(u, b, sign):
+    """(I (x) H_b / sqrt(b)) diag(sign) applied to the rows of u, from scipy's Sylvester matrix."""
+    import scipy.linalg
+
+    Hb = scipy.linalg.hadamard(b).astype(np.float64) / np.sqrt(b)
+    v = u * sign.astype(np.float64)[None, :]
+    T, n = v.shape
+    return (v.reshape(T, n // b, b) @ Hb.T).reshape(T, n)
+
+
+def _identity_vq3(n):
+    """W = I: entry 1 = (1, 0), entry 2 = (0, 1), everything else (0, 0); unit scales."""
+    cb = np.zeros((n // 8, 64, 2), np.float16)
+    cb[:, 1, 0] = 1
+    cb[:, 2, 1] = 1
+    codes = np.zeros((n // 2, n), np.uint8)
+    p = np.arange(n // 2)
+    codes[p, 2 * p] = 1
+    codes[p, 2 * p + 1] = 2
+    return synth.VQ3Matrix(codes, cb, np.ones(n, np.float16))
+
+
+@pytest.mark.parametrize("T", [1, 8, 64, 130])
+def test_identity_weights_closed_form(vq, torch_dev, T):
+    """Gate = up = down = I (exactly representable): y = R_I(silu(x~) x~) with x~ = R_H(x s), the
+    rotations built from scipy's Hadamard matrix: the kernels' decode, products, epilogue and
+    both rotations against the definition, with no oracle in between."""
+    import scipy.special
+
+    n = 1024
+    L = synth.mlp_layer(n, n, T, seed=40 + T, outliers=False)
+    L.gate = L.up = L.down = _identity_vq3(n)
+    _say("identity weights T=%d" % T)
+    y = _run(vq, torch_dev, L, 0, vq.MLP.from_layer(L, t_max=max(T, 8)))
+    xt = _blockdiag_rotation(L.x.astype(np.float64) * L.s.astype(np.float64), 128, L.sign_h)
+    expect = _blockdiag_rotation(xt * scipy.special.expit(xt) * xt, 128, L.sign_i)
+    assert _report("identity T=%d" % T, y, expect) <= MLP_TOL
+
+
+@pytest.mark.parametrize("T", [2, 8, 64, 96])
+def test_constant_codebooks_closed_form(vq, torch_dev, T):
+    """Every centroid of gate, up and down is (c, c): each projection output is its row scale
+    times c times the sum of its input, and the sum of a rotated row is sqrt(b) times the sum of
+    the first (signed) entry of each block (the first Hadamard column is the only one that does
+    not sum to zero).  So y[t][h] = c_d sc_d[h] sqrt(b_I) sum_B d_I[Bb] a[t][Bb] with a = silu(g) v,
+    g[t][r] = c_g sc_g[r] S_t, v[t][r] = c_u sc_u[r] S_t, S_t = sqrt(b_H) sum_B d_H[Bb] u[t][Bb]."""
+    import scipy.special
+
+    H, I = 1024, 2048
+    L = synth.mlp_layer(H, I, T, seed=50 + T, outliers=False)
+    cg, cu, cd = 0.375, -0.25, 0.125
+    L.gate = synth.VQ3Matrix(L.gate.codes, np.full((I // 8, 64, 2), cg, np.float16), L.gate.sc)
+    L.up = synth.VQ3Matrix(L.up.codes, np.full((I // 8, 64, 2), cu, np.float16), L.up.sc)
+    L.down = synth.VQ3Matrix(L.down.codes, np.full((H // 8, 64, 2), cd, np.float16), L.down.sc)
+    _say("constant codebooks T=%d" % T)
+    y = _run(vq, torch_dev, L, 0, vq.MLP.from_layer(L, t_max=max(T, 8)))
+    bh, bi = L.had_block_h, L.had_block_i
+    u = L.x.astype(np.float64) * L.s.astype(np.float64)
+    S = np.sqrt(bh) * (u[:, ::bh] * L.sign_h[::bh].astype(np.float64)).sum(axis=1)
+    g = cg * L.gate.sc.astype(np.float64)[None, :] * S[:, None]
+    v = cu * L.up.sc.astype(np.float64)[None, :] * S[:, None]
+    a = g * scipy.special.expit(g) * v
+    Sa = np.sqrt(bi) * (a[:, ::bi] * L.sign_i[::bi].astype(np.float64)).sum(axis=1)
+    expect = cd * L.down.sc.astype(np.float64)[None, :] * Sa[:, None]
+    # a token's outputs all share one factor, a signed sum over the rotation blocks that can
+    # nearly cancel: its rows are measured against the largest row
+    assert _report("constant T=%d" % T, y, expect, row_scale="global") <= MLP_TOL
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_lut_argmax_ties_pick_lowest_row(vq, torch_dev, bits):
+    """Two rows per token with bitwise equal logits (same codes, scale and table entries; x and
+    the tables are small integers and powers of two, so every partial sum is exact in FP32 in any
+    order): the head must return the lower of the two rows.  The pairs are placed both ways round
+    (lower row in an earlier and in a later 32-row block than the other, same block too)."""
+    N, K, T = 4096, 1024, 4
+    top = (1 << bits) - 1
+    span = K // T
+    rng = np.random.default_rng(77 + bits)
+    codes = rng.integers(0, top + 1, size=(N, K), dtype=np.uint8)
+    lut = (rng.standard_normal((N // 8, 1 << bits)) * 0.02).astype(np.float16)
+    sc = rng.uniform(0.5, 1.5, N).astype(np.float16)
+    pairs = [(3000, 17), (40, 41), (2048, 4095), (1000, 999)]
+    x = np.zeros((T, K), np.float16)
+    for t, rows in enumerate(pairs):
+        cols = slice(t * span, (t + 1) * span)
+        x[t, cols] = 1.0
+        for j in rows:
+            lut[j // 8, top], lut[j // 8, 0] = np.float16(1.0), np.float16(0.0)
+            codes[j, :] = 0
+            codes[j, cols] = top
+            sc[j] = np.float16(1.0)
+    # every other row of those groups stays below the planted logit (span): its table entries
+    # are 0, 1 or N(0, 0.02) values, and entry 'top' appears on about a (1 / 2^bits) share of
+    # the columns only
+    packed = vq.to_device(vq.lut_pack(bits, codes, lut, sc))
+    proj = vq.LUTProjection(bits, N, K, packed, None, None, None, None, 0)
+    _say("argmax ties bits=%d" % bits)
+    idx, val = proj.argmax(vq.to_device(x))
+    torch_dev.cuda.synchronize()
+    idx, val = idx.cpu().numpy(), val.cpu().numpy()
+    assert ((idx >= 0) & (idx < N)).all(), idx
+    assert list(idx) == [min(p) for p in pairs], (list(idx), pairs)
+    assert np.array_equal(val, np.full(T, float(span), np.float32))
