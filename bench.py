@@ -90,18 +90,15 @@ def probe(device):
     log("probe done: copy of %d bytes, %d forwards" % (n, len(layers)))
 
 
-def build_stream(n_layers, device):
-    """Generate, pack and upload the 64-layer stream (host copies dropped as we go)."""
-    import numpy as np
-    import torch
+def build_stream(n_layers, device, t_max=64):
+    """Generate, pack and upload the layer stream (host copies dropped as we go)."""
+    import torch  # noqa: F401
     from concurrent.futures import ThreadPoolExecutor
 
     from bit_vector_lut_amd import synth, vqmlp
 
-    seqs = np.random.SeedSequence(0).spawn(64)
-
     def job(i):
-        L = synth.mlp_layer(H, I, 8, seed=np.random.default_rng(seqs[i]), outliers=True)
+        L = synth.stream_layer(i)
         packs = [vqmlp.pack(*m.as_u16()) for m in (L.gate, L.up, L.down)]
         return L, packs
 
@@ -112,16 +109,160 @@ def build_stream(n_layers, device):
             dev = [vqmlp.to_device(p, device) for p in packs]
             mlp = vqmlp.MLP(H, I, *dev, vqmlp.to_device(L.s, device),
                             vqmlp.to_device(L.sign_h, device), vqmlp.to_device(L.sign_i, device),
-                            L.had_block_h, L.had_block_i, t_max=8)
+                            L.had_block_h, L.had_block_i, t_max=t_max)
             layers.append((mlp, vqmlp.to_device(L.x, device)))
             if i == 0 or (i + 1) % 16 == 0:
                 log("layer %d/%d ready (%.1f s)" % (i + 1, n_layers, time.time() - t0))
     return layers
 
 
+def host_cpu():
+    """Model name of the host CPU and the cores this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return model, usable
+
+
+def timed_events(stream, fn, reps):
+    """Average ms of fn() over reps calls, HIP events on `stream` around the calls."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def capture(stream, fn):
+    """A HIP graph of fn() captured on `stream` (after one eager run)."""
+    import torch
+
+    with torch.cuda.stream(stream):
+        fn()
+    stream.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    return g
+
+
+def extra_lines(device, stream, layers):
+    """The single-layer workloads: the tiny layer (H 256, I 704, T 1: launch-bound, microseconds),
+    one 27B-like layer at T = 8 with its weights hot in the on-die cache and cold (a 1 GiB write
+    between timed forwards evicts them), the 27B-like layers at T = 64 (the fixed prefill chunk;
+    a graph over the stream's layers so the weights come from HBM), and the streaming-read rate
+    of this GPU's HBM with the library's own read kernel."""
+    import numpy as np
+    import torch
+
+    from bit_vector_lut_amd import synth, vqmlp
+
+    out = {}
+    # tiny layer, T = 1
+    L1 = synth.tiny_layer()
+    m1 = vqmlp.MLP.from_layer(L1, device=device, t_max=8)
+    x1 = vqmlp.to_device(L1.x, device)
+    y1 = torch.empty_like(x1)
+    w1 = m1.workspace(8)
+    with torch.cuda.stream(stream):
+        for _ in range(20):
+            m1.forward(x1, y1, w1, stream=stream)
+        eager_us = timed_events(stream, lambda: m1.forward(x1, y1, w1, stream=stream), 200) * 1e3
+    g1 = capture(stream, lambda: [m1.forward(x1, y1, w1, stream=stream) for _ in range(100)])
+    with torch.cuda.stream(stream):
+        g1.replay()
+        graph_us = timed_events(stream, g1.replay, 20) * 1e3 / 100
+    out["tiny_t1"] = {"workload": "tiny MLP layer H=256 I=704 T=1 (259,328 weight bytes)",
+                      "us_eager": round(eager_us, 2), "us_graph": round(graph_us, 2)}
+    log("tiny layer T=1: %.2f us per forward (back-to-back launches), %.2f us (graph)" %
+        (eager_us, graph_us))
+    del g1
+
+    # one 27B-like layer at T = 8, hot and cold
+    L2 = synth.layer27b_t8()
+    m2 = vqmlp.MLP.from_layer(L2, device=device, t_max=8)
+    x2 = vqmlp.to_device(L2.x, device)
+    y2 = torch.empty_like(x2)
+    w2 = m2.workspace(8)
+    del L2
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            m2.forward(x2, y2, w2, stream=stream)
+        hot_us = timed_events(stream, lambda: m2.forward(x2, y2, w2, stream=stream), 50) * 1e3
+        scrub = torch.empty(1 << 30, dtype=torch.uint8, device=device)
+        cold = []
+        for i in range(20):
+            scrub.fill_(i & 255)
+            cold.append(timed_events(stream, lambda: m2.forward(x2, y2, w2, stream=stream), 1))
+        del scrub
+    cold_us = float(np.median(cold)) * 1e3
+    wb = weight_bytes(H, I)
+    out["layer27b_t8"] = {
+        "workload": "one 27B-like layer H=5120 I=17408 T=8, 1% outlier channels x20, seed 0",
+        "us_hot": round(hot_us, 2), "gbps_hot": round(wb / hot_us / 1e3, 1),
+        "us_cold": round(cold_us, 2), "gbps_cold": round(wb / cold_us / 1e3, 1),
+        "frac_hbm_cold": round(wb / cold_us / 1e3 / HBM_PEAK_GBS, 4),
+        "cold": "median of 20 forwards, each after an untimed 1 GiB write"}
+    log("27B-like layer T=8: hot %.1f us (%.0f GB/s), cold %.1f us (%.0f GB/s)" %
+        (hot_us, wb / hot_us / 1e3, cold_us, wb / cold_us / 1e3))
+    del m2, x2, y2, w2
+
+    # T = 64 over the stream's layers (weights from HBM), one graph of all forwards
+    rng = np.random.default_rng(64)
+    x64 = [vqmlp.to_device(synth.activations(rng, 64, H, False), device) for _ in layers]
+    y64 = [torch.empty_like(x) for x in x64]
+    w64 = layers[0][0].workspace(64)
+    g64 = capture(stream, lambda: [m.forward(x, y, w64, stream=stream)
+                                   for (m, _), x, y in zip(layers, x64, y64)])
+    with torch.cuda.stream(stream):
+        g64.replay()
+        us64 = timed_events(stream, g64.replay, 5) * 1e3 / len(layers)
+    flops64 = 2.0 * 64 * 3 * H * I
+    out["layer27b_t64"] = {
+        "workload": "27B-like layers at T=64 (fixed prefill chunk), inputs N(0,1), one graph over "
+                    "the %d stream layers" % len(layers),
+        "us": round(us64, 2), "gbps": round(wb / us64 / 1e3, 1),
+        "frac_hbm": round(wb / us64 / 1e3 / HBM_PEAK_GBS, 4),
+        "tflops": round(flops64 / us64 / 1e6, 1),
+        "frac_mfma": round(flops64 / us64 / 1e6 / MFMA_F16_PEAK_TFLOPS, 4)}
+    log("27B-like layer T=64: %.1f us, %.0f GB/s, %.1f TFLOP/s" % (us64, wb / us64 / 1e3,
+                                                                  flops64 / us64 / 1e6))
+    del g64, x64, y64, w64
+
+    # streaming read over 4 GiB
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=device).fill_(3)
+    sink = torch.zeros(1, dtype=torch.int32, device=device)
+    with torch.cuda.stream(stream):
+        vqmlp.stream_read(buf, sink, stream)
+        ms = timed_events(stream, lambda: vqmlp.stream_read(buf, sink, stream), 10)
+    rd = buf.numel() / (ms * 1e-3) / 1e9
+    out["achievable_read"] = {"bytes": buf.numel(), "us": round(ms * 1e3, 1), "gbps": round(rd, 1),
+                              "frac_hbm": round(rd / HBM_PEAK_GBS, 4),
+                              "kernel": "k_stream_read (16-byte loads, contiguous share per "
+                                        "workgroup, 8 workgroups per CU)"}
+    log("streaming read of 4 GiB: %.1f GB/s" % rd)
+    del buf
+    return out
+
+
 def lut_weight_bytes(bits, N, K, r):
-    """Bytes one scalar-LUT projection reads from its weights: codes, tables, scales, U and V."""
-    return N * K * bits // 8 + (N // 8) * (1 << bits) * 2 + N * 2 + 2 * r * (N + K) * 2
+    """Bytes one scalar-LUT projection reads from its weights: codes (bits per weight), tables
+    (2^bits binary16 per 8 rows), row scales (binary16), U [N][r] and V [r][K] (binary16)."""
+    return N * K * bits // 8 + (N // 8) * (1 << bits) * 2 + N * 2 + r * (N + K) * 2
 
 
 def t8_mixers(device, stream, n_proj=16):
@@ -259,10 +400,12 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--layers", type=int, default=64)
-    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-t512", action="store_true")
     ap.add_argument("--no-mixers8", action="store_true")
     ap.add_argument("--no-vq2", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the tiny, single-layer, T=64 and streaming-read lines")
     ap.add_argument("--probe", action="store_true",
                     help="counter run only: a known-size copy and 4 forwards, no timing")
     args = ap.parse_args()
@@ -289,49 +432,64 @@ def main():
     ys = [torch.empty_like(x) for _, x in layers]
     stream = torch.cuda.Stream()
     log("capturing the %d-layer graph" % len(layers))
+    graph = capture(stream, lambda: [m.forward(x, y, ws, stream=stream)
+                                     for (m, x), y in zip(layers, ys)])
     with torch.cuda.stream(stream):
-        for (m, x), y in zip(layers, ys):  # eager warm-up before capture
-            m.forward(x, y, ws, stream=stream)
-    stream.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        for (m, x), y in zip(layers, ys):
-            m.forward(x, y, ws, stream=stream)
-    torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
             graph.replay()
-    e1.record(stream)
+    stream.synchronize()
     torch.cuda.synchronize()
-    ms_step = e0.elapsed_time(e1) / args.steps
+    with torch.cuda.stream(stream):
+        ms_step = timed_events(stream, graph.replay, args.steps)
+    torch.cuda.synchronize()
     bytes_step = weight_bytes(H, I) * len(layers)
     gbs = bytes_step / (ms_step * 1e-3) / 1e9
     log("T=8 stream: %.3f ms/step, %.1f GB/s" % (ms_step, gbs))
+    err_bits = vqmlp.workspace_errors(ws, stream=stream)
+    if err_bits:
+        log("FAILED: a bounded wait of the fused kernel ran out (error bits %#x)" % err_bits)
+        sys.exit(3)
+
+    # the replayed outputs of the first and last layers against the oracle
+    from oracle import oracle as O
+
+    parity = {"tol_rel_fro": 2e-3, "layers": [], "rel_fro": [], "worst_row": []}
+    oracle_s = None
+    for li in sorted({0, len(layers) - 1}):
+        L = synth.stream_layer(li)
+        t0 = time.time()
+        ref = O.mlp_forward(L)
+        if li == 0:
+            oracle_s = time.time() - t0
+        got = ys[li].cpu().numpy().view(np.float16).astype(np.float64)
+        err = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+        row = float((np.linalg.norm(got - ref, axis=1) / np.linalg.norm(ref, axis=1)).max())
+        parity["layers"].append(li)
+        parity["rel_fro"].append(round(err, 6))
+        parity["worst_row"].append(round(row, 6))
+        log("layer %d of the replayed stream against the oracle: rel_fro %.3e, worst row %.3e" %
+            (li, err, row))
+        del L
+    parity["ok"] = all(e <= 2e-3 for e in parity["rel_fro"])
+    if not parity["ok"]:
+        log("FAILED: stream output outside the tolerance")
+        print(json.dumps({"parity": parity}), flush=True)
+        sys.exit(4)
 
     # dominant kernel: the T = 8 forward is one launch of the fused kernel; its average launch
     # duration is timed with events on the stream it runs on, over back-to-back launches that
     # cycle through the layers so that every launch reads weights that are not cache-resident
     n_fw = len(layers)
-    with torch.cuda.stream(stream):
-        for i in range(n_fw):  # warm
+
+    def all_layers():
+        for i in range(n_fw):
             layers[i][0].forward(layers[i][1], ys[i], ws, stream=stream)
-        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 3
-        f0.record(stream)
-        for _ in range(reps):
-            for i in range(n_fw):
-                layers[i][0].forward(layers[i][1], ys[i], ws, stream=stream)
-        f1.record(stream)
-    f1.synchronize()
-    fw_ms = f0.elapsed_time(f1) / (reps * n_fw)
+
+    with torch.cuda.stream(stream):
+        all_layers()  # warm
+        fw_ms = timed_events(stream, all_layers, 3) / n_fw
     fw_gbs = weight_bytes(H, I) / (fw_ms * 1e-3) / 1e9
-    log("fused forward launch (events, %d back-to-back): %.1f us, %.1f GB/s" % (reps * n_fw,
+    log("fused forward launch (events, %d back-to-back): %.1f us, %.1f GB/s" % (3 * n_fw,
                                                                               fw_ms * 1e3, fw_gbs))
     traffic = measured_traffic()
 
@@ -352,14 +510,18 @@ def main():
                                "(H=5120, I=17408, one HIP graph, 6.50 GB of weights)",
                    "layers": len(layers), "T": 8, "H": H, "I": I,
                    "weight_bytes_per_layer": weight_bytes(H, I)},
-        "roofline": {"bound": "hbm", "kernel": "k_fused<5, false> (whole T=8 forward of one layer, one launch)",
+        "roofline": {"bound": "hbm", "kernel": "k_fused<5> (whole T=8 forward of one layer, one launch)",
                      "achieved": round(fw_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(fw_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": weight_bytes(H, I),
                      "us_per_launch": round(fw_ms * 1e3, 2)},
+        "parity": parity,
+        "fused_error_bits": err_bits,
     }
     del graph
-    layers_keep = layers  # noqa: F841
+
+    if not args.no_extra:
+        result.update(extra_lines(device, stream, layers))
 
     # ---------------------------------------------------------------- T = 8 token mixers
     if not args.no_mixers8:
@@ -371,7 +533,7 @@ def main():
     # ---------------------------------------------------------------- T = 512 prefill MLP
     if not args.no_t512:
         del ys
-        L5, p2, p4 = synth.config5()
+        L5, p2, p4 = synth.prefill512()
         m5 = vqmlp.MLP.from_layer(L5, device=device, t_max=512)
         mixers = [vqmlp.LUTProjection.from_proj(p, device) for p in (p2, p4)]
         x5 = vqmlp.to_device(L5.x, device)
@@ -382,48 +544,58 @@ def main():
         reps = 10
 
         def timed(fn):
-            for _ in range(3):
-                fn()
-            torch.cuda.synchronize()
-            e0.record()
-            for _ in range(reps):
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) / reps
+            """(eager ms, graph ms) per call: back-to-back calls, and replays of a graph of one."""
+            with torch.cuda.stream(stream):
+                for _ in range(3):
+                    fn()
+                eager = timed_events(stream, fn, reps)
+            g = capture(stream, fn)
+            with torch.cuda.stream(stream):
+                g.replay()
+                graphed = timed_events(stream, g.replay, reps)
+            return eager, graphed
 
-        ms5 = timed(lambda: m5.forward(x5, y5, ws5))
-        ms_mix = [timed(lambda mx=mx, y=y, w=w: mx.forward(x5, y, w))
+        ms5e, ms5 = timed(lambda: m5.forward(x5, y5, ws5, stream=stream))
+        ms_mix = [timed(lambda mx=mx, y=y, w=w: mx.forward(x5, y, w, stream=stream))
                   for mx, y, w in zip(mixers, ym, wsm)]
         flops = 2.0 * 512 * 3 * H * I
         tf = flops / (ms5 * 1e-3) / 1e12
-        log("T=512 MLP: %.1f us, %.1f TFLOP/s" % (ms5 * 1e3, tf))
+        log("T=512 MLP: %.1f us (graph), %.1f us (back-to-back), %.1f TFLOP/s" % (
+            ms5 * 1e3, ms5e * 1e3, tf))
         result["t512"] = {"workload": "27B-like VQ3 MLP prefill, T=512", "us": round(ms5 * 1e3, 1),
+                          "us_eager": round(ms5e * 1e3, 1),
                           "tflops": round(tf, 1), "peak_tflops": MFMA_F16_PEAK_TFLOPS,
                           "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "token_mixers": []}
-        for p, ms in zip((p2, p4), ms_mix):
+        for p, (mse, ms) in zip((p2, p4), ms_mix):
             fl = 2.0 * 512 * (p.N * p.K + p.rank * (p.N + p.K))
             tfm = fl / (ms * 1e-3) / 1e12
-            log("T=512 %d-bit mixer %dx%d r=%d: %.1f us, %.1f TFLOP/s" % (p.bits, p.N, p.K, p.rank,
-                                                                         ms * 1e3, tfm))
+            log("T=512 %d-bit mixer %dx%d r=%d: %.1f us (graph), %.1f TFLOP/s" % (
+                p.bits, p.N, p.K, p.rank, ms * 1e3, tfm))
             result["t512"]["token_mixers"].append(
                 {"bits": p.bits, "N": p.N, "K": p.K, "rank": p.rank, "us": round(ms * 1e3, 1),
+                 "us_eager": round(mse * 1e3, 1),
                  "tflops": round(tfm, 1), "frac": round(tfm / MFMA_F16_PEAK_TFLOPS, 4)})
 
     # ---------------------------------------------------------------- CPU oracle baseline
     if not args.no_cpu:
-        from oracle import oracle as O
-
-        L0 = synth.mlp_layer(H, I, 8, seed=np.random.default_rng(np.random.SeedSequence(0).spawn(64)[0]),
-                             outliers=True)
+        model, usable = host_cpu()
+        all_threads = O.num_threads()
+        L0 = synth.stream_layer(0)
+        O.set_num_threads(1)
         t0 = time.time()
         O.mlp_forward(L0)
-        dt = time.time() - t0
-        result["cpu_baseline"] = {"value": round(weight_bytes(H, I) / dt / 1e9, 5), "unit": "GB/s",
-                                  "cores": O.num_threads(), "kind": "oracle",
-                                  "sample": "layer 0 of the 64-layer stream, all 8 tokens "
-                                            "(one full FP64 forward, %.1f s)" % dt}
-        log("oracle: %.2f s for one layer on %d threads" % (dt, O.num_threads()))
+        one_s = time.time() - t0
+        O.set_num_threads(all_threads)
+        wb = weight_bytes(H, I)
+        result["cpu_baseline"] = {
+            "value": round(wb / oracle_s / 1e9, 5), "unit": "GB/s", "cores": all_threads,
+            "kind": "oracle",
+            "sample": "layer 0 of the 64-layer stream, all 8 tokens: one full FP64 forward "
+                      "(%.2f s on %d threads; %.2f s on 1 thread)" % (oracle_s, all_threads, one_s),
+            "value_1_thread": round(wb / one_s / 1e9, 5),
+            "host_cpu": model, "usable_cores": usable}
+        log("oracle: %.2f s for one layer on %d threads, %.2f s on 1 thread (%s, %d usable cores)"
+            % (oracle_s, all_threads, one_s, model, usable))
 
     print(json.dumps(result), flush=True)
 
