@@ -139,6 +139,23 @@ def mlp_layer(H: int, I: int, T: int, seed=0, outliers: bool = False,
                     meta={"outliers": outliers})
 
 
+def vq2_mlp_layer(H: int, I: int, T: int, seed=0, outliers: bool = False,
+                  had_block_h: int | None = None, had_block_i: int | None = None) -> MLPLayer:
+    """One MLP layer in the 2x16 format: the draw order of mlp_layer with vq2_matrix in place of
+    vq3_matrix (codes 0..15, 16 centroids per 8 rows)."""
+    rng = _rng(seed)
+    x = activations(rng, T, H, outliers)
+    s = rng.lognormal(0.0, 0.3, size=H).astype(F16)
+    sign_h = signs(rng, H)
+    sign_i = signs(rng, I)
+    gate = vq2_matrix(rng, I, H)
+    up = vq2_matrix(rng, I, H)
+    down = vq2_matrix(rng, H, I)
+    return MLPLayer(H, I, T, x, s, sign_h, sign_i, gate, up, down,
+                    had_block_h or default_block(H), had_block_i or default_block(I),
+                    meta={"outliers": outliers, "format": "2x16"})
+
+
 # ---------------------------------------------------------------------------------------------
 # Scalar-LUT projection (token-mixer format): one table of 2**bits float16 entries per 8 output
 # rows, a float16 scale per output row and rank-r float16 factors U[N, r], V[r, K].  The input is

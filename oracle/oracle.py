@@ -237,6 +237,24 @@ def vq2_matmul(codes, cb, sc, xin) -> np.ndarray:
     return x @ W.T
 
 
+def vq2_mlp_forward(layer, tokens=None):
+    """FP64 forward of an MLP layer whose three matrices are 2x16 vector LUTs (the previous
+    packages' MLP format: model card "anemll/anemll-forge-qwen3.8-27B", section "Release 0.2:
+    three-bit MLP, token-mixer rotations, distilled weights", format table, "Previous packages"
+    column).  The same steps as ``mlp_forward`` (that card's rotation and activation bullets):
+    x~ = R_H(x . s), a = silu(W_gate x~) . (W_up x~) . sign_I rotated by R_I, y = W_down a~,
+    composed from ``rotate``, ``silu`` and ``vq2_matmul``; each step is one of the oracle's
+    pinned functions."""
+    x = layer.x if tokens is None else layer.x[np.asarray(tokens)]
+    u = f16_to_f64(x) * f16_to_f64(layer.s)[None, :]
+    xt = rotate(u, layer.had_block_h, layer.sign_h)
+    g = vq2_matmul(layer.gate.codes, layer.gate.cb, layer.gate.sc, xt)
+    v = vq2_matmul(layer.up.codes, layer.up.cb, layer.up.sc, xt)
+    a = silu(g) * v
+    at = rotate(a, layer.had_block_i, layer.sign_i)
+    return vq2_matmul(layer.down.codes, layer.down.cb, layer.down.sc, at)
+
+
 def num_threads() -> int:
     return lib().orc_num_threads()
 

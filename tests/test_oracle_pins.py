@@ -449,3 +449,44 @@ def test_vq2_matmul_brute_force(oracle_mod):
             for j in range(5):
                 want[t, r] += cb[r // 8, m.codes[r // 2, j], r % 2] * sc[r] * xv[t, j]
     np.testing.assert_allclose(oracle_mod.vq2_matmul(m.codes, m.cb, m.sc, x), want, rtol=1e-13, atol=1e-15)
+
+
+def test_vq2_mlp_is_vq3_mlp_with_padded_codebooks(oracle_mod):
+    """The 2x16 MLP oracle (numpy products over materialised 2x16 weights) against the C oracle's
+    three-bit MLP (weights decoded on the fly, sums in index order) on the same layer with every
+    16-entry codebook placed first in a 64-entry one: two independent implementations of the same
+    definition, equal up to summation order."""
+    L = synth.vq2_mlp_layer(128, 256, 3, seed=8, outliers=True)
+    y2 = oracle_mod.vq2_mlp_forward(L)
+
+    def pad(m):
+        cb = np.zeros((m.N // 8, 64, 2), np.float16)
+        cb[:, :16] = m.cb
+        return synth.VQ3Matrix(m.codes, cb, m.sc)
+
+    L3 = synth.MLPLayer(L.H, L.I, L.T, L.x, L.s, L.sign_h, L.sign_i, pad(L.gate), pad(L.up),
+                        pad(L.down), L.had_block_h, L.had_block_i)
+    y3 = oracle_mod.mlp_forward(L3)
+    assert np.linalg.norm(y2 - y3) <= 1e-12 * np.linalg.norm(y3)
+    # token independence (BLAS may order a one-row product's sums differently)
+    y1 = oracle_mod.vq2_mlp_forward(L, tokens=[1])
+    assert np.linalg.norm(y1 - y2[1:2]) <= 1e-13 * np.linalg.norm(y2[1:2])
+
+
+def test_vq2_mlp_identity_weights_closed_form(oracle_mod):
+    """2x16 codebooks can hold the identity (entries (1, 0), (0, 1), (0, 0)): y = R_I(silu(x~) x~)."""
+    n = 64
+    L = synth.vq2_mlp_layer(n, n, 2, seed=4)
+    cb = np.zeros((n // 8, 16, 2), np.float16)
+    cb[:, 1, 0] = 1
+    cb[:, 2, 1] = 1
+    codes = np.zeros((n // 2, n), np.uint8)
+    for p in range(n // 2):
+        codes[p, 2 * p], codes[p, 2 * p + 1] = 1, 2
+    ident = synth.VQ2Matrix(codes, cb, np.ones(n, np.float16))
+    L.gate = L.up = L.down = ident
+    y = oracle_mod.vq2_mlp_forward(L)
+    xt = _blockdiag_rotate_ref(L.x.astype(np.float64) * L.s.astype(np.float64), L.had_block_h,
+                               L.sign_h)
+    expect = _blockdiag_rotate_ref(xt * scipy.special.expit(xt) * xt, L.had_block_i, L.sign_i)
+    assert np.allclose(y, expect, rtol=1e-13, atol=1e-14)
