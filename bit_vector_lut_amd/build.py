@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libvqmlp.so")
 SOURCES = ["vqmlp_host.cpp", "kernels.hip", "fused.hip", "tiled.hip", "vq3mm.hip", "lut8.hip",
-           "vq2.hip"]
+           "vq2.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-FP32 VALU forms are kept out of the generated code: hipcc -O3 would otherwise form

@@ -24,6 +24,12 @@ static_assert(sizeof(PackedHeader) <= kHeaderBytes, "header");
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Host only: record the text of a failure for vqmlp_last_error() (this thread) and return st.
+int set_last_error(int st, const char* fmt, ...);
+// Host only: the allocation-free forward's per-device scratch array (noalloc.hip): fetch this
+// device's address and zero it, once per device (called by vqmlp_create).
+void noalloc_setup();
+
 struct VQ3View {          // device pointers into one packed buffer
     const uint8_t* codes;     // tiles
     const uint32_t* cb;       // [N/8][64] dwords: (binary16 even row) | (binary16 odd row) << 16

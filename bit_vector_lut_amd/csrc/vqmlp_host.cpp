@@ -29,6 +29,20 @@ vqmlp_status fail(vqmlp_status st, const char* fmt, ...) {
     return st;
 }
 
+}  // namespace
+
+int vqmlp::set_last_error(int st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+namespace {
+
 vqmlp_status ok() {
     g_last_error.clear();
     return VQMLP_OK;
@@ -571,6 +585,7 @@ vqmlp_status vqmlp_create(const vqmlp_desc* desc, vqmlp_plan** out) {
         (d.sign_i && !aligned(d.sign_i, 16)))
         return fail(VQMLP_ERR_INVALID_ARG, "s_in / sign pointers must be 16-byte aligned");
     if ((st = check_device())) return st;
+    noalloc_setup();  // the allocation-free forward's scratch array on this device (once)
     PackedHeader hg, hu, hd;
     if ((st = read_device_header(d.gate, &hg, "gate"))) return st;
     if ((st = read_device_header(d.up, &hu, "up"))) return st;

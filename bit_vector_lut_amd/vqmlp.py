@@ -56,6 +56,7 @@ def lib():
             "vqmlp_forward_path": [P, I, P, P, P, S, I, P],
             "vqmlp_workspace_errors": [P, S, I, C.POINTER(C.c_uint32), P],
             "vqmlp_stream_read": [P, S, P, P],
+            "vqmlp_forward_noalloc": [P, I, P, P, P],
             "vqmlp_rotate": [I, I, I, P, P, P, P, P],
             "vqmlp_lut_packed_bytes": [I, I, I, C.POINTER(S)],
             "vqmlp_lut_pack": [I, I, I, P, P, P, P, S],
@@ -282,6 +283,16 @@ class MLP:
             workspace = self.workspace(T)
         _check(lib().vqmlp_forward_path(self._plan, T, _dptr(x), _dptr(y), _dptr(workspace),
                                         workspace.numel(), path, _stream(stream)))
+        return y
+
+    def forward_noalloc(self, x, y=None, stream=None):
+        """The forward with the library's fixed per-GPU scratch array as its workspace."""
+        import torch
+
+        if y is None:
+            y = torch.empty_like(x)
+        _check(lib().vqmlp_forward_noalloc(self._plan, x.shape[0], _dptr(x), _dptr(y),
+                                           _stream(stream)))
         return y
 
     def __del__(self):

@@ -138,6 +138,21 @@ vqmlp_status vqmlp_forward(const vqmlp_plan *plan, int T, const void *x, void *y
 vqmlp_status vqmlp_forward_path(const vqmlp_plan *plan, int T, const void *x, void *y,
                                 void *workspace, size_t workspace_bytes, int path, void *stream);
 
+/* vqmlp_forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same kernels with the workspace in a
+ * fixed 16 MiB device array that the library holds, one per GPU, until the process ends.  This
+ * call allocates nothing and frees nothing.  The array is set up (address fetched, zero-filled)
+ * by the first vqmlp_create made with that device current; without one this returns
+ * VQMLP_ERR_UNSUPPORTED.  A forward whose workspace (vqmlp_workspace_bytes) exceeds 16 MiB
+ * returns VQMLP_ERR_WORKSPACE without launching anything: at H = 5120, I = 17408 every T <= 8
+ * fits, larger T only while its tiled-path buffers do.  Every call on one GPU shares that GPU's
+ * array, which keeps the last call's contents: calls that overlap in time on one GPU (other
+ * streams, other threads) race and give wrong results; serialise them.  The fused kernel's
+ * error word (see vqmlp_forward) lives in the array, out of the caller's reach.  Other
+ * arguments and errors as vqmlp_forward. */
+vqmlp_status vqmlp_forward_noalloc(const vqmlp_plan *plan, int T, const void *x, void *y,
+                                   void *stream);
+
 /* Error bits that the fused kernel's bounded waits left in a workspace (see vqmlp_forward):
  * 1 = a projection's operand never arrived, 2 = a rotation block of the gated intermediate never
  * completed, 4 = a partial sum of the down projection never arrived.  0 means every wait of
