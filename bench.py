@@ -355,6 +355,49 @@ def t8_vq2(device, stream, n_proj=16):
     return out
 
 
+def vq2_weight_bytes(H, I):
+    """Algorithmic bytes of one 2x16 layer: 4-bit codes per pair of rows (2 bits per weight),
+    16 two-component binary16 centroids per 8 rows, binary16 row scales; gate, up and down."""
+    per = lambda N, K: N * K // 4 + (N // 8) * 16 * 4 + N * 2
+    return 2 * per(I, H) + per(H, I)
+
+
+def vq2_mlp_lines(device, stream, n_layers=8):
+    """The 2x16 MLP (previous packages' format) at the 27B-like shape: a graph of n_layers
+    distinct seeded layers (more bytes than the on-die cache), at T = 8 and at T = 64."""
+    import numpy as np
+    import torch
+
+    from bit_vector_lut_amd import synth, vqmlp
+
+    mlps, xs8, xs64 = [], [], []
+    for i in range(n_layers):
+        L = synth.vq2_mlp_layer(H, I, 8, seed=8000 + i, outliers=True)
+        mlps.append(vqmlp.MLP.from_vq2_layer(L, device=device, t_max=64))
+        xs8.append(vqmlp.to_device(L.x, device))
+        xs64.append(vqmlp.to_device(synth.activations(np.random.default_rng(8100 + i), 64, H, False),
+                                    device))
+        del L
+    wb = vq2_weight_bytes(H, I)
+    out = {"workload": "27B-like MLP in the 2x16 format (H=5120, I=17408), graph of %d layers" % n_layers,
+           "weight_bytes_per_layer": wb}
+    for T, xs in ((8, xs8), (64, xs64)):
+        ys = [torch.empty_like(x) for x in xs]
+        ws = mlps[0].workspace(T)
+        g = capture(stream, lambda: [m.forward(x, y, ws, stream=stream) for m, x, y in zip(mlps, xs, ys)])
+        with torch.cuda.stream(stream):
+            g.replay()
+            us = timed_events(stream, g.replay, 10) * 1e3 / n_layers
+        fl = 2.0 * T * 3 * H * I
+        out["t%d" % T] = {"us": round(us, 2), "gbps": round(wb / us / 1e3, 1),
+                          "frac_hbm": round(wb / us / 1e3 / HBM_PEAK_GBS, 4),
+                          "tflops": round(fl / us / 1e6, 1)}
+        log("2x16 MLP T=%d: %.1f us per layer, %.0f GB/s of weights, %.1f TFLOP/s" % (
+            T, us, wb / us / 1e3, fl / us / 1e6))
+        del g, ys, ws
+    return out
+
+
 def t8_lm_head(device, stream):
     """The four-bit LUT output head (248,320 x 5120) with in-model argmax at T = 8: one seeded
     head (636 MB of codes, more than the on-die cache), timed over back-to-back calls with
@@ -529,6 +572,7 @@ def main():
     if not args.no_vq2:
         result["t8_vq2x16"] = t8_vq2(device, stream)
         result["t8_lm_head_argmax"] = t8_lm_head(device, stream)
+        result["vq2x16_mlp"] = vq2_mlp_lines(device, stream)
 
     # ---------------------------------------------------------------- T = 512 prefill MLP
     if not args.no_t512:

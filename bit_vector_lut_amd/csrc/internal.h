@@ -69,14 +69,19 @@ struct Lut8Args {
 hipError_t launch_lut8(const Lut8Args& a, hipStream_t st);
 // 2x16 vector-LUT projection at T <= 8: y[t][r] = sc[r] * sum_j cb[r/8][code[r/2][j]][r%2] x[t][j]
 // (x as given; FP32 accumulation, one rounding).  N % 32 == 0, K % 32 == 0, K <= kVq2MaxK.
+// K split: grid.y = nsplit slices of K columns each (the matrix and x have ldk = nsplit * K
+// columns); a split product writes unscaled FP32 partial sums instead of y.
 constexpr int kVq2MaxK = 5120;
 struct Vq2Args {
-    const uint32_t* codes;  // [N/2][K/8] words, code j of a pair row at bits 4 (j % 8) of word j / 8
+    const uint32_t* codes;  // [N/2][ldk/8] words, code j of a pair row at bits 4 (j % 8) of word j / 8
     const uint32_t* cb;     // [N/8][16] centroids, binary16 (component 0) | (component 1) << 16
     const uint16_t* sc;     // [N] binary16 row scales
-    const uint16_t* x;      // [T][K] binary16
-    uint16_t* y;            // [T][N] binary16
-    int N, K, T;
+    const uint16_t* x;      // [T][ldk] binary16
+    uint16_t* y;            // [T][N] binary16 (out32 == nullptr)
+    float* out32;           // unscaled sums: out32[split * o32_s + t * o32_t + row] (or nullptr)
+    int N, K, T;            // K: columns of one slice
+    int ldk, nsplit;        // full K = nsplit * K
+    int o32_t, o32_s;
 };
 hipError_t launch_vq2_8(const Vq2Args& a, hipStream_t st);
 // Pre-pass of the T <= 8 projection: x~ = R_K(x . s . sign) ([T][K] binary16, Hadamard block hb,
@@ -127,7 +132,7 @@ int fused_tpw(int H);  // tiles per wave of the fused kernel for hidden size H (
 hipError_t launch_fused(const FusedArgs& a, int tpw, int grid, hipStream_t st);
 
 // ---- tiled matrix-core path (T > 8): decoders, epilogues, kinds
-enum { kDecVQ3 = 0, kDecLUT2 = 1, kDecLUT4 = 2, kDecDense = 3 };
+enum { kDecVQ3 = 0, kDecLUT2 = 1, kDecLUT4 = 2, kDecDense = 3, kDecVQ2 = 4 };
 enum { kEgGateUp32 = 0, kEgGateUpRot = 1, kEgScale16 = 2, kEgLUT = 3, kEgPlain32 = 4, kEgPart2 = 5,
        kEgLUTPlane = 6 };
 enum {
@@ -156,6 +161,8 @@ struct GemmArgs {
     int r;
     float norm;                // 1/sqrt(rotation block); K-split planes of vq3mm: plane scale
     int ldo;                   // output row stride (0 = N)
+    int vq2;                   // the VQ3 kinds on 2x16 matrices (codes [N/2][K/8] words,
+                               // 16 centroids per 8 rows): tiled kernels with the 2x16 decoder
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 // VQ3 products for T > 64 rows with the weights decoded in registers (vq3mm.hip): gate/up kinds

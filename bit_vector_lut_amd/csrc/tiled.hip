@@ -8,6 +8,9 @@
 //         from 64 two-component centroids per 8 rows (the packed tile layout of the library);
 //   LUT2 / LUT4   same card, format table row "Token mixers": two- and four-bit lookup tables,
 //         one table of 2^bits binary16 scalars per 8 rows;
+//   VQ2   same card, format table, "Previous packages" column: the 2x16 vector LUT, four-bit
+//         codes selecting (W[2p][j], W[2p+1][j]) from 16 two-component centroids per 8 rows
+//         (codes row-major by row pair, 8 to a 32-bit word);
 //   DENSE binary16 rows (the rank-r factor V).
 // Row scales are applied to the accumulators in the epilogue (exact in real arithmetic).
 //
@@ -33,6 +36,7 @@ template <> struct DecTraits<kDecVQ3> { static constexpr int bits = 6; };
 template <> struct DecTraits<kDecLUT2> { static constexpr int bits = 2; };
 template <> struct DecTraits<kDecLUT4> { static constexpr int bits = 4; };
 template <> struct DecTraits<kDecDense> { static constexpr int bits = 16; };
+template <> struct DecTraits<kDecVQ2> { static constexpr int bits = 4; };
 
 template <int BM, int BN, int NMAT, int DEC, int EPI>
 __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
@@ -42,7 +46,7 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
     static_assert(TM >= 1 && TN >= 1, "tile too small");
     // One LDS block, the code tables first (address 0: a lookup address needs no base), then the
     // two activation and the two weight tile buffers.
-    constexpr int kTabWords = DEC == kDecVQ3 ? 0 : (BN / 8) * 8;
+    constexpr int kTabWords = DEC == kDecVQ3 ? 0 : DEC == kDecVQ2 ? NMAT * (BN / 8) * 16 : (BN / 8) * 8;
     constexpr int kOffX = (kTabWords * 4 + 255) / 256 * 256;
     constexpr int kOffW = kOffX + 2 * BM * LDK * 2;
     constexpr int kLds = kOffW + 2 * NMAT * BN * LDK * 2;
@@ -78,6 +82,13 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
         uint16_t* t16 = reinterpret_cast<uint16_t*>(tabs);
         for (int i = tid; i < (BN / 8) * E; i += kGThreads)
             t16[(i / E) * 16 + (i % E)] = lut[size_t(row0 / 8) * E + i];
+    } else if constexpr (DEC == kDecVQ2) {
+        // group G = m * (BN / 8) + g: its 16 centroid words
+        for (int i = tid; i < NMAT * (BN / 8) * 16; i += kGThreads) {
+            const int G = i >> 4, m = G / (BN / 8), g = G % (BN / 8);
+            const uint32_t* cb = (NMAT > 1 && m) ? a.cb[1] : a.cb[0];
+            tabs[i] = cb[size_t(row0 / 8 + g) * 16 + (i & 15)];
+        }
     }
 
     // ---- per-thread global fetch of one K tile
@@ -90,6 +101,7 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
     constexpr int WTASKS = DEC == kDecVQ3 ? kGThreads * GPW  // one code record per group
                          : DEC == kDecLUT2 ? BN * 4
                          : DEC == kDecLUT4 ? BN * 4
+                         : DEC == kDecVQ2  ? NMAT * BN  // (matrix, pair row, 32-column half)
                                            : BN * 8;
     constexpr int WPT = (WTASKS + kGThreads - 1) / kGThreads;
     constexpr int WW = DEC == kDecVQ3 ? 2 : DEC == kDecLUT2 ? 1 : DEC == kDecLUT4 ? 2 : 4;
@@ -123,6 +135,16 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
                     cbase + (size_t(mt) * KT + kt) * kTileBytes) + 3 * ll + (((l & 15) >> 3) & 1);
                 wr[set][i][0] = p[0];
                 wr[set][i][1] = p[1];
+            } else if constexpr (DEC == kDecVQ2) {
+                // 32 codes (4 words) of pair row pr, columns 64 kt + 32 h ..
+                const int m = task / BN, pr = (task % BN) >> 1, h = task & 1;
+                const uint32_t* cbase = reinterpret_cast<const uint32_t*>((NMAT > 1 && m) ? a.codes[1] : a.codes[0]);
+                const u32x4 v = *reinterpret_cast<const u32x4*>(
+                    cbase + size_t(row0 / 2 + pr) * (K / 8) + kt * (kGK / 8) + 4 * h);
+                wr[set][i][0] = v[0];
+                wr[set][i][1] = v[1];
+                wr[set][i][2] = v[2];
+                wr[set][i][3] = v[3];
             } else if constexpr (DEC == kDecLUT2) {
                 const int r = task >> 2, q = task & 3;  // 16 codes per word
                 const uint32_t* p = reinterpret_cast<const uint32_t*>(a.codes[0]) +
@@ -181,6 +203,29 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
                 *reinterpret_cast<u32x2*>(&Ws[buf][m][r + 1][c]) =
                     u32x2{__builtin_amdgcn_perm(e[1], e[0], 0x07060302u),
                           __builtin_amdgcn_perm(e[3], e[2], 0x07060302u)};
+            } else if constexpr (DEC == kDecVQ2) {
+                // each code selects a centroid word: its low half goes to row 2 pr, its high half
+                // to row 2 pr + 1, column 32 h + j
+                const int m = task / BN, pr = (task % BN) >> 1, h = task & 1;
+                const uint32_t* tg = tabs + (m * (BN / 8) + (pr >> 2)) * 16;
+                uint32_t ev[16], od[16];
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const uint32_t wv = wr[set][i][q >> 2];
+                    const uint32_t c0 = (wv >> (8 * (q & 3))) & 15u, c1 = (wv >> (8 * (q & 3) + 4)) & 15u;
+                    const uint32_t e0 = tg[c0], e1 = tg[c1];
+                    ev[q] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+                    od[q] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);
+                }
+                uint16_t* d0 = &Ws[buf][m][2 * pr][32 * h];
+                uint16_t* d1 = &Ws[buf][m][2 * pr + 1][32 * h];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    *reinterpret_cast<u32x4*>(d0 + 8 * q) =
+                        u32x4{ev[4 * q], ev[4 * q + 1], ev[4 * q + 2], ev[4 * q + 3]};
+                    *reinterpret_cast<u32x4*>(d1 + 8 * q) =
+                        u32x4{od[4 * q], od[4 * q + 1], od[4 * q + 2], od[4 * q + 3]};
+                }
             } else if constexpr (DEC == kDecLUT2 || DEC == kDecLUT4) {
                 constexpr int B = DecTraits<DEC>::bits;
                 const int r = task >> 2, q = task & 3;
@@ -539,8 +584,41 @@ hipError_t launch_gateup_combine(int T, int N, int splits, const float* part,
     return hipGetLastError();
 }
 
+// The VQ3 kinds on 2x16 matrices: the tiled kernels with the 2x16 decoder at every T.
+static hipError_t launch_gemm_vq2(const GemmArgs& a, hipStream_t st) {
+    if (a.K % kGK || a.N <= 0 || a.N % 64) return hipErrorInvalidValue;
+    if (a.ksplit > 1 && (a.kind != kGemmVQ3DownSplit && a.kind != kGemmVQ3GateUpSplit))
+        return hipErrorInvalidValue;
+    if (a.ksplit > 1 && (a.K / kGK) < a.ksplit) return hipErrorInvalidValue;
+    const bool big = a.T > 64, n128 = a.N % 128 == 0;
+    switch (a.kind) {
+        case kGemmVQ3GateUp:
+            if (n128)
+                return big ? launch_gemm_t<128, 128, 2, kDecVQ2, kEgGateUp32>(a, st)
+                           : launch_gemm_t<64, 128, 2, kDecVQ2, kEgGateUp32>(a, st);
+            return big ? launch_gemm_t<128, 64, 2, kDecVQ2, kEgGateUp32>(a, st)
+                       : launch_gemm_t<64, 64, 2, kDecVQ2, kEgGateUp32>(a, st);
+        case kGemmVQ3GateUpRot:
+            if (!n128) return hipErrorInvalidValue;
+            return big ? launch_gemm_t<128, 128, 2, kDecVQ2, kEgGateUpRot>(a, st)
+                       : launch_gemm_t<64, 128, 2, kDecVQ2, kEgGateUpRot>(a, st);
+        case kGemmVQ3Down:
+            return big ? launch_gemm_t<128, 64, 1, kDecVQ2, kEgScale16>(a, st)
+                       : launch_gemm_t<64, 64, 1, kDecVQ2, kEgScale16>(a, st);
+        case kGemmVQ3DownSplit:
+            return big ? launch_gemm_t<128, 64, 1, kDecVQ2, kEgPlain32>(a, st)
+                       : launch_gemm_t<64, 64, 1, kDecVQ2, kEgPlain32>(a, st);
+        case kGemmVQ3GateUpSplit:
+            if (!n128) return hipErrorInvalidValue;
+            return big ? launch_gemm_t<128, 128, 2, kDecVQ2, kEgPart2>(a, st)
+                       : launch_gemm_t<64, 128, 2, kDecVQ2, kEgPart2>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
+    if (a.vq2) return launch_gemm_vq2(a, st);
     if (a.T >= kVq3mmMinT &&
         (a.kind == kGemmVQ3GateUp || a.kind == kGemmVQ3GateUpRot || a.kind == kGemmVQ3Down ||
          a.kind == kGemmVQ3GateUpSplit || a.kind == kGemmVQ3DownSplit || a.kind == kGemmLUT2 ||

@@ -34,7 +34,7 @@ __device__ __forceinline__ uint32_t vq2_addr(uint32_t d, uint32_t sh, uint32_t l
 
 }  // namespace
 
-// Persistent: workgroup b takes the tiles b, b + G, ...; x is staged once, and while a tile's
+// Persistent: workgroup b takes the tiles b, b + G, ... (of its K slice blockIdx.y); x is staged once, and while a tile's
 // lookups run, the next tile's code runs, centroid words and row scales are already in flight
 // (centroid tables double-buffered in LDS).
 __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
@@ -47,13 +47,14 @@ __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int K = a.K, T = a.T, N = a.N, ntile = a.N / 32, G = gridDim.x;
+    const int ldk = a.ldk, k0 = int(blockIdx.y) * K;  // this workgroup's K slice
     const int nu = K / 32, u0 = w * nu / kVW, nus = (w + 1) * nu / kVW - u0;
 
     // lane (pair i, group g): kVRunV 16-byte loads of its code run whatever nus is; words past
     // the run are unused and past the last pair row they fall in the codebook section
     const int i = l & 15, g = l >> 4;
     auto load_codes = [&](int b, uint32_t (&c)[kVRunV * 4]) {
-        const uint32_t* crun = a.codes + size_t(b * 16 + i) * (K / 8) + u0 * 4 + g * nus;
+        const uint32_t* crun = a.codes + size_t(b * 16 + i) * (ldk / 8) + k0 / 8 + u0 * 4 + g * nus;
 #pragma unroll
         for (int v = 0; v < kVRunV; ++v) {
             const u32x4a q = *reinterpret_cast<const u32x4a*>(crun + 4 * v);
@@ -83,7 +84,7 @@ __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
 #pragma unroll
         for (int k = 0; k < kXPer; ++k) {
             const int q = tid + k * kVW * 64, t = q / c8n, c8 = (q % c8n) * 8;
-            xv[k] = q < kSkinnyT * c8n && t < T ? *reinterpret_cast<const u32x4*>(a.x + size_t(t) * K + c8)
+            xv[k] = q < kSkinnyT * c8n && t < T ? *reinterpret_cast<const u32x4*>(a.x + size_t(t) * ldk + k0 + c8)
                                                : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
@@ -143,8 +144,13 @@ __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
             float v = 0.f;
 #pragma unroll
             for (int s = 0; s < kVW; ++s) v += red[s][el][eq];
-            const int t = en & 7;
-            if (t < T) a.y[size_t(t) * N + 2 * (blk * 16 + ei) + (en >> 3)] = uint16_t(f2h(v * h2f(esc)));
+            const int t = en & 7, row = 2 * (blk * 16 + ei) + (en >> 3);
+            if (t < T) {
+                if (a.out32)
+                    a.out32[size_t(blockIdx.y) * a.o32_s + size_t(t) * a.o32_t + row] = v;
+                else
+                    a.y[size_t(t) * N + row] = uint16_t(f2h(v * h2f(esc)));
+            }
         }
         if (more) {
 #pragma unroll
@@ -172,12 +178,15 @@ int vq2_cus() {
 }  // namespace
 
 hipError_t launch_vq2_8(const Vq2Args& a, hipStream_t st) {
-    if (!a.codes || !a.cb || !a.sc || !a.x || !a.y || a.N < 32 || a.N % 32 || a.K < 32 || a.K % 32 ||
-        a.K > kVMaxK || a.T < 1 || a.T > kSkinnyT)
+    if (!a.codes || !a.cb || !a.sc || !a.x || !(a.y || a.out32) || a.N < 32 || a.N % 32 ||
+        a.K < 32 || a.K % 32 || a.K > kVMaxK || a.T < 1 || a.T > kSkinnyT || a.nsplit < 1 ||
+        a.ldk != a.K * a.nsplit || (a.nsplit > 1 && !a.out32))
         return hipErrorInvalidValue;
     const int ntile = a.N / 32, cus = vq2_cus();
-    const int G = ntile < cus ? ntile : cus;
-    hipLaunchKernelGGL(k_vq2_8, dim3(G), dim3(kVW * 64), 0, st, a);
+    // persistent over the row tiles of each slice: about one workgroup per CU in all
+    const int per = (cus + a.nsplit - 1) / a.nsplit;
+    const int G = ntile < per ? ntile : per;
+    hipLaunchKernelGGL(k_vq2_8, dim3(G, a.nsplit), dim3(kVW * 64), 0, st, a);
     return hipGetLastError();
 }
 

@@ -198,6 +198,9 @@ struct vqmlp_plan {
     FusedGeom fz;
     int cus;                              // compute units: workgroups of the fused kernel
     bool tiled_ok;
+    bool vq2;                             // 2x16 matrices (vqmlp_create_vq2)
+    int v2_ng, v2_nd;                     // 2x16 at T <= 8: K slices of gate/up and of down
+                                          // (0: that path does not take the shape)
 };
 
 namespace {
@@ -266,11 +269,22 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
     const size_t o_xt = take(size_t(Tt) * H * 2);
     const size_t o_at32 = take(size_t(Tt) * I * 4);
     const size_t o_at = take(size_t(Tt) * I * 2);
-    const int dsplit = T > kSkinnyT ? gemm_split(kGemmVQ3DownSplit, H, I, T, p->cus) : 1;
+    int dsplit = T > kSkinnyT ? gemm_split(kGemmVQ3DownSplit, H, I, T, p->cus) : 1;
+    GateUpSplit gs = T > kSkinnyT ? gateup_split(I, H, T, p->cus) : GateUpSplit{I, 0, 1};
+    size_t gpart_bytes = gs.rows_split ? size_t(gs.splits) * Tt * 2 * gs.rows_split * 4 : 0;
+    if (p->vq2) {
+        // 2x16: the tiled kernels (no leftover split of gate/up) or, at T <= 8, the projection
+        // kernel's K slices: gate/up planes [ng][T][2][I], down planes [nd][T][H]
+        gs = GateUpSplit{I, 0, 1};
+        gpart_bytes = 0;
+        dsplit = gemm_split(kGemmVQ3DownSplit, H, I, std::min(T, 64), p->cus);
+        if (T <= kSkinnyT && p->v2_ng) {
+            dsplit = p->v2_nd;
+            gpart_bytes = size_t(p->v2_ng) * Tt * 2 * I * 4;
+        }
+    }
     const size_t o_dpart = take(dsplit > 1 ? size_t(dsplit) * Tt * H * 4 : 0);
-    const GateUpSplit gs = T > kSkinnyT ? gateup_split(I, H, T, p->cus) : GateUpSplit{I, 0, 1};
-    const size_t o_gpart =
-        take(gs.rows_split ? size_t(gs.splits) * Tt * 2 * gs.rows_split * 4 : 0);
+    const size_t o_gpart = take(gpart_bytes);
     w.bytes = off;
     w.dsplit = dsplit;
     w.gs = gs;
@@ -357,6 +371,7 @@ vqmlp_status run_tiled(const vqmlp_plan* p, int T, const void* x, void* y, const
     if (e != hipSuccess) return hip_fail(e, "rotate (input)");
     GemmArgs g;
     memset(&g, 0, sizeof g);
+    g.vq2 = p->vq2 ? 1 : 0;
     g.N = I;
     g.K = H;
     g.T = T;
@@ -409,6 +424,7 @@ vqmlp_status run_tiled(const vqmlp_plan* p, int T, const void* x, void* y, const
     }
     GemmArgs d;
     memset(&d, 0, sizeof d);
+    d.vq2 = p->vq2 ? 1 : 0;
     d.kind = kGemmVQ3Down;
     d.N = H;
     d.K = I;
@@ -433,6 +449,146 @@ vqmlp_status run_tiled(const vqmlp_plan* p, int T, const void* x, void* y, const
     e = launch_gemm(d, st);
     if (e != hipSuccess) return hip_fail(e, "tiled down");
     return ok();
+}
+
+// 2x16 matrices at T <= 8: rotate x, the gate and up products as unscaled FP32 planes (K
+// slices of at most kVq2MaxK columns), a = silu(g) u sign with its rotation, the down product
+// (K slices), the slice sum scaled into y.
+vqmlp_status run_vq2_skinny(const vqmlp_plan* p, int T, const void* x, void* y,
+                            const Workspace& w, hipStream_t st) {
+    const int H = p->d.H, I = p->d.I, ng = p->v2_ng, nd = p->v2_nd;
+    hipError_t e = launch_rotate(T, H, p->bh, x, 0, p->d.s_in, p->d.sign_h, w.xt, 1, st);
+    if (e != hipSuccess) return hip_fail(e, "rotate (input)");
+    Vq2Args a;
+    memset(&a, 0, sizeof a);
+    a.x = w.xt;
+    a.N = I;
+    a.K = H / ng;
+    a.T = T;
+    a.ldk = H;
+    a.nsplit = ng;
+    a.o32_t = 2 * I;
+    a.o32_s = T * 2 * I;
+    for (int m = 0; m < 2; ++m) {
+        const VQ3View& v = m ? p->up : p->gate;
+        a.codes = reinterpret_cast<const uint32_t*>(v.codes);
+        a.cb = v.cb;
+        a.sc = v.sc;
+        a.out32 = w.gpart + (m ? I : 0);
+        e = launch_vq2_8(a, st);
+        if (e != hipSuccess) return hip_fail(e, m ? "2x16 up" : "2x16 gate");
+    }
+    const bool rot128 = p->bi == 128;
+    e = launch_gateup_combine(T, I, ng, w.gpart, p->gate.sc, p->up.sc, p->d.sign_i,
+                              rot128 ? 1 : 0, float(1.0 / std::sqrt(128.0)), I, w.at, w.a_t, st);
+    if (e != hipSuccess) return hip_fail(e, "2x16 gate/up combine");
+    if (!rot128) {
+        e = launch_rotate(T, I, p->bi, w.a_t, 1, nullptr, nullptr, w.at, 1, st);
+        if (e != hipSuccess) return hip_fail(e, "rotate (intermediate)");
+    }
+    Vq2Args d;
+    memset(&d, 0, sizeof d);
+    d.codes = reinterpret_cast<const uint32_t*>(p->down.codes);
+    d.cb = p->down.cb;
+    d.sc = p->down.sc;
+    d.x = w.at;
+    d.N = H;
+    d.K = I / nd;
+    d.T = T;
+    d.ldk = I;
+    d.nsplit = nd;
+    if (nd > 1) {
+        d.out32 = w.dpart;
+        d.o32_t = H;
+        d.o32_s = T * H;
+    } else {
+        d.y = static_cast<uint16_t*>(y);
+    }
+    e = launch_vq2_8(d, st);
+    if (e != hipSuccess) return hip_fail(e, "2x16 down");
+    if (nd > 1) {
+        e = launch_split_reduce(T, H, nd, w.dpart, p->down.sc, static_cast<uint16_t*>(y), st);
+        if (e != hipSuccess) return hip_fail(e, "2x16 down slice sum");
+    }
+    return ok();
+}
+
+// Validate one packed VQ3 matrix (header read through a synchronous copy) and view it.
+vqmlp_status vq3_view_checked(const void* dev, int N, int K, const char* name, VQ3View* v) {
+    PackedHeader h;
+    vqmlp_status st;
+    if ((st = read_device_header(dev, &h, name))) return st;
+    if ((st = check_header(h, N, K, 0, kCodebook, layout_of(N, K), name))) return st;
+    *v = view_of(dev, N, K);
+    return VQMLP_OK;
+}
+
+using ViewChecked = vqmlp_status (*)(const void*, int, int, const char*, VQ3View*);
+int vq2_slices(int K);
+
+// The plan of either format: shapes, blocks, pointers, device, headers (view_checked).
+vqmlp_status create_plan(const vqmlp_desc* desc, vqmlp_plan** out, bool vq2,
+                         ViewChecked view_checked) {
+    if (!desc || !out) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_create: null pointer");
+    *out = nullptr;
+    const vqmlp_desc& d = *desc;
+    vqmlp_status st;
+    if ((st = check_shape(d.I, d.H))) return st;  // gate/up: N = I, K = H
+    if ((st = check_shape(d.H, d.I))) return st;  // down:    N = H, K = I
+    if (d.t_max < 0 || d.t_max > (1 << 20))
+        return fail(VQMLP_ERR_INVALID_ARG, "t_max=%d out of range", d.t_max);
+    const int bh = d.had_block_h ? d.had_block_h : default_block(d.H);
+    const int bi = d.had_block_i ? d.had_block_i : default_block(d.I);
+    if (!is_pow2(bh) || bh < 2 || bh > 1024 || d.H % bh)
+        return fail(VQMLP_ERR_INVALID_ARG, "Hadamard block %d does not divide H=%d", bh, d.H);
+    if (!is_pow2(bi) || bi < 2 || bi > 1024 || d.I % bi)
+        return fail(VQMLP_ERR_INVALID_ARG, "Hadamard block %d does not divide I=%d", bi, d.I);
+    if (!d.s_in) return fail(VQMLP_ERR_INVALID_ARG, "s_in is NULL");
+    if (!aligned(d.s_in, 16) || (d.sign_h && !aligned(d.sign_h, 16)) ||
+        (d.sign_i && !aligned(d.sign_i, 16)))
+        return fail(VQMLP_ERR_INVALID_ARG, "s_in / sign pointers must be 16-byte aligned");
+    if ((st = check_device())) return st;
+    noalloc_setup();  // the allocation-free forward's scratch array on this device (once)
+    VQ3View vg, vu, vd;
+    if ((st = view_checked(d.gate, d.I, d.H, "gate", &vg))) return st;
+    if ((st = view_checked(d.up, d.I, d.H, "up", &vu))) return st;
+    if ((st = view_checked(d.down, d.H, d.I, "down", &vd))) return st;
+    vqmlp_plan* p = new (std::nothrow) vqmlp_plan;
+    if (!p) return fail(VQMLP_ERR_INVALID_ARG, "out of host memory");
+    p->d = d;
+    p->bh = bh;
+    p->bi = bi;
+    p->gate = vg;
+    p->up = vu;
+    p->down = vd;
+    p->vq2 = vq2;
+    if (vq2) {
+        memset(&p->fz, 0, sizeof p->fz);  // the fused kernel reads the three-bit tiles only
+        const bool ok_i = d.I % 128 == 0;  // the gate/up combine pass rotates 128-row blocks
+        p->v2_ng = ok_i ? vq2_slices(d.H) : 0;
+        p->v2_nd = ok_i ? vq2_slices(d.I) : 0;
+    } else {
+        p->fz = fused_geom(d.H, d.I, bh, bi);
+        p->v2_ng = p->v2_nd = 0;
+    }
+    {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1)
+            cus = 256;
+        p->cus = cus;
+    }
+    p->tiled_ok = d.H % 64 == 0 && d.I % 64 == 0;
+    *out = p;
+    return ok();
+}
+
+// K slices of at most kVq2MaxK columns, each a multiple of 32 (0: none fits)
+int vq2_slices(int K) {
+    for (int s = 1; s <= 64; ++s)
+        if (K % s == 0 && (K / s) % 32 == 0 && K / s <= kVq2MaxK) return s;
+    return 0;
 }
 
 }  // namespace
@@ -566,53 +722,7 @@ vqmlp_status vqmlp_rotate(int T, int n, int b, const uint16_t* x, const uint16_t
 }
 
 vqmlp_status vqmlp_create(const vqmlp_desc* desc, vqmlp_plan** out) {
-    if (!desc || !out) return fail(VQMLP_ERR_INVALID_ARG, "vqmlp_create: null pointer");
-    *out = nullptr;
-    const vqmlp_desc& d = *desc;
-    vqmlp_status st;
-    if ((st = check_shape(d.I, d.H))) return st;  // gate/up: N = I, K = H
-    if ((st = check_shape(d.H, d.I))) return st;  // down:    N = H, K = I
-    if (d.t_max < 0 || d.t_max > (1 << 20))
-        return fail(VQMLP_ERR_INVALID_ARG, "t_max=%d out of range", d.t_max);
-    const int bh = d.had_block_h ? d.had_block_h : default_block(d.H);
-    const int bi = d.had_block_i ? d.had_block_i : default_block(d.I);
-    if (!is_pow2(bh) || bh < 2 || bh > 1024 || d.H % bh)
-        return fail(VQMLP_ERR_INVALID_ARG, "Hadamard block %d does not divide H=%d", bh, d.H);
-    if (!is_pow2(bi) || bi < 2 || bi > 1024 || d.I % bi)
-        return fail(VQMLP_ERR_INVALID_ARG, "Hadamard block %d does not divide I=%d", bi, d.I);
-    if (!d.s_in) return fail(VQMLP_ERR_INVALID_ARG, "s_in is NULL");
-    if (!aligned(d.s_in, 16) || (d.sign_h && !aligned(d.sign_h, 16)) ||
-        (d.sign_i && !aligned(d.sign_i, 16)))
-        return fail(VQMLP_ERR_INVALID_ARG, "s_in / sign pointers must be 16-byte aligned");
-    if ((st = check_device())) return st;
-    noalloc_setup();  // the allocation-free forward's scratch array on this device (once)
-    PackedHeader hg, hu, hd;
-    if ((st = read_device_header(d.gate, &hg, "gate"))) return st;
-    if ((st = read_device_header(d.up, &hu, "up"))) return st;
-    if ((st = read_device_header(d.down, &hd, "down"))) return st;
-    if ((st = check_header(hg, d.I, d.H, 0, kCodebook, layout_of(d.I, d.H), "gate"))) return st;
-    if ((st = check_header(hu, d.I, d.H, 0, kCodebook, layout_of(d.I, d.H), "up"))) return st;
-    if ((st = check_header(hd, d.H, d.I, 0, kCodebook, layout_of(d.H, d.I), "down"))) return st;
-    vqmlp_plan* p = new (std::nothrow) vqmlp_plan;
-    if (!p) return fail(VQMLP_ERR_INVALID_ARG, "out of host memory");
-    p->d = d;
-    p->bh = bh;
-    p->bi = bi;
-    p->gate = view_of(d.gate, d.I, d.H);
-    p->up = view_of(d.up, d.I, d.H);
-    p->down = view_of(d.down, d.H, d.I);
-    p->fz = fused_geom(d.H, d.I, bh, bi);
-    {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus < 1)
-            cus = 256;
-        p->cus = cus;
-    }
-    p->tiled_ok = d.H % 64 == 0 && d.I % 64 == 0;
-    *out = p;
-    return ok();
+    return create_plan(desc, out, false, vq3_view_checked);
 }
 
 vqmlp_status vqmlp_destroy(vqmlp_plan* plan) {
@@ -650,6 +760,21 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
     const size_t xy = size_t(T) * p->d.H * 2;
     if ((xb < wb + w.bytes && wb < xb + xy) || (yb < wb + w.bytes && wb < yb + xy))
         return fail(VQMLP_ERR_INVALID_ARG, "x or y overlaps the workspace");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p->vq2) {
+        // 1: the 2x16 projection kernels (T <= 8), 2: the tiled kernels; 0 picks the first for
+        // T <= 8 where they apply
+        const bool skinny = p->v2_ng > 0 && p->v2_nd > 0;
+        if (path == 1 && (T > kSkinnyT || !skinny))
+            return fail(VQMLP_ERR_UNSUPPORTED,
+                        "the 2x16 T <= 8 path takes T <= %d and I a multiple of 128 (T=%d)",
+                        kSkinnyT, T);
+        const int use = path == 0 ? (T <= kSkinnyT && skinny ? 1 : 2) : path;
+        if (use == 1) return run_vq2_skinny(p, T, x, y, w, st);
+        if (!p->tiled_ok)
+            return fail(VQMLP_ERR_UNSUPPORTED, "the tiled path takes H and I multiples of 64");
+        return run_tiled(p, T, x, y, w, st);
+    }
     // 1: the fused single-launch kernel (T <= 8), 2: the tiled kernels; 0 picks the fused
     // kernel for T <= 8 where it applies, else the tiled kernels
     const bool fused_ok = p->fz.tpw > 0;
@@ -663,7 +788,6 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
     const int use = path == 0 ? (T <= kSkinnyT && fused_ok ? 1 : 2) : path;
     if (use == 2 && !p->tiled_ok)
         return fail(VQMLP_ERR_UNSUPPORTED, "the tiled path takes H and I multiples of 64");
-    hipStream_t st = static_cast<hipStream_t>(stream);
     if (use == 1) return run_fused(p, T, x, y, w, st);
     return run_tiled(p, T, x, y, w, st);
 }
@@ -1107,6 +1231,23 @@ Layout vq2_layout(int N, int K) {
     return L;
 }
 
+// Validate one packed 2x16 matrix (header read through a synchronous copy) and view it.
+vqmlp_status vq2_view_checked(const void* dev, int N, int K, const char* name, VQ3View* v) {
+    vqmlp_status st = vq2_shape(N, K);
+    if (st) return st;
+    const Layout L = vq2_layout(N, K);
+    PackedHeader h;
+    if ((st = read_device_header(dev, &h, name))) return st;
+    if ((st = check_header(h, N, K, kKindVq2, 16, L, name))) return st;
+    const uint8_t* base = static_cast<const uint8_t*>(dev);
+    v->codes = base + L.codes_off;
+    v->cb = reinterpret_cast<const uint32_t*>(base + L.cb_off);
+    v->sc = reinterpret_cast<const uint16_t*>(base + L.sc_off);
+    v->N = N;
+    v->K = K;
+    return VQMLP_OK;
+}
+
 }  // namespace
 
 struct vqmlp_vq2_plan {
@@ -1191,6 +1332,10 @@ vqmlp_status vqmlp_vq2_create(int N, int K, const void* packed, vqmlp_vq2_plan**
     return ok();
 }
 
+vqmlp_status vqmlp_create_vq2(const vqmlp_desc* desc, vqmlp_plan** out) {
+    return create_plan(desc, out, true, vq2_view_checked);
+}
+
 vqmlp_status vqmlp_vq2_destroy(vqmlp_vq2_plan* plan) {
     delete plan;
     return ok();
@@ -1211,9 +1356,13 @@ vqmlp_status vqmlp_vq2_plan_forward(const vqmlp_vq2_plan* plan, int T, const voi
     a.sc = reinterpret_cast<const uint16_t*>(p.base + p.L.sc_off);
     a.x = static_cast<const uint16_t*>(x);
     a.y = static_cast<uint16_t*>(y);
+    a.out32 = nullptr;
     a.N = p.N;
     a.K = p.K;
     a.T = T;
+    a.ldk = p.K;
+    a.nsplit = 1;
+    a.o32_t = a.o32_s = 0;
     const hipError_t e = launch_vq2_8(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "2x16 projection");
     return ok();

@@ -50,6 +50,7 @@ def lib():
             "vqmlp_unpack": [I, I, P, S, P, P, P],
             "vqmlp_dequant": [I, I, P, P, P],
             "vqmlp_create": [C.POINTER(_Desc), C.POINTER(P)],
+            "vqmlp_create_vq2": [C.POINTER(_Desc), C.POINTER(P)],
             "vqmlp_destroy": [P],
             "vqmlp_workspace_bytes": [P, I, C.POINTER(S)],
             "vqmlp_forward": [P, I, P, P, P, S, P],
@@ -241,7 +242,8 @@ class MLP:
     """Device-resident packed weights of one MLP layer plus its plan."""
 
     def __init__(self, H, I, gate, up, down, s, sign_h=None, sign_i=None, had_block_h=0,
-                 had_block_i=0, t_max=512):
+                 had_block_i=0, t_max=512, vq2=False):
+        """vq2: the three matrices are packed 2x16 buffers (vq2_pack), else three-bit (pack)."""
         self.H, self.I, self.t_max = H, I, t_max
         self._keep = (gate, up, down, s, sign_h, sign_i)  # the plan does not own these
         d = _Desc(H, I, had_block_h, had_block_i, t_max, gate.data_ptr(), up.data_ptr(),
@@ -249,7 +251,8 @@ class MLP:
                   sign_h.data_ptr() if sign_h is not None else None,
                   sign_i.data_ptr() if sign_i is not None else None)
         self._plan = C.c_void_p()
-        _check(lib().vqmlp_create(C.byref(d), C.byref(self._plan)))
+        create = lib().vqmlp_create_vq2 if vq2 else lib().vqmlp_create
+        _check(create(C.byref(d), C.byref(self._plan)))
         self.device = gate.device
 
     @classmethod
@@ -260,6 +263,15 @@ class MLP:
                    to_device(layer.sign_h, device), to_device(layer.sign_i, device),
                    layer.had_block_h, layer.had_block_i,
                    t_max if t_max is not None else max(layer.T, 8))
+
+    @classmethod
+    def from_vq2_layer(cls, layer, device="cuda", t_max=None):
+        """Pack a ``synth.vq2_mlp_layer`` (2x16 matrices) on the host and upload it."""
+        packs = [to_device(vq2_pack(*m.as_u16()), device) for m in (layer.gate, layer.up, layer.down)]
+        return cls(layer.H, layer.I, *packs, to_device(layer.s, device),
+                   to_device(layer.sign_h, device), to_device(layer.sign_i, device),
+                   layer.had_block_h, layer.had_block_i,
+                   t_max if t_max is not None else max(layer.T, 8), vq2=True)
 
     def workspace_bytes(self, T: int) -> int:
         n = C.c_size_t()

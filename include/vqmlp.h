@@ -264,6 +264,17 @@ vqmlp_status vqmlp_vq2_unpack(int N, int K, const void *packed, size_t packed_by
  * no workspace, no allocation, no host-device synchronisation (stream: a hipStream_t, NULL =
  * default).  Errors: VQMLP_ERR_UNSUPPORTED for T > 8; VQMLP_ERR_INVALID_ARG for null or
  * unaligned pointers; VQMLP_ERR_HIP if the launch fails.  T == 0 is a no-op. */
+/* The MLP of the previous packages (same card, format table, "Previous packages" column: gate, up
+ * and down as 2x16 vector LUTs): vqmlp_create with every matrix a DEVICE buffer written by
+ * vqmlp_vq2_pack (gate and up N = I, K = H; down N = H, K = I).  Same description, rotations,
+ * activation, plan rules and errors as vqmlp_create; H and I multiples of 64.  The plan works with
+ * vqmlp_workspace_bytes, vqmlp_forward, vqmlp_forward_path, vqmlp_forward_noalloc and
+ * vqmlp_destroy: T <= 8 (with I a multiple of 128) runs the 2x16 projection kernel (path 1:
+ * gate and up as FP32 planes in K slices of at most 5120 columns, one pass for SiLU, sign and
+ * the 128-wide rotation, the down product in K slices, one pass summing the slices), any T the
+ * tiled matrix-core kernels with the 2x16 decoder (path 2). */
+vqmlp_status vqmlp_create_vq2(const vqmlp_desc *desc, vqmlp_plan **out);
+
 typedef struct vqmlp_vq2_plan vqmlp_vq2_plan;
 vqmlp_status vqmlp_vq2_create(int N, int K, const void *packed, vqmlp_vq2_plan **out);
 vqmlp_status vqmlp_vq2_destroy(vqmlp_vq2_plan *plan);

@@ -697,3 +697,43 @@ def test_lut_argmax_ties_pick_lowest_row(vq, torch_dev, bits):
     assert ((idx >= 0) & (idx < N)).all(), idx
     assert list(idx) == [min(p) for p in pairs], (list(idx), pairs)
     assert np.array_equal(val, np.full(T, float(span), np.float32))
+
+
+# ------------------------------------------------------------------ 2x16 MLP (previous format)
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 9, 64, 130])
+@pytest.mark.parametrize("H,I", [(256, 512), (512, 1024), (320, 640), (256, 704)])
+def test_vq2_mlp_small_shapes(vq, oracle_mod, torch_dev, H, I, T):
+    """The 2x16 MLP against the oracle's composition, every output: the T <= 8 projection path
+    (path 1, where I is a multiple of 128) and the tiled path with the 2x16 decoder (path 2)."""
+    L = synth.vq2_mlp_layer(H, I, T, seed=H + 5 * I + T, outliers=(T % 2 == 1))
+    _say("2x16 MLP H=%d I=%d T=%d" % (H, I, T))
+    mlp = vq.MLP.from_vq2_layer(L, t_max=max(T, 8))
+    ref = oracle_mod.vq2_mlp_forward(L)
+    paths = [0, 2] + ([1] if T <= 8 and I % 128 == 0 else [])
+    for path in paths:
+        y = _run(vq, torch_dev, L, path, mlp)
+        assert _report("2x16 H=%d I=%d T=%d path %d" % (H, I, T, path), y, ref) <= MLP_TOL
+    if T <= 8 and I % 128:
+        with pytest.raises(vq.VqmlpError) as e:
+            mlp.forward(vq.to_device(L.x), path=1)
+        assert e.value.status == vq.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("T,paths", [(8, (0, 2)), (64, (0,))])
+def test_vq2_mlp_27b_shape(vq, oracle_mod, torch_dev, T, paths):
+    """The 27B-like shape in the 2x16 format (down K = 17408: four K slices on the T <= 8 path),
+    every output; repeated calls are bitwise identical."""
+    L = synth.vq2_mlp_layer(5120, 17408, T, seed=T, outliers=(T == 8))
+    _say("2x16 MLP 27B-like T=%d" % T)
+    mlp = vq.MLP.from_vq2_layer(L, t_max=T)
+    ref = oracle_mod.vq2_mlp_forward(L)
+    x = vq.to_device(L.x)
+    ws = mlp.workspace(T)
+    for path in paths:
+        y1 = mlp.forward(x, workspace=ws, path=path)
+        y2 = mlp.forward(x, workspace=ws, path=path).clone()
+        torch_dev.cuda.synchronize()
+        assert torch_dev.equal(y1, y2), "path %d not bitwise repeatable" % path
+        assert _report("2x16 27B-like T=%d path %d" % (T, path), _f64(y1), ref) <= MLP_TOL

@@ -85,3 +85,19 @@ def test_noalloc_matches_forward_small(vq, oracle_mod, torch_dev, H, I, T1, T2):
     x2 = x[:T2].clone()
     y_ref2, y2 = _pair(vq, torch, mlp, x2)
     assert torch.equal(y2, y_ref2)
+
+
+def test_noalloc_matches_forward_vq2(vq, oracle_mod, torch_dev):
+    """A 2x16 MLP plan through the allocation-free entry: the T <= 8 projection path, then the
+    tiled path (T = 16), then a smaller T <= 8 call again."""
+    torch = torch_dev
+    L = synth.vq2_mlp_layer(512, 1024, 16, seed=31, outliers=True)
+    mlp = vq.MLP.from_vq2_layer(L, t_max=16)
+    x = vq.to_device(L.x)
+    ref = oracle_mod.vq2_mlp_forward(L)
+    for T in (8, 16, 3):
+        _say("no-alloc 2x16 T=%d" % T)
+        y_ref, y = _pair(vq, torch, mlp, x[:T].clone())
+        assert torch.equal(y, y_ref)
+        got = y.cpu().numpy().view(np.float16).astype(np.float64)
+        assert np.linalg.norm(got - ref[:T]) / np.linalg.norm(ref[:T]) <= 2e-3
