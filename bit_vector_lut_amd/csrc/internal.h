@@ -170,9 +170,9 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 struct Vq3Tile {
     int bm, bn;
 };
-Vq3Tile vq3mm_tile(int nmat);
+Vq3Tile vq3mm_tile(int nmat, int T);
 hipError_t launch_vq3mm(const GemmArgs& a, hipStream_t st);
-constexpr int kVq3mmMinT = 65;  // launch_gemm sends VQ3 kinds with at least this many rows there
+constexpr int kVq3mmMinT = 33;  // launch_gemm sends VQ3 kinds with at least this many rows there
 // K splits for a product of this kind and shape on `cus` CUs (1 = none).  A split product
 // writes unscaled FP32 planes [ksplit][T][N]; the reductions below finish it.
 int gemm_split(int kind, int N, int K, int T, int cus);

@@ -448,7 +448,7 @@ int gemm_split(int kind, int N, int K, int T, int cus) {
     const int kt = K / kGK;
     if ((kind == kGemmVQ3DownSplit || lut) && T >= kVq3mmMinT) {
         // whole rounds of workgroups, each extra plane priced at 3% of the product
-        const Vq3Tile t = vq3mm_tile(1);
+        const Vq3Tile t = vq3mm_tile(1, T);
         const long tiles = long((N + t.bn - 1) / t.bn) * ((T + t.bm - 1) / t.bm);
         int best = 1;
         double best_cost = 1e9;

@@ -54,7 +54,7 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                   __builtin_bit_cast(half8, b), c, 0, 0, 0);
 }
 
-template <int NW, int BM, int RW, int NMAT, int DEC, int EPI>
+template <int NW, int BM, int RW, int NMAT, int DEC, int EPI, int CQ>
 __global__ void __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_vq3mm(GemmArgs a) {
     constexpr bool VQ = DEC == kDecVQ3;
@@ -171,7 +171,9 @@ k_vq3mm(GemmArgs a) {
         const_cast<uint16_t*>(a.x), 0, int(uint32_t(T) * uint32_t(K) * 2u), kRsrcWord3);
 
     u32x4 xr[XCH];            // activation chunks of the next K tile
-    uint32_t rn[NMAT][RF][CW];  // code words of the next K tile
+    // code words of the next CQ K tiles: tile t lives in slot t % CQ, requested CQ tiles before
+    // the products reach it (the K loop is unrolled by CQ so every slot index is a constant)
+    uint32_t rn[CQ][NMAT][RF][CW];
     uint32_t rc[NMAT][RF][CW];  // code words being decoded
     u32x4 Bf[4][NMAT][RF];    // B operands [ks][m][j]
 
@@ -181,7 +183,7 @@ k_vq3mm(GemmArgs a) {
             xr[x] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs_x, int(xoff[x]), kt * kXK * 2, 0));
     };
-    auto load_codes = [&](int kt) {
+    auto load_codes = [&](int kt, int slot) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
@@ -191,7 +193,7 @@ k_vq3mm(GemmArgs a) {
                         u32x3, __builtin_amdgcn_raw_buffer_load_b96(rs_code[m], int(voff[j]),
                                                                     kt * kTileCode, 0));
 #pragma unroll
-                    for (int q = 0; q < 3; ++q) rn[m][j][q] = v[q];
+                    for (int q = 0; q < 3; ++q) rn[slot][m][j][q] = v[q];
                 } else {
 #pragma unroll
                     for (int h = 0; h < CW / 4; ++h) {
@@ -199,7 +201,7 @@ k_vq3mm(GemmArgs a) {
                             u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                        rs_code[m], int(voff[j]) + 16 * h, kt * kTileCode, 0));
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) rn[m][j][4 * h + q] = v[q];
+                        for (int q = 0; q < 4; ++q) rn[slot][m][j][4 * h + q] = v[q];
                     }
                 }
             }
@@ -210,13 +212,13 @@ k_vq3mm(GemmArgs a) {
         for (int x = 0; x < XCH; ++x)
             *reinterpret_cast<u32x4*>(base + x * (NT / 8) * 128) = xr[x];
     };
-    auto take_codes = [&]() {
+    auto take_codes = [&](int slot) {
 #pragma unroll
         for (int m = 0; m < NMAT; ++m)
 #pragma unroll
             for (int j = 0; j < RF; ++j)
 #pragma unroll
-                for (int q = 0; q < CW; ++q) rc[m][j][q] = rn[m][j][q];
+                for (int q = 0; q < CW; ++q) rc[m][j][q] = rn[slot][m][j][q];
     };
 
     // Decoding B operand (ks, b = (m, j)), in two phases: the four table reads (centroids of the
@@ -308,12 +310,13 @@ k_vq3mm(GemmArgs a) {
     auto tile = [&](int t) { return kb + min(t, nk - 1); };  // loads past the end repeat the last
 
     // Prologue: tables, tile 0's activations in buffer 0, its K steps 0 and 1 decoded; the codes
-    // and activations of tile 1 requested.
-    load_codes(tile(0));
+    // of tiles 1 .. CQ and the activations of tile 1 requested.
+    load_codes(tile(0), 0);
     load_x(tile(0));
     __syncthreads();  // tables
-    take_codes();
-    load_codes(tile(1));
+    take_codes(0);
+#pragma unroll
+    for (int q = 1; q <= CQ; ++q) load_codes(tile(q), q % CQ);
     stage(0);
     load_x(tile(1));
 #pragma unroll
@@ -337,7 +340,12 @@ k_vq3mm(GemmArgs a) {
     constexpr int DU = 4 * NB;  // decoded operands per K tile
     static_assert(MU % DU == 0 && MU / DU >= 1, "whole product units per decoded operand");
     constexpr int PER = MU / DU;
-    for (int t = 0; t < nk; ++t) {
+    for (int t0 = 0; t0 < nk; t0 += CQ)
+#pragma unroll
+    for (int tu = 0; tu < CQ; ++tu) {
+        const int t = t0 + tu;
+        if (t >= nk) break;
+        const int slot = (tu + 1) % CQ;  // holds tile t + 1 (t0 is a multiple of CQ)
         const uint32_t cur = uint32_t(t & 1) * kXBuf, nxt = uint32_t(kXBuf) - cur;
         u32x4 Ar[3];
         Ar[0] = readA(cur, 0, 0);
@@ -358,8 +366,8 @@ k_vq3mm(GemmArgs a) {
                 if (d + 1 < DU) {
                     const int nks = ((d + 1) / NB + 2) % 4, nb = (d + 1) % NB;
                     if (d + 1 == 2 * NB) {  // tile t's records are read: take tile t + 1's
-                        take_codes();
-                        load_codes(tile(t + 2));
+                        take_codes(slot);
+                        load_codes(tile(t + 1 + CQ), slot);
                     }
                     dec_read(nks, nb);
                 }
@@ -513,11 +521,15 @@ k_vq3mm(GemmArgs a) {
     }
 }
 
+// K tiles of codes in flight beyond the next one: at 64-token tiles a K tile's products take
+// well under the memory latency, so the codes are requested four tiles ahead
+constexpr int kCQ = 4;
+
 template <int NW, int BM, int RW, int NMAT, int EPI, int DEC = kDecVQ3>
 hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
     constexpr int BNW = NW * RW;
     const dim3 grid((a.N + BNW - 1) / BNW, (a.T + BM - 1) / BM, a.ksplit > 1 ? a.ksplit : 1);
-    hipLaunchKernelGGL((k_vq3mm<NW, BM, RW, NMAT, DEC, EPI>), grid, dim3(NW * 64), 0, st, a);
+    hipLaunchKernelGGL((k_vq3mm<NW, BM, RW, NMAT, DEC, EPI, kCQ>), grid, dim3(NW * 64), 0, st, a);
     return hipGetLastError();
 }
 
@@ -535,39 +547,49 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
 #ifndef VQ3MM_DN_RW
 #define VQ3MM_DN_RW 64
 #endif
+// 128-token tiles, or 64 when T <= 64 (fewer padded rows at the fixed 64-row prefill chunk)
 constexpr int kGuNW = VQ3MM_GU_NW, kGuBM = 128, kGuRW = VQ3MM_GU_RW;
 constexpr int kDnNW = VQ3MM_DN_NW, kDnBM = 128, kDnRW = VQ3MM_DN_RW;
+constexpr int kSmallBM = 64;
 
 }  // namespace
 
-Vq3Tile vq3mm_tile(int nmat) {
-    return nmat == 2 ? Vq3Tile{kGuBM, kGuNW * kGuRW} : Vq3Tile{kDnBM, kDnNW * kDnRW};
+Vq3Tile vq3mm_tile(int nmat, int T) {
+    const bool small = T <= kSmallBM;
+    return nmat == 2 ? Vq3Tile{small ? kSmallBM : kGuBM, kGuNW * kGuRW}
+                     : Vq3Tile{small ? kSmallBM : kDnBM, kDnNW * kDnRW};
 }
 
-hipError_t launch_vq3mm(const GemmArgs& a, hipStream_t st) {
+template <int BMG, int BMD>
+hipError_t launch_vq3mm_bm(const GemmArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     if (a.K % kXK || a.N <= 0 || a.N % 32) return hipErrorInvalidValue;
     if (a.ksplit > 1 && (a.K / kXK) < a.ksplit) return hipErrorInvalidValue;
     switch (a.kind) {
         case kGemmVQ3GateUp:
-            return launch_t<kGuNW, kGuBM, kGuRW, 2, kEgGateUp32>(a, st);
+            return launch_t<kGuNW, BMG, kGuRW, 2, kEgGateUp32>(a, st);
         case kGemmVQ3GateUpRot:  // whole 128-row rotation blocks
             if (a.N % 128) return hipErrorInvalidValue;
-            return launch_t<kGuNW, kGuBM, kGuRW, 2, kEgGateUpRot>(a, st);
+            return launch_t<kGuNW, BMG, kGuRW, 2, kEgGateUpRot>(a, st);
         case kGemmVQ3GateUpSplit:
-            return launch_t<kGuNW, kGuBM, kGuRW, 2, kEgPart2>(a, st);
+            return launch_t<kGuNW, BMG, kGuRW, 2, kEgPart2>(a, st);
         case kGemmVQ3Down:
-            return launch_t<kDnNW, kDnBM, kDnRW, 1, kEgScale16>(a, st);
+            return launch_t<kDnNW, BMD, kDnRW, 1, kEgScale16>(a, st);
         case kGemmVQ3DownSplit:
-            return launch_t<kDnNW, kDnBM, kDnRW, 1, kEgPlain32>(a, st);
+            return launch_t<kDnNW, BMD, kDnRW, 1, kEgPlain32>(a, st);
         case kGemmLUT2:  // scalar LUT + rank-r term: binary16 y, or scaled FP32 planes per K split
-            return a.ksplit > 1 ? launch_t<kDnNW, kDnBM, kDnRW, 1, kEgLUTPlane, kDecLUT2>(a, st)
-                                : launch_t<kDnNW, kDnBM, kDnRW, 1, kEgLUT, kDecLUT2>(a, st);
+            return a.ksplit > 1 ? launch_t<kDnNW, BMD, kDnRW, 1, kEgLUTPlane, kDecLUT2>(a, st)
+                                : launch_t<kDnNW, BMD, kDnRW, 1, kEgLUT, kDecLUT2>(a, st);
         case kGemmLUT4:
-            return a.ksplit > 1 ? launch_t<kDnNW, kDnBM, kDnRW, 1, kEgLUTPlane, kDecLUT4>(a, st)
-                                : launch_t<kDnNW, kDnBM, kDnRW, 1, kEgLUT, kDecLUT4>(a, st);
+            return a.ksplit > 1 ? launch_t<kDnNW, BMD, kDnRW, 1, kEgLUTPlane, kDecLUT4>(a, st)
+                                : launch_t<kDnNW, BMD, kDnRW, 1, kEgLUT, kDecLUT4>(a, st);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_vq3mm(const GemmArgs& a, hipStream_t st) {
+    return a.T <= kSmallBM ? launch_vq3mm_bm<kSmallBM, kSmallBM>(a, st)
+                           : launch_vq3mm_bm<kGuBM, kDnBM>(a, st);
 }
 
 }  // namespace vqmlp
