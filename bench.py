@@ -71,23 +71,41 @@ def measured_traffic():
         return None
 
 
-def probe(device):
-    """Counter run: a device copy of known size, then a few fused forwards on distinct layers
-    (run under rocprofv3 --pmc to scale FETCH_SIZE / WRITE_SIZE)."""
+def probe(device, t512=False):
+    """Counter run (under rocprofv3 --pmc): two kernels of known size to scale the byte counters
+    (a 256 MiB device copy, and one streaming read of the same 256 MiB with the library's read
+    kernel), then four fused T=8 forwards on four distinct seeded layers; with t512, two T=512
+    forwards of the prefill layer instead of the T=8 ones."""
     import torch
+
+    from bit_vector_lut_amd import synth, vqmlp
 
     n = 256 << 20
     src = torch.empty(n, dtype=torch.uint8, device=device).fill_(1)
     dst = torch.empty_like(src)
+    sink = torch.zeros(1, dtype=torch.int32, device=device)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
+    vqmlp.stream_read(src, sink)
+    torch.cuda.synchronize()
+    del src, dst
+    if t512:
+        L5, _, _ = synth.prefill512()
+        m5 = vqmlp.MLP.from_layer(L5, device=device, t_max=512)
+        x5 = vqmlp.to_device(L5.x, device)
+        ws5 = m5.workspace(512)
+        for _ in range(2):
+            m5.forward(x5, torch.empty_like(x5), ws5)
+        torch.cuda.synchronize()
+        log("probe done: copy and read of %d bytes, 2 T=512 forwards" % n)
+        return
     layers = build_stream(4, device)
     ws = layers[0][0].workspace(8)
     for m, x in layers:
         m.forward(x, torch.empty_like(x), ws)
     torch.cuda.synchronize()
-    log("probe done: copy of %d bytes, %d forwards" % (n, len(layers)))
+    log("probe done: copy and read of %d bytes, %d forwards" % (n, len(layers)))
 
 
 def build_stream(n_layers, device, t_max=64):
@@ -450,7 +468,9 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the tiny, single-layer, T=64 and streaming-read lines")
     ap.add_argument("--probe", action="store_true",
-                    help="counter run only: a known-size copy and 4 forwards, no timing")
+                    help="counter run only: known-size copy and read, 4 T=8 forwards, no timing")
+    ap.add_argument("--probe512", action="store_true",
+                    help="counter run only: known-size copy and read, 2 T=512 forwards")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d "
@@ -465,8 +485,8 @@ def main():
     device = "cuda:0"
     torch.cuda.set_device(0)
     vqmlp.lib()
-    if args.probe:
-        probe(device)
+    if args.probe or args.probe512:
+        probe(device, t512=args.probe512)
         return
 
     # ---------------------------------------------------------------- T = 8, 64-layer stream

@@ -511,7 +511,8 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
         // (H) the products; the code ring streams on into the next item's tiles (or reloads
         // this item's own when there is none)
         {
-            const Item pit = decode(nxt_u < a.total ? nxt_u : cur_u);
+            const bool has_next = nxt_u < a.total;  // uniform
+            const Item pit = decode(has_next ? nxt_u : cur_u);
             int nkt0, nntile, nlast_kt;
             wave_tiles(pit, nkt0, nntile, nlast_kt);
             const uint8_t* nbase0 = (pit.kind == kKindD ? a.down.codes : a.gate.codes) +
@@ -554,10 +555,13 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                     else if (t + 1 < TPW)
                         look(ring[(t + 1) % D], 0, A[cp1]);
                     if (s == 2) {
-                        // slot t + P: tile t + P of this item, or of the next one past the end
+                        // slot t + P: tile t + P of this item, or of the next one past the end.
+                        // With no next item the load repeats tile t, just read and still in the
+                        // on-die cache: the refill stays unconditional without fetching again a
+                        // tile that left the cache long ago.
                         const int tt = (t + P) % TPW;
-                        const bool own = t + P < TPW;
-                        int kt = own ? ckt0 + tt : nkt0 + tt;
+                        const bool own = t + P < TPW || !has_next;
+                        int kt = t + P < TPW ? ckt0 + tt : (has_next ? nkt0 + tt : ckt0 + t);
                         const int lim = own ? clast_kt : nlast_kt;
                         kt = kt < lim ? kt : lim;
                         const uint32_t* p0 = reinterpret_cast<const uint32_t*>(
