@@ -85,8 +85,9 @@ struct Vq2Args {
 };
 hipError_t launch_vq2_8(const Vq2Args& a, hipStream_t st);
 // Pre-pass of the T <= 8 projection: x~ = R_K(x . s . sign) ([T][K] binary16, Hadamard block hb,
-// 1 = none) and, for r > 0, the partial sums zp[c][t][j] = sum over chunk c of V[j][k] x~[t][k]
-// (chunks of lut8_chunk(K, hb) columns; x~ rounded to binary16 first).
+// 1 = none) and, for r > 0, the partial sums zp[c][t][j] = sum over part c of V[j][k] x~[t][k]
+// (rotated in chunks of lut8_chunk(K, hb) columns, summed in parts of at most 256 of them:
+// lut8_planes(K, hb) planes; x~ rounded to binary16 first).
 int lut8_chunk(int K, int hb);
 // Greedy argmax of a scalar-LUT output head (r == 0): out_idx[t] = the lowest row of the largest
 // logit sc . (W_lut x~) of token t (x~ = a.x as given), out_val[t] that logit (FP32, may be NULL).
@@ -95,6 +96,7 @@ constexpr int kArgmaxMaxGroups = 1024;  // workgroups of the argmax head at most
 int lut8_argmax_grid(int N, int cus);
 hipError_t launch_lut8_argmax(const Lut8Args& a, int cus, float* pval, int* pidx, int* out_idx,
                               float* out_val, hipStream_t st);
+int lut8_planes(int K, int hb);
 hipError_t launch_lut8_pre(int T, int K, int hb, const uint16_t* x, const uint16_t* s,
                            const int8_t* sign, const uint16_t* V, int r, uint16_t* xt, float* zp,
                            hipStream_t st);

@@ -118,9 +118,18 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
 #pragma unroll
     for (int k = 0; k < kZPer; ++k) {
         const int q = tid + k * kW * 64;
+        // the planes in order, eight loads in flight at a time
         float zsum = 0.f;
-        if (q < kSkinnyT * a.r && q / a.r < T)
-            for (int c = 0; c < a.nch; ++c) zsum += a.zp[size_t(c) * kSkinnyT * a.r + q];
+        const bool zon = q < kSkinnyT * a.r && q / a.r < T;
+        for (int c0 = 0; c0 < a.nch; c0 += 8) {
+            float zq[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                zq[c] = zon && c0 + c < a.nch ? a.zp[size_t(c0 + c) * kSkinnyT * a.r + q] : 0.f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                if (c0 + c < a.nch) zsum += zq[c];
+        }
         zv[k] = zsum;
     }
     constexpr int kXPer = kSkinnyT * kMaxK / 8 / (kW * 64);  // 16-byte chunks per thread at most
@@ -440,32 +449,34 @@ hipError_t launch_lut8_argmax(const Lut8Args& a, int cus, float* pval, int* pidx
     return hipGetLastError();
 }
 
-// ---- pre-pass: workgroup (chunk c of C = 64 V columns, group of 16 rows of V); wave t < 8 holds
-// token row t of the chunk, V consecutive columns per lane (16-byte loads of x, s, sign).  The
-// Walsh-Hadamard butterflies (blocks of hb, distances 1 .. hb/2 in that order, each pair (lo, hi)
-// -> (lo + hi, lo - hi)) run in registers below V and across lanes above, as the rotation
-// kernels do; x~ = . / sqrt(hb) is rounded to binary16, written out by group 0 and kept in LDS,
-// where the group's 16 rows of V (loaded up front) meet it on the matrix cores: wave w takes the
-// 32-column steps w, w + 8, ... (A = 16 rows of V, B = x~, column n = token n, zero for n >= 8).
+// ---- pre-pass: workgroup (chunk c of C = 64 V columns, group of 16 rows of V, part p of the
+// chunk's CS = min(C, 256) columns); wave t < 8 holds token row t of the whole chunk, V
+// consecutive columns per lane (16-byte loads of x, s, sign).  The Walsh-Hadamard butterflies
+// (blocks of hb, distances 1 .. hb/2 in that order, each pair (lo, hi) -> (lo + hi, lo - hi)) run
+// in registers below V and across lanes above (lane_xor: DPP moves for distances of 1, 2 and 8
+// lanes, swizzles for 4 and 16, a permute for 32);
+// x~ = . / sqrt(hb) is rounded to binary16, written out by the chunk's first workgroup and kept
+// in LDS for the part's columns, where the group's 16 rows of V (one 16-byte load per thread,
+// issued first) meet it on the matrix cores: wave w takes the 32-column steps w, w + 8, ... (A =
+// 16 rows of V, B = x~, column n = token n, zero for n >= 8).  Partial sums of z go to plane
+// c * (C / CS) + p.
 template <int V>
 __global__ void __launch_bounds__(512) k_lut8_pre(int T, int K, int hb, const uint16_t* x,
                                                   const uint16_t* s, const int8_t* sign,
                                                   const uint16_t* Vm, int r, uint16_t* xt,
                                                   float* zp, float norm) {
-    constexpr int C = 64 * V, XR = C + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t vs[16 * C];
+    constexpr int C = 64 * V, CS = C < 256 ? C : 256, XR = CS + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t vs[16 * CS];
     __shared__ __attribute__((aligned(16))) uint16_t xh[kSkinnyT * XR];
     __shared__ f32x4 zred[8][64];
-    const int tid = threadIdx.x, l = tid & 63, w = tid >> 6, c = blockIdx.x, rg = blockIdx.y;
+    const int tid = threadIdx.x, l = tid & 63, w = tid >> 6;
+    const int c = blockIdx.x, rg = blockIdx.y, part = blockIdx.z;
     const int c0 = c * C, col = c0 + V * l;
-    // the group's V rows: 16 x C in 16-byte chunks, issued first
-    constexpr int kVPer = (16 * C / 8 + 511) / 512;
-    u32x4 vv[kVPer];
-#pragma unroll
-    for (int k = 0; k < kVPer; ++k) {
-        const int q = tid + 512 * k, jr = q / (C / 8), cc = (q % (C / 8)) * 8;
-        vv[k] = r > 0 && q < 16 * C / 8 ? *reinterpret_cast<const u32x4*>(Vm + size_t(rg * 16 + jr) * K + c0 + cc)
-                                        : u32x4{0u, 0u, 0u, 0u};
+    // the group's V rows over the part's columns: 16 x CS in 16-byte chunks, issued first
+    u32x4 vv = u32x4{0u, 0u, 0u, 0u};
+    if (r > 0 && tid < 2 * CS) {
+        const int jr = tid / (CS / 8), cc = (tid % (CS / 8)) * 8;
+        vv = *reinterpret_cast<const u32x4*>(Vm + size_t(rg * 16 + jr) * K + c0 + part * CS + cc);
     }
     // row w of x . s . sign
     float v[V];
@@ -513,32 +524,52 @@ __global__ void __launch_bounds__(512) k_lut8_pre(int T, int K, int hb, const ui
                     v[e | h] = x0 - x1;
                 }
         }
-    for (int h = V; h < hb; h <<= 1) {
-        const int d = h / V;
-        const bool upper = (l & d) != 0;
+    // across lanes: distance V d pairs lane l with l ^ d; the upper lane takes (lo - hi) as
+    // partner - own, the lower one own + partner (a multiply by -1 or 1 is exact, so the fused
+    // form rounds as the plain sum does)
+#define VQ_PRE_STAGE(DD)                                                \
+    if (V * DD < hb) {                                                  \
+        const float sg = (l & DD) ? -1.f : 1.f;                         \
+        _Pragma("unroll") for (int e = 0; e < V; ++e)                   \
+            v[e] = __builtin_fmaf(v[e], sg, lane_xor<DD>(v[e]));        \
+    }
+    VQ_PRE_STAGE(1) VQ_PRE_STAGE(2) VQ_PRE_STAGE(4) VQ_PRE_STAGE(8) VQ_PRE_STAGE(16) VQ_PRE_STAGE(32)
+#undef VQ_PRE_STAGE
+    uint32_t hp[(V + 1) / 2];
 #pragma unroll
-        for (int e = 0; e < V; ++e) {
-            const float p = __shfl_xor(v[e], d);
-            v[e] = upper ? p - v[e] : v[e] + p;
+    for (int e = 0; e < V; e += 2)
+        hp[e / 2] = f2h(v[e] * norm) | (e + 1 < V ? f2h(v[e + 1] * norm) << 16 : 0u);
+    if (rg == 0 && part == 0 && w < T) {
+        uint16_t* dst = xt + size_t(w) * K + col;
+        if constexpr (V >= 8) {
+#pragma unroll
+            for (int q = 0; q < V / 8; ++q)
+                *reinterpret_cast<u32x4*>(dst + 8 * q) = u32x4{hp[4 * q], hp[4 * q + 1], hp[4 * q + 2], hp[4 * q + 3]};
+        } else if constexpr (V >= 2) {
+#pragma unroll
+            for (int q = 0; q < V / 2; ++q) *reinterpret_cast<uint32_t*>(dst + 2 * q) = hp[q];
+        } else {
+            *dst = uint16_t(hp[0]);
         }
     }
-#pragma unroll
-    for (int e = 0; e < V; ++e) {
-        const uint16_t hv = uint16_t(f2h(v[e] * norm));
-        if (rg == 0 && w < T) xt[size_t(w) * K + col + e] = hv;
-        xh[w * XR + V * l + e] = hv;  // z is formed from the rounded x~, as the product reads it
-    }
-#pragma unroll
-    for (int k = 0; k < kVPer; ++k) {
-        const int q = tid + 512 * k;
-        if (q < 16 * C / 8) *reinterpret_cast<u32x4*>(&vs[(q / (C / 8)) * C + (q % (C / 8)) * 8]) = vv[k];
-    }
     if (r == 0) return;
+    // z is formed from the rounded x~, as the product reads it: the part's columns into LDS
+    const int lc = V * l - part * CS;
+    if (lc >= 0 && lc < CS) {
+#pragma unroll
+        for (int e = 0; e < V; e += 2) {
+            if (V >= 2)
+                *reinterpret_cast<uint32_t*>(&xh[w * XR + lc + e]) = hp[e / 2];
+            else
+                xh[w * XR + lc] = uint16_t(hp[0]);
+        }
+    }
+    if (tid < 2 * CS) *reinterpret_cast<u32x4*>(&vs[(tid / (CS / 8)) * CS + (tid % (CS / 8)) * 8]) = vv;
     __syncthreads();
     const int i = l & 15, g = l >> 4;
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kk = 32 * w; kk < C; kk += 256) {
-        const u32x4 A = *reinterpret_cast<const u32x4*>(&vs[i * C + kk + 8 * g]);
+    for (int kk = 32 * w; kk < CS; kk += 256) {
+        const u32x4 A = *reinterpret_cast<const u32x4*>(&vs[i * CS + kk + 8 * g]);
         const u32x4 B = i < kSkinnyT ? *reinterpret_cast<const u32x4*>(&xh[(i < kSkinnyT ? i : 0) * XR + kk + 8 * g])
                                      : u32x4{0u, 0u, 0u, 0u};
         acc = mfma16x16x32(A, B, acc);
@@ -552,7 +583,8 @@ __global__ void __launch_bounds__(512) k_lut8_pre(int T, int K, int hb, const ui
             float sum = 0.f;
 #pragma unroll
             for (int ww = 0; ww < 8; ++ww) sum += zred[ww][ll][q];
-            zp[(size_t(c) * kSkinnyT + t) * r + rg * 16 + jl] = sum;
+            const int pl = c * (C / CS) + part;
+            zp[(size_t(pl) * kSkinnyT + t) * r + rg * 16 + jl] = sum;
         }
     }
 }
@@ -567,6 +599,11 @@ int lut8_chunk(int K, int hb) {
     return best;
 }
 
+int lut8_planes(int K, int hb) {
+    const int C = lut8_chunk(K, hb);
+    return C < 64 ? 0 : K / (C < 256 ? C : 256);
+}
+
 hipError_t launch_lut8_pre(int T, int K, int hb, const uint16_t* x, const uint16_t* s,
                            const int8_t* sign, const uint16_t* V, int r, uint16_t* xt, float* zp,
                            hipStream_t st) {
@@ -575,7 +612,8 @@ hipError_t launch_lut8_pre(int T, int K, int hb, const uint16_t* x, const uint16
         hb < 1 || hb > 1024 || (hb & (hb - 1)))
         return hipErrorInvalidValue;
     const float norm = float(1.0 / __builtin_sqrt(double(hb)));
-    const dim3 grid(K / C, r > 0 ? r / 16 : 1);
+    // z's parts: chunks of more than 256 columns are cut in 256-column parts (one workgroup each)
+    const dim3 grid(K / C, r > 0 ? r / 16 : 1, r > 0 && C > 256 ? C / 256 : 1);
 #define VQ_PRE(VV)                                                                                \
     if (C == 64 * VV) {                                                                           \
         hipLaunchKernelGGL(k_lut8_pre<VV>, grid, dim3(512), 0, st, T, K, hb, x, s, sign, V, r, xt, \

@@ -1039,7 +1039,7 @@ vqmlp_status lut_run(const vqmlp_lut_plan& p, int T, const void* x, void* y, voi
         q.y = static_cast<uint16_t*>(y);
         q.U = U;
         q.zp = zp;
-        q.nch = K / lut8_chunk(K, hb);
+        q.nch = lut8_planes(K, hb);
         q.bits = bits;
         q.N = N;
         q.K = K;

@@ -354,6 +354,8 @@ LUT8_CASES = [  # decode-size T: the code-stream kernel (K <= 5120), and K past 
     (128, 1024, 4, 20, 1024),   # rank not a multiple of 8: tiled kernels
     (64, 1024, 7, 256, 256),    # largest rank
     (128, 512, 6, 32, 0),       # no rotation
+    (128, 768, 8, 32, 256),     # 256-column chunks (4 columns per lane in the pre-pass)
+    (64, 384, 4, 16, 128),      # 128-column chunks (2 columns per lane)
 ]
 
 
