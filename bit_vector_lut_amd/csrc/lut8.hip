@@ -55,7 +55,6 @@ __device__ __forceinline__ uint32_t look_pair2(const char* tb, uint32_t lb, uint
     return *reinterpret_cast<const uint32_t*>(tb + lut_addr(d, sh, lb));
 }
 constexpr int kMaxR = 256;              // rank of the low-rank term
-constexpr int kUPre = 8;                // 16-byte chunks of a U row held from the start (r <= 64)
 typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));  // 4-byte aligned
 }  // namespace
 
@@ -64,12 +63,15 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
     constexpr int CW = BITS == 2 ? 1 : 2;  // code words per lane and unit
     // one LDS block with the tables at address 0 (a lookup address is the entry and lane bits)
     constexpr int kOffX = 2 * kTabDw * 4, kOffRed = kOffX + kSkinnyT * kXRow * 2;
-    constexpr int kOffZ = kOffRed + kW * 64 * 16;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[kOffZ + kSkinnyT * kMaxR * 4];
+    constexpr int kOffZ = kOffRed + kW * 64 * 16, kOffZP = kOffZ + kSkinnyT * kMaxR * 4;
+    constexpr int kOffU = kOffZP + kSkinnyT * kMaxR * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kOffU + 32 * kMaxR * 2];
     auto& tab = *reinterpret_cast<uint32_t (*)[2][kTabDw]>(lds);
     auto& xs = *reinterpret_cast<uint16_t (*)[kSkinnyT][kXRow]>(lds + kOffX);
     auto& red = *reinterpret_cast<f32x4 (*)[kW][64]>(lds + kOffRed);
-    float* zs = reinterpret_cast<float*>(lds + kOffZ);  // z [8][r] (rows past T zero)
+    float* zs = reinterpret_cast<float*>(lds + kOffZ);    // z [8][r] (rows past T zero)
+    float* zpart = reinterpret_cast<float*>(lds + kOffZP);  // partial sums of z by plane class
+    uint16_t* us = reinterpret_cast<uint16_t*>(lds + kOffU);  // U rows of the workgroup [32][r]
 
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -94,17 +96,19 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
         for (int e = 0; e < 4; ++e) cw[4 * v + e] = q[e];
     }
 
-    // ---- the epilogue's U row (threads 0 .. 255 own one output row each), requested now
+    // ---- the epilogue's U rows, requested now: the workgroup's 32 rows are one contiguous block
+    // of 32 r binary16, one 16-byte chunk per thread (threads 0 .. 255 own one output each)
     const int ert = tid >> 7, ej = tid & 127, ell = ej >> 2, eq = ej & 3;
     const int el = (ell >> 3) * 16 + (ell & 7);  // lanes holding tokens 0 .. 7
     const int erow = row0 + ert * 16 + 4 * (el >> 4) + eq;
-    const float esc = tid < 256 ? h2f(a.sc[erow]) : 0.f;
-    u32x4 upre[kUPre];
-#pragma unroll
-    for (int c = 0; c < kUPre; ++c)
-        upre[c] = tid < 256 && 8 * c < a.r
-                      ? *reinterpret_cast<const u32x4*>(a.U + size_t(erow) * a.r + 8 * c)
-                      : u32x4{0u, 0u, 0u, 0u};
+    // Loads are issued without a branch around them (clamped to a valid address where the value
+    // is not needed): a load under a divergent branch has its value used inside the branch, and
+    // that wait would cover every load issued before it.
+    const uint16_t escb = a.sc[tid < 256 ? erow : row0];
+    const int nuc = 4 * a.r;  // 16-byte chunks of the 32 U rows
+    u32x4 uv = u32x4{0u, 0u, 0u, 0u};
+    if (a.r > 0)  // uniform
+        uv = *reinterpret_cast<const u32x4*>(a.U + size_t(row0) * a.r + 8 * (tid < nuc ? tid : 0));
 
     // ---- every other global load before the first LDS store (a store that needs a loaded value
     // waits for every older load, so one round trip covers them all): table entries (thread: row
@@ -113,46 +117,87 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
     const int grp = (row0 + trt * 16) / 8 + ((tc & 15) >> 3);
     const uint32_t t0 = a.lut[BITS == 2 ? grp * 4 + (te & 3) : grp * 16 + te];
     const uint32_t t1 = BITS == 2 ? a.lut[grp * 4 + (te >> 2)] : 0u;
-    constexpr int kZPer = kSkinnyT * kMaxR / (kW * 64);
-    float zv[kZPer];
+    // z = the sum of the pre-pass planes: ZG threads share an entry q, thread class p summing the
+    // planes p, p + ZG, ... in order; the classes are summed in order after the barrier (entries
+    // of tokens past T are zero).  The first kZL planes of the first entry are requested here and
+    // summed after the x~ loads are issued; more planes or a second entry (E > 1024) follow.
+    const int E = kSkinnyT * a.r, ZG = E == 0 || E >= kW * 64 ? 1 : (kW * 64) / E;
+    constexpr int kZL = 16;
+    auto zentry = [&](int k, int& q, int& p) -> bool {
+        q = ZG > 1 ? tid % E : tid + k * kW * 64;
+        p = ZG > 1 ? tid / E : 0;
+        return (k == 0 || ZG == 1) && p < ZG && q < E && q / a.r < T;
+    };
+    // (with r == 0 the first batch reads the codes instead, a valid address, and is discarded)
+    const float* zsrc = a.r > 0 ? a.zp : reinterpret_cast<const float*>(a.codes);
+    auto zload = [&](float (&zq)[kZL], int c0, int q) {
 #pragma unroll
-    for (int k = 0; k < kZPer; ++k) {
-        const int q = tid + k * kW * 64;
-        // the planes in order, eight loads in flight at a time
-        float zsum = 0.f;
-        const bool zon = q < kSkinnyT * a.r && q / a.r < T;
-        for (int c0 = 0; c0 < a.nch; c0 += 8) {
-            float zq[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                zq[c] = zon && c0 + c < a.nch ? a.zp[size_t(c0 + c) * kSkinnyT * a.r + q] : 0.f;
-#pragma unroll
-            for (int c = 0; c < 8; ++c)
-                if (c0 + c < a.nch) zsum += zq[c];
+        for (int c = 0; c < kZL; ++c) {
+            const int pl = c0 + c * ZG < a.nch ? c0 + c * ZG : 0;
+            zq[c] = zsrc[size_t(pl) * E + q];
         }
-        zv[k] = zsum;
-    }
+    };
+    auto zadd = [&](float& zsum, const float (&zq)[kZL], int c0) {
+#pragma unroll
+        for (int c = 0; c < kZL; ++c)
+            if (c0 + c * ZG < a.nch) zsum += zq[c];
+    };
+    int zq0, zp0;
+    const bool zon0 = a.r > 0 && zentry(0, zq0, zp0);
+    float zfirst[kZL];
+    zload(zfirst, a.r > 0 ? zp0 : 0, zon0 ? zq0 : 0);
     constexpr int kXPer = kSkinnyT * kMaxK / 8 / (kW * 64);  // 16-byte chunks per thread at most
     const int c8n = K / 8;
     u32x4 xv[kXPer];
 #pragma unroll
     for (int k = 0; k < kXPer; ++k) {
         const int q = tid + k * kW * 64, t = q / c8n, c8 = (q % c8n) * 8;
-        xv[k] = q < kSkinnyT * c8n && t < T ? *reinterpret_cast<const u32x4*>(a.x + size_t(t) * K + c8)
-                                           : u32x4{0u, 0u, 0u, 0u};
+        const bool on = q < kSkinnyT * c8n && t < T;
+        xv[k] = *reinterpret_cast<const u32x4*>(a.x + (on ? size_t(t) * K + c8 : 0));
+        if (!on) xv[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+    float zv[2] = {0.f, 0.f};
+    if (a.r > 0) {  // uniform
+        float zsum = 0.f;
+        zadd(zsum, zfirst, zp0);
+        for (int c0 = zp0 + kZL * ZG; c0 < a.nch; c0 += kZL * ZG) {
+            float zq[kZL];
+            zload(zq, c0, zon0 ? zq0 : 0);
+            zadd(zsum, zq, c0);
+        }
+        zv[0] = zon0 ? zsum : 0.f;
+        if (ZG == 1 && E > kW * 64) {
+            int q1, p1;
+            const bool zon1 = zentry(1, q1, p1);
+            float zsum1 = 0.f;
+            for (int c0 = 0; c0 < a.nch; c0 += kZL) {
+                float zq[kZL];
+                zload(zq, c0, zon1 ? q1 : 0);
+                zadd(zsum1, zq, c0);
+            }
+            zv[1] = zon1 ? zsum1 : 0.f;
+        }
     }
     tab[trt][te * 32 + tc] = BITS == 2 ? (t0 | (t1 << 16)) : t0;
+    if (ZG > 1) {
+        if (tid < ZG * E) zpart[tid] = zv[0];  // class tid / E, entry tid % E
+    } else {
 #pragma unroll
-    for (int k = 0; k < kZPer; ++k) {
-        const int q = tid + k * kW * 64;
-        if (q < kSkinnyT * a.r) zs[q] = zv[k];
+        for (int k = 0; k < 2; ++k)
+            if (tid + k * kW * 64 < E) zpart[tid + k * kW * 64] = zv[k];
     }
+    if (tid < nuc) *reinterpret_cast<u32x4*>(us + 8 * tid) = uv;
 #pragma unroll
     for (int k = 0; k < kXPer; ++k) {
         const int q = tid + k * kW * 64, t = q / c8n, c8 = (q % c8n) * 8;
         if (q < kSkinnyT * c8n) *reinterpret_cast<u32x4*>(&xs[t][c8]) = xv[k];
     }
     __syncthreads();
+    for (int q = tid; q < E; q += kW * 64) {
+        float zsum = 0.f;
+        for (int p = 0; p < ZG; ++p) zsum += zpart[p * E + q];
+        zs[q] = zsum;
+    }
 
     // ---- products
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -191,22 +236,19 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
         for (int s = 0; s < kKS; ++s) v += red[ert * kKS + s][el][eq];
         const int t = el & 15;
         if (t < T) {
-            v *= esc;
-            // rank-r term in FP32: U row chunks of 8 (the first kUPre held since the start)
+            v *= h2f(escb);
+            // rank-r term in FP32: the U row from LDS in chunks of 8
             float rs = 0.f;
             const float* zt = zs + t * a.r;
-            auto chunk = [&](const u32x4& uv, int c) {
+            const uint16_t* ur = us + (erow - row0) * a.r;
+            for (int c = 0; 8 * c < a.r; ++c) {
+                const u32x4 u8 = *reinterpret_cast<const u32x4*>(ur + 8 * c);
                 const f32x4 z0 = *reinterpret_cast<const f32x4*>(zt + 8 * c);
                 const f32x4 z1 = *reinterpret_cast<const f32x4*>(zt + 8 * c + 4);
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
-                    rs += h2f(uint16_t(uv[e / 2] >> (16 * (e & 1)))) * (e < 4 ? z0[e] : z1[e - 4]);
-            };
-#pragma unroll
-            for (int c = 0; c < kUPre; ++c)
-                if (8 * c < a.r) chunk(upre[c], c);
-            for (int c = kUPre; 8 * c < a.r; ++c)
-                chunk(*reinterpret_cast<const u32x4*>(a.U + size_t(erow) * a.r + 8 * c), c);
+                    rs += h2f(uint16_t(u8[e / 2] >> (16 * (e & 1)))) * (e < 4 ? z0[e] : z1[e - 4]);
+            }
             v += rs;
             a.y[size_t(t) * N + erow] = uint16_t(f2h(v));
         }

@@ -83,9 +83,12 @@ __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
         u32x4 xv[kXPer];
 #pragma unroll
         for (int k = 0; k < kXPer; ++k) {
+            // no branch around the load (a load under a divergent branch is waited for inside
+            // it, and that wait covers every older load): a valid address, zeroed if unused
             const int q = tid + k * kVW * 64, t = q / c8n, c8 = (q % c8n) * 8;
-            xv[k] = q < kSkinnyT * c8n && t < T ? *reinterpret_cast<const u32x4*>(a.x + size_t(t) * ldk + k0 + c8)
-                                               : u32x4{0u, 0u, 0u, 0u};
+            const bool on = q < kSkinnyT * c8n && t < T;
+            xv[k] = *reinterpret_cast<const u32x4*>(a.x + (on ? size_t(t) * ldk + k0 + c8 : 0));
+            if (!on) xv[k] = u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int k = 0; k < kXPer; ++k) {
