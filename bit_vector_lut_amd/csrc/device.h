@@ -69,28 +69,6 @@ __device__ __forceinline__ uint32_t code_of(uint32_t d0, uint32_t d1, uint32_t d
     return code_shl<Q, 0>(d0, d1, d2);
 }
 
-// The value of lane l ^ D (D a power of two below 64) in lane l of a wave: row-local DPP moves for
-// 1 (quad_perm [1,0,3,2]), 2 (quad_perm [2,3,0,1]) and 8 (row_ror:8, which is xor 8 inside a row
-// of 16), a swizzle inside each half-wave for 4 and 16 (bit-mask mode: xor mask D, and mask 0x1F),
-// a backward permute across the halves for 32.
-template <int D>
-__device__ __forceinline__ float lane_xor(float v) {
-    static_assert(D > 0 && D < 64 && (D & (D - 1)) == 0, "lane distance");
-    const int i = __builtin_bit_cast(int, v);
-    int r;
-    if constexpr (D == 1)
-        r = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false);
-    else if constexpr (D == 2)
-        r = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false);
-    else if constexpr (D == 8)
-        r = __builtin_amdgcn_mov_dpp(i, 0x128, 0xF, 0xF, false);
-    else if constexpr (D == 4 || D == 16)
-        r = __builtin_amdgcn_ds_swizzle(i, (D << 10) | 0x1F);
-    else
-        r = __builtin_amdgcn_ds_bpermute(int(((threadIdx.x & 63) ^ D) << 2), i);
-    return __builtin_bit_cast(float, r);
-}
-
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a),
                                                   __builtin_bit_cast(half8, b), c, 0, 0, 0);

@@ -35,6 +35,28 @@ constexpr int kMaxU = (kMaxK / 64 + kKS - 1) / kKS;  // units per slice
 constexpr int kTabDw = 16 * 32;         // one table: 16 entries x 32 bank columns
 
 typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+// The value of lane l ^ D (D a power of two below 64) in lane l of a wave: row-local DPP moves for
+// 1 (quad_perm [1,0,3,2]), 2 (quad_perm [2,3,0,1]) and 8 (row_ror:8, which is xor 8 inside a row
+// of 16), a swizzle inside each half-wave for 4 and 16 (bit-mask mode: xor mask D, and mask 0x1F),
+// a backward permute across the halves for 32.
+template <int D>
+__device__ __forceinline__ float lane_xor(float v) {
+    static_assert(D > 0 && D < 64 && (D & (D - 1)) == 0, "lane distance");
+    const int i = __builtin_bit_cast(int, v);
+    int r;
+    if constexpr (D == 1)
+        r = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, false);
+    else if constexpr (D == 2)
+        r = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, false);
+    else if constexpr (D == 8)
+        r = __builtin_amdgcn_mov_dpp(i, 0x128, 0xF, 0xF, false);
+    else if constexpr (D == 4 || D == 16)
+        r = __builtin_amdgcn_ds_swizzle(i, (D << 10) | 0x1F);
+    else
+        r = __builtin_amdgcn_ds_bpermute(int(((threadIdx.x & 63) ^ D) << 2), i);
+    return __builtin_bit_cast(float, r);
+}
+
 // The table words of two 4-bit codes (bits sh..sh+3 and sh+4..sh+7 of d) as one binary16 pair:
 // two 16-bit LDS reads joined by one byte permute (two field extracts, two address merges).
 // LDS byte address of the entry that bits sh..sh+3 of d select, in the table column lb: a field
