@@ -82,6 +82,12 @@ struct Vq2Args {
     int N, K, T;            // K: columns of one slice
     int ldk, nsplit;        // full K = nsplit * K
     int o32_t, o32_s;
+    // A second matrix over the same x (gate and up in one launch; out32 required): grid rows
+    // nsplit .. 2 nsplit - 1 take it and write their planes at out32 + o32_m.  NULL: one matrix.
+    const uint32_t* codes2;
+    const uint32_t* cb2;
+    const uint16_t* sc2;
+    int o32_m;
 };
 hipError_t launch_vq2_8(const Vq2Args& a, hipStream_t st);
 // Pre-pass of the T <= 8 projection: x~ = R_K(x . s . sign) ([T][K] binary16, Hadamard block hb,

@@ -34,7 +34,7 @@ __device__ __forceinline__ uint32_t vq2_addr(uint32_t d, uint32_t sh, uint32_t l
 
 }  // namespace
 
-// Persistent: workgroup b takes the tiles b, b + G, ... (of its K slice blockIdx.y); x is staged once, and while a tile's
+// Persistent: workgroup b takes the tiles b, b + G, ... of its (matrix, K slice) grid row; x is staged once, and while a tile's
 // lookups run, the next tile's code runs, centroid words and row scales are already in flight
 // (centroid tables double-buffered in LDS).
 __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
@@ -47,14 +47,19 @@ __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int K = a.K, T = a.T, N = a.N, ntile = a.N / 32, G = gridDim.x;
-    const int ldk = a.ldk, k0 = int(blockIdx.y) * K;  // this workgroup's K slice
+    // grid row: matrix mat (the second one when a.codes2 is set), K slice sl
+    const int mat = int(blockIdx.y) / a.nsplit, sl = int(blockIdx.y) % a.nsplit;
+    const uint32_t* const mcodes = mat ? a.codes2 : a.codes;
+    const uint32_t* const mcb = mat ? a.cb2 : a.cb;
+    const uint16_t* const msc = mat ? a.sc2 : a.sc;
+    const int ldk = a.ldk, k0 = sl * K;  // this workgroup's K slice
     const int nu = K / 32, u0 = w * nu / kVW, nus = (w + 1) * nu / kVW - u0;
 
     // lane (pair i, group g): kVRunV 16-byte loads of its code run whatever nus is; words past
     // the run are unused and past the last pair row they fall in the codebook section
     const int i = l & 15, g = l >> 4;
     auto load_codes = [&](int b, uint32_t (&c)[kVRunV * 4]) {
-        const uint32_t* crun = a.codes + size_t(b * 16 + i) * (ldk / 8) + k0 / 8 + u0 * 4 + g * nus;
+        const uint32_t* crun = mcodes + size_t(b * 16 + i) * (ldk / 8) + k0 / 8 + u0 * 4 + g * nus;
 #pragma unroll
         for (int v = 0; v < kVRunV; ++v) {
             const u32x4a q = *reinterpret_cast<const u32x4a*>(crun + 4 * v);
@@ -65,11 +70,11 @@ __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
     // centroid words: thread (entry te, bank column tc), column tc serving pair row tc mod 16
     // (a group of 4 pairs = 8 output rows); stored by threads below kVTab
     const int te = (tid >> 5) & 15, tc = tid & 31;
-    auto load_tw = [&](int b) { return a.cb[size_t((b * 16 + (tc & 15)) >> 2) * 16 + te]; };
+    auto load_tw = [&](int b) { return mcb[size_t((b * 16 + (tc & 15)) >> 2) * 16 + te]; };
     // epilogue thread (pair ei, column en): every thread loads a scale (past 256 a duplicate), so
     // no load sits under a branch
     const int ei = (tid >> 4) & 15, en = tid & 15;
-    auto load_sc = [&](int b) { return a.sc[2 * (b * 16 + ei) + (en >> 3)]; };
+    auto load_sc = [&](int b) { return msc[2 * (b * 16 + ei) + (en >> 3)]; };
 
     int blk = blockIdx.x;
     uint32_t tw = load_tw(blk);
@@ -150,7 +155,7 @@ __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
             const int t = en & 7, row = 2 * (blk * 16 + ei) + (en >> 3);
             if (t < T) {
                 if (a.out32)
-                    a.out32[size_t(blockIdx.y) * a.o32_s + size_t(t) * a.o32_t + row] = v;
+                    a.out32[size_t(mat) * a.o32_m + size_t(sl) * a.o32_s + size_t(t) * a.o32_t + row] = v;
                 else
                     a.y[size_t(t) * N + row] = uint16_t(f2h(v * h2f(esc)));
             }
@@ -183,13 +188,14 @@ int vq2_cus() {
 hipError_t launch_vq2_8(const Vq2Args& a, hipStream_t st) {
     if (!a.codes || !a.cb || !a.sc || !a.x || !(a.y || a.out32) || a.N < 32 || a.N % 32 ||
         a.K < 32 || a.K % 32 || a.K > kVMaxK || a.T < 1 || a.T > kSkinnyT || a.nsplit < 1 ||
-        a.ldk != a.K * a.nsplit || (a.nsplit > 1 && !a.out32))
+        a.ldk != a.K * a.nsplit || (a.nsplit > 1 && !a.out32) ||
+        (a.codes2 && (!a.cb2 || !a.sc2 || !a.out32)))
         return hipErrorInvalidValue;
-    const int ntile = a.N / 32, cus = vq2_cus();
-    // persistent over the row tiles of each slice: about one workgroup per CU in all
-    const int per = (cus + a.nsplit - 1) / a.nsplit;
+    const int ntile = a.N / 32, cus = vq2_cus(), rows = a.nsplit * (a.codes2 ? 2 : 1);
+    // persistent over the row tiles of each (matrix, slice): about one workgroup per CU in all
+    const int per = (cus + rows - 1) / rows;
     const int G = ntile < per ? ntile : per;
-    hipLaunchKernelGGL(k_vq2_8, dim3(G, a.nsplit), dim3(kVW * 64), 0, st, a);
+    hipLaunchKernelGGL(k_vq2_8, dim3(G, rows), dim3(kVW * 64), 0, st, a);
     return hipGetLastError();
 }
 

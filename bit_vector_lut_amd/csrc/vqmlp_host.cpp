@@ -469,15 +469,17 @@ vqmlp_status run_vq2_skinny(const vqmlp_plan* p, int T, const void* x, void* y,
     a.nsplit = ng;
     a.o32_t = 2 * I;
     a.o32_s = T * 2 * I;
-    for (int m = 0; m < 2; ++m) {
-        const VQ3View& v = m ? p->up : p->gate;
-        a.codes = reinterpret_cast<const uint32_t*>(v.codes);
-        a.cb = v.cb;
-        a.sc = v.sc;
-        a.out32 = w.gpart + (m ? I : 0);
-        e = launch_vq2_8(a, st);
-        if (e != hipSuccess) return hip_fail(e, m ? "2x16 up" : "2x16 gate");
-    }
+    // gate and up in one launch: planes [slice][t][g | u]
+    a.codes = reinterpret_cast<const uint32_t*>(p->gate.codes);
+    a.cb = p->gate.cb;
+    a.sc = p->gate.sc;
+    a.codes2 = reinterpret_cast<const uint32_t*>(p->up.codes);
+    a.cb2 = p->up.cb;
+    a.sc2 = p->up.sc;
+    a.o32_m = I;
+    a.out32 = w.gpart;
+    e = launch_vq2_8(a, st);
+    if (e != hipSuccess) return hip_fail(e, "2x16 gate/up");
     const bool rot128 = p->bi == 128;
     e = launch_gateup_combine(T, I, ng, w.gpart, p->gate.sc, p->up.sc, p->d.sign_i,
                               rot128 ? 1 : 0, float(1.0 / std::sqrt(128.0)), I, w.at, w.a_t, st);
@@ -1351,6 +1353,7 @@ vqmlp_status vqmlp_vq2_plan_forward(const vqmlp_vq2_plan* plan, int T, const voi
     if (!aligned(x, 16)) return fail(VQMLP_ERR_INVALID_ARG, "x must be 16-byte aligned");
     const vqmlp_vq2_plan& p = *plan;
     Vq2Args a;
+    memset(&a, 0, sizeof a);  // one matrix (no second codes)
     a.codes = reinterpret_cast<const uint32_t*>(p.base + p.L.codes_off);
     a.cb = reinterpret_cast<const uint32_t*>(p.base + p.L.cb_off);
     a.sc = reinterpret_cast<const uint16_t*>(p.base + p.L.sc_off);
