@@ -207,7 +207,8 @@ namespace {
 
 // The gate/up product of the tiled path in 128-row by 128- (or 64-) token tiles: the first
 // rows_main rows take whole rounds of workgroups on the CUs; the last rows_split rows, which
-// would leave a partial round, are split along K into `splits` parts over the CUs.
+// would leave a partial round, are split along K into `splits` parts over the CUs.  With fewer
+// tiles than CUs every row is split (rows_main = 0).
 struct GateUpSplit {
     int rows_main, rows_split, splits;
 };
@@ -217,10 +218,29 @@ GateUpSplit gateup_split(int I, int H, int T, int cus) {
     const Vq3Tile t = T >= kVq3mmMinT ? vq3mm_tile(2, T) : Vq3Tile{64, 128};
     if (I % t.bn) return g;
     const int rt = I / t.bn, tt = (T + t.bm - 1) / t.bm, total = rt * tt;
+    const int kt = H / 64;
+    if (total < cus && T >= kVq3mmMinT) {
+        // fewer tiles than CUs (the 64-row prefill chunk: 136 tiles): split every row's K so
+        // that whole rounds of workgroups cover the CUs, each extra plane priced at 5%
+        int best = 1;
+        double best_cost = 1.0;
+        for (int s = 2; s <= 8 && s <= kt / 8; ++s) {
+            const double cost = double((total * s + cus - 1) / cus) / s + 0.05 * s;
+            if (cost < best_cost - 1e-9) {
+                best = s;
+                best_cost = cost;
+            }
+        }
+        if (best > 1) {
+            g.rows_main = 0;
+            g.rows_split = I;
+            g.splits = best;
+        }
+        return g;
+    }
     if (total <= cus || total % cus == 0) return g;
     const int main_rt = (total / cus) * cus / tt;
     const int left = (rt - main_rt) * tt;  // leftover tiles
-    const int kt = H / 64;
     const int s = std::min(kt / 8, std::max(1, cus / left));
     if (main_rt <= 0 || s < 2) return g;
     g.rows_main = main_rt * t.bn;
@@ -392,8 +412,10 @@ vqmlp_status run_tiled(const vqmlp_plan* p, int T, const void* x, void* y, const
     g.kind = fused_rot ? kGemmVQ3GateUpRot : kGemmVQ3GateUp;
     g.out16 = w.at;
     g.out32 = w.a_t;
-    e = launch_gemm(g, st);
-    if (e != hipSuccess) return hip_fail(e, "tiled gate/up");
+    if (gs.rows_main > 0) {
+        e = launch_gemm(g, st);
+        if (e != hipSuccess) return hip_fail(e, "tiled gate/up");
+    }
     if (gs.rows_split) {
         // the rows that would leave a partial round of workgroups: K split over the CUs, then
         // one pass that sums the parts and applies the same epilogue
