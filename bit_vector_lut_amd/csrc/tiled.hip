@@ -447,13 +447,14 @@ int gemm_split(int kind, int N, int K, int T, int cus) {
     if (lut && T < kVq3mmMinT) return 1;
     const int kt = K / kGK;
     if ((kind == kGemmVQ3DownSplit || lut) && T >= kVq3mmMinT) {
-        // whole rounds of workgroups, each extra plane priced at 3% of the product
+        // whole rounds of workgroups, each extra plane priced at 1% of the product (the 64-row
+        // prefill chunk's down projection: 10 splits of 20 tiles, 200 workgroups)
         const Vq3Tile t = vq3mm_tile(1, T);
         const long tiles = long((N + t.bn - 1) / t.bn) * ((T + t.bm - 1) / t.bm);
         int best = 1;
         double best_cost = 1e9;
         for (int s = 1; s <= 16 && kt >= 4 * s; ++s) {
-            const double cost = double((tiles * s + cus - 1) / cus) / s + 0.03 * (s - 1);
+            const double cost = double((tiles * s + cus - 1) / cus) / s + 0.01 * (s - 1);
             if (cost < best_cost - 1e-9) {
                 best = s;
                 best_cost = cost;
