@@ -173,12 +173,13 @@ struct GemmArgs {
                                // 16 centroids per 8 rows): tiled kernels with the 2x16 decoder
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
-// VQ3 products for T > 64 rows with the weights decoded in registers (vq3mm.hip): gate/up kinds
-// (two matrices) and down kinds (one).  Tile of one workgroup: bm tokens x bn rows.
+// VQ3 products for T > 32 rows with the weights decoded in registers (vq3mm.hip): gate/up kinds
+// (two matrices), down and scalar-LUT kinds (one).  Tile of one workgroup of a product of this
+// kind with T rows: bm tokens x bn rows.
 struct Vq3Tile {
     int bm, bn;
 };
-Vq3Tile vq3mm_tile(int nmat, int T);
+Vq3Tile vq3mm_tile(int kind, int T);
 hipError_t launch_vq3mm(const GemmArgs& a, hipStream_t st);
 constexpr int kVq3mmMinT = 33;  // launch_gemm sends VQ3 kinds with at least this many rows there
 // K splits for a product of this kind and shape on `cus` CUs (1 = none).  A split product

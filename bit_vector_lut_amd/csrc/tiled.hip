@@ -449,7 +449,7 @@ int gemm_split(int kind, int N, int K, int T, int cus) {
     if ((kind == kGemmVQ3DownSplit || lut) && T >= kVq3mmMinT) {
         // whole rounds of workgroups, each extra plane priced at 1% of the product (the 64-row
         // prefill chunk's down projection: 10 splits of 20 tiles, 200 workgroups)
-        const Vq3Tile t = vq3mm_tile(1, T);
+        const Vq3Tile t = vq3mm_tile(kind, T);
         const long tiles = long((N + t.bn - 1) / t.bn) * ((T + t.bm - 1) / t.bm);
         int best = 1;
         double best_cost = 1e9;

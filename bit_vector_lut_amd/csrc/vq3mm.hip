@@ -55,7 +55,7 @@ __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 template <int NW, int BM, int RW, int NMAT, int DEC, int EPI, int CQ>
-__global__ void __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 k_vq3mm(GemmArgs a) {
     constexpr bool VQ = DEC == kDecVQ3;
     constexpr int BITS = DEC == kDecLUT2 ? 2 : 4;  // scalar-LUT code width
@@ -534,7 +534,10 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
 }
 
 // Tile shapes: waves, tokens and rows per wave of the gate/up product (two matrices) and of the
-// down product (one matrix).  One wave per SIMD: the accumulators live in the AGPRs.
+// down product (one matrix).  One wave per SIMD: the accumulators live in the AGPRs.  Prefill
+// (T >= kWideT) runs the VQ3 kinds with two waves per SIMD (kWideNW per workgroup, 256 registers
+// each): with one wave the decode and the matrix-core steps of a SIMD mostly take turns, with two
+// one wave's decode runs beside the other's products.
 #ifndef VQ3MM_GU_NW
 #define VQ3MM_GU_NW 4
 #endif
@@ -551,13 +554,27 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t st) {
 constexpr int kGuNW = VQ3MM_GU_NW, kGuBM = 128, kGuRW = VQ3MM_GU_RW;
 constexpr int kDnNW = VQ3MM_DN_NW, kDnBM = 128, kDnRW = VQ3MM_DN_RW;
 constexpr int kSmallBM = 64;
+#ifndef VQ3MM_WIDE_DN_RW
+#define VQ3MM_WIDE_DN_RW 64
+#endif
+constexpr int kWideT = 256, kWideNW = 8, kWideGuRW = 32, kWideDnRW = VQ3MM_WIDE_DN_RW;
+
+bool vq3_kind(int kind) {
+    return kind == kGemmVQ3GateUp || kind == kGemmVQ3GateUpRot || kind == kGemmVQ3GateUpSplit ||
+           kind == kGemmVQ3Down || kind == kGemmVQ3DownSplit;
+}
+bool gateup_kind(int kind) {
+    return kind == kGemmVQ3GateUp || kind == kGemmVQ3GateUpRot || kind == kGemmVQ3GateUpSplit;
+}
 
 }  // namespace
 
-Vq3Tile vq3mm_tile(int nmat, int T) {
-    const bool small = T <= kSmallBM;
-    return nmat == 2 ? Vq3Tile{small ? kSmallBM : kGuBM, kGuNW * kGuRW}
-                     : Vq3Tile{small ? kSmallBM : kDnBM, kDnNW * kDnRW};
+Vq3Tile vq3mm_tile(int kind, int T) {
+    if (T <= kSmallBM)
+        return Vq3Tile{kSmallBM, gateup_kind(kind) ? kGuNW * kGuRW : kDnNW * kDnRW};
+    if (T >= kWideT && vq3_kind(kind))
+        return Vq3Tile{kGuBM, gateup_kind(kind) ? kWideNW * kWideGuRW : kWideNW * kWideDnRW};
+    return gateup_kind(kind) ? Vq3Tile{kGuBM, kGuNW * kGuRW} : Vq3Tile{kDnBM, kDnNW * kDnRW};
 }
 
 template <int BMG, int BMD>
@@ -587,9 +604,30 @@ hipError_t launch_vq3mm_bm(const GemmArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+hipError_t launch_vq3mm_wide(const GemmArgs& a, hipStream_t st) {
+    if (a.K % kXK || a.N <= 0 || a.N % 32) return hipErrorInvalidValue;
+    if (a.ksplit > 1 && (a.K / kXK) < a.ksplit) return hipErrorInvalidValue;
+    switch (a.kind) {
+        case kGemmVQ3GateUp:
+            return launch_t<kWideNW, kGuBM, kWideGuRW, 2, kEgGateUp32>(a, st);
+        case kGemmVQ3GateUpRot:
+            if (a.N % 128) return hipErrorInvalidValue;
+            return launch_t<kWideNW, kGuBM, kWideGuRW, 2, kEgGateUpRot>(a, st);
+        case kGemmVQ3GateUpSplit:
+            return launch_t<kWideNW, kGuBM, kWideGuRW, 2, kEgPart2>(a, st);
+        case kGemmVQ3Down:
+            return launch_t<kWideNW, kDnBM, kWideDnRW, 1, kEgScale16>(a, st);
+        case kGemmVQ3DownSplit:
+            return launch_t<kWideNW, kDnBM, kWideDnRW, 1, kEgPlain32>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_vq3mm(const GemmArgs& a, hipStream_t st) {
-    return a.T <= kSmallBM ? launch_vq3mm_bm<kSmallBM, kSmallBM>(a, st)
-                           : launch_vq3mm_bm<kGuBM, kDnBM>(a, st);
+    if (a.T <= 0) return hipSuccess;
+    if (a.T <= kSmallBM) return launch_vq3mm_bm<kSmallBM, kSmallBM>(a, st);
+    if (a.T >= kWideT && vq3_kind(a.kind)) return launch_vq3mm_wide(a, st);
+    return launch_vq3mm_bm<kGuBM, kDnBM>(a, st);
 }
 
 }  // namespace vqmlp

@@ -215,7 +215,7 @@ struct GateUpSplit {
 GateUpSplit gateup_split(int I, int H, int T, int cus) {
     GateUpSplit g{I, 0, 1};
     if (I % 128 || T <= kSkinnyT || cus <= 0) return g;
-    const Vq3Tile t = T >= kVq3mmMinT ? vq3mm_tile(2, T) : Vq3Tile{64, 128};
+    const Vq3Tile t = T >= kVq3mmMinT ? vq3mm_tile(kGemmVQ3GateUpSplit, T) : Vq3Tile{64, 128};
     if (I % t.bn) return g;
     const int rt = I / t.bn, tt = (T + t.bm - 1) / t.bm, total = rt * tt;
     const int kt = H / 64;

@@ -144,7 +144,7 @@ def test_tiny_layer(vq, oracle_mod, torch_dev, path):
 SMALL = [(256, 704), (128, 192), (512, 1024), (320, 640)]
 
 
-@pytest.mark.parametrize("T", [1, 2, 7, 8, 9, 16, 33, 64, 65, 130])
+@pytest.mark.parametrize("T", [1, 2, 7, 8, 9, 16, 33, 64, 65, 130, 300])
 @pytest.mark.parametrize("H,I", SMALL)
 def test_mlp_small_shapes(vq, oracle_mod, torch_dev, H, I, T):
     L = synth.mlp_layer(H, I, T, seed=H * 31 + I + T, outliers=(T % 2 == 1))
