@@ -19,6 +19,13 @@ __device__ __forceinline__ uint32_t f2h(float f) {  // round to nearest even
     return __builtin_bit_cast(uint16_t, (_Float16)f);
 }
 
+// silu(g) = g / (1 + e^-g) with the hardware exponential and reciprocal (v_exp_f32 and v_rcp_f32,
+// about 1 ulp each): g * rcp(1 + 2^(-g log2 e)).  Large |g| saturate correctly (e^-g -> inf
+// gives 0, e^-g -> 0 gives g).
+__device__ __forceinline__ float silu(float g) {
+    return g * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-g * 1.4426950408889634f));
+}
+
 // Code q (0..15) of a lane's 96-bit code word {d2:d1:d0}, returned as code << SH (SH >= 0),
 // i.e. already scaled to the byte stride of one entry in a lookup table.
 template <int Q, int SH>

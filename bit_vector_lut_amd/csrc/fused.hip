@@ -385,7 +385,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                     const int rl = 2 * (4 * (e_l >> 4) + e_r) + (e_l & 1), t = (e_l & 15) >> 1;
                     g *= esc[eb][0][rl];
                     u *= esc[eb][1][rl];
-                    const float act = g / (1.f + expf(-g)) * u;
+                    const float act = silu(g) * u;
                     const uint32_t bits = __builtin_bit_cast(uint32_t, act) ^ esg[eb][rl];
                     st_relaxed64(a.act + size_t(t) * I + prev.id * kTileRows + rl,
                                  (uint64_t(tag) << 32) | bits);

@@ -365,7 +365,7 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int tl = wm * WM + 16 * i + 4 * (l >> 4) + r;
                     const float g = acc[0][i][j][r] * sg, u = acc[1][i][j][r] * su;
-                    float v = g / (1.f + expf(-g)) * u;
+                    float v = silu(g) * u;
                     Ab[tl * (BN + 1) + rl] = neg ? -v : v;
                 }
         }
@@ -414,7 +414,7 @@ __global__ void __launch_bounds__(kGThreads, 1) k_gemm(GemmArgs a) {
                 const float v0 = acc[0][i][j][r];
                 if constexpr (EPI == kEgGateUp32) {
                     const float g = v0 * s0, u = acc[NMAT - 1][i][j][r] * s1;
-                    const float act = g / (1.f + expf(-g)) * u;
+                    const float act = silu(g) * u;
                     a.out32[size_t(tok) * ldo + row] = neg ? -act : act;
                 } else if constexpr (EPI == kEgScale16 || EPI == kEgLUT) {
                     a.out16[size_t(tok) * ldo + row] = (uint16_t)f2h(v0 * s0);
@@ -549,7 +549,7 @@ __global__ void __launch_bounds__(256) k_gateup_combine(int T, int N, int splits
         }
         g *= h2f(scg[row]);
         u *= h2f(scu[row]);
-        const float act = g / (1.f + expf(-g)) * u;
+        const float act = silu(g) * u;
         v[e] = sign && sign[row] < 0 ? -act : act;
     }
     if (!rotate) {

@@ -399,7 +399,7 @@ k_vq3mm(GemmArgs a) {
                 for (int q = 0; q < 16; ++q) {
                     const int tl = 32 * i + 8 * (q >> 2) + 4 * kh + (q & 3);
                     const float g = acc[0][j][i][q] * sg, u = acc[1][j][i][q] * su;
-                    const float v = g / (1.f + expf(-g)) * u;
+                    const float v = silu(g) * u;
                     Ab[tl * (BNW + 1) + rl] = neg ? -v : v;
                 }
         }
@@ -503,7 +503,7 @@ k_vq3mm(GemmArgs a) {
                 const float v0 = acc[0][j][i][q];
                 if constexpr (EPI == kEgGateUp32) {
                     const float g = v0 * s0, u = acc[NMAT - 1][j][i][q] * s1;
-                    const float act = g / (1.f + expf(-g)) * u;
+                    const float act = silu(g) * u;
                     a.out32[size_t(tok) * ldo + row] = neg ? -act : act;
                 } else if constexpr (EPI == kEgScale16) {
                     a.out16[size_t(tok) * ldo + row] = (uint16_t)f2h(v0 * s0);
