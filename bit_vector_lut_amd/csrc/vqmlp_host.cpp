@@ -297,7 +297,10 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
         // kernel's K slices: gate/up planes [ng][T][2][I], down planes [nd][T][H]
         gs = GateUpSplit{I, 0, 1};
         gpart_bytes = 0;
-        dsplit = gemm_split(kGemmVQ3DownSplit, H, I, std::min(T, 64), p->cus);
+        // T >= 33: the tiled kernel's 64 x 64 tiles with 8 K splits of down (at the 64-row
+        // chunk 3, 6, 8 and 10 splits measured 185, 153, 152 and 164 us per layer)
+        dsplit = T >= kVq3mmMinT ? std::max(1, std::min(8, I / 64 / 8))
+                                 : gemm_split(kGemmVQ3DownSplit, H, I, T, p->cus);
         if (T <= kSkinnyT && p->v2_ng) {
             dsplit = p->v2_nd;
             gpart_bytes = size_t(p->v2_ng) * Tt * 2 * I * 4;
