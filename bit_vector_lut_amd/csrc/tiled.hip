@@ -619,7 +619,7 @@ static hipError_t launch_gemm_vq2(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    if (a.vq2) return launch_gemm_vq2(a, st);
+    if (a.vq2 && a.T < kVq3mmMinT) return launch_gemm_vq2(a, st);
     if (a.T >= kVq3mmMinT &&
         (a.kind == kGemmVQ3GateUp || a.kind == kGemmVQ3GateUpRot || a.kind == kGemmVQ3Down ||
          a.kind == kGemmVQ3GateUpSplit || a.kind == kGemmVQ3DownSplit || a.kind == kGemmLUT2 ||

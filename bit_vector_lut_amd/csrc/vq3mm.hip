@@ -58,6 +58,8 @@ template <int NW, int BM, int RW, int NMAT, int DEC, int EPI, int CQ>
 __global__ void __launch_bounds__(NW * 64, 1) __attribute__((amdgpu_waves_per_eu(NW / 4, NW / 4)))
 k_vq3mm(GemmArgs a) {
     constexpr bool VQ = DEC == kDecVQ3;
+    constexpr bool V2 = DEC == kDecVQ2;  // 2x16: 4-bit codes into 16 centroids per 8 rows
+    constexpr bool PAIR = VQ || V2;      // a centroid holds both rows of a pair
     constexpr int BITS = DEC == kDecLUT2 ? 2 : 4;  // scalar-LUT code width
     constexpr int NT = NW * 64;
     constexpr int RF = RW / 32;       // 32-row B operands per wave per matrix
@@ -72,7 +74,7 @@ k_vq3mm(GemmArgs a) {
     constexpr int kXBuf = BM * kXK * 2;         // one activation tile
     constexpr int kMain = kOffX + 2 * kXBuf;
     constexpr int kEpBytes = EPI == kEgGateUpRot ? BM * (BNW + 1) * 4 : 0;
-    static_assert(VQ || (NMAT == 1 && (EPI == kEgLUT || EPI == kEgLUTPlane)), "LUT: one matrix");
+    static_assert(PAIR || (NMAT == 1 && (EPI == kEgLUT || EPI == kEgLUTPlane)), "LUT: one matrix");
     constexpr int kLds = kMain > kEpBytes ? kMain : kEpBytes;
     static_assert(kLds <= 160 * 1024, "LDS");
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
@@ -88,8 +90,9 @@ k_vq3mm(GemmArgs a) {
     // ---- lookup tables.  Table (m, j) serves B operand j of matrix m (rows wrow + 32 j ..,
     // four 8-row groups): word (e, b) -- entry e, bank column b -- holds entry e of group b / 8.
     // Lane l reads column l % 32 only, which holds its own row's group, so a lookup never meets a
-    // bank conflict.  Entries: VQ3, the 64 two-component centroids; LUT2, the 16 pairs
-    // (lut[e % 4], lut[e / 4]) of two neighbouring codes; LUT4, the 16 scalars (low half).
+    // bank conflict.  Entries: VQ3, the 64 two-component centroids; 2x16, the 16 two-component
+    // centroids; LUT2, the 16 pairs (lut[e % 4], lut[e / 4]) of two neighbouring codes; LUT4, the
+    // 16 scalars (low half).
 #pragma unroll
     for (int m = 0; m < NMAT; ++m) {
         const uint32_t* cb = (NMAT > 1 && m) ? a.cb[1] : a.cb[0];
@@ -105,6 +108,8 @@ k_vq3mm(GemmArgs a) {
                 uint32_t v;
                 if constexpr (VQ)
                     v = cb[size_t(grp) * 64 + e];
+                else if constexpr (V2)
+                    v = cb[size_t(grp) * 16 + e];
                 else if constexpr (DEC == kDecLUT2)
                     v = uint32_t(lut[size_t(grp) * 4 + (e & 3)]) | (uint32_t(lut[size_t(grp) * 4 + (e >> 2)]) << 16);
                 else
@@ -119,10 +124,13 @@ k_vq3mm(GemmArgs a) {
     // columns 16 ks + 8 kh .. + 7 of each 16-column K step ks.  It looks up its pair's centroids
     // for columns 4 c0 .. 4 c0 + 3 of those eight: for all four K steps these are the 16 codes of
     // lane record (2 kh + c0, pair) of the packed tile, K step ks in its 24-bit slot ks.
+    // 2x16 codes are packed by pair row, 8 columns per word.  Their K steps take the columns of
+    // a tile in another order (below), in which the lane's 16 codes of a tile are the two words
+    // 4 c0 + 2 kh and 4 c0 + 2 kh + 1 of its pair row: K step ks in half ks % 2 of word ks / 2.
     // Scalar LUTs are packed row by row (32 / BITS codes per word, low bits first): a K tile is
     // 8 BITS bytes of each row, K step ks in word ks (LUT2, half kh) or word 2 ks + kh (LUT4).
-    constexpr int CW = VQ ? 3 : 2 * BITS;          // code words per lane per operand and K tile
-    constexpr int kTileCode = VQ ? kTileBytes : 8 * BITS;  // bytes a K tile advances the codes
+    constexpr int CW = VQ ? 3 : V2 ? 2 : 2 * BITS;  // code words per lane per operand and K tile
+    constexpr int kTileCode = VQ ? kTileBytes : V2 ? 32 : 8 * BITS;  // bytes per K tile
     uint32_t voff[RF];
 #pragma unroll
     for (int j = 0; j < RF; ++j) {
@@ -130,6 +138,9 @@ k_vq3mm(GemmArgs a) {
             const int mt = min(wrow / 32 + j, mt_last);
             voff[j] = uint32_t(mt) * uint32_t(KT) * kTileBytes +
                       12u * uint32_t(((2 * kh + c0) << 4) | pr);
+        } else if constexpr (V2) {
+            const int pair = min((wrow + 32 * j) / 2 + pr, N / 2 - 1);
+            voff[j] = uint32_t(pair) * uint32_t(K / 2) + 4u * uint32_t(4 * c0 + 2 * kh);
         } else {
             const int row = min(wrow + 32 * j + n, N - 1);
             voff[j] = uint32_t(row) * uint32_t(K / 8 * BITS);
@@ -149,6 +160,15 @@ k_vq3mm(GemmArgs a) {
     // all of a thread's chunks share row % 8, hence one address plus constant offsets
     static_assert((NT / 8) % 8 == 0, "chunks of one thread share the row swizzle");
     const uint32_t xw = kOffX + uint32_t(tid >> 3) * 128u + (uint32_t((tid & 7) ^ ((tid >> 3) & 7)) << 4);
+    // 2x16 column order: slot (ks, kh, i) of the A and B operands is column 32 (i / 4) + 16 kh +
+    // 4 ks + i % 4 of the tile, so that half h of the thread's chunk q (columns 8 q + 4 h ..) goes
+    // to 8 bytes 8 (q / 4) of 16-byte chunk 2 ks + kh, ks = (2 q + h) % 4, kh = (q / 2) % 2
+    uint32_t xw2[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int q = tid & 7, c = 2 * ((2 * q + h) & 3) + ((q >> 1) & 1);
+        xw2[h] = kOffX + uint32_t(tid >> 3) * 128u + (uint32_t(c ^ ((tid >> 3) & 7)) << 4) + 8u * uint32_t(q >> 2);
+    }
     uint32_t xoff[XCH];  // global byte offset of the chunk in K tile 0
 #pragma unroll
     for (int x = 0; x < XCH; ++x) {
@@ -165,7 +185,9 @@ k_vq3mm(GemmArgs a) {
     for (int m = 0; m < NMAT; ++m)
         rs_code[m] = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>((NMAT > 1 && m) ? a.codes[1] : a.codes[0]), 0,
-            int(VQ ? uint32_t(N / 32) * uint32_t(KT) * kTileBytes : uint32_t(N) * uint32_t(K / 8 * BITS)),
+            int(VQ   ? uint32_t(N / 32) * uint32_t(KT) * kTileBytes
+                : V2 ? uint32_t(N / 2) * uint32_t(K / 2)
+                     : uint32_t(N) * uint32_t(K / 8 * BITS)),
             kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rs_x = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(a.x), 0, int(uint32_t(T) * uint32_t(K) * 2u), kRsrcWord3);
@@ -194,6 +216,12 @@ k_vq3mm(GemmArgs a) {
                                                                     kt * kTileCode, 0));
 #pragma unroll
                     for (int q = 0; q < 3; ++q) rn[slot][m][j][q] = v[q];
+                } else if constexpr (V2) {
+                    const u32x2 v = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs_code[m], int(voff[j]),
+                                                                    kt * kTileCode, 0));
+                    rn[slot][m][j][0] = v[0];
+                    rn[slot][m][j][1] = v[1];
                 } else {
 #pragma unroll
                     for (int h = 0; h < CW / 4; ++h) {
@@ -207,10 +235,18 @@ k_vq3mm(GemmArgs a) {
             }
     };
     auto stage = [&](uint32_t bufoff) {
-        unsigned char* base = lds + (xw + bufoff);
+        if constexpr (V2) {
 #pragma unroll
-        for (int x = 0; x < XCH; ++x)
-            *reinterpret_cast<u32x4*>(base + x * (NT / 8) * 128) = xr[x];
+            for (int x = 0; x < XCH; ++x) {
+                *reinterpret_cast<u32x2*>(lds + xw2[0] + bufoff + x * (NT / 8) * 128) = u32x2{xr[x][0], xr[x][1]};
+                *reinterpret_cast<u32x2*>(lds + xw2[1] + bufoff + x * (NT / 8) * 128) = u32x2{xr[x][2], xr[x][3]};
+            }
+        } else {
+            unsigned char* base = lds + (xw + bufoff);
+#pragma unroll
+            for (int x = 0; x < XCH; ++x)
+                *reinterpret_cast<u32x4*>(base + x * (NT / 8) * 128) = xr[x];
+        }
     };
     auto take_codes = [&](int slot) {
 #pragma unroll
@@ -247,6 +283,13 @@ k_vq3mm(GemmArgs a) {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
                 ev[b & 1][k] = *reinterpret_cast<const uint32_t*>(tb + and_or(x[k], 0x1F80u, tab_lane));
+        } else if constexpr (V2) {
+            // the lane's 16 bits of K step ks: code k (4 bits) at bit 4 k, moved to bits 10:7
+            const uint32_t wk = rc[m][j][ks >> 1] >> (16 * (ks & 1));
+            const uint32_t x[4] = {wk << 7, wk << 3, wk >> 1, wk >> 5};
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                ev[b & 1][k] = *reinterpret_cast<const uint32_t*>(tb + and_or(x[k], 0x780u, tab_lane));
         } else if constexpr (DEC == kDecLUT2) {
             // the lane's 16 bits of word ks: code pair p (4 bits) at bit 4 p, moved to bits 10:7
             const uint32_t wk = rc[m][j][ks] >> (16 * kh);
@@ -426,7 +469,7 @@ k_vq3mm(GemmArgs a) {
         return;
     }
 
-    if constexpr (!VQ) {
+    if constexpr (!PAIR) {
         // scalar LUT: row scales, then the rank-r term z U^T (split 0 only) as r / 16 more K
         // steps with both operands read straight from global memory (z rounded to binary16)
 #pragma unroll
@@ -577,23 +620,24 @@ Vq3Tile vq3mm_tile(int kind, int T) {
     return gateup_kind(kind) ? Vq3Tile{kGuBM, kGuNW * kGuRW} : Vq3Tile{kDnBM, kDnNW * kDnRW};
 }
 
-template <int BMG, int BMD>
+// DV: the decoder of the VQ kinds (VQ3, or 2x16 for a 2x16 plan)
+template <int BMG, int BMD, int DV>
 hipError_t launch_vq3mm_bm(const GemmArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
     if (a.K % kXK || a.N <= 0 || a.N % 32) return hipErrorInvalidValue;
     if (a.ksplit > 1 && (a.K / kXK) < a.ksplit) return hipErrorInvalidValue;
     switch (a.kind) {
         case kGemmVQ3GateUp:
-            return launch_t<kGuNW, BMG, kGuRW, 2, kEgGateUp32>(a, st);
+            return launch_t<kGuNW, BMG, kGuRW, 2, kEgGateUp32, DV>(a, st);
         case kGemmVQ3GateUpRot:  // whole 128-row rotation blocks
             if (a.N % 128) return hipErrorInvalidValue;
-            return launch_t<kGuNW, BMG, kGuRW, 2, kEgGateUpRot>(a, st);
+            return launch_t<kGuNW, BMG, kGuRW, 2, kEgGateUpRot, DV>(a, st);
         case kGemmVQ3GateUpSplit:
-            return launch_t<kGuNW, BMG, kGuRW, 2, kEgPart2>(a, st);
+            return launch_t<kGuNW, BMG, kGuRW, 2, kEgPart2, DV>(a, st);
         case kGemmVQ3Down:
-            return launch_t<kDnNW, BMD, kDnRW, 1, kEgScale16>(a, st);
+            return launch_t<kDnNW, BMD, kDnRW, 1, kEgScale16, DV>(a, st);
         case kGemmVQ3DownSplit:
-            return launch_t<kDnNW, BMD, kDnRW, 1, kEgPlain32>(a, st);
+            return launch_t<kDnNW, BMD, kDnRW, 1, kEgPlain32, DV>(a, st);
         case kGemmLUT2:  // scalar LUT + rank-r term: binary16 y, or scaled FP32 planes per K split
             return a.ksplit > 1 ? launch_t<kDnNW, BMD, kDnRW, 1, kEgLUTPlane, kDecLUT2>(a, st)
                                 : launch_t<kDnNW, BMD, kDnRW, 1, kEgLUT, kDecLUT2>(a, st);
@@ -604,30 +648,35 @@ hipError_t launch_vq3mm_bm(const GemmArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+template <int DV>
 hipError_t launch_vq3mm_wide(const GemmArgs& a, hipStream_t st) {
     if (a.K % kXK || a.N <= 0 || a.N % 32) return hipErrorInvalidValue;
     if (a.ksplit > 1 && (a.K / kXK) < a.ksplit) return hipErrorInvalidValue;
     switch (a.kind) {
         case kGemmVQ3GateUp:
-            return launch_t<kWideNW, kGuBM, kWideGuRW, 2, kEgGateUp32>(a, st);
+            return launch_t<kWideNW, kGuBM, kWideGuRW, 2, kEgGateUp32, DV>(a, st);
         case kGemmVQ3GateUpRot:
             if (a.N % 128) return hipErrorInvalidValue;
-            return launch_t<kWideNW, kGuBM, kWideGuRW, 2, kEgGateUpRot>(a, st);
+            return launch_t<kWideNW, kGuBM, kWideGuRW, 2, kEgGateUpRot, DV>(a, st);
         case kGemmVQ3GateUpSplit:
-            return launch_t<kWideNW, kGuBM, kWideGuRW, 2, kEgPart2>(a, st);
+            return launch_t<kWideNW, kGuBM, kWideGuRW, 2, kEgPart2, DV>(a, st);
         case kGemmVQ3Down:
-            return launch_t<kWideNW, kDnBM, kWideDnRW, 1, kEgScale16>(a, st);
+            return launch_t<kWideNW, kDnBM, kWideDnRW, 1, kEgScale16, DV>(a, st);
         case kGemmVQ3DownSplit:
-            return launch_t<kWideNW, kDnBM, kWideDnRW, 1, kEgPlain32>(a, st);
+            return launch_t<kWideNW, kDnBM, kWideDnRW, 1, kEgPlain32, DV>(a, st);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_vq3mm(const GemmArgs& a, hipStream_t st) {
     if (a.T <= 0) return hipSuccess;
-    if (a.T <= kSmallBM) return launch_vq3mm_bm<kSmallBM, kSmallBM>(a, st);
-    if (a.T >= kWideT && vq3_kind(a.kind)) return launch_vq3mm_wide(a, st);
-    return launch_vq3mm_bm<kGuBM, kDnBM>(a, st);
+    if (a.vq2 && !vq3_kind(a.kind)) return hipErrorInvalidValue;
+    if (a.T <= kSmallBM)
+        return a.vq2 ? launch_vq3mm_bm<kSmallBM, kSmallBM, kDecVQ2>(a, st)
+                     : launch_vq3mm_bm<kSmallBM, kSmallBM, kDecVQ3>(a, st);
+    if (a.T >= kWideT && vq3_kind(a.kind))
+        return a.vq2 ? launch_vq3mm_wide<kDecVQ2>(a, st) : launch_vq3mm_wide<kDecVQ3>(a, st);
+    return a.vq2 ? launch_vq3mm_bm<kGuBM, kDnBM, kDecVQ2>(a, st) : launch_vq3mm_bm<kGuBM, kDnBM, kDecVQ3>(a, st);
 }
 
 }  // namespace vqmlp

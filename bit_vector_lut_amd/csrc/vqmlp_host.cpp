@@ -292,15 +292,13 @@ Workspace carve(const vqmlp_plan* p, int T, void* base) {
     int dsplit = T > kSkinnyT ? gemm_split(kGemmVQ3DownSplit, H, I, T, p->cus) : 1;
     GateUpSplit gs = T > kSkinnyT ? gateup_split(I, H, T, p->cus) : GateUpSplit{I, 0, 1};
     size_t gpart_bytes = gs.rows_split ? size_t(gs.splits) * Tt * 2 * gs.rows_split * 4 : 0;
-    if (p->vq2) {
-        // 2x16: the tiled kernels (no leftover split of gate/up) or, at T <= 8, the projection
-        // kernel's K slices: gate/up planes [ng][T][2][I], down planes [nd][T][H]
+    if (p->vq2 && T < kVq3mmMinT) {
+        // 2x16 below the register-decode kernels: the tiled kernels (no leftover split of
+        // gate/up) or, at T <= 8, the projection kernel's K slices: gate/up planes
+        // [ng][T][2][I], down planes [nd][T][H].  From T = 33 a 2x16 plan takes the VQ3 rules.
         gs = GateUpSplit{I, 0, 1};
         gpart_bytes = 0;
-        // T >= 33: the tiled kernel's 64 x 64 tiles with 8 K splits of down (at the 64-row
-        // chunk 3, 6, 8 and 10 splits measured 185, 153, 152 and 164 us per layer)
-        dsplit = T >= kVq3mmMinT ? std::max(1, std::min(8, I / 64 / 8))
-                                 : gemm_split(kGemmVQ3DownSplit, H, I, T, p->cus);
+        dsplit = gemm_split(kGemmVQ3DownSplit, H, I, T, p->cus);
         if (T <= kSkinnyT && p->v2_ng) {
             dsplit = p->v2_nd;
             gpart_bytes = size_t(p->v2_ng) * Tt * 2 * I * 4;
@@ -429,8 +427,11 @@ vqmlp_status run_tiled(const vqmlp_plan* p, int T, const void* x, void* y, const
         q.ldo = 0;
         q.ksplit = gs.splits;
         for (int m = 0; m < 2; ++m) {
-            q.codes[m] = g.codes[m] + size_t(r0 / kTileRows) * (H / kTileCols) * kTileBytes;
-            q.cb[m] = g.cb[m] + size_t(r0 / 8) * 64;
+            // row r0 of the packed codes and codebooks (VQ3 tiles, or 2x16 pair rows of H / 8
+            // words and 16 centroids per 8 rows)
+            q.codes[m] = p->vq2 ? g.codes[m] + size_t(r0 / 2) * (H / 2)
+                                : g.codes[m] + size_t(r0 / kTileRows) * (H / kTileCols) * kTileBytes;
+            q.cb[m] = g.cb[m] + size_t(r0 / 8) * (p->vq2 ? 16 : 64);
             q.sc[m] = g.sc[m] + r0;
         }
         q.sign = nullptr;

@@ -272,7 +272,8 @@ vqmlp_status vqmlp_vq2_unpack(int N, int K, const void *packed, size_t packed_by
  * vqmlp_destroy: T <= 8 (with I a multiple of 128) runs the 2x16 projection kernel (path 1:
  * gate and up as FP32 planes in K slices of at most 5120 columns, one pass for SiLU, sign and
  * the 128-wide rotation, the down product in K slices, one pass summing the slices), any T the
- * tiled matrix-core kernels with the 2x16 decoder (path 2). */
+ * matrix-core kernels with a 2x16 decoder (path 2: the tiled kernels up to T = 32, the
+ * register-decode kernels of the three-bit form from T = 33). */
 vqmlp_status vqmlp_create_vq2(const vqmlp_desc *desc, vqmlp_plan **out);
 
 typedef struct vqmlp_vq2_plan vqmlp_vq2_plan;

@@ -704,7 +704,7 @@ def test_lut_argmax_ties_pick_lowest_row(vq, torch_dev, bits):
 # ------------------------------------------------------------------ 2x16 MLP (previous format)
 
 
-@pytest.mark.parametrize("T", [1, 3, 8, 9, 64, 130])
+@pytest.mark.parametrize("T", [1, 3, 8, 9, 33, 64, 130, 300])
 @pytest.mark.parametrize("H,I", [(256, 512), (512, 1024), (320, 640), (256, 704)])
 def test_vq2_mlp_small_shapes(vq, oracle_mod, torch_dev, H, I, T):
     """The 2x16 MLP against the oracle's composition, every output: the T <= 8 projection path
