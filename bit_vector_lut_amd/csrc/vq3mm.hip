@@ -478,32 +478,52 @@ k_vq3mm(GemmArgs a) {
 #pragma unroll
             for (int i = 0; i < TF; ++i) acc[0][j][i] *= sr;
         }
-        if (a.r > 0 && blockIdx.z == 0) {
-            for (int kr = 0; kr < a.r; kr += 16) {
+        // The rank-r term's K steps of 16 are spread over the K splits (step kr / 16 in split
+        // (kr / 16) % nsplit): the split planes are summed later, and no split carries it alone.
+        // With r a multiple of 16 and 16-byte aligned rows a lane's 8 columns of U are one 16-byte
+        // load and of z two; otherwise one element at a time.
+        const bool vec = a.r % 16 == 0 && (reinterpret_cast<uintptr_t>(a.U) & 15) == 0 &&
+                         (reinterpret_cast<uintptr_t>(a.z) & 15) == 0;
+        if (a.r > 0) {
+            for (int kr = 16 * int(blockIdx.z); kr < a.r; kr += 16 * nsplit) {
                 const int k0 = kr + 8 * kh;  // this lane's 8 columns of the step
                 u32x4 Bu[RF];
 #pragma unroll
                 for (int j = 0; j < RF; ++j) {
                     const uint16_t* up = a.U + size_t(min(wrow + 32 * j + n, N - 1)) * a.r;
-                    uint32_t h[4];
+                    if (vec) {
+                        Bu[j] = *reinterpret_cast<const u32x4*>(up + k0);
+                    } else {
+                        uint32_t h[4];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const uint32_t u0 = k0 + 2 * q < a.r ? up[k0 + 2 * q] : 0u;
-                        const uint32_t u1 = k0 + 2 * q + 1 < a.r ? up[k0 + 2 * q + 1] : 0u;
-                        h[q] = u0 | (u1 << 16);
+                        for (int q = 0; q < 4; ++q) {
+                            const uint32_t u0 = k0 + 2 * q < a.r ? up[k0 + 2 * q] : 0u;
+                            const uint32_t u1 = k0 + 2 * q + 1 < a.r ? up[k0 + 2 * q + 1] : 0u;
+                            h[q] = u0 | (u1 << 16);
+                        }
+                        Bu[j] = u32x4{h[0], h[1], h[2], h[3]};
                     }
-                    Bu[j] = u32x4{h[0], h[1], h[2], h[3]};
                 }
 #pragma unroll
                 for (int i = 0; i < TF; ++i) {
+                    // rows past T repeat row T - 1: their products are never stored
                     const int tok = tok0 + 32 * i + n;
                     const float* zp = a.z + size_t(min(tok, T - 1)) * a.r;
                     uint32_t h[4];
+                    if (vec) {
+                        const f32x4 z0 = *reinterpret_cast<const f32x4*>(zp + k0);
+                        const f32x4 z1 = *reinterpret_cast<const f32x4*>(zp + k0 + 4);
+                        h[0] = f2h(z0[0]) | (f2h(z0[1]) << 16);
+                        h[1] = f2h(z0[2]) | (f2h(z0[3]) << 16);
+                        h[2] = f2h(z1[0]) | (f2h(z1[1]) << 16);
+                        h[3] = f2h(z1[2]) | (f2h(z1[3]) << 16);
+                    } else {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float z0 = tok < T && k0 + 2 * q < a.r ? zp[k0 + 2 * q] : 0.f;
-                        const float z1 = tok < T && k0 + 2 * q + 1 < a.r ? zp[k0 + 2 * q + 1] : 0.f;
-                        h[q] = f2h(z0) | (f2h(z1) << 16);
+                        for (int q = 0; q < 4; ++q) {
+                            const float z0 = k0 + 2 * q < a.r ? zp[k0 + 2 * q] : 0.f;
+                            const float z1 = k0 + 2 * q + 1 < a.r ? zp[k0 + 2 * q + 1] : 0.f;
+                            h[q] = f2h(z0) | (f2h(z1) << 16);
+                        }
                     }
                     const u32x4 Az = u32x4{h[0], h[1], h[2], h[3]};
 #pragma unroll
