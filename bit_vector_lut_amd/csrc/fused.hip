@@ -58,9 +58,17 @@ __device__ __forceinline__ float dpp_xor1(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1,
                                                               0xF, 0xF, false));
 }
-__device__ __forceinline__ float dpp_xor2(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E,
-                                                              0xF, 0xF, false));
+
+// Sum of the 16 floats p[0], p[stride], ..., p[15 stride] in a fixed pairwise order.
+__device__ __forceinline__ float sum16(const float* p, int stride) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = p[i * stride];
+#pragma unroll
+    for (int h = 1; h < 16; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2 * h) v[i] += v[i + h];
+    return v[0];
 }
 
 constexpr int kRotVals = 4;  // values per lane of a rotated row (rows of up to 256 columns)
@@ -364,24 +372,14 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
             const Item prev = decode(prev_u);
             const int eb = (j - 1) & 3;
             if (prev.kind == kKindG) {
-                const int o = tid >> 2, qq = tid & 3;  // output o, quarter of the waves
-                const int e_l = o & 63, e_r = o >> 6;
-                // one float per read (a register-indexed vector element would serialize the
-                // reads behind one another)
-                const float* rf = reinterpret_cast<const float*>(&red[0][0][0]) + e_l * 4 + e_r;
-                float gv[4], uv[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    gv[i] = rf[((4 * qq + i) * 2 + 0) * 256];
-                    uv[i] = rf[((4 * qq + i) * 2 + 1) * 256];
-                }
-                float g = (gv[0] + gv[1]) + (gv[2] + gv[3]);
-                float u = (uv[0] + uv[1]) + (uv[2] + uv[3]);
-                g += dpp_xor1(g);
-                u += dpp_xor1(u);
-                g += dpp_xor2(g);
-                u += dpp_xor2(u);
-                if (qq == 0) {
+                // Thread tid < 256 sums the 16 waves' partials of accumulator element
+                // e_r = tid % 4 of lane e_l = tid / 4 (both matrices).  Float 4 e_l + e_r of a
+                // wave's block is tid, so a wave's 64 reads of one block fall in 64 consecutive
+                // words: every bank once per half-wave.
+                const int e_l = tid >> 2, e_r = tid & 3;
+                if (tid < 256) {
+                    const float* rf = reinterpret_cast<const float*>(&red[0][0][0]) + e_l * 4 + e_r;
+                    float g = sum16(rf, 512), u = sum16(rf + 256, 512);
                     const int rl = 2 * (4 * (e_l >> 4) + e_r) + (e_l & 1), t = (e_l & 15) >> 1;
                     g *= esc[eb][0][rl];
                     u *= esc[eb][1][rl];
@@ -391,25 +389,21 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                                  (uint64_t(tag) << 32) | bits);
                 }
                 // One tile of each rotation unit rotates the whole unit once the others' values
-                // are in; which tile is hashed from the unit, so that round-robin assignment does
-                // not hand every rotation to the same workgroups.
-                // Round-robin order: which tile is hashed from the unit, so that the rotations do
-                // not all fall to the same workgroups.  Queue order: the unit's last tile, so the
-                // rotation only ever waits for tiles handed out before it.
+                // are in.  Round-robin order: which tile is hashed from the unit, so that the
+                // rotations do not all fall to the same workgroups.  Queue order: the unit's last
+                // tile, so the rotation only ever waits for tiles handed out before it.
                 const int unit = prev.id / tpu;
                 const int owner = a.dyn ? tpu - 1 : int((unit ^ (unit >> 2) ^ (unit >> 5)) % tpu);
                 if (prev.id % tpu == owner) job = unit;
             } else {
-                const int o = tid >> 1, hh = tid & 1;  // output o of 512, half of the waves
-                const int mm = o >> 8, e_l = o & 63, e_r = (o >> 6) & 3;
-                const float* rf = reinterpret_cast<const float*>(&red[0][0][0]) + e_l * 4 + e_r;
-                float vv[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i) vv[i] = rf[((8 * hh + i) * 2 + mm) * 256];
-                float v = ((vv[0] + vv[1]) + (vv[2] + vv[3])) + ((vv[4] + vv[5]) + (vv[6] + vv[7]));
-                v += dpp_xor1(v);
+                // Thread tid < 512 sums the 16 waves' partials of element e_r of lane e_l of
+                // operand slot mm (bank tid % 32, as in the gate/up epilogue).
+                const int mm = tid >> 8, e_l = (tid >> 2) & 63, e_r = tid & 3;
                 const int tile = 2 * prev.id + mm;
-                if (hh == 0 && tile < MTh) {
+                if (tid < 512 && tile < MTh) {
+                    const float* rf =
+                        reinterpret_cast<const float*>(&red[0][0][0]) + mm * 256 + e_l * 4 + e_r;
+                    const float v = sum16(rf, 512);
                     const int rl = 2 * (4 * (e_l >> 4) + e_r) + (e_l & 1), t = (e_l & 15) >> 1;
                     const int row = tile * kTileRows + rl;
                     if (a.nsl == 1) {
