@@ -43,13 +43,16 @@ KERNEL_SOURCES = ["fused.hip", "device.h", "internal.h"]
 
 
 def kernel_source_hash():
-    """SHA-256 of the sources the fused kernel is compiled from."""
+    """SHA-256 of the sources the fused kernel is compiled from and of its compiler flags."""
     import hashlib
+
+    from bit_vector_lut_amd import build as hipbuild
 
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, "bit_vector_lut_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
+    h.update(" ".join(hipbuild.HIP_FLAGS + hipbuild.SOURCE_FLAGS.get("fused.hip", [])).encode())
     return h.hexdigest()
 
 

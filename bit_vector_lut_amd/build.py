@@ -26,7 +26,10 @@ HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 # Per-source flags.  The register-decode product is one wave per SIMD with long independent
 # chains (cross-lane reads, matrix-core steps): the ILP-first scheduler batches its LDS reads and
 # keeps the accumulators in place, where the default one serialises them to save registers.
-SOURCE_FLAGS = {"vq3mm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+# The fused T <= 8 kernel measured 1-2% faster per layer with the same scheduler (its product loop
+# then keeps more lookups in flight ahead of the matrix-core steps).
+SOURCE_FLAGS = {"vq3mm.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+                "fused.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def build(verbose: bool = False) -> str:
