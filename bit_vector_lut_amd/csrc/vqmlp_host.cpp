@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -53,6 +54,22 @@ vqmlp_status hip_fail(hipError_t e, const char* what) {
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// VQMLP_TRACE set to anything but "0": one line per call on stderr naming the kernels that the
+// dispatch chose.  Read on every call (one getenv), so a process can switch it on and off.
+bool trace_on() {
+    const char* v = getenv("VQMLP_TRACE");
+    return v && *v && strcmp(v, "0") != 0;
+}
+
+void trace(const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    fprintf(stderr, "vqmlp: %s\n", buf);
+}
 
 bool is_pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 
@@ -477,6 +494,22 @@ vqmlp_status run_tiled(const vqmlp_plan* p, int T, const void* x, void* y, const
     return ok();
 }
 
+// The trace line of a forward on the tiled / register-decode kernels.
+void trace_tiled(const vqmlp_plan* p, int T, const Workspace& w) {
+    const char* fam = T >= kVq3mmMinT ? "register-decode" : "tiled";
+    char split[96] = "";
+    if (w.gs.rows_split)
+        snprintf(split, sizeof split, ", rows %d.. K-split %d ways + combine", w.gs.rows_main,
+                 w.gs.splits);
+    char dsplit[64] = "";
+    if (w.dsplit > 1) snprintf(dsplit, sizeof dsplit, " K-split %d ways + reduction", w.dsplit);
+    trace("forward%s H=%d I=%d T=%d: input rotation; %s gate/up on rows 0..%d%s; %s; %s down%s",
+          p->vq2 ? " 2x16" : "", p->d.H, p->d.I, T, fam, w.gs.rows_main, split,
+          p->bi == 128 && p->d.I % 128 == 0 ? "intermediate rotation in the gate/up epilogue"
+                                           : "intermediate rotation kernel",
+          fam, dsplit);
+}
+
 // 2x16 matrices at T <= 8: rotate x, the gate and up products as unscaled FP32 planes (K
 // slices of at most kVq2MaxK columns), a = silu(g) u sign with its rotation, the down product
 // (K slices), the slice sum scaled into y.
@@ -798,9 +831,16 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
                         "the 2x16 T <= 8 path takes T <= %d and I a multiple of 128 (T=%d)",
                         kSkinnyT, T);
         const int use = path == 0 ? (T <= kSkinnyT && skinny ? 1 : 2) : path;
-        if (use == 1) return run_vq2_skinny(p, T, x, y, w, st);
+        if (use == 1) {
+            if (trace_on())
+                trace("forward 2x16 H=%d I=%d T=%d: input rotation; 2x16 projection kernel, gate "
+                      "and up in one launch (%d K slices); gate/up combine; down (%d K slices)%s",
+                      p->d.H, p->d.I, T, p->v2_ng, p->v2_nd, p->v2_nd > 1 ? " + slice sum" : "");
+            return run_vq2_skinny(p, T, x, y, w, st);
+        }
         if (!p->tiled_ok)
             return fail(VQMLP_ERR_UNSUPPORTED, "the tiled path takes H and I multiples of 64");
+        if (trace_on()) trace_tiled(p, T, w);
         return run_tiled(p, T, x, y, w, st);
     }
     // 1: the fused single-launch kernel (T <= 8), 2: the tiled kernels; 0 picks the fused
@@ -816,7 +856,15 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
     const int use = path == 0 ? (T <= kSkinnyT && fused_ok ? 1 : 2) : path;
     if (use == 2 && !p->tiled_ok)
         return fail(VQMLP_ERR_UNSUPPORTED, "the tiled path takes H and I multiples of 64");
-    if (use == 1) return run_fused(p, T, x, y, w, st);
+    if (use == 1) {
+        if (trace_on())
+            trace("forward H=%d I=%d T=%d: fused kernel (%d tiles per wave, %d workgroups; items: "
+                  "%d input rotation, %d gate/up, %d down in %d K slices)",
+                  p->d.H, p->d.I, T, p->fz.tpw, p->cus, p->fz.n_r, p->fz.n_g,
+                  p->fz.nsl * p->fz.nqd, p->fz.nsl);
+        return run_fused(p, T, x, y, w, st);
+    }
+    if (trace_on()) trace_tiled(p, T, w);
     return run_tiled(p, T, x, y, w, st);
 }
 
@@ -1054,6 +1102,9 @@ vqmlp_status lut_run(const vqmlp_lut_plan& p, int T, const void* x, void* y, voi
         aligned(p.s, 16) && aligned(p.sign, 8)) {  // (the pre-pass reads s and sign in vectors)
         // decode-size T: one pre-pass (rotation and per-chunk partial sums of z), then the
         // code-stream kernel (its epilogue adds U z in FP32)
+        if (trace_on())
+            trace("scalar-LUT %d-bit N=%d K=%d T=%d r=%d: pre-pass (rotation, %d planes of z), "
+                  "code-stream kernel", bits, N, K, T, r, lut8_planes(K, hb));
         float* zp = reinterpret_cast<float*>(wb + align256(size_t(T) * K * 2));
         hipError_t e = launch_lut8_pre(T, K, hb, static_cast<const uint16_t*>(x), p.s, p.sign, V, r,
                                        xt, zp, hs);
@@ -1117,6 +1168,11 @@ vqmlp_status lut_run(const vqmlp_lut_plan& p, int T, const void* x, void* y, voi
     g.out16 = static_cast<uint16_t*>(y);
     // too few row tiles to fill the CUs: split K into scaled FP32 planes, then sum them
     const int ls = gemm_split(g.kind, N, K, T, kLutSplitCUs);
+    if (trace_on())
+        trace("scalar-LUT %d-bit N=%d K=%d T=%d r=%d: rotation; %s; %s LUT product%s", bits, N,
+              K, T, r, r > 0 ? "rank-r product z = V x~ (K split, sum)" : "no rank term",
+              T >= kVq3mmMinT ? "register-decode" : "tiled",
+              ls > 1 ? " K-split + reduction" : "");
     if (ls > 1) {
         const int zs = gemm_split(kGemmDense32, r ? r : 1, K, T, kLutSplitCUs);
         float* lp = reinterpret_cast<float*>(wb + align256(size_t(T) * K * 2) +
@@ -1216,6 +1272,9 @@ vqmlp_status vqmlp_lut_plan_argmax(const vqmlp_lut_plan* plan, int T, const void
     float* pval = reinterpret_cast<float*>(wb + align256(size_t(T) * K * 2));
     int* pidx = reinterpret_cast<int*>(pval + kArgmaxMaxGroups * kSkinnyT);
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (trace_on())
+        trace("argmax head %d-bit N=%d K=%d T=%d: pre-pass (rotation); persistent head "
+              "(%d workgroups); candidate merge", p.bits, N, K, T, lut8_argmax_grid(N, p.cus));
     hipError_t e = launch_lut8_pre(T, K, hb, static_cast<const uint16_t*>(x), p.s, p.sign, nullptr, 0,
                                    xt, nullptr, hs);
     if (e != hipSuccess) return hip_fail(e, "argmax head: input scale and rotation");
@@ -1392,6 +1451,7 @@ vqmlp_status vqmlp_vq2_plan_forward(const vqmlp_vq2_plan* plan, int T, const voi
     a.ldk = p.K;
     a.nsplit = 1;
     a.o32_t = a.o32_s = 0;
+    if (trace_on()) trace("2x16 projection N=%d K=%d T=%d: projection kernel", p.N, p.K, T);
     const hipError_t e = launch_vq2_8(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "2x16 projection");
     return ok();
