@@ -26,6 +26,10 @@
  * host memory owned by the caller.  `stream` is a hipStream_t (NULL = the legacy default
  * stream); device work is only enqueued, never waited for, and asynchronous device faults
  * surface at the caller's next synchronisation.
+ *
+ * Tracing: with the environment variable VQMLP_TRACE set to anything but "0", every forward
+ * (MLP, 2x16, scalar-LUT, argmax head) writes one line to stderr that names the kernels its
+ * dispatch chose and their K splits.  The variable is read on each call.
  */
 #ifndef VQMLP_H
 #define VQMLP_H
