@@ -418,13 +418,16 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
             }
         }
         __syncthreads();  // (B) partials consumed: red is free
-        // (D) the rotation unit or row pair that this epilogue completed
+        // (D) the rotation unit or row pair that this epilogue completed (waves 0-7).  No barrier
+        // after it, so the other waves start the next item at once: the jobs touch no LDS, and
+        // what this iteration writes to LDS from here on (the idle table buffer, scale slots two
+        // items ahead, red and the queue slot after barrier (B), each wave's own activation
+        // columns) is read by no wave before the next barrier (A).
         if (job >= 0) {
             if (job >> 30)
                 job_reduce_y(job & ((1 << 30) - 1));
             else
                 job_rotate_mid(job);
-            __syncthreads();
         }
         if (cur_u >= a.total) break;
 
