@@ -447,23 +447,48 @@ k_vq3mm(GemmArgs a) {
                 }
         }
         __syncthreads();
-        for (int h = 1; h < 128; h <<= 1) {
-            for (int e = tid; e < BM * (BNW / 2); e += NT) {
-                const int tl = e / (BNW / 2), jj = e % (BNW / 2);
-                const int lo = (jj / h) * 2 * h + (jj % h), hi = lo + h;
-                const float x0 = Ab[tl * (BNW + 1) + lo], x1 = Ab[tl * (BNW + 1) + hi];
-                Ab[tl * (BNW + 1) + lo] = x0 + x1;
-                Ab[tl * (BNW + 1) + hi] = x0 - x1;
+        // The butterflies of distance 1, 2, 4, then of 8, 16, 32, three stages per LDS pass on 8
+        // values in registers (thread: one token and 8 rows h apart; consecutive threads take
+        // consecutive tokens, whose rows lie one bank apart in the padded layout); the stage of
+        // distance 64 runs in the binary16 stores.  Every value meets the same additions in the
+        // same order as with one pass per stage.
+        auto radix8 = [&](const int h) {
+            for (int e = tid; e < BM * (BNW / 8); e += NT) {
+                const int tl = e % BM, jj = e / BM;
+                float* p = Ab + tl * (BNW + 1) + (jj / h) * 8 * h + (jj % h);
+                float v[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[k] = p[k * h];
+#pragma unroll
+                for (int d = 1; d < 8; d <<= 1)
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        if (!(k & d)) {
+                            const float x0 = v[k], x1 = v[k | d];
+                            v[k] = x0 + x1;
+                            v[k | d] = x0 - x1;
+                        }
+#pragma unroll
+                for (int k = 0; k < 8; ++k) p[k * h] = v[k];
             }
             __syncthreads();
-        }
-        for (int e = tid; e < BM * BNW / 2; e += NT) {
-            const int tl = e / (BNW / 2), cc = (e % (BNW / 2)) * 2;
+        };
+        radix8(1);
+        radix8(8);
+        // thread (token, rows c, c + 1 of the lower half of a 128-row block): the distance-64
+        // butterflies of both rows, then both halves out
+        for (int e = tid; e < BM * (BNW / 4); e += NT) {
+            const int tl = e / (BNW / 4), q = e % (BNW / 4);
+            const int c = (q / 32) * 128 + 2 * (q % 32);
             const int tok = tok0 + tl;
-            if (tok < T && row0 + cc < N) {
-                const uint32_t hv = f2h(Ab[tl * (BNW + 1) + cc] * a.norm) |
-                                    (f2h(Ab[tl * (BNW + 1) + cc + 1] * a.norm) << 16);
-                *reinterpret_cast<uint32_t*>(a.out16 + size_t(tok) * ldo + row0 + cc) = hv;
+            if (tok < T && row0 + c < N) {  // N and row0 are multiples of 128: whole blocks
+                const float* p = Ab + tl * (BNW + 1) + c;
+                const float a0 = p[0], a1 = p[1], b0 = p[64], b1 = p[65];
+                uint16_t* o = a.out16 + size_t(tok) * ldo + row0 + c;
+                *reinterpret_cast<uint32_t*>(o) =
+                    f2h((a0 + b0) * a.norm) | (f2h((a1 + b1) * a.norm) << 16);
+                *reinterpret_cast<uint32_t*>(o + 64) =
+                    f2h((a0 - b0) * a.norm) | (f2h((a1 - b1) * a.norm) << 16);
             }
         }
         return;
