@@ -171,6 +171,7 @@ struct GemmArgs {
     int ldo;                   // output row stride (0 = N)
     int vq2;                   // the VQ3 kinds on 2x16 matrices (codes [N/2][K/8] words,
                                // 16 centroids per 8 rows): tiled kernels with the 2x16 decoder
+    int bm64;                  // K-split gate/up of vq3mm above 64 rows: 64-token tiles
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t st);
 // VQ3 products for T > 32 rows with the weights decoded in registers (vq3mm.hip): gate/up kinds

@@ -677,8 +677,9 @@ hipError_t launch_vq3mm_bm(const GemmArgs& a, hipStream_t st) {
         case kGemmVQ3GateUpRot:  // whole 128-row rotation blocks
             if (a.N % 128) return hipErrorInvalidValue;
             return launch_t<kGuNW, BMG, kGuRW, 2, kEgGateUpRot, DV>(a, st);
-        case kGemmVQ3GateUpSplit:
-            return launch_t<kGuNW, BMG, kGuRW, 2, kEgPart2, DV>(a, st);
+        case kGemmVQ3GateUpSplit:  // the leftover rows of a larger product: 64-token tiles
+            return a.bm64 ? launch_t<kGuNW, kSmallBM, kGuRW, 2, kEgPart2, DV>(a, st)
+                          : launch_t<kGuNW, BMG, kGuRW, 2, kEgPart2, DV>(a, st);
         case kGemmVQ3Down:
             return launch_t<kDnNW, BMD, kDnRW, 1, kEgScale16, DV>(a, st);
         case kGemmVQ3DownSplit:
@@ -704,7 +705,8 @@ hipError_t launch_vq3mm_wide(const GemmArgs& a, hipStream_t st) {
             if (a.N % 128) return hipErrorInvalidValue;
             return launch_t<kWideNW, kGuBM, kWideGuRW, 2, kEgGateUpRot, DV>(a, st);
         case kGemmVQ3GateUpSplit:
-            return launch_t<kWideNW, kGuBM, kWideGuRW, 2, kEgPart2, DV>(a, st);
+            return a.bm64 ? launch_t<kWideNW, kSmallBM, kWideGuRW, 2, kEgPart2, DV>(a, st)
+                          : launch_t<kWideNW, kGuBM, kWideGuRW, 2, kEgPart2, DV>(a, st);
         case kGemmVQ3Down:
             return launch_t<kWideNW, kDnBM, kWideDnRW, 1, kEgScale16, DV>(a, st);
         case kGemmVQ3DownSplit:

@@ -225,12 +225,14 @@ namespace {
 // The gate/up product of the tiled path in 128-row by 128- (or 64-) token tiles: the first
 // rows_main rows take whole rounds of workgroups on the CUs; the last rows_split rows, which
 // would leave a partial round, are split along K into `splits` parts over the CUs.  With fewer
-// tiles than CUs every row is split (rows_main = 0).
+// tiles than CUs every row is split (rows_main = 0).  The rows left over after whole rounds run in
+// 64-token tiles where the whole-K product's tiles hold 128 tokens (bm64): twice the workgroups,
+// each with half the products, so that more CUs share the split rows and fewer planes are needed.
 struct GateUpSplit {
-    int rows_main, rows_split, splits;
+    int rows_main, rows_split, splits, bm64;
 };
 GateUpSplit gateup_split(int I, int H, int T, int cus) {
-    GateUpSplit g{I, 0, 1};
+    GateUpSplit g{I, 0, 1, 0};
     if (I % 128 || T <= kSkinnyT || cus <= 0) return g;
     const Vq3Tile t = T >= kVq3mmMinT ? vq3mm_tile(kGemmVQ3GateUpSplit, T) : Vq3Tile{64, 128};
     if (I % t.bn) return g;
@@ -257,12 +259,14 @@ GateUpSplit gateup_split(int I, int H, int T, int cus) {
     }
     if (total <= cus || total % cus == 0) return g;
     const int main_rt = (total / cus) * cus / tt;
-    const int left = (rt - main_rt) * tt;  // leftover tiles
+    const int bms = t.bm > 64 ? 64 : t.bm;  // tokens per tile of the split rows
+    const int left = (rt - main_rt) * ((T + bms - 1) / bms);  // their tiles
     const int s = std::min(kt / 8, std::max(1, cus / left));
     if (main_rt <= 0 || s < 2) return g;
     g.rows_main = main_rt * t.bn;
     g.rows_split = I - g.rows_main;
     g.splits = s;
+    g.bm64 = bms < t.bm && T >= kVq3mmMinT ? 1 : 0;
     return g;
 }
 
@@ -443,6 +447,7 @@ vqmlp_status run_tiled(const vqmlp_plan* p, int T, const void* x, void* y, const
         q.N = gs.rows_split;
         q.ldo = 0;
         q.ksplit = gs.splits;
+        q.bm64 = gs.bm64;
         for (int m = 0; m < 2; ++m) {
             // row r0 of the packed codes and codebooks (VQ3 tiles, or 2x16 pair rows of H / 8
             // words and 16 centroids per 8 rows)
@@ -499,8 +504,8 @@ void trace_tiled(const vqmlp_plan* p, int T, const Workspace& w) {
     const char* fam = T >= kVq3mmMinT ? "register-decode" : "tiled";
     char split[96] = "";
     if (w.gs.rows_split)
-        snprintf(split, sizeof split, ", rows %d.. K-split %d ways + combine", w.gs.rows_main,
-                 w.gs.splits);
+        snprintf(split, sizeof split, ", rows %d.. K-split %d ways%s + combine", w.gs.rows_main,
+                 w.gs.splits, w.gs.bm64 ? " in 64-token tiles" : "");
     char dsplit[64] = "";
     if (w.dsplit > 1) snprintf(dsplit, sizeof dsplit, " K-split %d ways + reduction", w.dsplit);
     trace("forward%s H=%d I=%d T=%d: input rotation; %s gate/up on rows 0..%d%s; %s; %s down%s",
