@@ -1,4 +1,4 @@
-// vq3mm.hip -- matrix-core product with the VQ3 weights decoded in registers, for T > 64 rows
+// vq3mm.hip -- matrix-core product with the VQ3 weights decoded in registers, for T > 32 rows
 // (gfx950).
 //
 //   D[t][n] = sum_k X[t][k] W[n][k],   X binary16 [T][K] (rotated activations), W packed VQ3.
@@ -6,27 +6,27 @@
 // Model card "anemll/anemll-forge-qwen3.8-27B", section "Release 0.2: three-bit MLP, token-mixer
 // rotations, distilled weights": a six-bit code selects the pair (W[2p][j], W[2p+1][j]) from 64
 // two-component binary16 centroids shared by 8 rows; row scales are applied in the epilogue.
+// The same kernel serves the 2x16 format (4-bit codes, 16 centroids) and the scalar-LUT
+// projections (2- or 4-bit codes into per-8-row tables of scalars).
 //
-// Work split.  A workgroup of NW waves (one per SIMD) owns BM tokens x NW*RW rows (of each of
-// NMAT matrices that share X).  Each wave owns RW rows and all BM tokens, so no weight is used by
-// two waves and the decoded weights never pass through LDS: a wave turns its own codes straight
-// into the B operands of v_mfma_f32_16x16x32_f16.  Only the activation tile is staged through
-// LDS, where all waves read it.
+// Work split.  A workgroup of NW waves owns BM tokens x NW*RW rows (of each of NMAT matrices
+// that share X).  Each wave owns RW rows and all BM tokens, so no weight is used by two waves and
+// the decoded weights never pass through LDS: a wave turns its own codes straight into the B
+// operands of v_mfma_f32_32x32x16_f16.  Only the activation tile is staged through LDS, where
+// all waves read it.  NW = 4 is one wave per SIMD (accumulators in the AGPRs); from 256 tokens the
+// VQ kinds run NW = 8, two waves per SIMD, so that one wave decodes while the other multiplies.
 //
-// Decoding.  The centroids of the two 8-row groups of a 16-row operand sit in one LDS table,
-// replicated over the 32 bank columns: column b holds the first group's 64 centroids for
-// b % 16 < 8 and the second group's otherwise, matching the row (lane % 16) of the lanes that
-// read column lane % 32.  A lookup is one 4-byte LDS read at (code, own column), free of bank
-// conflicts whatever the codes.  A centroid holds both rows of a pair, so lane n fetches the
-// centroids of its pair for four of the operand's eight columns, keeps its own row's halves and
-// trades the other halves with lane n ^ 1 (one DPP quad permute).  The tables are written once
+// Decoding.  A B operand is 32 rows x 16 K columns.  The centroids of its four 8-row groups sit
+// in one LDS table replicated over the 32 bank columns (column b holds group b / 8), and lane l,
+// whose row is l % 32, reads column l % 32 only: a lookup is one 4-byte LDS read at (code, own
+// column), free of bank conflicts whatever the codes.  A centroid holds both rows of a pair, so a
+// lane fetches its pair's centroids for four of its eight columns, keeps its own row's halves and
+// trades the other halves with lane l ^ 1 (one DPP quad permute).  The tables are written once
 // per workgroup: the codebooks are shared by all K.
 //
-// Column order.  Within a 64-column K tile, operand slot (ks, kg, i) -- K step ks (of 2), lane
-// group kg = lane / 16, element i (of 8) -- holds column 16 (i / 2) + 4 kg + 2 ks + (i % 2).  With
-// this order the codes a lane needs for one K tile are 48 contiguous bits of its pair's 96-bit
-// lane record in the packed tile.  The activations are staged into LDS in the same order, so an
-// A operand is still one 16-byte LDS read.
+// Codes and activations.  The codes a lane needs for one 64-column K tile (four K steps) are one
+// 96-bit lane record of the packed tile, 24 bits per K step.  The activations are staged into LDS
+// with 16-byte chunks XOR-swizzled by row, so an A operand is one conflict-free 16-byte read.
 #include "device.h"
 #include "internal.h"
 
