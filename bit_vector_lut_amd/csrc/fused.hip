@@ -539,48 +539,58 @@ __global__ void __launch_bounds__(kW * 64, 1) k_fused(FusedArgs a) {
                 }
             };
             f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-            u32x4 A[2][2];
-            look(ring[0], 0, A[0]);
+            // slot t + P: tile t + P of this item, or of the next one past the end.  With no
+            // next item the load repeats tile t, just read and still in the on-die cache: the
+            // refill stays unconditional without fetching again a tile that left the cache.
+            auto refill = [&](const int t) {
+                const int tt = (t + P) % TPW;
+                const bool own = t + P < TPW || !has_next;
+                int kt = t + P < TPW ? ckt0 + tt : (has_next ? nkt0 + tt : ckt0 + t);
+                const int lim = own ? clast_kt : nlast_kt;
+                kt = kt < lim ? kt : lim;
+                const uint32_t* p0 = reinterpret_cast<const uint32_t*>(
+                                         (own ? cbase0 : nbase0) + size_t(kt) * kTileBytes) + 3 * l;
+                const uint32_t* p1 = reinterpret_cast<const uint32_t*>(
+                                         (own ? cbase1 : nbase1) + size_t(kt) * kTileBytes) + 3 * l;
+                ring[tt][0][0] = p0[0];
+                ring[tt][0][1] = p0[1];
+                ring[tt][0][2] = p0[2];
+                ring[tt][1][0] = p1[0];
+                ring[tt][1][1] = p1[1];
+                ring[tt][1][2] = p1[2];
+            };
+            if (cntile == 0) {
+                // no tile of this item (the last K slice is short): only the refills that
+                // fetch the next item's first tiles
 #pragma unroll
-            for (int t = 0; t < TPW; ++t) {
+                for (int t = TPW - P; t < TPW; ++t)
+                    if (t >= 0) refill(t);
+            } else {
+                u32x4 A[2][2];
+                look(ring[0], 0, A[0]);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int cp0 = (4 * t + s) & 1, cp1 = cp0 ^ 1;
-                    const u32x2 bv = *reinterpret_cast<const u32x2*>(bl + t * kTileCols + 16 * s);
-                    if (s < 3)
-                        look(ring[t % D], s + 1, A[cp1]);
-                    else if (t + 1 < TPW)
-                        look(ring[(t + 1) % D], 0, A[cp1]);
-                    if (s == 2) {
-                        // slot t + P: tile t + P of this item, or of the next one past the end.
-                        // With no next item the load repeats tile t, just read and still in the
-                        // on-die cache: the refill stays unconditional without fetching again a
-                        // tile that left the cache long ago.
-                        const int tt = (t + P) % TPW;
-                        const bool own = t + P < TPW || !has_next;
-                        int kt = t + P < TPW ? ckt0 + tt : (has_next ? nkt0 + tt : ckt0 + t);
-                        const int lim = own ? clast_kt : nlast_kt;
-                        kt = kt < lim ? kt : lim;
-                        const uint32_t* p0 = reinterpret_cast<const uint32_t*>(
-                                                 (own ? cbase0 : nbase0) + size_t(kt) * kTileBytes) + 3 * l;
-                        const uint32_t* p1 = reinterpret_cast<const uint32_t*>(
-                                                 (own ? cbase1 : nbase1) + size_t(kt) * kTileBytes) + 3 * l;
-                        ring[tt][0][0] = p0[0];
-                        ring[tt][0][1] = p0[1];
-                        ring[tt][0][2] = p0[2];
-                        ring[tt][1][0] = p1[0];
-                        ring[tt][1][1] = p1[1];
-                        ring[tt][1][2] = p1[2];
-                        // keep each refill where it is, one item ahead of its use
-                        __builtin_amdgcn_sched_barrier(0);
+                for (int t = 0; t < TPW; ++t) {
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
+                        const int cp0 = (4 * t + s) & 1, cp1 = cp0 ^ 1;
+                        const u32x2 bv = *reinterpret_cast<const u32x2*>(bl + t * kTileCols + 16 * s);
+                        if (s < 3)
+                            look(ring[t % D], s + 1, A[cp1]);
+                        else if (t + 1 < TPW)
+                            look(ring[(t + 1) % D], 0, A[cp1]);
+                        if (s == 2) {
+                            refill(t);
+                            // keep each refill where it is, one item ahead of its use
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        const uint32_t b0 = bv[0], b1 = bv[1];
+                        const u32x4 Bx = u32x4{__builtin_amdgcn_perm(b0, 0u, sel_e),
+                                               __builtin_amdgcn_perm(b0, 0u, sel_o),
+                                               __builtin_amdgcn_perm(b1, 0u, sel_e),
+                                               __builtin_amdgcn_perm(b1, 0u, sel_o)};
+                        acc[0] = mfma16x16x32(A[cp0][0], Bx, acc[0]);
+                        acc[1] = mfma16x16x32(A[cp0][1], Bx, acc[1]);
                     }
-                    const uint32_t b0 = bv[0], b1 = bv[1];
-                    const u32x4 Bx = u32x4{__builtin_amdgcn_perm(b0, 0u, sel_e),
-                                           __builtin_amdgcn_perm(b0, 0u, sel_o),
-                                           __builtin_amdgcn_perm(b1, 0u, sel_e),
-                                           __builtin_amdgcn_perm(b1, 0u, sel_o)};
-                    acc[0] = mfma16x16x32(A[cp0][0], Bx, acc[0]);
-                    acc[1] = mfma16x16x32(A[cp0][1], Bx, acc[1]);
                 }
             }
             // (I) next item's tables into the idle buffers, this item's partials
