@@ -482,21 +482,48 @@ int gemm_split(int kind, int N, int K, int T, int cus) {
     return best;
 }
 
+// y = sc . (sum of the K-split planes), binary16.  Thread: V consecutive outputs (V = 4: 16-byte
+// plane loads, N a multiple of 4), the planes' loads issued four at a time ahead of their sums; the
+// sum of each output runs over the planes in order, whatever V.
+template <int V>
 __global__ void __launch_bounds__(256) k_split_reduce(int T, int N, int splits, const float* part,
                                                       const uint16_t* sc, uint16_t* y) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= T * N) return;
-    const int row = i % N;
-    float sum = 0.f;
-    for (int z = 0; z < splits; ++z) sum += part[size_t(z) * T * N + i];
-    y[i] = (uint16_t)f2h(sc ? sum * h2f(sc[row]) : sum);
+    typedef float fv __attribute__((ext_vector_type(V)));
+    const size_t n = size_t(T) * N;
+    const size_t i = (size_t(blockIdx.x) * 256 + threadIdx.x) * V;
+    if (i >= n) return;
+    auto plane = [&](int z) { return *reinterpret_cast<const fv*>(part + size_t(z) * n + i); };
+    fv sum = fv(0.f);
+    int z = 0;
+    for (; z + 4 <= splits; z += 4) {
+        const fv p0 = plane(z), p1 = plane(z + 1), p2 = plane(z + 2), p3 = plane(z + 3);
+        sum += p0;
+        sum += p1;
+        sum += p2;
+        sum += p3;
+    }
+    for (; z < splits; ++z) sum += plane(z);
+    const int row = int(i % size_t(N));
+    uint32_t h[V];
+#pragma unroll
+    for (int e = 0; e < V; ++e) h[e] = f2h(sc ? sum[e] * h2f(sc[row + e]) : sum[e]);
+    if constexpr (V == 4)  // 8-byte aligned (checked at launch)
+        *reinterpret_cast<u32x2*>(y + i) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+    else
+        y[i] = uint16_t(h[0]);
 }
 
 hipError_t launch_split_reduce(int T, int N, int splits, const float* part, const uint16_t* sc,
                                uint16_t* y, hipStream_t st) {
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(k_split_reduce, dim3((T * N + 255) / 256), dim3(256), 0, st, T, N, splits,
-                       part, sc, y);
+    const size_t n = size_t(T) * N;
+    if (N % 4 == 0 && (reinterpret_cast<uintptr_t>(part) & 15) == 0 &&
+        (reinterpret_cast<uintptr_t>(y) & 7) == 0)
+        hipLaunchKernelGGL(k_split_reduce<4>, dim3(unsigned((n / 4 + 255) / 256)), dim3(256), 0, st,
+                           T, N, splits, part, sc, y);
+    else
+        hipLaunchKernelGGL(k_split_reduce<1>, dim3(unsigned((n + 255) / 256)), dim3(256), 0, st, T,
+                           N, splits, part, sc, y);
     return hipGetLastError();
 }
 
@@ -541,11 +568,27 @@ __global__ void __launch_bounds__(256) k_gateup_combine(int T, int N, int splits
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
         const int row = r0 + 64 * e + l;
+        // the planes' loads four at a time ahead of their sums, each sum over the planes in order
+        const float* p = part + size_t(t) * 2 * N + row;
+        const size_t zs = size_t(T) * 2 * N;  // plane stride
         float g = 0.f, u = 0.f;
-        for (int z = 0; z < splits; ++z) {
-            const float* p = part + (size_t(z) * T + t) * 2 * N + row;
-            g += p[0];
-            u += p[N];
+        int z = 0;
+        for (; z + 4 <= splits; z += 4) {
+            float pg[4], pu[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                pg[k] = p[(z + k) * zs];
+                pu[k] = p[(z + k) * zs + N];
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                g += pg[k];
+                u += pu[k];
+            }
+        }
+        for (; z < splits; ++z) {
+            g += p[z * zs];
+            u += p[z * zs + N];
         }
         g *= h2f(scg[row]);
         u *= h2f(scu[row]);
