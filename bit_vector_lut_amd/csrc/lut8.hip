@@ -76,11 +76,45 @@ __device__ __forceinline__ uint32_t look_pair4(const char* tb, uint32_t lb, uint
 __device__ __forceinline__ uint32_t look_pair2(const char* tb, uint32_t lb, uint32_t d, int sh) {
     return *reinterpret_cast<const uint32_t*>(tb + lut_addr(d, sh, lb));
 }
+// A wave's products over its K slice: nus units of 64 columns, two matrix-core steps each, on the
+// lane's code run cw.  A = the decoded weights of the wave's 16 rows, B = x~ (column n = token n mod 8;
+// columns 8..15 repeat tokens 0..7 and their outputs are never read, so no masking).  FULL: the
+// slice has all kMaxU units, and the loop runs without a check per unit, so that the scheduler can
+// move a unit's lookups ahead of the previous unit's waits.
+template <int BITS, bool FULL, int NW>
+__device__ __forceinline__ f32x4 lut_products(const uint32_t (&cw)[NW], int nus, int u0, int g,
+                                              const char* tb, uint32_t lb,
+                                              const uint16_t (&xs)[kSkinnyT][kXRow], int n) {
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < kMaxU; ++u) {
+        if (FULL || u < nus) {  // uniform
+            const int kb = u0 * 64 + 16 * (g * nus + u);
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 A;
+                if constexpr (BITS == 2) {
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) A[p] = look_pair2(tb, lb, cw[u], 16 * s + 4 * p);
+                } else {
+                    const uint32_t d = cw[2 * u + s];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) A[p] = look_pair4(tb, lb, d, 8 * p);
+                }
+                const u32x4 B = *reinterpret_cast<const u32x4*>(&xs[n & (kSkinnyT - 1)][kb + 8 * s]);
+                acc = mfma16x16x32(A, B, acc);
+            }
+        }
+    }
+    return acc;
+}
 constexpr int kMaxR = 256;              // rank of the low-rank term
 typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));  // 4-byte aligned
 }  // namespace
 
-template <int BITS>
+// FULL: K = kMaxK, so that every wave's K slice holds all kMaxU units (the products then run
+// without a check per unit; chosen at launch)
+template <int BITS, bool FULL>
 __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
     constexpr int CW = BITS == 2 ? 1 : 2;  // code words per lane and unit
     // one LDS block with the tables at address 0 (a lookup address is the entry and lane bits)
@@ -222,31 +256,10 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
     }
 
     // ---- products
-    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
     const char* tbase = reinterpret_cast<const char*>(&tab[0][0]);
     const uint32_t lb = (uint32_t(l & 31) << 2) | uint32_t(rt * kTabDw * 4);
     const int n = l & 15;  // B column: token n
-#pragma unroll
-    for (int u = 0; u < kMaxU; ++u) {
-        if (u < nus) {  // uniform
-            const int kb = u0 * 64 + 16 * (g * nus + u);
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                u32x4 A;
-                if constexpr (BITS == 2) {
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) A[p] = look_pair2(tbase, lb, cw[u], 16 * s + 4 * p);
-                } else {
-                    const uint32_t d = cw[2 * u + s];
-#pragma unroll
-                    for (int p = 0; p < 4; ++p) A[p] = look_pair4(tbase, lb, d, 8 * p);
-                }
-                // columns 8..15 repeat tokens 0..7: those outputs are never read, so no masking
-                const u32x4 B = *reinterpret_cast<const u32x4*>(&xs[n & (kSkinnyT - 1)][kb + 8 * s]);
-                acc = mfma16x16x32(A, B, acc);
-            }
-        }
-    }
+    const f32x4 acc = lut_products<BITS, FULL>(cw, nus, u0, g, tbase, lb, xs, n);
     red[w][l] = acc;
     __syncthreads();
 
@@ -284,7 +297,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
 // epilogue keeps, per output thread, the best (value, row) seen (rows only grow, so a strictly
 // larger value is needed to replace: the lowest row wins ties); at the end the workgroup's
 // threads of a token are merged into part[b][t], and k_argmax_merge merges the workgroups.
-template <int BITS>
+template <int BITS, bool FULL>
 __global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* pval, int* pidx) {
     constexpr int CW = BITS == 2 ? 1 : 2;
     constexpr int kOffX = 2 * 2 * kTabDw * 4, kOffRed = kOffX + kSkinnyT * kXRow * 2;
@@ -369,28 +382,7 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* p
         }
         __syncthreads();  // tables of this block written; red of the last block consumed
         const uint32_t lb = (uint32_t(l & 31) << 2) | uint32_t(((par * 2 + rt) * kTabDw) * 4);
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < kMaxU; ++u) {
-            if (u < nus) {  // uniform
-                const int kb = u0 * 64 + 16 * (g * nus + u);
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    u32x4 A;
-                    if constexpr (BITS == 2) {
-#pragma unroll
-                        for (int p = 0; p < 4; ++p) A[p] = look_pair2(tb0, lb, cw[u], 16 * s + 4 * p);
-                    } else {
-                        const uint32_t d = cw[2 * u + s];
-#pragma unroll
-                        for (int p = 0; p < 4; ++p) A[p] = look_pair4(tb0, lb, d, 8 * p);
-                    }
-                    // columns 8..15 repeat tokens 0..7: those outputs are never read, so no masking
-                    const u32x4 B = *reinterpret_cast<const u32x4*>(&xs[n & (kSkinnyT - 1)][kb + 8 * s]);
-                    acc = mfma16x16x32(A, B, acc);
-                }
-            }
-        }
+        const f32x4 acc = lut_products<BITS, FULL>(cw, nus, u0, g, tb0, lb, xs, n);
         red[w][l] = acc;
         __syncthreads();
         if (tid < 256) {
@@ -505,10 +497,17 @@ hipError_t launch_lut8_argmax(const Lut8Args& a, int cus, float* pval, int* pidx
         a.K > kMaxK || a.T < 1 || a.T > kSkinnyT || a.r != 0 || cus < 1)
         return hipErrorInvalidValue;
     const int G = lut8_argmax_grid(a.N, cus);
-    if (a.bits == 2)
-        hipLaunchKernelGGL(k_lut8_argmax<2>, dim3(G), dim3(kW * 64), 0, st, a, pval, pidx);
+    const bool full = a.K == kMaxK;  // every K slice holds kMaxU units
+#define VQ_ARGMAX(B, F) hipLaunchKernelGGL((k_lut8_argmax<B, F>), dim3(G), dim3(kW * 64), 0, st, a, pval, pidx)
+    if (a.bits == 2 && full)
+        VQ_ARGMAX(2, true);
+    else if (a.bits == 2)
+        VQ_ARGMAX(2, false);
+    else if (full)
+        VQ_ARGMAX(4, true);
     else
-        hipLaunchKernelGGL(k_lut8_argmax<4>, dim3(G), dim3(kW * 64), 0, st, a, pval, pidx);
+        VQ_ARGMAX(4, false);
+#undef VQ_ARGMAX
     hipLaunchKernelGGL(k_argmax_merge, dim3(1), dim3(256), 0, st, G, a.T, pval, pidx, out_idx, out_val);
     return hipGetLastError();
 }
@@ -694,10 +693,17 @@ hipError_t launch_lut8(const Lut8Args& a, hipStream_t st) {
         a.N % 32 || a.K < 64 || a.K % 64 || a.K > kMaxK || a.T < 1 || a.T > kSkinnyT || a.r < 0 ||
         a.r > kMaxR || a.r % 8 || (a.r > 0 && (!a.U || !a.zp || a.nch < 1)))
         return hipErrorInvalidValue;
-    if (a.bits == 2)
-        hipLaunchKernelGGL(k_lut8<2>, dim3(a.N / 32), dim3(kW * 64), 0, st, a);
+    const bool full = a.K == kMaxK;  // every K slice holds kMaxU units
+#define VQ_LUT8(B, F) hipLaunchKernelGGL((k_lut8<B, F>), dim3(a.N / 32), dim3(kW * 64), 0, st, a)
+    if (a.bits == 2 && full)
+        VQ_LUT8(2, true);
+    else if (a.bits == 2)
+        VQ_LUT8(2, false);
+    else if (full)
+        VQ_LUT8(4, true);
     else
-        hipLaunchKernelGGL(k_lut8<4>, dim3(a.N / 32), dim3(kW * 64), 0, st, a);
+        VQ_LUT8(4, false);
+#undef VQ_LUT8
     return hipGetLastError();
 }
 
