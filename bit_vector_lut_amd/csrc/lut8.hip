@@ -293,7 +293,8 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8(Lut8Args a) {
 // ---- greedy argmax of a scalar-LUT output head (no rotation, no factors): y = sc . (W_lut x~)
 // is never written; the largest logit of each token and its row are.  Persistent workgroups of
 // the same shape as k_lut8 stage x~ once and walk the 32-row blocks b, b + G, ...; a block's code
-// runs and table words are requested one block ahead (tables double-buffered in LDS).  The
+// runs and table words are requested one block ahead (tables and partial sums double-buffered in
+// LDS, one barrier per block: a block's epilogue runs beside the next block's products).  The
 // epilogue keeps, per output thread, the best (value, row) seen (rows only grow, so a strictly
 // larger value is needed to replace: the lowest row wins ties); at the end the workgroup's
 // threads of a token are merged into part[b][t], and k_argmax_merge merges the workgroups.
@@ -301,10 +302,10 @@ template <int BITS, bool FULL>
 __global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* pval, int* pidx) {
     constexpr int CW = BITS == 2 ? 1 : 2;
     constexpr int kOffX = 2 * 2 * kTabDw * 4, kOffRed = kOffX + kSkinnyT * kXRow * 2;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[kOffRed + kW * 64 * 16];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kOffRed + 2 * kW * 64 * 16];
     auto& tab = *reinterpret_cast<uint32_t (*)[2][2][kTabDw]>(lds);  // [buffer][row tile][.]
     auto& xs = *reinterpret_cast<uint16_t (*)[kSkinnyT][kXRow]>(lds + kOffX);
-    auto& red = *reinterpret_cast<f32x4 (*)[kW][64]>(lds + kOffRed);
+    auto& red = *reinterpret_cast<f32x4 (*)[2][kW][64]>(lds + kOffRed);  // [buffer][wave][lane]
     float* mval = reinterpret_cast<float*>(lds + kOffRed);       // final merge (reuses red)
     int* midx = reinterpret_cast<int*>(lds + kOffRed + 256 * 4);
 
@@ -368,6 +369,24 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* p
     const int n = l & 15;
     float best = -__builtin_inff();
     int bidx = 0x7fffffff;
+    // epilogue of block pblk from partials buffer pb: thread (row tile, lane holding a token < 8,
+    // reg) sums the 8 slices, scales, and keeps a strictly larger value
+    auto take = [&](int pb, int pblk, uint16_t pesc) {
+        if (tid < 256) {
+            float v = 0.f;
+#pragma unroll
+            for (int s = 0; s < kKS; ++s) v += red[pb][ert * kKS + s][el][eq];
+            v *= h2f(pesc);
+            if (v > best) {
+                best = v;
+                bidx = pblk * 32 + erl;
+            }
+        }
+    };
+    // The partials alternate between two buffers, so one barrier per block suffices: a block's
+    // epilogue runs after the next block's barrier, beside that block's products.
+    int pblk = -1, ppar = 0;
+    uint16_t pesc = 0;
     for (int it = 0; blk < nb; ++it, blk += G) {
         const int par = it & 1;
         tab[par][trt][te * 32 + tc] = tv;
@@ -380,21 +399,16 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* p
             escn = a.sc[(blk + G) * 32 + erw];
             load_codes(blk + G, cn);
         }
-        __syncthreads();  // tables of this block written; red of the last block consumed
+        // this block's tables written; the last block's partials complete, and those of the
+        // block before it (this buffer) consumed
+        __syncthreads();
+        if (pblk >= 0) take(ppar, pblk, pesc);
         const uint32_t lb = (uint32_t(l & 31) << 2) | uint32_t(((par * 2 + rt) * kTabDw) * 4);
         const f32x4 acc = lut_products<BITS, FULL>(cw, nus, u0, g, tb0, lb, xs, n);
-        red[w][l] = acc;
-        __syncthreads();
-        if (tid < 256) {
-            float v = 0.f;
-#pragma unroll
-            for (int s = 0; s < kKS; ++s) v += red[ert * kKS + s][el][eq];
-            v *= h2f(esc);
-            if (v > best) {
-                best = v;
-                bidx = blk * 32 + erl;
-            }
-        }
+        red[par][w][l] = acc;
+        pblk = blk;
+        ppar = par;
+        pesc = esc;
         if (more) {
 #pragma unroll
             for (int k = 0; k < kRunV * 4; ++k) cw[k] = cn[k];
@@ -402,6 +416,8 @@ __global__ void __launch_bounds__(kW * 64, 1) k_lut8_argmax(Lut8Args a, float* p
             esc = escn;
         }
     }
+    __syncthreads();
+    if (pblk >= 0) take(ppar, pblk, pesc);
     // merge the 32 threads of each token (2 row tiles x 4 lane groups x 4 regs): larger value,
     // then lower row
     __syncthreads();

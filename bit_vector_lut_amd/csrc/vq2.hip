@@ -34,15 +34,16 @@ __device__ __forceinline__ uint32_t vq2_addr(uint32_t d, uint32_t sh, uint32_t l
 
 }  // namespace
 
-// Persistent: workgroup b takes the tiles b, b + G, ... of its (matrix, K slice) grid row; x is staged once, and while a tile's
-// lookups run, the next tile's code runs, centroid words and row scales are already in flight
-// (centroid tables double-buffered in LDS).
+// Persistent: workgroup b takes the tiles b, b + G, ... of its (matrix, K slice) grid row; x is
+// staged once, and while a tile's lookups run, the next tile's code runs, centroid words and row
+// scales are already in flight (centroid tables and partial sums double-buffered in LDS, one
+// barrier per tile: a tile's epilogue runs beside the next tile's products).
 __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
     constexpr int kOffX = 2 * kVTab * 4, kOffRed = kOffX + kSkinnyT * kVXRow * 2;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[kOffRed + kVW * 64 * 16];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kOffRed + 2 * kVW * 64 * 16];
     auto& tab = *reinterpret_cast<uint32_t (*)[2][kVTab]>(lds);
     auto& xs = *reinterpret_cast<uint16_t (*)[kSkinnyT][kVXRow]>(lds + kOffX);
-    auto& red = *reinterpret_cast<f32x4 (*)[kVW][64]>(lds + kOffRed);
+    auto& red = *reinterpret_cast<f32x4 (*)[2][kVW][64]>(lds + kOffRed);  // [buffer][wave][lane]
 
     const int tid = threadIdx.x, l = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -109,6 +110,27 @@ __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
     const int n = l & 15, tok = n & 7;
     const uint32_t selE = n < 8 ? 0x0C0C0504u : 0x05040C0Cu;  // low half of the word
     const uint32_t selO = n < 8 ? 0x0C0C0706u : 0x07060C0Cu;  // high half
+    // output (pair ei, column en) of tile pblk from partials buffer pb: register ei mod 4 of lane
+    // 16 (ei / 4) + en; the 16 slices summed in order, scaled in FP32, rounded once
+    auto finish = [&](int pb, int pblk, uint16_t pesc) {
+        if (tid < 256) {
+            const int el = 16 * (ei >> 2) + en, eq = ei & 3;
+            float v = 0.f;
+#pragma unroll
+            for (int s = 0; s < kVW; ++s) v += red[pb][s][el][eq];
+            const int t = en & 7, row = 2 * (pblk * 16 + ei) + (en >> 3);
+            if (t < T) {
+                if (a.out32)
+                    a.out32[size_t(mat) * a.o32_m + size_t(sl) * a.o32_s + size_t(t) * a.o32_t + row] = v;
+                else
+                    a.y[size_t(t) * N + row] = uint16_t(f2h(v * h2f(pesc)));
+            }
+        }
+    };
+    // The partials alternate between two buffers, so one barrier per tile suffices: a tile's
+    // epilogue runs after the next tile's barrier, beside that tile's products.
+    int pblk = -1, ppar = 0;
+    uint16_t pesc = 0;
     for (int it = 0; blk < ntile; ++it, blk += G) {
         const int par = it & 1;
         if (tid < kVTab) tab[par][te * 32 + tc] = tw;
@@ -121,7 +143,10 @@ __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
             escn = load_sc(blk + G);
             load_codes(blk + G, cn);
         }
-        __syncthreads();  // this tile's table (and x) written; red of the last tile consumed
+        // this tile's table (and x) written; the last tile's partials complete, and those of the
+        // tile before it (this buffer) consumed
+        __syncthreads();
+        if (pblk >= 0) finish(ppar, pblk, pesc);
         const uint32_t lb = (uint32_t(l & 31) << 2) | uint32_t(par * kVTab * 4);
         f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -143,23 +168,10 @@ __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
                 }
             }
         }
-        red[w][l] = acc;
-        __syncthreads();
-        // output (pair ei, column en) is register ei mod 4 of lane 16 (ei / 4) + en: sum the 16
-        // slices in order, scale in FP32, round once
-        if (tid < 256) {
-            const int el = 16 * (ei >> 2) + en, eq = ei & 3;
-            float v = 0.f;
-#pragma unroll
-            for (int s = 0; s < kVW; ++s) v += red[s][el][eq];
-            const int t = en & 7, row = 2 * (blk * 16 + ei) + (en >> 3);
-            if (t < T) {
-                if (a.out32)
-                    a.out32[size_t(mat) * a.o32_m + size_t(sl) * a.o32_s + size_t(t) * a.o32_t + row] = v;
-                else
-                    a.y[size_t(t) * N + row] = uint16_t(f2h(v * h2f(esc)));
-            }
-        }
+        red[par][w][l] = acc;
+        pblk = blk;
+        ppar = par;
+        pesc = esc;
         if (more) {
 #pragma unroll
             for (int k = 0; k < kVRunV * 4; ++k) cw[k] = cn[k];
@@ -167,6 +179,8 @@ __global__ void __launch_bounds__(kVW * 64, 1) k_vq2_8(Vq2Args a) {
             esc = escn;
         }
     }
+    __syncthreads();
+    if (pblk >= 0) finish(ppar, pblk, pesc);
 }
 
 namespace {
