@@ -401,7 +401,10 @@ vqmlp_status run_fused(const vqmlp_plan* p, int T, const void* x, void* y, const
     a.part = w.fpart;
     a.spin_limit = 1u << 18;
     a.dyn = 1;
-    const hipError_t e = launch_fused(a, g.tpw, p->cus, st);
+    // one workgroup per CU, or one per streaming item when there are fewer (a small layer): the
+    // others would only start and leave
+    const int grid = std::max(1, std::min(p->cus, g.total - g.n_r));
+    const hipError_t e = launch_fused(a, g.tpw, grid, st);
     if (e != hipSuccess) return hip_fail(e, "fused forward");
     return ok();
 }
@@ -865,7 +868,8 @@ vqmlp_status vqmlp_forward_path(const vqmlp_plan* p, int T, const void* x, void*
         if (trace_on())
             trace("forward H=%d I=%d T=%d: fused kernel (%d tiles per wave, %d workgroups; items: "
                   "%d input rotation, %d gate/up, %d down in %d K slices)",
-                  p->d.H, p->d.I, T, p->fz.tpw, p->cus, p->fz.n_r, p->fz.n_g,
+                  p->d.H, p->d.I, T, p->fz.tpw, std::max(1, std::min(p->cus, p->fz.total - p->fz.n_r)),
+                  p->fz.n_r, p->fz.n_g,
                   p->fz.nsl * p->fz.nqd, p->fz.nsl);
         return run_fused(p, T, x, y, w, st);
     }
