@@ -476,7 +476,7 @@ def main():
                     help="counter run only: known-size copy and read, 2 T=512 forwards")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d "
+        print("bench.py measures one GPU: the library has no multi-GPU path (--gpus %d "
               "requested); run with --gpus 1" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
